@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for the multi-LoRA batched adapter path.
+
+This package is the only code that both the GPU path's tests/bench and the
+CPU oracle's tests consume.  It draws random numbers and lays them out in
+memory; it contains none of the method's arithmetic (no shrink, no expand, no
+sort, no scale).  Every array is a numpy array on the host.
+"""
+
+from .synth import (  # noqa: F401
+    LoraProblem,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    make_config,
+    make_problem,
+    make_integer_problem,
+    CONFIG_NAMES,
+    zipf_probs,
+)
