@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA adapter path on one MI355X.
+
+    python bench.py [--config decode|prefill|hetero|fused|tiny] [--steps K] [--warmup W]
+
+A step is one adapted layer-projection over one batch: shrink + expand for
+every token (BGMV for the decode workload, SGMV from a prebuilt plan for the
+others) or one fused call.  Steps rotate over L independent per-layer
+instances (own adapters, activations and outputs) whose total footprint is at
+least twice the 256 MB last-level cache, so timed calls read HBM as real
+layers do.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s per layer, ms per step, achieved algorithmic
+HBM GB/s and its fraction of the 8 TB/s peak, a roofline object for the
+dominant kernel (HIP events on the launch stream) and the fp64 CPU oracle
+timed on the host cores (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
+MALL_BYTES = 256 << 20
+
+METRIC = "SGMV/BGMV tokens/s per layer + achieved HBM GB/s (% of MI355X peak)"
+CONFIG_OF = {"tiny": 1, "decode": 2, "prefill": 3, "hetero": 4, "fused": 5}
+
+
+def algorithmic_bytes(prob):
+    """Bytes the method must move for one layer: x once, each distinct adapter's
+    A and B once (unpadded), y read + written once (written only when fused),
+    W0 once (fused).  Returned per kernel: (shrink, expand, total)."""
+    es = prob.esize
+    distinct = prob.distinct_adapters()
+    a_bytes = sum(int(prob.ranks[a]) * prob.d_in * es for a in distinct)
+    b_bytes = sum(int(prob.ranks[a]) * prob.d_out * es for a in distinct)
+    x_bytes = prob.T * prob.d_in * es
+    if prob.meta.get("fused"):
+        w_bytes = prob.d_out * prob.d_in * es
+        y_bytes = prob.T * prob.d_out * es
+        total = x_bytes + a_bytes + b_bytes + w_bytes + y_bytes
+        return {"shrink": x_bytes + a_bytes, "fused": total, "total": total}
+    n_adapted = int(np.count_nonzero(prob.ids >= 0))
+    y_bytes = 2 * n_adapted * prob.d_out * es
+    return {"shrink": x_bytes + a_bytes, "expand": b_bytes + y_bytes, "total": x_bytes + a_bytes + b_bytes + y_bytes}
+
+
+def algorithmic_flops(prob):
+    per_tok = [int(prob.ranks[a]) * (prob.d_in + prob.d_out) for a in prob.ids if a >= 0]
+    f = 2 * sum(per_tok)
+    if prob.meta.get("fused"):
+        f += 2 * prob.T * prob.d_in * prob.d_out
+    return f
+
+
+class Instance:
+    """One layer's worth of device-resident inputs."""
+
+    def __init__(self, prob, kind):
+        import torch
+
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        self.prob = prob
+        self.kind = kind
+        self.dt = prob.dtype
+        self.pool = B.DevicePool.from_problem(prob)
+        self.x = B.to_device(prob.x, self.dt)
+        self.y = B.to_device(prob.y_base(), self.dt)
+        self.ids = torch.from_numpy(np.ascontiguousarray(prob.ids, dtype=np.int32)).cuda()
+        self.ldv = B.v_pitch(prob.max_rank)
+        self.v = torch.zeros((max(prob.T, 1), self.ldv), device="cuda")
+        self.plan = None
+        if kind != "bgmv":
+            self.plan = B.Plan(prob.T).build(prob.ids, self.pool).upload()
+        if kind == "fused":
+            self.W0 = B.to_device(prob.W0, self.dt)
+            nbytes = B.lora_workspace_bytes(B.LORA_OP_FUSED, prob.T, prob.d_in, prob.d_out, prob.max_rank)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def shrink(self):
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        if self.kind == "bgmv":
+            B.bgmv_shrink(self.x, self.ids, self.pool, self.v, self.dt)
+        else:
+            B.sgmv_shrink(self.x, self.plan, self.v, self.dt)
+
+    def expand(self):
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        if self.kind == "bgmv":
+            B.bgmv_expand(self.v, self.ids, self.pool, self.y, self.dt)
+        else:
+            B.sgmv_expand(self.v, self.plan, self.y, self.dt)
+
+    def fused(self):
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        B.fused_linear(self.x, self.W0, self.plan, self.y, self.ws, self.dt)
+
+    def step(self):
+        if self.kind == "fused":
+            self.fused()
+        else:
+            self.shrink()
+            self.expand()
+
+
+def rotation_count(bytes_per_instance):
+    n = max(8, math.ceil(2 * MALL_BYTES / max(bytes_per_instance, 1)))
+    return 1 << (n - 1).bit_length()
+
+
+def cpu_baseline(prob, budget_s):
+    """The fp64 oracle as it stands, on the host cores, over whole layers of the
+    same workload (repeated, or a prefix of the tokens when one layer would
+    exceed the budget)."""
+    import copy
+
+    import oracle
+
+    cores = max(1, min(16, os.cpu_count() or 1))
+    oracle.build(force=False)
+    sample = prob
+    # one-token timing probe to size the sample
+    probe = copy.copy(prob)
+    n_probe = min(prob.T, 8)
+    probe.T = n_probe
+    probe.ids = prob.ids[:n_probe]
+    probe.x = prob.x[:n_probe]
+    probe.y_in = None if prob.y_in is None else prob.y_in[:n_probe]
+    t0 = time.perf_counter()
+    oracle.lora_forward(probe, nthreads=1, fused=bool(prob.meta.get("fused")))
+    per_tok_1core = (time.perf_counter() - t0) / n_probe
+    est_layer = per_tok_1core * prob.T / cores
+    if est_layer > budget_s:
+        n = max(cores, int(budget_s / per_tok_1core * cores))
+        n = min(n, prob.T)
+        sample = copy.copy(prob)
+        sample.T = n
+        sample.ids = prob.ids[:n]
+        sample.x = prob.x[:n]
+        sample.y_in = None if prob.y_in is None else prob.y_in[:n]
+        desc = f"first {n} of {prob.T} tokens of one layer"
+    else:
+        desc = None
+    reps, tokens = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.lora_forward(sample, nthreads=cores, fused=bool(prob.meta.get("fused")))
+        reps += 1
+        tokens += sample.T
+        el = time.perf_counter() - t0
+        if el >= budget_s or desc is not None:
+            break
+    if desc is None:
+        desc = f"{reps} full layers of {prob.T} tokens"
+    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{desc} ({el:.1f} s, fp64, OpenMP over tokens)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", choices=sorted(CONFIG_OF), default="decode")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from lora_workloads import CONFIG_NAMES, make_config
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load()
+    k = CONFIG_OF[args.config]
+    kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
+
+    prob0 = make_config(k)
+    ab = algorithmic_bytes(prob0)
+    L = args.rotation or rotation_count(ab["total"])
+    print(f"[bench] {CONFIG_NAMES[k]}: T={prob0.T} d_in={prob0.d_in} d_out={prob0.d_out} rotation={L} "
+          f"bytes/layer={ab['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
+    insts = [Instance(prob0, kind)]
+    for i in range(1, L):
+        insts.append(Instance(make_config(k, seed=1000 * k + i), kind))
+    # every instance has its own distinct-adapter count; average the algorithmic bytes
+    ab_all = [algorithmic_bytes(inst.prob) for inst in insts]
+    bytes_step = float(np.mean([a["total"] for a in ab_all]))
+    flops_step = float(np.mean([algorithmic_flops(inst.prob) for inst in insts]))
+    T = prob0.T
+
+    K = args.steps if args.steps is not None else 20 * L
+    W = args.warmup if args.warmup is not None else 10 * L
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        insts[i % L].step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        insts[i % L].step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    tokens_per_s = T / (ms_step * 1e-3)
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+
+    # ---- per-kernel durations: event pairs around each launch, same stream
+    names = ["fused"] if kind == "fused" else ["shrink", "expand"]
+    K2 = max(L, min(K, 20 * L))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K2)]
+    for i in range(K2):
+        inst = insts[i % L]
+        e = evs[i]
+        e[0].record(stream)
+        if kind == "fused":
+            inst.fused()
+            e[1].record(stream)
+        else:
+            inst.shrink()
+            e[1].record(stream)
+            inst.expand()
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    per_kernel_us = {}
+    for j, n in enumerate(names):
+        per_kernel_us[n] = float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K2)])) * 1e3
+    dominant = max(names, key=lambda n: per_kernel_us[n])
+    dom_bytes = float(np.mean([a[dominant] for a in ab_all]))
+    dom_us = per_kernel_us[dominant]
+    if kind == "fused":
+        achieved = flops_step / (dom_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof["kernel"] = {"shrink": "bgmv_shrink" if kind == "bgmv" else "sgmv_shrink",
+                      "expand": "bgmv_expand" if kind == "bgmv" else "sgmv_expand",
+                      "fused": "fused_linear"}[dominant]
+    roof["algorithmic_bytes_per_launch"] = round(dom_bytes)
+    roof["avg_launch_us"] = round(dom_us, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob0, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob0.dtype,
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[k], "T": T, "d_in": prob0.d_in, "d_out": prob0.d_out,
+                   "ranks": sorted(set(int(r) for r in prob0.ranks)), "pool_adapters": prob0.n_adapters,
+                   "distinct_adapters": int(len(prob0.distinct_adapters())), "rotated_instances": L,
+                   "path": kind},
+        "achieved_GBps": round(gbps, 1),
+        "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": round(bytes_step),
+        "algorithmic_flops_per_step": round(flops_step),
+        "per_kernel_us": {n: round(v, 3) for n, v in per_kernel_us.items()},
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+/*
+ * lora_mi355x.h -- C ABI of the multi-LoRA batched adapter path on MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operation.  For every token t of a batch, with adapter i = a(t) chosen
+ * per token from a pool of adapters resident in device memory:
+ *
+ *     y[t] += (alpha_i / r_i) * (x[t] A_i) B_i
+ *
+ * "Multi-LoRA Serving in Production: Comparing S-LoRA, Punica, LoRAX, and
+ * vLLM ..." (llms.blog), section "Mathematical Formulation and the Batching
+ * Challenge" gives the layer equation (base x W0 plus (alpha/r)(x A) B) and,
+ * in section "Kernel Architectures: SGMV, MBGMV, and Grouped GEMMs", the two
+ * stages: a shrink x A_i (d_in -> r_i) over contiguous segments of tokens that
+ * share an adapter, found "via pointer array lookups", then an expand
+ * (r_i -> d_out) that scales and accumulates into the base output.  Ranks may
+ * differ between adapters and are never padded (same page, "S-LoRA: MBGMV and
+ * MBGMM Kernels": r in [1, 256]).  "Multi-LoRA serving: the single translator
+ * with a thousand glossaries" (blog.lo0.es), section "SGMV: the kernel that
+ * holds it all up", defines the per-token adapter a(t).
+ *
+ * Storage (row-major everywhere; element type per lora_dtype):
+ *   x   [T, ldx]          activations, row pitch ldx elements
+ *   A_i [r_i, d_in]       stored contiguously, row pitch d_in (the pages' A^T)
+ *   B_i [d_out, r_i]      stored contiguously, row pitch r_i  (the pages' B^T)
+ *   W0  [d_out, d_in]     base weight of the fused entry, row pitch d_in
+ *   y   [T, ldy]          output, row pitch ldy elements
+ *   v   [rows, ldv] fp32  the shrink result (the pages' h), row pitch ldv
+ * Accumulation is fp32; bf16 outputs are rounded to nearest-even once.
+ *
+ * Ownership and ordering.  The caller owns every buffer (activations, pool,
+ * plans, v, workspace).  The library never allocates, frees or synchronises;
+ * every GPU call is enqueued on the caller's stream (a hipStream_t passed as
+ * void*, NULL = the null stream) and returns before the work runs.  Buffers
+ * must stay alive until the stream has passed the call.  x, v and y must not
+ * overlap.  The library keeps no mutable global state except a thread-local
+ * copy of the last error message, so it may be used from several threads.
+ *
+ * Errors.  Every call returns LORA_OK (0) or a negative lora_status, after
+ * checking every argument the host can see and before enqueuing anything;
+ * lora_last_error() then describes the failure.  A call with T = 0 (or no
+ * segments) is a successful no-op.  Device-resident tables (the BGMV id and
+ * pool tables) cannot be read by the host: their contents are a precondition
+ * (ids in [-1, n_adapters), ranks in [1, max_rank]); a BGMV kernel treats a
+ * token whose id or rank breaks it as having no adapter.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_ARG = -1,        /* null pointer, negative size, bad op code */
+    LORA_ERR_RANK = -2,       /* a rank outside [1, 256], or ldv < max rank */
+    LORA_ERR_ADAPTER_ID = -3, /* an id < -1 or >= n_adapters (host-visible ids) */
+    LORA_ERR_ALIGN = -4,      /* pointer not 16-byte aligned, or row pitch not a multiple of 16 bytes */
+    LORA_ERR_DTYPE = -5,      /* unknown lora_dtype */
+    LORA_ERR_WORKSPACE = -6,  /* workspace or plan buffer smaller than required */
+    LORA_ERR_HIP = -7,        /* a HIP runtime call or kernel launch failed */
+    LORA_ERR_PLAN = -8        /* plan buffer does not hold a valid plan */
+} lora_status;
+
+typedef enum lora_dtype {
+    LORA_F32 = 0,  /* x, A, B, W0, y in fp32 */
+    LORA_BF16 = 1  /* x, A, B, W0, y in bf16 (stored as 16-bit patterns) */
+} lora_dtype;
+
+#define LORA_MAX_RANK 256     /* largest adapter rank accepted */
+#define LORA_PLAN_ROW_BLOCK 16 /* rows per block in a plan's block list */
+
+/* ------------------------------------------------------------------ plans
+ * A plan is the grouping of one batch's tokens into segments: tokens sorted by
+ * adapter id (ascending), the original order kept inside a segment, tokens with
+ * id -1 left out.  The pages fix the grouping but not its order; the ascending
+ * stable order makes the plan unique.  ("Multi-LoRA Serving in Production ...",
+ * section "Punica and Segmented Gather Matrix-Vector Multiplication (SGMV)":
+ * the batch is split into contiguous segments whose tokens reference one
+ * adapter id; the adapters are reached through a pointer array.)
+ *
+ * A plan lives in one contiguous buffer with the same layout on the host and
+ * the device, so a single copy moves it:
+ *
+ *   [lora_plan_header][lora_seg_desc x S][int32 blk_seg x n_blocks][int32 perm x T']
+ *
+ * perm[p] is the original token index at sorted position p.  Segment s covers
+ * sorted positions [start, start + len).  The block list cuts every segment
+ * into blocks of LORA_PLAN_ROW_BLOCK rows (the last one ragged); blk_seg[b]
+ * is the segment of block b and segment s owns blocks [blk0, blk0 + ceil(len/16)).
+ */
+typedef struct lora_seg_desc {
+    uint64_t A;      /* device address of A_i, [rank, d_in] */
+    uint64_t B;      /* device address of B_i, [d_out, rank] */
+    int32_t start;   /* first sorted position */
+    int32_t len;     /* number of tokens (>= 1) */
+    int32_t rank;    /* r_i in [1, 256] */
+    int32_t adapter; /* adapter id i */
+    float scale;     /* alpha_i / r_i, fp32 */
+    int32_t blk0;    /* first block of this segment */
+} lora_seg_desc;
+
+typedef struct lora_plan_header {
+    uint32_t magic;       /* LORA_PLAN_MAGIC when valid */
+    int32_t num_tokens;   /* T of the batch */
+    int32_t num_sorted;   /* T' = tokens that have an adapter */
+    int32_t num_segments; /* S */
+    int32_t num_blocks;   /* sum over segments of ceil(len / 16) */
+    int32_t max_rank;     /* largest rank among the segments (0 if S = 0) */
+    int32_t max_len;      /* longest segment */
+    int32_t capacity;     /* T the buffer was sized for */
+    uint64_t seg_offset;  /* byte offset of the lora_seg_desc array */
+    uint64_t blk_offset;  /* byte offset of blk_seg */
+    uint64_t perm_offset; /* byte offset of perm */
+    uint64_t bytes_used;  /* bytes from the start of the buffer that hold the plan */
+} lora_plan_header;
+
+#define LORA_PLAN_MAGIC 0x4C6F5241u
+
+/* Bytes a plan buffer needs for a batch of up to `capacity` tokens (>= 0). */
+size_t lora_plan_bytes(int32_t capacity);
+
+/* Build the plan of one batch on the host (no GPU call).  O(T + n_adapters).
+ *   ids        [T] host, adapter per token, -1 = none
+ *   pool_A/B   [n_adapters] host, device addresses of A_i / B_i (16-byte aligned)
+ *   pool_rank  [n_adapters] host, r_i in [1, 256]
+ *   pool_alpha [n_adapters] host, alpha_i; the plan stores alpha_i / r_i in fp32
+ *   plan       host buffer of plan_bytes >= lora_plan_bytes(T), 8-byte aligned
+ * Errors: LORA_ERR_ARG, LORA_ERR_ADAPTER_ID, LORA_ERR_RANK, LORA_ERR_ALIGN,
+ * LORA_ERR_WORKSPACE (buffer too small). */
+int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters,
+                    const uint64_t *pool_A, const uint64_t *pool_B,
+                    const int32_t *pool_rank, const float *pool_alpha,
+                    void *plan, size_t plan_bytes);
+
+/* Enqueue one host-to-device copy of header.bytes_used bytes of a built plan
+ * (plan_host should be pinned memory; it must stay unchanged until the copy
+ * has run).  plan_dev must hold at least that many bytes.
+ * Errors: LORA_ERR_ARG, LORA_ERR_PLAN, LORA_ERR_HIP. */
+int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_bytes, void *stream);
+
+/* ------------------------------------------------------------------ SGMV
+ * Segmented shrink, the pages' "Shrink Stage" ("Multi-LoRA Serving in
+ * Production ...", section "Punica and Segmented Gather Matrix-Vector
+ * Multiplication (SGMV)"):
+ *     v[p, j] = sum_k x[perm[p], k] * A_s[j, k]    for j < r_s,
+ * for every sorted position p of segment s.  v rows are in sorted order; the
+ * columns j >= r_s of a row are left untouched.  Overwrites v.
+ *   plan_host / plan_dev  the same plan, on the host (read for the launch
+ *                         geometry) and on the device (read by the kernels)
+ *   v                     device fp32 [header.num_sorted, ldv], ldv >= max_rank,
+ *                         ldv a multiple of 4
+ * Errors: LORA_ERR_ARG, LORA_ERR_DTYPE, LORA_ERR_RANK, LORA_ERR_ALIGN,
+ * LORA_ERR_PLAN, LORA_ERR_HIP. */
+int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
+                     const void *plan_host, const void *plan_dev,
+                     float *v, int64_t ldv, void *ws, size_t ws_bytes);
+
+/* Segmented expand, the pages' "Expand Stage" (same section): scale and
+ * accumulate into the base output,
+ *     y[perm[p], n] += scale_s * sum_{j < r_s} v[p, j] * B_s[n, j]   for n < d_out.
+ * Rows of tokens without an adapter are not touched.
+ * Errors: as lora_sgmv_shrink. */
+int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
+                     const void *plan_host, const void *plan_dev,
+                     void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------ BGMV
+ * Decode-shaped gather (one row per request, "Multi-LoRA Serving in
+ * Production ...", section "S-LoRA: MBGMV and MBGMM Kernels": single-token
+ * vectors, heterogeneous ranks, no padding).  No plan: the adapter of token t
+ * is read from ids_dev[t] on the device, its A/B addresses and rank from the
+ * device pool tables.  v rows are in token order.
+ *   ids_dev        [T] device int32, -1 = none
+ *   pool_A_dev     [n_adapters] device uint64 addresses
+ *   pool_rank_dev  [n_adapters] device int32
+ *   max_rank       an upper bound of every rank used (host), in [1, 256]
+ * Shrink: v[t, j] = sum_k x[t, k] A_{ids[t]}[j, k]; rows of tokens without an
+ * adapter are left untouched.  T must be <= 65536.
+ * Errors: LORA_ERR_ARG, LORA_ERR_DTYPE, LORA_ERR_RANK, LORA_ERR_ALIGN, LORA_ERR_HIP. */
+int lora_bgmv_shrink(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+                     const int32_t *ids_dev, const uint64_t *pool_A_dev,
+                     const int32_t *pool_rank_dev, int32_t n_adapters, int32_t max_rank,
+                     float *v, int64_t ldv, void *ws, size_t ws_bytes);
+
+/* Expand: y[t, n] += (alpha_i / r_i) * sum_j v[t, j] B_i[n, j], i = ids[t]
+ * (alpha_i / r_i formed in fp32 on the device).
+ *   pool_B_dev [n_adapters] device uint64; pool_alpha_dev [n_adapters] device fp32. */
+int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t ldv,
+                     const int32_t *ids_dev, const uint64_t *pool_B_dev,
+                     const int32_t *pool_rank_dev, const float *pool_alpha_dev,
+                     int32_t n_adapters, int32_t max_rank,
+                     void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------ fused layer
+ * The whole adapted layer: the shared base product once for every token plus
+ * each token's correction, y = x W0 + scale_s (x A_s) B_s, overwriting y
+ * ("Multi-LoRA Serving" (fp-ai-systems.pages.dev), section "Serving it: batch
+ * across adapters": one shared matmul for all requests plus a per-request
+ * low-rank correction; "Multi-LoRA Serving in Production ...", layer equation).
+ * Tokens without an adapter get x W0 only.  W0 is [d_out, d_in], bf16 only.
+ * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_FUSED, T, d_in, d_out, max_rank).
+ * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */
+int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
+                      const void *W0, int32_t d_out,
+                      const void *plan_host, const void *plan_dev,
+                      void *y, int64_t ldy, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------ helpers */
+enum {
+    LORA_OP_SGMV_SHRINK = 0,
+    LORA_OP_SGMV_EXPAND = 1,
+    LORA_OP_BGMV_SHRINK = 2,
+    LORA_OP_BGMV_EXPAND = 3,
+    LORA_OP_FUSED = 4
+};
+
+/* Workspace bytes an op needs (0 = none; ws may then be NULL); -1 cast to
+ * size_t on a bad op code. */
+size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank);
+
+/* Adapter parameters of one adapted d_in -> d_out projection at rank r:
+ * r (d_in + d_out) ("Multi-LoRA Serving: Many Adapters on One GPU"
+ * (gpusmith.com), section "LoRA recap and why adapters are small").
+ * Returns -1 for a negative argument. */
+int64_t lora_adapter_numel(int32_t r, int32_t d_in, int32_t d_out);
+
+/* Static text for a status code; never NULL. */
+const char *lora_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *lora_last_error(void);
+
+/* Library version string. */
+const char *lora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

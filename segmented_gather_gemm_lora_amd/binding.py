@@ -1,0 +1,333 @@
+"""ctypes binding of liblora_mi355x.so.
+
+Argument marshalling only: every step of the adapter path (plan building,
+shrink, expand, the fused layer) runs inside the library.  PyTorch is used for
+device memory, pinned host memory and streams.  If the library has not been
+built, every entry point raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+LORA_F32 = 0
+LORA_BF16 = 1
+DTYPES = {"f32": LORA_F32, "bf16": LORA_BF16}
+
+LORA_OP_SGMV_SHRINK = 0
+LORA_OP_SGMV_EXPAND = 1
+LORA_OP_BGMV_SHRINK = 2
+LORA_OP_BGMV_EXPAND = 3
+LORA_OP_FUSED = 4
+
+STATUS = {
+    0: "LORA_OK", -1: "LORA_ERR_ARG", -2: "LORA_ERR_RANK", -3: "LORA_ERR_ADAPTER_ID",
+    -4: "LORA_ERR_ALIGN", -5: "LORA_ERR_DTYPE", -6: "LORA_ERR_WORKSPACE", -7: "LORA_ERR_HIP",
+    -8: "LORA_ERR_PLAN",
+}
+
+# Every symbol the public header declares.
+EXPORTS = [
+    "lora_plan_bytes", "lora_build_plan", "lora_plan_upload", "lora_sgmv_shrink",
+    "lora_sgmv_expand", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_fused_linear",
+    "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
+    "lora_version",
+]
+
+PLAN_HEADER_BYTES = 64
+PLAN_MAGIC = 0x4C6F5241
+ROW_BLOCK = 16
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_i32, _i64, _u64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t
+_LIB = None
+_LOCK = threading.Lock()
+
+_SIGS = {
+    "lora_plan_bytes": (_sz, [_i32]),
+    "lora_build_plan": (ctypes.c_int, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "lora_plan_upload": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "lora_sgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _sz]),
+    "lora_sgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz]),
+    "lora_bgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32,
+                                        _vp, _i64, _vp, _sz]),
+    "lora_bgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
+                                        _vp, _i64, _i32, _vp, _sz]),
+    "lora_fused_linear": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _i64,
+                                         _vp, _sz]),
+    "lora_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32, _i32]),
+    "lora_adapter_numel": (_i64, [_i32, _i32, _i32]),
+    "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lora_last_error": (ctypes.c_char_p, []),
+    "lora_version": (ctypes.c_char_p, []),
+}
+
+
+def lib_path() -> str:
+    return _build.lib_path()
+
+
+def load():
+    """Load the built library (raises if it is missing)."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m segmented_gather_gemm_lora_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+        return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LoraError(status, where, load().lora_last_error().decode())
+
+
+def last_error() -> str:
+    return load().lora_last_error().decode()
+
+
+# ------------------------------------------------------------------ raw C calls (same names)
+def lora_plan_bytes(capacity: int) -> int:
+    return int(load().lora_plan_bytes(capacity))
+
+
+def lora_workspace_bytes(op: int, T: int, d_in: int, d_out: int, max_rank: int) -> int:
+    return int(load().lora_workspace_bytes(op, T, d_in, d_out, max_rank))
+
+
+def lora_adapter_numel(r: int, d_in: int, d_out: int) -> int:
+    return int(load().lora_adapter_numel(r, d_in, d_out))
+
+
+def lora_version() -> str:
+    return load().lora_version().decode()
+
+
+def lora_status_string(status: int) -> str:
+    return load().lora_status_string(status).decode()
+
+
+def lora_build_plan(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr, pool_alpha_ptr,
+                    plan_ptr, plan_bytes) -> int:
+    return int(load().lora_build_plan(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr,
+                                      pool_alpha_ptr, plan_ptr, plan_bytes))
+
+
+def lora_plan_upload(plan_host_ptr, plan_dev_ptr, plan_dev_bytes, stream) -> int:
+    return int(load().lora_plan_upload(plan_host_ptr, plan_dev_ptr, plan_dev_bytes, stream))
+
+
+def lora_sgmv_shrink(stream, dtype, x, ldx, d_in, plan_host, plan_dev, v, ldv, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv_shrink(stream, dtype, x, ldx, d_in, plan_host, plan_dev, v, ldv, ws, ws_bytes))
+
+
+def lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes))
+
+
+def lora_bgmv_shrink(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_rank, n_adapters, max_rank, v, ldv,
+                     ws, ws_bytes) -> int:
+    return int(load().lora_bgmv_shrink(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_rank, n_adapters,
+                                       max_rank, v, ldv, ws, ws_bytes))
+
+
+def lora_bgmv_expand(stream, dtype, T, v, ldv, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank,
+                     y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_bgmv_expand(stream, dtype, T, v, ldv, ids, pool_B, pool_rank, pool_alpha,
+                                       n_adapters, max_rank, y, ldy, d_out, ws, ws_bytes))
+
+
+def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy, ws, ws_bytes) -> int:
+    return int(load().lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy,
+                                        ws, ws_bytes))
+
+
+# ------------------------------------------------------------------ torch-facing helpers
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def torch_dtype(dtype: str):
+    torch = _torch()
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    """Host array (bf16 bit patterns as uint16, or float32) -> device tensor."""
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host_bits(t, dtype: str) -> np.ndarray:
+    """Device tensor -> host array in the stored representation."""
+    torch = _torch()
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy().astype(np.float32, copy=False)
+
+
+@dataclass
+class DevicePool:
+    """Adapters resident in device memory, with their pointer and rank tables."""
+
+    storage: object  # device tensor holding every A_i and B_i (unpadded)
+    n_adapters: int
+    dtype: str
+    d_in: int
+    d_out: int
+    addr_A: np.ndarray  # uint64 host copies of the tables
+    addr_B: np.ndarray
+    rank: np.ndarray  # int32
+    alpha: np.ndarray  # float32
+    addr_A_dev: object = None  # device tables (for BGMV)
+    addr_B_dev: object = None
+    rank_dev: object = None
+    alpha_dev: object = None
+
+    @property
+    def max_rank(self) -> int:
+        return int(self.rank.max()) if self.rank.size else 0
+
+    @classmethod
+    def from_problem(cls, prob, device="cuda") -> "DevicePool":
+        torch = _torch()
+        storage = to_device(prob.pool, prob.dtype, device)
+        base = storage.data_ptr()
+        es = prob.esize
+        addr_A = (base + prob.a_off.astype(np.uint64) * np.uint64(es)).astype(np.uint64)
+        addr_B = (base + prob.b_off.astype(np.uint64) * np.uint64(es)).astype(np.uint64)
+        rank = np.ascontiguousarray(prob.ranks, dtype=np.int32)
+        alpha = np.ascontiguousarray(prob.alphas, dtype=np.float32)
+        p = cls(storage=storage, n_adapters=prob.n_adapters, dtype=prob.dtype, d_in=prob.d_in, d_out=prob.d_out,
+                addr_A=addr_A, addr_B=addr_B, rank=rank, alpha=alpha)
+        p.addr_A_dev = torch.from_numpy(addr_A.view(np.int64)).to(device)
+        p.addr_B_dev = torch.from_numpy(addr_B.view(np.int64)).to(device)
+        p.rank_dev = torch.from_numpy(rank).to(device)
+        p.alpha_dev = torch.from_numpy(alpha).to(device)
+        return p
+
+
+class Plan:
+    """A batch's segment plan: pinned host copy + device copy (one upload)."""
+
+    def __init__(self, capacity: int, device="cuda"):
+        torch = _torch()
+        self.capacity = int(capacity)
+        self.nbytes = lora_plan_bytes(self.capacity)
+        self.host = torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True)
+        self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+    def build(self, ids: np.ndarray, pool: DevicePool):
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        if ids.shape[0] > self.capacity:
+            raise ValueError("batch larger than the plan capacity")
+        st = lora_build_plan(ids.shape[0], ids.ctypes.data, pool.n_adapters, pool.addr_A.ctypes.data,
+                             pool.addr_B.ctypes.data, pool.rank.ctypes.data, pool.alpha.ctypes.data,
+                             self.host.data_ptr(), self.nbytes)
+        _check(st, "lora_build_plan")
+        return self
+
+    def upload(self, stream=None):
+        _check(lora_plan_upload(self.host.data_ptr(), self.dev.data_ptr(), self.nbytes, _stream_handle(stream)),
+               "lora_plan_upload")
+        return self
+
+    def header(self) -> dict:
+        h = self.host[:PLAN_HEADER_BYTES].numpy()
+        i32 = h[:32].view(np.int32)
+        u64 = h[32:64].view(np.uint64)
+        return {"magic": int(h[:4].view(np.uint32)[0]), "num_tokens": int(i32[1]), "num_sorted": int(i32[2]),
+                "num_segments": int(i32[3]), "num_blocks": int(i32[4]), "max_rank": int(i32[5]),
+                "max_len": int(i32[6]), "capacity": int(i32[7]), "seg_offset": int(u64[0]),
+                "blk_offset": int(u64[1]), "perm_offset": int(u64[2]), "bytes_used": int(u64[3])}
+
+    def arrays(self) -> dict:
+        """Host copies of the plan's arrays (for tests)."""
+        h = self.header()
+        buf = self.host.numpy()
+        S, nb, Tp = h["num_segments"], h["num_blocks"], h["num_sorted"]
+        desc = np.frombuffer(buf[h["seg_offset"]: h["seg_offset"] + 40 * S].tobytes(), dtype=np.dtype([
+            ("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
+            ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")]))
+        blk = buf[h["blk_offset"]: h["blk_offset"] + 4 * nb].view(np.int32).copy()
+        perm = buf[h["perm_offset"]: h["perm_offset"] + 4 * Tp].view(np.int32).copy()
+        return {"desc": desc, "blk_seg": blk, "perm": perm}
+
+
+def sgmv_shrink(x, plan: Plan, v, dtype: str, stream=None):
+    d_in = x.shape[1]
+    _check(lora_sgmv_shrink(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), d_in,
+                            plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(v), v.stride(0), None, 0),
+           "lora_sgmv_shrink")
+
+
+def sgmv_expand(v, plan: Plan, y, dtype: str, stream=None):
+    _check(lora_sgmv_expand(_stream_handle(stream), DTYPES[dtype], _ptr(v), v.stride(0), plan.host.data_ptr(),
+                            plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1], None, 0),
+           "lora_sgmv_expand")
+
+
+def bgmv_shrink(x, ids_dev, pool: DevicePool, v, dtype: str, max_rank: Optional[int] = None, stream=None):
+    _check(lora_bgmv_shrink(_stream_handle(stream), DTYPES[dtype], x.shape[0], _ptr(x), x.stride(0), x.shape[1],
+                            _ptr(ids_dev), _ptr(pool.addr_A_dev), _ptr(pool.rank_dev), pool.n_adapters,
+                            max_rank or pool.max_rank, _ptr(v), v.stride(0), None, 0),
+           "lora_bgmv_shrink")
+
+
+def bgmv_expand(v, ids_dev, pool: DevicePool, y, dtype: str, max_rank: Optional[int] = None, stream=None):
+    _check(lora_bgmv_expand(_stream_handle(stream), DTYPES[dtype], y.shape[0], _ptr(v), v.stride(0), _ptr(ids_dev),
+                            _ptr(pool.addr_B_dev), _ptr(pool.rank_dev), _ptr(pool.alpha_dev), pool.n_adapters,
+                            max_rank or pool.max_rank, _ptr(y), y.stride(0), y.shape[1], None, 0),
+           "lora_bgmv_expand")
+
+
+def fused_linear(x, W0, plan: Plan, y, ws, dtype: str = "bf16", stream=None):
+    _check(lora_fused_linear(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1], _ptr(W0),
+                             W0.shape[0], plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(y), y.stride(0),
+                             _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_fused_linear")
+
+
+def v_pitch(max_rank: int) -> int:
+    """Row pitch (fp32 elements) for v: max rank rounded up to a multiple of 4."""
+    return max(4, (int(max_rank) + 3) // 4 * 4)

@@ -1,0 +1,390 @@
+// C ABI entry points: argument checks, the host-side plan builder, dispatch to
+// the kernel launchers.  Nothing here touches device memory except through
+// hipMemcpyAsync (plan upload) and kernel launches on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+namespace lora {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+static size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
+
+static int esize_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+
+static bool elem_aligned(const void *p, int es)
+{
+    return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(es)) == 0;
+}
+
+// Validates a host plan buffer and returns its header.
+static int check_plan(const void *plan_host, const lora_plan_header **out)
+{
+    if (!plan_host) return fail(LORA_ERR_ARG, "plan_host is NULL");
+    if (reinterpret_cast<uintptr_t>(plan_host) & 7u)
+        return fail(LORA_ERR_ALIGN, "plan_host is not 8-byte aligned");
+    const auto *h = static_cast<const lora_plan_header *>(plan_host);
+    if (h->magic != LORA_PLAN_MAGIC) return fail(LORA_ERR_PLAN, "plan buffer holds no built plan");
+    if (h->num_segments < 0 || h->num_sorted < 0 || h->num_blocks < 0 ||
+        h->num_sorted > h->num_tokens || h->max_rank < 0 || h->max_rank > LORA_MAX_RANK)
+        return fail(LORA_ERR_PLAN, "plan header is inconsistent");
+    *out = h;
+    return LORA_OK;
+}
+
+static int check_dtype(int dtype)
+{
+    if (dtype != LORA_F32 && dtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "unknown dtype %d", dtype);
+    return LORA_OK;
+}
+
+static int check_v(const float *v, int64_t ldv, int32_t max_rank)
+{
+    if (!v) return fail(LORA_ERR_ARG, "v is NULL");
+    if (!aligned16(v)) return fail(LORA_ERR_ALIGN, "v is not 16-byte aligned");
+    if (ldv < max_rank || ldv < 1) return fail(LORA_ERR_RANK, "ldv %lld < max rank %d", (long long)ldv, max_rank);
+    if (ldv % 4) return fail(LORA_ERR_ALIGN, "ldv %lld is not a multiple of 4", (long long)ldv);
+    return LORA_OK;
+}
+
+// Shared checks of x / d_in for both shrink flavours; fills ShrinkArgs.
+static int make_shrink_args(int dtype, const void *x, int64_t ldx, int32_t d_in, float *v, int64_t ldv,
+                            int32_t max_rank, ShrinkArgs *sa)
+{
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (!x) return fail(LORA_ERR_ARG, "x is NULL");
+    if (d_in < 1) return fail(LORA_ERR_ARG, "d_in %d < 1", d_in);
+    if (ldx < d_in) return fail(LORA_ERR_ARG, "ldx %lld < d_in %d", (long long)ldx, d_in);
+    const int es = esize_of(dtype);
+    if (!elem_aligned(x, es)) return fail(LORA_ERR_ALIGN, "x is not aligned to its element size");
+    if ((st = check_v(v, ldv, max_rank))) return st;
+    sa->dtype = dtype;
+    sa->x = x;
+    sa->ldx = ldx;
+    sa->d_in = d_in;
+    sa->v = v;
+    sa->ldv = ldv;
+    // 16-byte row loads need aligned x rows and A rows (A_i row pitch = d_in).
+    sa->vec = aligned16(x) && ((ldx * es) % 16 == 0) && ((int64_t(d_in) * es) % 16 == 0);
+    return LORA_OK;
+}
+
+static int make_expand_args(int dtype, const float *v, int64_t ldv, int32_t max_rank, void *y, int64_t ldy,
+                            int32_t d_out, bool ranks_vec, ExpandArgs *ea)
+{
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (!y) return fail(LORA_ERR_ARG, "y is NULL");
+    if (d_out < 1) return fail(LORA_ERR_ARG, "d_out %d < 1", d_out);
+    if (ldy < d_out) return fail(LORA_ERR_ARG, "ldy %lld < d_out %d", (long long)ldy, d_out);
+    const int es = esize_of(dtype);
+    if (!elem_aligned(y, es)) return fail(LORA_ERR_ALIGN, "y is not aligned to its element size");
+    if ((st = check_v(v, ldv, max_rank))) return st;
+    ea->dtype = dtype;
+    ea->v = v;
+    ea->ldv = ldv;
+    ea->y = y;
+    ea->ldy = ldy;
+    ea->d_out = d_out;
+    ea->vec_b = ranks_vec;
+    ea->vec_y = aligned16(y) && ((ldy * es) % 16 == 0);
+    return LORA_OK;
+}
+
+} // namespace lora
+
+using namespace lora;
+
+extern "C" {
+
+const char *lora_version(void) { return "lora_mi355x 0.1.0 (gfx950)"; }
+
+const char *lora_last_error(void) { return g_last_error; }
+
+const char *lora_status_string(int status)
+{
+    switch (status) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_ARG: return "LORA_ERR_ARG";
+    case LORA_ERR_RANK: return "LORA_ERR_RANK";
+    case LORA_ERR_ADAPTER_ID: return "LORA_ERR_ADAPTER_ID";
+    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN";
+    case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+    case LORA_ERR_PLAN: return "LORA_ERR_PLAN";
+    default: return "LORA_ERR_UNKNOWN";
+    }
+}
+
+int64_t lora_adapter_numel(int32_t r, int32_t d_in, int32_t d_out)
+{
+    if (r < 0 || d_in < 0 || d_out < 0) return -1;
+    return int64_t(r) * (int64_t(d_in) + int64_t(d_out));
+}
+
+size_t lora_plan_bytes(int32_t capacity)
+{
+    if (capacity < 0) capacity = 0;
+    const size_t c = size_t(capacity);
+    // header, descriptors (S <= T), block list (blocks <= T'), perm (T' <= T)
+    return sizeof(lora_plan_header) + sizeof(lora_seg_desc) * c + 16 + 4 * c + 16 + 4 * c + 16;
+}
+
+size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank)
+{
+    (void)d_in;
+    (void)d_out;
+    switch (op) {
+    case LORA_OP_SGMV_SHRINK:
+    case LORA_OP_SGMV_EXPAND:
+    case LORA_OP_BGMV_SHRINK:
+    case LORA_OP_BGMV_EXPAND: return 0;
+    case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, max_rank < 1 ? 1 : max_rank);
+    default: return size_t(-1);
+    }
+}
+
+int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uint64_t *pool_A,
+                    const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha, void *plan,
+                    size_t plan_bytes)
+{
+    clear_error();
+    if (T < 0) return fail(LORA_ERR_ARG, "T %d < 0", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (!plan) return fail(LORA_ERR_ARG, "plan is NULL");
+    if (reinterpret_cast<uintptr_t>(plan) & 7u) return fail(LORA_ERR_ALIGN, "plan is not 8-byte aligned");
+    if (plan_bytes < lora_plan_bytes(T))
+        return fail(LORA_ERR_WORKSPACE, "plan buffer %zu B < %zu B needed", plan_bytes, lora_plan_bytes(T));
+    if (T > 0 && !ids) return fail(LORA_ERR_ARG, "ids is NULL");
+
+    // Count tokens per adapter; reject ids outside [-1, n_adapters).
+    static thread_local std::vector<int32_t> count;
+    count.assign(size_t(n_adapters), 0);
+    int32_t sorted = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        const int32_t a = ids[t];
+        if (a < -1 || a >= n_adapters)
+            return fail(LORA_ERR_ADAPTER_ID, "ids[%d] = %d outside [-1, %d)", t, a, n_adapters);
+        if (a >= 0) {
+            ++count[size_t(a)];
+            ++sorted;
+        }
+    }
+    if (sorted > 0 && (!pool_A || !pool_B || !pool_rank || !pool_alpha))
+        return fail(LORA_ERR_ARG, "pool tables are NULL");
+
+    // Segments in ascending adapter id; check the adapters actually used.
+    int32_t S = 0, nblk = 0, max_rank = 0, max_len = 0;
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        if (!count[size_t(a)]) continue;
+        const int32_t r = pool_rank[a];
+        if (r < 1 || r > LORA_MAX_RANK) return fail(LORA_ERR_RANK, "adapter %d has rank %d outside [1, 256]", a, r);
+        if (!pool_A[a] || !pool_B[a]) return fail(LORA_ERR_ARG, "adapter %d has a NULL A or B address", a);
+        if ((pool_A[a] & 15u) || (pool_B[a] & 15u))
+            return fail(LORA_ERR_ALIGN, "adapter %d: A or B address is not 16-byte aligned", a);
+        ++S;
+        nblk += (count[size_t(a)] + LORA_PLAN_ROW_BLOCK - 1) / LORA_PLAN_ROW_BLOCK;
+        if (r > max_rank) max_rank = r;
+        if (count[size_t(a)] > max_len) max_len = count[size_t(a)];
+    }
+
+    char *base = static_cast<char *>(plan);
+    auto *h = reinterpret_cast<lora_plan_header *>(base);
+    std::memset(h, 0, sizeof *h);
+    h->num_tokens = T;
+    h->num_sorted = sorted;
+    h->num_segments = S;
+    h->num_blocks = nblk;
+    h->max_rank = max_rank;
+    h->max_len = max_len;
+    h->capacity = T;
+    h->seg_offset = sizeof(lora_plan_header);
+    h->blk_offset = align16(h->seg_offset + sizeof(lora_seg_desc) * size_t(S));
+    h->perm_offset = align16(h->blk_offset + 4 * size_t(nblk));
+    h->bytes_used = h->perm_offset + 4 * size_t(sorted);
+
+    auto *seg = reinterpret_cast<lora_seg_desc *>(base + h->seg_offset);
+    auto *blk = reinterpret_cast<int32_t *>(base + h->blk_offset);
+    auto *perm = reinterpret_cast<int32_t *>(base + h->perm_offset);
+
+    // Prefix offsets (reusing count as the running write position), descriptors
+    // and the block list.
+    int32_t s = 0, pos = 0, b = 0;
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        const int32_t c = count[size_t(a)];
+        if (!c) continue;
+        lora_seg_desc &d = seg[s];
+        d.A = pool_A[a];
+        d.B = pool_B[a];
+        d.start = pos;
+        d.len = c;
+        d.rank = pool_rank[a];
+        d.adapter = a;
+        d.scale = pool_alpha[a] / float(pool_rank[a]);
+        d.blk0 = b;
+        const int32_t nb = (c + LORA_PLAN_ROW_BLOCK - 1) / LORA_PLAN_ROW_BLOCK;
+        for (int32_t i = 0; i < nb; ++i) blk[b++] = s;
+        count[size_t(a)] = pos;
+        pos += c;
+        ++s;
+    }
+    // Stable scatter: tokens in their original order.
+    for (int32_t t = 0; t < T; ++t) {
+        const int32_t a = ids[t];
+        if (a >= 0) perm[count[size_t(a)]++] = t;
+    }
+    h->magic = LORA_PLAN_MAGIC;
+    return LORA_OK;
+}
+
+int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_bytes, void *stream)
+{
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (!aligned16(plan_dev)) return fail(LORA_ERR_ALIGN, "plan_dev is not 16-byte aligned");
+    if (plan_dev_bytes < h->bytes_used)
+        return fail(LORA_ERR_WORKSPACE, "plan_dev %zu B < %llu B used", plan_dev_bytes,
+                    (unsigned long long)h->bytes_used);
+    hipError_t e = hipMemcpyAsync(plan_dev, plan_host, h->bytes_used, hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LORA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    return LORA_OK;
+}
+
+int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
+                     const void *plan_dev, float *v, int64_t ldv, void *ws, size_t ws_bytes)
+{
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    if (h->num_sorted == 0) return LORA_OK;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, v, ldv, h->max_rank, &sa))) return st;
+    return launch_sgmv_shrink(static_cast<hipStream_t>(stream), sa, PlanView{h, static_cast<const char *>(plan_dev)});
+}
+
+int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv, const void *plan_host,
+                     const void *plan_dev, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
+{
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    if (h->num_sorted == 0) return LORA_OK;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    // B rows are r_s elements long: vector loads of 4 elements need r % 4 == 0 for
+    // every segment; decided per segment on the device, so pass true here.
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, v, ldv, h->max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_sgmv_expand(static_cast<hipStream_t>(stream), ea, PlanView{h, static_cast<const char *>(plan_dev)});
+}
+
+int lora_bgmv_shrink(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+                     const int32_t *ids_dev, const uint64_t *pool_A_dev, const int32_t *pool_rank_dev,
+                     int32_t n_adapters, int32_t max_rank, float *v, int64_t ldv, void *ws, size_t ws_bytes)
+{
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (T < 0 || T > 65536) return fail(LORA_ERR_ARG, "T %d outside [0, 65536]", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return fail(LORA_ERR_RANK, "max_rank %d outside [1, 256]", max_rank);
+    if (T == 0) return LORA_OK;
+    if (!ids_dev || !pool_A_dev || !pool_rank_dev) return fail(LORA_ERR_ARG, "device tables are NULL");
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, v, ldv, max_rank, &sa))) return st;
+    return launch_bgmv_shrink(static_cast<hipStream_t>(stream), sa, T, ids_dev, pool_A_dev, pool_rank_dev,
+                              n_adapters, max_rank);
+}
+
+int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t ldv, const int32_t *ids_dev,
+                     const uint64_t *pool_B_dev, const int32_t *pool_rank_dev, const float *pool_alpha_dev,
+                     int32_t n_adapters, int32_t max_rank, void *y, int64_t ldy, int32_t d_out, void *ws,
+                     size_t ws_bytes)
+{
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (T < 0 || T > 65536) return fail(LORA_ERR_ARG, "T %d outside [0, 65536]", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return fail(LORA_ERR_RANK, "max_rank %d outside [1, 256]", max_rank);
+    if (T == 0) return LORA_OK;
+    if (!ids_dev || !pool_B_dev || !pool_rank_dev || !pool_alpha_dev)
+        return fail(LORA_ERR_ARG, "device tables are NULL");
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, v, ldv, max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_bgmv_expand(static_cast<hipStream_t>(stream), ea, T, ids_dev, pool_B_dev, pool_rank_dev,
+                              pool_alpha_dev, n_adapters, max_rank);
+}
+
+int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *W0,
+                      int32_t d_out, const void *plan_host, const void *plan_dev, void *y, int64_t ldy, void *ws,
+                      size_t ws_bytes)
+{
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    if (dtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "the fused entry takes bf16 only");
+    const int32_t T = h->num_tokens;
+    if (T == 0) return LORA_OK;
+    if (!x || !W0 || !y) return fail(LORA_ERR_ARG, "x, W0 or y is NULL");
+    if (d_in < 1 || d_out < 1) return fail(LORA_ERR_ARG, "d_in %d or d_out %d < 1", d_in, d_out);
+    if (ldx < d_in || ldy < d_out) return fail(LORA_ERR_ARG, "row pitch smaller than the row");
+    if (!aligned16(x) || !aligned16(W0) || !aligned16(y) || (ldx * 2) % 16 || (ldy * 2) % 16 || (d_in * 2) % 16)
+        return fail(LORA_ERR_ALIGN, "fused entry needs 16-byte aligned x, W0, y rows and d_in %% 8 == 0");
+    if (h->num_sorted > 0 && !plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    const size_t need = fused_workspace_bytes(T, h->max_rank < 1 ? 1 : h->max_rank);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    ShrinkArgs sa{};
+    sa.dtype = dtype;
+    sa.x = x;
+    sa.ldx = ldx;
+    sa.d_in = d_in;
+    sa.vec = true;
+    ExpandArgs ea{};
+    ea.dtype = dtype;
+    ea.y = y;
+    ea.ldy = ldy;
+    ea.d_out = d_out;
+    ea.vec_b = true;
+    ea.vec_y = true;
+    return launch_fused_linear(static_cast<hipStream_t>(stream), sa, W0, ea,
+                               PlanView{h, static_cast<const char *>(plan_dev)}, ws, ws_bytes);
+}
+
+} // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host shim and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "lora_mi355x.h"
+
+namespace lora {
+
+// Records the message of a failed call for lora_last_error() and returns status.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Parsed view of a plan: host header plus the device base address.
+struct PlanView {
+    const lora_plan_header *h; // host copy (counts, offsets)
+    const char *dev;           // device copy (same layout)
+};
+
+// Launch geometry / path choices made on the host.
+struct ShrinkArgs {
+    int dtype;
+    const void *x;
+    int64_t ldx;
+    int32_t d_in;
+    float *v;
+    int64_t ldv;
+    bool vec; // 16-byte loads of x rows and A rows are legal
+};
+
+struct ExpandArgs {
+    int dtype;
+    const float *v;
+    int64_t ldv;
+    void *y;
+    int64_t ldy;
+    int32_t d_out;
+    bool vec_b; // 8-byte (bf16) / 16-byte (f32) loads of B rows are legal
+    bool vec_y; // 16-byte loads/stores of y rows are legal
+};
+
+int launch_sgmv_shrink(hipStream_t s, const ShrinkArgs &a, const PlanView &p);
+int launch_sgmv_expand(hipStream_t s, const ExpandArgs &a, const PlanView &p);
+int launch_bgmv_shrink(hipStream_t s, const ShrinkArgs &a, int32_t T, const int32_t *ids,
+                       const uint64_t *pool_A, const int32_t *pool_rank, int32_t n_adapters,
+                       int32_t max_rank);
+int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int32_t *ids,
+                       const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                       int32_t n_adapters, int32_t max_rank);
+int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
+                        const PlanView &p, void *ws, size_t ws_bytes);
+
+size_t fused_workspace_bytes(int32_t T, int32_t max_rank);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+} // namespace lora

@@ -1,0 +1,233 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+builds plans identical to the oracle's brute-force segments, and rejects bad
+arguments from the host before any GPU call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from segmented_gather_gemm_lora_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_mi355x.h")
+
+FAKE_BASE = 0x7F0000000000  # plan building never dereferences device addresses
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_header_function():
+    lib = B.load()
+    names = header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+    assert "gfx950" in B.lora_version()
+
+
+def test_status_strings():
+    for code, name in B.STATUS.items():
+        assert B.lora_status_string(code) == name
+    assert B.lora_status_string(-99) == "LORA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("r,d_in,d_out", [(16, 8192, 8192), (8, 4096, 14336), (1, 1, 1), (256, 4096, 12288),
+                                          (0, 5, 5)])
+def test_adapter_numel_matches_oracle(r, d_in, d_out):
+    assert B.lora_adapter_numel(r, d_in, d_out) == oracle.adapter_numel(r, d_in, d_out)
+
+
+def test_adapter_numel_negative():
+    assert B.lora_adapter_numel(-1, 3, 3) == -1
+
+
+class HostPlan:
+    """A plan in plain host memory (numpy), read back through the header layout."""
+
+    def __init__(self, capacity):
+        self.nbytes = B.lora_plan_bytes(capacity)
+        self.buf = np.zeros((self.nbytes + 7) // 8, dtype=np.uint64)
+
+    @property
+    def ptr(self):
+        return self.buf.ctypes.data
+
+    def header(self):
+        b = self.buf.view(np.uint8)
+        i32 = b[:32].view(np.int32)
+        u64 = b[32:64].view(np.uint64)
+        return dict(magic=int(b[:4].view(np.uint32)[0]), T=int(i32[1]), Tp=int(i32[2]), S=int(i32[3]),
+                    nblk=int(i32[4]), max_rank=int(i32[5]), max_len=int(i32[6]), seg=int(u64[0]),
+                    blk=int(u64[1]), perm=int(u64[2]), used=int(u64[3]))
+
+    def arrays(self):
+        h = self.header()
+        b = self.buf.view(np.uint8)
+        desc = np.frombuffer(b[h["seg"]: h["seg"] + 40 * h["S"]].tobytes(), dtype=np.dtype([
+            ("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
+            ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")]))
+        blk = b[h["blk"]: h["blk"] + 4 * h["nblk"]].view(np.int32)
+        perm = b[h["perm"]: h["perm"] + 4 * h["Tp"]].view(np.int32)
+        return desc, blk, perm
+
+
+def make_tables(N, rng, ranks=None):
+    if ranks is None:
+        ranks = rng.integers(1, 257, N).astype(np.int32)
+    ranks = np.asarray(ranks, dtype=np.int32)
+    alpha = rng.uniform(0.5, 64, N).astype(np.float32)
+    A = (FAKE_BASE + 4096 * np.arange(N, dtype=np.uint64) * 2).astype(np.uint64)
+    Bt = (A + np.uint64(4096)).astype(np.uint64)
+    return A, Bt, ranks, alpha
+
+
+def build(ids, N, A, Bt, ranks, alpha, plan=None, nbytes=None):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    plan = plan or HostPlan(len(ids))
+    st = B.lora_build_plan(len(ids), ids.ctypes.data if len(ids) else None, N, A.ctypes.data, Bt.ctypes.data,
+                           ranks.ctypes.data, alpha.ctypes.data, plan.ptr, nbytes or plan.nbytes)
+    return st, plan
+
+
+@pytest.mark.parametrize("T,N,none_p,seed", [(0, 3, 0.0, 0), (1, 1, 0.0, 1), (8, 2, 0.0, 2), (64, 32, 0.0, 3),
+                                             (200, 9, 0.3, 4), (1000, 3, 0.1, 5), (4096, 1000, 0.0, 6),
+                                             (50, 4, 1.0, 7)])
+def test_plan_matches_oracle_segments(T, N, none_p, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, N, T).astype(np.int32)
+    ids[rng.random(T) < none_p] = -1
+    A, Bt, ranks, alpha = make_tables(N, rng)
+    st, plan = build(ids, N, A, Bt, ranks, alpha)
+    assert st == 0, B.last_error()
+    perm_o, indptr_o, adapter_o = oracle.segments(ids, N)
+    h = plan.header()
+    desc, blk, perm = plan.arrays()
+    assert h["magic"] == B.PLAN_MAGIC and h["T"] == T and h["Tp"] == len(perm_o)
+    assert h["S"] == len(adapter_o)
+    assert np.array_equal(perm, perm_o)
+    assert np.array_equal(desc["adapter"], adapter_o)
+    assert np.array_equal(desc["start"], indptr_o[:-1])
+    assert np.array_equal(desc["len"], np.diff(indptr_o))
+    assert np.array_equal(desc["rank"], ranks[adapter_o])
+    assert np.array_equal(desc["A"], A[adapter_o]) and np.array_equal(desc["B"], Bt[adapter_o])
+    # scale = alpha / rank in fp32 (correctly rounded division)
+    assert np.array_equal(desc["scale"], (alpha[adapter_o] / ranks[adapter_o].astype(np.float32)).astype(np.float32))
+    nb = (np.diff(indptr_o) + 15) // 16
+    assert h["nblk"] == int(nb.sum())
+    assert np.array_equal(desc["blk0"], np.concatenate([[0], np.cumsum(nb)[:-1]]).astype(np.int32) if len(nb) else [])
+    assert np.array_equal(blk, np.repeat(np.arange(len(nb)), nb))
+    assert h["max_rank"] == (int(ranks[adapter_o].max()) if len(adapter_o) else 0)
+    assert h["used"] <= plan.nbytes
+
+
+def test_plan_errors():
+    rng = np.random.default_rng(0)
+    A, Bt, ranks, alpha = make_tables(4, rng, ranks=[8, 16, 0, 300])
+    ok_ids = np.array([0, 1, 1, -1], dtype=np.int32)
+    st, _ = build(ok_ids, 4, A, Bt, ranks, alpha)
+    assert st == 0  # unused adapters with bad ranks are not looked at
+    assert build([0, 4], 4, A, Bt, ranks, alpha)[0] == -3  # id >= n_adapters
+    assert build([0, -2], 4, A, Bt, ranks, alpha)[0] == -3  # id < -1
+    assert build([2], 4, A, Bt, ranks, alpha)[0] == -2  # rank 0
+    assert build([3], 4, A, Bt, ranks, alpha)[0] == -2  # rank 300
+    A2 = A.copy()
+    A2[1] += 8
+    assert build([1], 4, A2, Bt, ranks, alpha)[0] == -4  # misaligned adapter address
+    plan = HostPlan(4)
+    assert build(ok_ids, 4, A, Bt, ranks, alpha, plan=plan, nbytes=64)[0] == -6  # buffer too small
+    assert "ids[1]" in (build([0, 9], 4, A, Bt, ranks, alpha)[0] and B.last_error())
+    lib = B.load()
+    assert lib.lora_build_plan(3, None, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data, alpha.ctypes.data,
+                               plan.ptr, plan.nbytes) == -1  # NULL ids
+    assert lib.lora_build_plan(-1, None, 4, None, None, None, None, plan.ptr, plan.nbytes) == -1
+    assert lib.lora_build_plan(2, ok_ids.ctypes.data, 4, None, None, None, None, plan.ptr, plan.nbytes) == -1
+    assert lib.lora_build_plan(2, ok_ids.ctypes.data, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data,
+                               alpha.ctypes.data, plan.ptr + 4, plan.nbytes) == -4  # misaligned plan buffer
+
+
+def _valid_plan(T=8, N=2, rank=8):
+    rng = np.random.default_rng(1)
+    A, Bt, ranks, alpha = make_tables(N, rng, ranks=[rank] * N)
+    ids = rng.integers(0, N, T).astype(np.int32)
+    st, plan = build(ids, N, A, Bt, ranks, alpha)
+    assert st == 0
+    return plan
+
+
+FX = 0x7F1000000000  # fake 16-byte-aligned device pointers: validation fails before any use
+
+
+def test_sgmv_argument_errors():
+    plan = _valid_plan()
+    empty = HostPlan(0)
+    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
+    sh = B.lora_sgmv_shrink
+    # bad dtype
+    assert sh(None, 7, FX, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -5
+    # NULL plan / plan without magic
+    assert sh(None, 1, FX, 256, 256, None, FX, FX, 8, None, 0) == -1
+    junk = np.zeros(64, dtype=np.uint64)
+    assert sh(None, 1, FX, 256, 256, junk.ctypes.data, FX, FX, 8, None, 0) == -8
+    # an empty batch is a successful no-op, even with NULL buffers
+    assert sh(None, 1, None, 0, 0, empty.ptr, None, None, 0, None, 0) == 0
+    assert B.lora_sgmv_expand(None, 1, None, 0, empty.ptr, None, None, 0, 0, None, 0) == 0
+    # NULL x, v, plan_dev
+    assert sh(None, 1, None, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, None, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 256, plan.ptr, None, FX, 8, None, 0) == -1
+    # ldv smaller than the plan's max rank; ldv not a multiple of 4; v misaligned
+    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX, 4, None, 0) == -2
+    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX, 10, None, 0) == -4
+    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX + 4, 8, None, 0) == -4
+    # x not aligned to its element size; ldx < d_in; d_in < 1
+    assert sh(None, 1, FX + 1, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -4
+    assert sh(None, 1, FX, 100, 256, plan.ptr, FX, FX, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 0, plan.ptr, FX, FX, 8, None, 0) == -1
+    ex = B.lora_sgmv_expand
+    assert ex(None, 1, FX, 8, plan.ptr, FX, None, 256, 256, None, 0) == -1
+    assert ex(None, 1, FX, 8, plan.ptr, FX, FX, 100, 256, None, 0) == -1
+    assert ex(None, 0, FX, 8, plan.ptr, FX, FX + 2, 256, 256, None, 0) == -4  # f32 y misaligned
+    assert ex(None, 1, FX, 2, plan.ptr, FX, FX, 256, 256, None, 0) == -2
+
+
+def test_bgmv_argument_errors():
+    sh = B.lora_bgmv_shrink
+    ex = B.lora_bgmv_expand
+    assert sh(None, 1, 0, None, 0, 0, None, None, None, 0, 16, None, 0, None, 0) == 0  # T = 0
+    assert sh(None, 1, -1, FX, 64, 64, FX, FX, FX, 4, 16, FX, 16, None, 0) == -1
+    assert sh(None, 1, 70000, FX, 64, 64, FX, FX, FX, 4, 16, FX, 16, None, 0) == -1
+    assert sh(None, 1, 4, FX, 64, 64, FX, FX, FX, 4, 0, FX, 16, None, 0) == -2
+    assert sh(None, 1, 4, FX, 64, 64, FX, FX, FX, 4, 257, FX, 16, None, 0) == -2
+    assert sh(None, 1, 4, FX, 64, 64, None, FX, FX, 4, 16, FX, 16, None, 0) == -1
+    assert sh(None, 1, 4, FX, 64, 64, FX, FX, FX, 4, 16, FX, 8, None, 0) == -2
+    assert sh(None, 3, 4, FX, 64, 64, FX, FX, FX, 4, 16, FX, 16, None, 0) == -5
+    assert ex(None, 1, 0, None, 0, None, None, None, None, 0, 16, None, 0, 0, None, 0) == 0
+    assert ex(None, 1, 4, FX, 16, FX, FX, FX, None, 4, 16, FX, 64, 64, None, 0) == -1
+    assert ex(None, 1, 4, FX, 16, FX, FX, FX, FX, 4, 16, FX, 32, 64, None, 0) == -1
+
+
+def test_fused_argument_errors():
+    plan = _valid_plan()
+    f = B.lora_fused_linear
+    assert f(None, 0, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -5  # f32 not offered
+    assert f(None, 1, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 16) == -6  # workspace too small
+    assert f(None, 1, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, None, 1 << 20) == -6
+    assert f(None, 1, FX + 2, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -4
+    assert f(None, 1, None, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -1
+    need = B.lora_workspace_bytes(B.LORA_OP_FUSED, 8, 256, 256, 8)
+    assert need >= 8 * 16 * 4
+
+
+def test_workspace_bytes():
+    for op in (0, 1, 2, 3):
+        assert B.lora_workspace_bytes(op, 4096, 4096, 4096, 16) == 0
+    assert B.lora_workspace_bytes(99, 1, 1, 1, 1) == ctypes.c_size_t(-1).value

@@ -1,0 +1,167 @@
+"""Invariants of the method checked on the GPU path, each against a reference
+that does not come from the GPU: the merge identity, zero adapters, mixed vs
+per-request batches, token permutation, scale doubling, determinism, NaN
+locality, and a non-default stream."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import GpuCase, assert_close, decode, require_gpu, say  # noqa: F401
+from lora_workloads import make_config, make_problem
+from segmented_gather_gemm_lora_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ["sgmv", "bgmv"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    oracle.build(force=False)
+    return require_gpu()
+
+
+def run(prob, path, y_init="stored"):
+    c = GpuCase(prob, y_init=y_init)
+    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    return c
+
+
+def bits(c):
+    return B.to_host_bits(c.y, c.dt)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_merge_identity(dtype, path):
+    """One adapter on every token, y preset to x W0 (rounded once): the result
+    equals x (W0 + s B A) formed by merging the weights (numpy, fp64)."""
+    if dtype == "f32":
+        prob = make_config(1)
+    else:
+        prob = make_problem(name="merge_bf16", dtype="bf16", ids=[0] * 37, ranks=[16], alphas=[32.0], d_in=512,
+                            d_out=384, seed=3, a_std=0.05, b_std=0.05, w0_std=0.05, y_mode="zero")
+    prob.ids = np.zeros(prob.T, dtype=np.int32)
+    # base output x W0 from the oracle (no adapter), rounded once to the dtype
+    base, _ = oracle.lora_forward(prob, ids=np.full(prob.T, -1, dtype=np.int32), fused=True)
+    if dtype == "bf16":
+        from lora_workloads import f32_to_bf16_bits
+
+        y_in = f32_to_bf16_bits(base.astype(np.float32))
+    else:
+        y_in = base.astype(np.float32)
+    say(f"case merge {dtype} {path}")
+    c = run(prob, path, y_init=y_in)
+    s = float(prob.alphas[0]) / float(prob.ranks[0])
+    W = decode(prob.W0, dtype) + s * (decode(prob.B(0), dtype) @ decode(prob.A(0), dtype))
+    ref = decode(prob.x, dtype) @ W.T
+    # The identity holds for the exact base; the preset base was rounded once to
+    # the dtype, so the bound adds that known rounding |y_in - x W0|.
+    y = c.y_out()
+    delta = np.abs(decode(y_in, dtype) - base)
+    rel, floor = (1e-5, 1.0) if dtype == "f32" else (2e-2, 1e-2)
+    bound = rel * (np.abs(ref) + floor) + delta
+    assert (np.abs(y - ref) <= bound).all(), float(np.max(np.abs(y - ref) / bound))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("which", ["A", "B"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_adapter_leaves_y_bitwise(dtype, which, path):
+    rng = np.random.default_rng(4)
+    ids = rng.integers(-1, 3, 45).astype(np.int32)
+    prob = make_problem(name="zero", dtype=dtype, ids=ids, ranks=[4, 16, 40], alphas=[1.0, 2.0, 3.0], d_in=300,
+                        d_out=200, seed=5)
+    for a in range(prob.n_adapters):
+        (prob.A(a) if which == "A" else prob.B(a))[:] = 0
+    say(f"case zero-{which} {dtype} {path}")
+    c = run(prob, path)
+    assert np.array_equal(bits(c), prob.y_in)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mixed_equals_per_request(path):
+    """A batch of mixed adapters equals each adapter's tokens run alone
+    (decode workload; same kernels and split, so bitwise)."""
+    prob = make_config(2)
+    say(f"case mixed-vs-alone {path}")
+    full = bits(run(prob, path))
+    alone = prob.y_in.copy()
+    for a in np.unique(prob.ids):
+        rows = np.nonzero(prob.ids == a)[0]
+        sub = make_problem(name="alone", dtype="bf16", ids=np.full(len(rows), a, dtype=np.int32),
+                           ranks=prob.ranks, alphas=prob.alphas, d_in=prob.d_in, d_out=prob.d_out, seed=0,
+                           a_std=0.0, b_std=0.0)
+        sub.pool = prob.pool
+        sub.x = prob.x[rows]
+        sub.y_in = prob.y_in[rows]
+        alone[rows] = bits(run(sub, path))
+    assert np.array_equal(full, alone)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("k", [2, 4])
+def test_permutation_invariance(k, path):
+    prob = make_config(k)
+    say(f"case permutation k={k} {path}")
+    y1 = bits(run(prob, path))
+    perm = np.random.default_rng(7).permutation(prob.T)
+    prob.ids = prob.ids[perm]
+    prob.x = prob.x[perm]
+    prob.y_in = prob.y_in[perm]
+    y2 = bits(run(prob, path))
+    assert np.array_equal(y2, y1[perm])
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scale_doubling_bitwise(dtype, path):
+    rng = np.random.default_rng(8)
+    ids = rng.integers(0, 4, 50).astype(np.int32)
+    prob = make_problem(name="scale", dtype=dtype, ids=ids, ranks=[8, 16, 3, 64], alphas=[16.0, 32.0, 6.0, 12.0],
+                        d_in=640, d_out=272, seed=9)
+    say(f"case scale-doubling {dtype} {path}")
+    y1 = run(prob, path, y_init="zero").y_out()
+    prob.alphas = prob.alphas * 2
+    y2 = run(prob, path, y_init="zero").y_out()
+    assert np.array_equal(y2, 2 * y1)
+    assert np.abs(y1).max() > 0
+
+
+@pytest.mark.parametrize("path,k", [("sgmv", 3), ("sgmv", 4), ("bgmv", 2)])
+def test_determinism(path, k):
+    prob = make_config(k)
+    say(f"case determinism k={k} {path}")
+    assert np.array_equal(bits(run(prob, path)), bits(run(prob, path)))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_nan_locality(path):
+    prob = make_config(2)
+    prob.x = prob.x.copy()
+    t_bad = int(np.nonzero(prob.ids == prob.ids[5])[0][0])  # a token that shares its adapter with others
+    prob.x[t_bad, 100] = 0x7FC0  # bf16 quiet NaN
+    say(f"case nan-locality {path}")
+    y = run(prob, path).y_out()
+    bad_rows = ~np.isfinite(y).all(axis=1)
+    assert bad_rows.tolist() == [t == t_bad for t in range(prob.T)]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_side_stream(path):
+    """Work enqueued on a non-default stream (default priority) is correct."""
+    import torch
+
+    prob = make_config(2)
+    say(f"case side-stream {path}")
+    c = GpuCase(prob)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        if path == "sgmv":
+            c.run_sgmv(stream=s)
+        else:
+            c.run_bgmv(stream=s)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.lora_forward(prob, nthreads=16)
+    assert_close(c.y_out(), y_ref, "bf16", "side stream")

@@ -1,0 +1,200 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (per element): fp32 |gpu - ref| <= 1e-5 (|ref| + 1); bf16 inputs
+with fp32 accumulation |gpu - ref| <= 2e-2 (|ref| + 1e-2).  The shrink result v
+is checked against the oracle's v with the rigorous fp32 summation bound
+d_in * 2^-24 * sum_k |x_k A_jk|.  Each named workload runs as specified (y
+preset) and with a zero base, so that the tolerance scales with the
+correction itself.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import GpuCase, assert_close, decode, require_gpu, say, v_bound
+from lora_workloads import make_config, make_integer_problem, make_problem
+
+pytestmark = pytest.mark.gpu
+
+_ORACLE_CACHE = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    oracle.build(force=False)
+    return require_gpu()
+
+
+def oracle_ref(key, prob, zero_base=False):
+    if key not in _ORACLE_CACHE:
+        p = prob
+        if zero_base:
+            p = _with_zero_base(prob)
+        _ORACLE_CACHE[key] = oracle.lora_forward(p, want_v=True, nthreads=16)
+    return _ORACLE_CACHE[key]
+
+
+def _with_zero_base(prob):
+    import copy
+
+    q = copy.copy(prob)
+    q.y_in = None
+    return q
+
+
+def check_case(prob, path, zero_base, key=None):
+    say(f"case {prob.name} T={prob.T} d_in={prob.d_in} d_out={prob.d_out} dtype={prob.dtype} path={path} "
+        f"zero_base={zero_base}")
+    c = GpuCase(prob, y_init="zero" if zero_base else "stored")
+    if path == "sgmv":
+        v, plan = c.run_sgmv()
+        perm = plan.arrays()["perm"]
+        vrows = perm
+    else:
+        v = c.run_bgmv()
+        vrows = np.nonzero(prob.ids >= 0)[0]
+    y = c.y_out()
+    y_ref, v_ref = oracle_ref(key, prob, zero_base) if key else oracle.lora_forward(
+        _with_zero_base(prob) if zero_base else prob, want_v=True, nthreads=16)
+    worst = assert_close(y, y_ref, prob.dtype, f"{prob.name}/{path}/y")
+    # v: rows in sorted order (SGMV) or token order (BGMV)
+    vv = v[: len(vrows)] if path == "sgmv" else v[vrows]
+    tok = perm if path == "sgmv" else vrows
+    ranks = prob.ranks[prob.ids[tok]] if len(tok) else np.zeros(0, dtype=np.int32)
+    bound = v_bound(prob, tok, prob.ids[tok])
+    for i, t in enumerate(tok):
+        r = int(ranks[i])
+        err = np.abs(vv[i, :r] - v_ref[t, :r])
+        assert (err <= bound[i, :r] + 1e-6 * np.abs(v_ref[t, :r])).all(), (prob.name, path, "v", t)
+    # rows of tokens without an adapter are untouched (bitwise)
+    none = np.nonzero(prob.ids < 0)[0]
+    if len(none):
+        y0 = decode(c.y_host_in, prob.dtype)
+        assert np.array_equal(y[none], y0[none])
+    return worst
+
+
+@pytest.mark.parametrize("zero_base", [False, True], ids=["y_preset", "y_zero"])
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_named_workloads(k, path, zero_base):
+    prob = make_config(k)
+    check_case(prob, path, zero_base, key=(k, zero_base))
+
+
+@pytest.mark.parametrize("k,seed", [(2, 102), (3, 103), (4, 104)])
+def test_named_workloads_other_seeds(k, seed):
+    prob = make_config(k, seed=seed)
+    check_case(prob, "sgmv" if k != 2 else "bgmv", False)
+
+
+SHAPES = [
+    # name, dtype, T, d_in, d_out, ranks, none_frac, seed
+    ("ragged_d", "bf16", 53, 37, 29, [3, 1, 16, 7], 0.1, 1),
+    ("ragged_d_f32", "f32", 41, 45, 301, [5, 8, 2], 0.2, 2),
+    ("rank1", "bf16", 33, 256, 300, [1], 0.0, 3),
+    ("rank256", "bf16", 40, 512, 520, [256, 200], 0.0, 4),
+    ("rank256_f32", "f32", 19, 136, 264, [256, 33], 0.0, 5),
+    ("one_token", "bf16", 1, 4096, 4096, [16], 0.0, 6),
+    ("many_tiny_segments", "bf16", 300, 1024, 768, list(range(1, 65)), 0.05, 7),
+    ("long_and_short", "bf16", 700, 2048, 1100, [64, 8, 32, 16], 0.0, 8),
+    ("wide_out", "bf16", 24, 128, 14336, [8, 64], 0.0, 9),
+]
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_shapes(shape, path):
+    name, dt, T, d_in, d_out, ranks, none_frac, seed = shape
+    rng = np.random.default_rng(seed)
+    n = len(ranks)
+    if name == "long_and_short":
+        ids = np.concatenate([np.full(600, 0), rng.integers(1, n, T - 600)]).astype(np.int32)
+    else:
+        ids = rng.integers(0, n, T).astype(np.int32)
+    ids[rng.random(T) < none_frac] = -1
+    prob = make_problem(name=name, dtype=dt, ids=ids, ranks=ranks, alphas=[2.0 * r for r in ranks], d_in=d_in,
+                        d_out=d_out, seed=seed, a_std=0.05, b_std=0.05)
+    check_case(prob, path, False)
+    check_case(prob, path, True)
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_tokens_without_adapter(dtype, path):
+    prob = make_problem(name="none", dtype=dtype, ids=[-1] * 20, ranks=[4, 8], alphas=[1.0, 1.0], d_in=64, d_out=48,
+                        seed=1)
+    say(f"case all-none {dtype} {path}")
+    c = GpuCase(prob)
+    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    assert np.array_equal(B_bits(c), prob.y_in)
+
+
+def B_bits(c):
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    return B.to_host_bits(c.y, c.dt)
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_batch(dtype, path):
+    """T = 0 is a successful no-op on both paths."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob = make_problem(name="empty", dtype=dtype, ids=np.zeros(0, dtype=np.int32), ranks=[4], alphas=[1.0], d_in=64,
+                        d_out=48, seed=1)
+    pool = B.DevicePool.from_problem(prob)
+    say(f"case empty {dtype} {path}")
+    x = torch.zeros((0, 64), dtype=B.torch_dtype(dtype), device="cuda")
+    y = torch.zeros((0, 48), dtype=B.torch_dtype(dtype), device="cuda")
+    v = torch.zeros((1, 4), device="cuda")
+    if path == "sgmv":
+        plan = B.Plan(1).build(prob.ids, pool).upload()
+        assert plan.header()["num_sorted"] == 0
+        B.sgmv_shrink(x, plan, v, dtype)
+        B.sgmv_expand(v, plan, y, dtype)
+    else:
+        ids = torch.zeros(0, dtype=torch.int32, device="cuda")
+        B.bgmv_shrink(x, ids, pool, v, dtype)
+        B.bgmv_expand(v, ids, pool, y, dtype)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_integer_bitwise(seed, dtype, path):
+    """Entries in {-1,0,1}, scale 1: every partial sum is a small integer, so
+    the GPU must reproduce the oracle exactly (bitwise)."""
+    prob = make_integer_problem(seed=seed, dtype=dtype, T=40, d_in=16, d_out=16, n_adapters=3, none_frac=0.1)
+    say(f"case integer seed={seed} {dtype} {path}")
+    c = GpuCase(prob)
+    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    y = c.y_out()
+    y_ref, _ = oracle.lora_forward(prob)
+    assert np.array_equal(y, y_ref)
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_integer_bitwise_larger(dtype, path):
+    """Larger integer case (d_in 200, ranks 1..4, d_out 333): fp32 sums are
+    exact; a bf16 output equals the exact integer rounded once to bf16."""
+    from lora_workloads import f32_to_bf16_bits
+
+    prob = make_integer_problem(seed=11, dtype=dtype, T=70, d_in=200, d_out=333, n_adapters=5, none_frac=0.1)
+    say(f"case integer-larger {dtype} {path}")
+    c = GpuCase(prob)
+    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    y_ref, _ = oracle.lora_forward(prob)
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    bits = B.to_host_bits(c.y, dtype)
+    if dtype == "bf16":
+        assert np.array_equal(bits, f32_to_bf16_bits(y_ref.astype(np.float32)))
+    else:
+        assert np.array_equal(bits, y_ref.astype(np.float32))
