@@ -29,12 +29,14 @@
  * Accumulation is fp32; bf16 outputs are rounded to nearest-even once.
  *
  * Ownership and ordering.  The caller owns every buffer (activations, pool,
- * plans, v, workspace).  The library never allocates, frees or synchronises;
+ * plans, v, workspace).  The library never frees or synchronises;
  * every GPU call is enqueued on the caller's stream (a hipStream_t passed as
  * void*, NULL = the null stream) and returns before the work runs.  Buffers
  * must stay alive until the stream has passed the call.  x, v and y must not
- * overlap.  The library keeps no mutable global state except a thread-local
- * copy of the last error message, so it may be used from several threads.
+ * overlap.  The library allocates no device memory and keeps no mutable
+ * global state; per thread it keeps the last error message, a pending
+ * launch-timing request (lora_profile_launches) and a host scratch array for
+ * the plan builder's counts, so it may be used from several threads.
  *
  * Errors.  Every call returns LORA_OK (0) or a negative lora_status, after
  * checking every argument the host can see and before enqueuing anything;
@@ -86,12 +88,15 @@ typedef enum lora_dtype {
  * A plan lives in one contiguous buffer with the same layout on the host and
  * the device, so a single copy moves it:
  *
- *   [lora_plan_header][lora_seg_desc x S][int32 blk_seg x n_blocks][int32 perm x T']
+ *   [lora_plan_header][lora_seg_desc x S][lora_blk_desc x n_blocks][int32 perm x T']
+ *   [lora_chunk_desc x n_chunks]
  *
  * perm[p] is the original token index at sorted position p.  Segment s covers
  * sorted positions [start, start + len).  The block list cuts every segment
- * into blocks of LORA_PLAN_ROW_BLOCK rows (the last one ragged); blk_seg[b]
- * is the segment of block b and segment s owns blocks [blk0, blk0 + ceil(len/16)).
+ * into blocks of LORA_PLAN_ROW_BLOCK rows (the last one ragged); segment s
+ * owns blocks [blk0, blk0 + ceil(len/16)).  A block descriptor repeats what a
+ * kernel needs about its segment and lists its rows, so a workgroup reads one
+ * 128-byte record before it can fetch activations and adapter weights.
  */
 typedef struct lora_seg_desc {
     uint64_t A;      /* device address of A_i, [rank, d_in] */
@@ -104,6 +109,18 @@ typedef struct lora_seg_desc {
     int32_t blk0;    /* first block of this segment */
 } lora_seg_desc;
 
+typedef struct lora_blk_desc {
+    uint64_t A;       /* as the segment's descriptor */
+    uint64_t B;
+    float scale;
+    int32_t rank;
+    int32_t n;        /* rows in this block, 1..16 */
+    int32_t p0;       /* sorted position of the block's first row (rows are p0 .. p0+n-1) */
+    int32_t seg;      /* segment index */
+    int32_t reserved[7];
+    int32_t rows[LORA_PLAN_ROW_BLOCK]; /* original token index of each row; -1 past n */
+} lora_blk_desc; /* 128 bytes */
+
 typedef struct lora_plan_header {
     uint32_t magic;       /* LORA_PLAN_MAGIC when valid */
     int32_t num_tokens;   /* T of the batch */
@@ -112,12 +129,34 @@ typedef struct lora_plan_header {
     int32_t num_blocks;   /* sum over segments of ceil(len / 16) */
     int32_t max_rank;     /* largest rank among the segments (0 if S = 0) */
     int32_t max_len;      /* longest segment */
-    int32_t capacity;     /* T the buffer was sized for */
+    int32_t num_chunks;   /* sum over segments of ceil(blocks / LORA_PLAN_CHUNK_BLOCKS) */
     uint64_t seg_offset;  /* byte offset of the lora_seg_desc array */
-    uint64_t blk_offset;  /* byte offset of blk_seg */
+    uint64_t blk_offset;  /* byte offset of the lora_blk_desc array (128-byte aligned) */
     uint64_t perm_offset; /* byte offset of perm */
     uint64_t bytes_used;  /* bytes from the start of the buffer that hold the plan */
-} lora_plan_header;
+    uint64_t chunk_offset; /* byte offset of the lora_chunk_desc array (64-byte aligned) */
+    uint64_t reserved[3];
+} lora_plan_header; /* 96 bytes */
+
+/* A chunk is up to this many consecutive blocks of one segment (64 rows): the
+ * unit of expand work that reuses one adapter's B tile across its rows.  Like a
+ * block descriptor it is self-contained. */
+#define LORA_PLAN_CHUNK_BLOCKS 4
+#define LORA_PLAN_CHUNK_ROWS (LORA_PLAN_ROW_BLOCK * LORA_PLAN_CHUNK_BLOCKS)
+
+typedef struct lora_chunk_desc {
+    uint64_t A;
+    uint64_t B;
+    float scale;
+    int32_t rank;
+    int32_t n;          /* rows in this chunk, 1..64 */
+    int32_t p0;         /* sorted position of the first row (rows are p0 .. p0+n-1) */
+    int32_t seg;
+    int32_t first_blk;  /* first of the chunk's blocks */
+    int32_t nblk;       /* blocks in the chunk, 1..4 */
+    int32_t reserved[5];
+    int32_t rows[LORA_PLAN_CHUNK_ROWS]; /* original token index of each row; -1 past n */
+} lora_chunk_desc; /* 320 bytes */
 
 #define LORA_PLAN_MAGIC 0x4C6F5241u
 
@@ -169,6 +208,18 @@ int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
                      const void *plan_host, const void *plan_dev,
                      void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
+/* One call for the whole correction of a batch from a plan, shrink then
+ * expand (same section): y[perm[p], :] += scale_s (x[perm[p], :] A_s) B_s.
+ * The low-rank intermediate stays in the workspace as fp32 partial sums over
+ * slices of d_in (summed in a fixed order by the expand, so results are
+ * reproducible run to run).  Two kernel launches on `stream`.
+ * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_SGMV, T, d_in, d_out, max_rank)
+ * with T >= header.num_sorted and max_rank >= header.max_rank.
+ * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */
+int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
+              const void *plan_host, const void *plan_dev,
+              void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------ BGMV
  * Decode-shaped gather (one row per request, "Multi-LoRA Serving in
  * Production ...", section "S-LoRA: MBGMV and MBGMM Kernels": single-token
@@ -196,6 +247,17 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
                      int32_t n_adapters, int32_t max_rank,
                      void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
+/* Decode correction in one call: bgmv_shrink then bgmv_expand, with the
+ * intermediate kept in the workspace as fp32 partial sums over slices of d_in
+ * (fixed summation order).  Needs ws_bytes >=
+ * lora_workspace_bytes(LORA_OP_BGMV, T, d_in, d_out, max_rank).
+ * Errors: as lora_bgmv_shrink, plus LORA_ERR_WORKSPACE. */
+int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+              const int32_t *ids_dev, const uint64_t *pool_A_dev, const uint64_t *pool_B_dev,
+              const int32_t *pool_rank_dev, const float *pool_alpha_dev,
+              int32_t n_adapters, int32_t max_rank,
+              void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------ fused layer
  * The whole adapted layer: the shared base product once for every token plus
  * each token's correction, y = x W0 + scale_s (x A_s) B_s, overwriting y
@@ -216,7 +278,9 @@ enum {
     LORA_OP_SGMV_EXPAND = 1,
     LORA_OP_BGMV_SHRINK = 2,
     LORA_OP_BGMV_EXPAND = 3,
-    LORA_OP_FUSED = 4
+    LORA_OP_FUSED = 4,
+    LORA_OP_SGMV = 5,
+    LORA_OP_BGMV = 6
 };
 
 /* Workspace bytes an op needs (0 = none; ws may then be NULL); -1 cast to
@@ -234,6 +298,15 @@ const char *lora_status_string(int status);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *lora_last_error(void);
+
+/* Timing of the library's own kernels, for benchmarks: the next `count`
+ * kernels this thread enqueues through the library record start_events[i]
+ * when kernel i begins and stop_events[i] when it ends (hipEvent_t handles
+ * created by the caller with hipEventCreate; the arrays and events must stay
+ * valid until those launches have been enqueued).  count = 0 cancels a
+ * pending request.  The request is per thread.
+ * Errors: LORA_ERR_ARG (negative count, NULL array or event). */
+int lora_profile_launches(void **start_events, void **stop_events, int32_t count);
 
 /* Library version string. */
 const char *lora_version(void);

@@ -13,14 +13,17 @@ from .binding import (  # noqa: F401
     DevicePool,
     LoraError,
     Plan,
+    bgmv,
     bgmv_expand,
     bgmv_shrink,
     fused_linear,
     lib_path,
     load,
+    sgmv,
     sgmv_expand,
     sgmv_shrink,
     to_device,
     to_host_bits,
     v_pitch,
+    workspace,
 )

@@ -27,6 +27,8 @@ LORA_OP_SGMV_EXPAND = 1
 LORA_OP_BGMV_SHRINK = 2
 LORA_OP_BGMV_EXPAND = 3
 LORA_OP_FUSED = 4
+LORA_OP_SGMV = 5
+LORA_OP_BGMV = 6
 
 STATUS = {
     0: "LORA_OK", -1: "LORA_ERR_ARG", -2: "LORA_ERR_RANK", -3: "LORA_ERR_ADAPTER_ID",
@@ -37,12 +39,13 @@ STATUS = {
 # Every symbol the public header declares.
 EXPORTS = [
     "lora_plan_bytes", "lora_build_plan", "lora_plan_upload", "lora_sgmv_shrink",
-    "lora_sgmv_expand", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_fused_linear",
+    "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
-    "lora_version",
+    "lora_version", "lora_profile_launches",
 ]
 
-PLAN_HEADER_BYTES = 64
+PLAN_HEADER_BYTES = 96
+CHUNK_BLOCKS = 4
 PLAN_MAGIC = 0x4C6F5241
 ROW_BLOCK = 16
 
@@ -63,6 +66,9 @@ _SIGS = {
     "lora_plan_upload": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "lora_sgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _sz]),
     "lora_sgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz]),
+    "lora_sgmv": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i32, _vp, _sz]),
+    "lora_bgmv": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                 _vp, _i64, _i32, _vp, _sz]),
     "lora_bgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32,
                                         _vp, _i64, _vp, _sz]),
     "lora_bgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
@@ -74,6 +80,7 @@ _SIGS = {
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_last_error": (ctypes.c_char_p, []),
     "lora_version": (ctypes.c_char_p, []),
+    "lora_profile_launches": (ctypes.c_int, [_vp, _vp, _i32]),
 }
 
 
@@ -147,6 +154,16 @@ def lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, 
     return int(load().lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes))
 
 
+def lora_sgmv(stream, dtype, x, ldx, d_in, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv(stream, dtype, x, ldx, d_in, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes))
+
+
+def lora_bgmv(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank,
+              y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_bgmv(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_B, pool_rank, pool_alpha,
+                                n_adapters, max_rank, y, ldy, d_out, ws, ws_bytes))
+
+
 def lora_bgmv_shrink(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_rank, n_adapters, max_rank, v, ldv,
                      ws, ws_bytes) -> int:
     return int(load().lora_bgmv_shrink(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_rank, n_adapters,
@@ -162,6 +179,57 @@ def lora_bgmv_expand(stream, dtype, T, v, ldv, ids, pool_B, pool_rank, pool_alph
 def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy, ws, ws_bytes) -> int:
     return int(load().lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy,
                                         ws, ws_bytes))
+
+
+def lora_profile_launches(start_events, stop_events, count) -> int:
+    return int(load().lora_profile_launches(start_events, stop_events, count))
+
+
+class KernelTimer:
+    """Times the library's next kernel launches with HIP events attached to the
+    kernels themselves (hipExtLaunchKernelGGL start/stop events)."""
+
+    _hip = None
+
+    def __init__(self, n: int):
+        if KernelTimer._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            KernelTimer._hip = hip
+        self.n = n
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for i in range(n):
+            for arr in (self.start, self.stop):
+                h = ctypes.c_void_p()
+                if KernelTimer._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = h
+
+    def arm(self, first: int, count: int):
+        """The next `count` launches record events first .. first+count-1."""
+        st = lora_profile_launches(ctypes.addressof(self.start) + 8 * first,
+                                   ctypes.addressof(self.stop) + 8 * first, count)
+        _check(st, "lora_profile_launches")
+
+    def disarm(self):
+        _check(lora_profile_launches(None, None, 0), "lora_profile_launches")
+
+    def elapsed_us(self, i: int) -> float:
+        hip = KernelTimer._hip
+        hip.hipEventSynchronize(self.stop[i])
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def close(self):
+        for i in range(self.n):
+            KernelTimer._hip.hipEventDestroy(self.start[i])
+            KernelTimer._hip.hipEventDestroy(self.stop[i])
 
 
 # ------------------------------------------------------------------ torch-facing helpers
@@ -247,6 +315,41 @@ class DevicePool:
         return p
 
 
+SEG_DESC = np.dtype([("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
+                     ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")])
+BLK_DESC = np.dtype([("A", "<u8"), ("B", "<u8"), ("scale", "<f4"), ("rank", "<i4"), ("n", "<i4"), ("p0", "<i4"),
+                     ("seg", "<i4"), ("reserved", "<i4", (7,)), ("rows", "<i4", (ROW_BLOCK,))])
+CHUNK_DESC = np.dtype([("A", "<u8"), ("B", "<u8"), ("scale", "<f4"), ("rank", "<i4"), ("n", "<i4"),
+                       ("p0", "<i4"), ("seg", "<i4"), ("first_blk", "<i4"), ("nblk", "<i4"),
+                       ("reserved", "<i4", (5,)), ("rows", "<i4", (ROW_BLOCK * CHUNK_BLOCKS,))])
+assert SEG_DESC.itemsize == 40 and BLK_DESC.itemsize == 128 and CHUNK_DESC.itemsize == 320
+
+
+def plan_header(h: np.ndarray) -> dict:
+    """Fields of a plan header held in `h` (uint8, at least 96 bytes)."""
+    i32 = h[:32].view(np.int32)
+    u64 = h[32:96].view(np.uint64)
+    return {"magic": int(h[:4].view(np.uint32)[0]), "num_tokens": int(i32[1]), "num_sorted": int(i32[2]),
+            "num_segments": int(i32[3]), "num_blocks": int(i32[4]), "max_rank": int(i32[5]),
+            "max_len": int(i32[6]), "num_chunks": int(i32[7]), "seg_offset": int(u64[0]),
+            "blk_offset": int(u64[1]), "perm_offset": int(u64[2]), "bytes_used": int(u64[3]),
+            "chunk_offset": int(u64[4])}
+
+
+def plan_arrays(buf: np.ndarray, h: dict) -> dict:
+    """Segment descriptors, block descriptors and perm of a plan held in `buf` (uint8)."""
+    S, nb, Tp = h["num_segments"], h["num_blocks"], h["num_sorted"]
+    so, bo, po = h["seg_offset"], h["blk_offset"], h["perm_offset"]
+    seg = np.frombuffer(buf[so: so + SEG_DESC.itemsize * S].tobytes(), dtype=SEG_DESC)
+    blk = np.frombuffer(buf[bo: bo + BLK_DESC.itemsize * nb].tobytes(), dtype=BLK_DESC)
+    perm = buf[po: po + 4 * Tp].view(np.int32).copy()
+    out = {"desc": seg, "blocks": blk, "perm": perm}
+    if "chunk_offset" in h:
+        co = h["chunk_offset"]
+        out["chunks"] = np.frombuffer(buf[co: co + CHUNK_DESC.itemsize * h["num_chunks"]].tobytes(), dtype=CHUNK_DESC)
+    return out
+
+
 class Plan:
     """A batch's segment plan: pinned host copy + device copy (one upload)."""
 
@@ -273,25 +376,11 @@ class Plan:
         return self
 
     def header(self) -> dict:
-        h = self.host[:PLAN_HEADER_BYTES].numpy()
-        i32 = h[:32].view(np.int32)
-        u64 = h[32:64].view(np.uint64)
-        return {"magic": int(h[:4].view(np.uint32)[0]), "num_tokens": int(i32[1]), "num_sorted": int(i32[2]),
-                "num_segments": int(i32[3]), "num_blocks": int(i32[4]), "max_rank": int(i32[5]),
-                "max_len": int(i32[6]), "capacity": int(i32[7]), "seg_offset": int(u64[0]),
-                "blk_offset": int(u64[1]), "perm_offset": int(u64[2]), "bytes_used": int(u64[3])}
+        return plan_header(self.host[:PLAN_HEADER_BYTES].numpy())
 
     def arrays(self) -> dict:
         """Host copies of the plan's arrays (for tests)."""
-        h = self.header()
-        buf = self.host.numpy()
-        S, nb, Tp = h["num_segments"], h["num_blocks"], h["num_sorted"]
-        desc = np.frombuffer(buf[h["seg_offset"]: h["seg_offset"] + 40 * S].tobytes(), dtype=np.dtype([
-            ("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
-            ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")]))
-        blk = buf[h["blk_offset"]: h["blk_offset"] + 4 * nb].view(np.int32).copy()
-        perm = buf[h["perm_offset"]: h["perm_offset"] + 4 * Tp].view(np.int32).copy()
-        return {"desc": desc, "blk_seg": blk, "perm": perm}
+        return plan_arrays(self.host.numpy(), self.header())
 
 
 def sgmv_shrink(x, plan: Plan, v, dtype: str, stream=None):
@@ -305,6 +394,29 @@ def sgmv_expand(v, plan: Plan, y, dtype: str, stream=None):
     _check(lora_sgmv_expand(_stream_handle(stream), DTYPES[dtype], _ptr(v), v.stride(0), plan.host.data_ptr(),
                             plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1], None, 0),
            "lora_sgmv_expand")
+
+
+def workspace(op: int, T: int, d_in: int, d_out: int, max_rank: int, device="cuda"):
+    """A device workspace of the size the library asks for (uint8 tensor)."""
+    torch = _torch()
+    n = lora_workspace_bytes(op, T, d_in, d_out, max_rank)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def sgmv(x, plan: Plan, y, ws, dtype: str, stream=None):
+    """y[perm] += scale (x[perm] A) B for the whole plan (shrink + expand)."""
+    _check(lora_sgmv(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1], plan.host.data_ptr(),
+                     plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_sgmv")
+
+
+def bgmv(x, ids_dev, pool: DevicePool, y, ws, dtype: str, max_rank: Optional[int] = None, stream=None):
+    """Decode: y[t] += scale (x[t] A_ids[t]) B_ids[t] (shrink + expand)."""
+    _check(lora_bgmv(_stream_handle(stream), DTYPES[dtype], x.shape[0], _ptr(x), x.stride(0), x.shape[1],
+                     _ptr(ids_dev), _ptr(pool.addr_A_dev), _ptr(pool.addr_B_dev), _ptr(pool.rank_dev),
+                     _ptr(pool.alpha_dev), pool.n_adapters, max_rank or pool.max_rank, _ptr(y), y.stride(0),
+                     y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_bgmv")
 
 
 def bgmv_shrink(x, ids_dev, pool: DevicePool, v, dtype: str, max_rank: Optional[int] = None, stream=None):

@@ -3,10 +3,16 @@
 // hipMemcpyAsync (plan upload) and kernel launches on the caller's stream.
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
 #include "internal.h"
+
+static_assert(sizeof(lora_blk_desc) == 128, "block descriptor is one 128-byte record");
+static_assert(sizeof(lora_seg_desc) == 40, "segment descriptor layout");
+static_assert(sizeof(lora_chunk_desc) == 320, "chunk descriptor layout");
+static_assert(sizeof(lora_plan_header) == 96, "plan header layout");
 
 namespace lora {
 
@@ -22,6 +28,12 @@ int fail(int status, const char *fmt, ...)
 }
 
 void clear_error() { g_last_error[0] = '\0'; }
+
+LaunchEvents &launch_events()
+{
+    static thread_local LaunchEvents le;
+    return le;
+}
 
 static size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
@@ -113,6 +125,21 @@ using namespace lora;
 
 extern "C" {
 
+int lora_profile_launches(void **start_events, void **stop_events, int32_t count)
+{
+    clear_error();
+    if (count < 0) return fail(LORA_ERR_ARG, "count %d < 0", count);
+    if (count > 0 && (!start_events || !stop_events)) return fail(LORA_ERR_ARG, "event arrays are NULL");
+    for (int32_t i = 0; i < count; ++i)
+        if (!start_events[i] || !stop_events[i]) return fail(LORA_ERR_ARG, "event %d is NULL", i);
+    LaunchEvents &le = launch_events();
+    le.start = start_events;
+    le.stop = stop_events;
+    le.count = count;
+    le.next = 0;
+    return LORA_OK;
+}
+
 const char *lora_version(void) { return "lora_mi355x 0.1.0 (gfx950)"; }
 
 const char *lora_last_error(void) { return g_last_error; }
@@ -143,13 +170,14 @@ size_t lora_plan_bytes(int32_t capacity)
 {
     if (capacity < 0) capacity = 0;
     const size_t c = size_t(capacity);
-    // header, descriptors (S <= T), block list (blocks <= T'), perm (T' <= T)
-    return sizeof(lora_plan_header) + sizeof(lora_seg_desc) * c + 16 + 4 * c + 16 + 4 * c + 16;
+    // header, segment descriptors (S <= T), block descriptors (blocks <= T'),
+    // perm (T' <= T), alignment slack
+    return sizeof(lora_plan_header) + sizeof(lora_seg_desc) * c + 128 + sizeof(lora_blk_desc) * c + 4 * c + 64 +
+           sizeof(lora_chunk_desc) * c + 16;
 }
 
 size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank)
 {
-    (void)d_in;
     (void)d_out;
     switch (op) {
     case LORA_OP_SGMV_SHRINK:
@@ -157,6 +185,9 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_BGMV_SHRINK:
     case LORA_OP_BGMV_EXPAND: return 0;
     case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, max_rank < 1 ? 1 : max_rank);
+    case LORA_OP_SGMV:
+    case LORA_OP_BGMV:
+        return combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     default: return size_t(-1);
     }
 }
@@ -191,7 +222,7 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
         return fail(LORA_ERR_ARG, "pool tables are NULL");
 
     // Segments in ascending adapter id; check the adapters actually used.
-    int32_t S = 0, nblk = 0, max_rank = 0, max_len = 0;
+    int32_t S = 0, nblk = 0, nchunk = 0, max_rank = 0, max_len = 0;
     for (int32_t a = 0; a < n_adapters; ++a) {
         if (!count[size_t(a)]) continue;
         const int32_t r = pool_rank[a];
@@ -200,7 +231,9 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
         if ((pool_A[a] & 15u) || (pool_B[a] & 15u))
             return fail(LORA_ERR_ALIGN, "adapter %d: A or B address is not 16-byte aligned", a);
         ++S;
-        nblk += (count[size_t(a)] + LORA_PLAN_ROW_BLOCK - 1) / LORA_PLAN_ROW_BLOCK;
+        const int32_t nb = (count[size_t(a)] + LORA_PLAN_ROW_BLOCK - 1) / LORA_PLAN_ROW_BLOCK;
+        nblk += nb;
+        nchunk += (nb + LORA_PLAN_CHUNK_BLOCKS - 1) / LORA_PLAN_CHUNK_BLOCKS;
         if (r > max_rank) max_rank = r;
         if (count[size_t(a)] > max_len) max_len = count[size_t(a)];
     }
@@ -214,19 +247,21 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
     h->num_blocks = nblk;
     h->max_rank = max_rank;
     h->max_len = max_len;
-    h->capacity = T;
+    h->num_chunks = nchunk;
     h->seg_offset = sizeof(lora_plan_header);
-    h->blk_offset = align16(h->seg_offset + sizeof(lora_seg_desc) * size_t(S));
-    h->perm_offset = align16(h->blk_offset + 4 * size_t(nblk));
-    h->bytes_used = h->perm_offset + 4 * size_t(sorted);
+    h->blk_offset = (h->seg_offset + sizeof(lora_seg_desc) * size_t(S) + 127) & ~size_t(127);
+    h->perm_offset = align16(h->blk_offset + sizeof(lora_blk_desc) * size_t(nblk));
+    h->chunk_offset = (h->perm_offset + 4 * size_t(sorted) + 63) & ~size_t(63);
+    h->bytes_used = h->chunk_offset + sizeof(lora_chunk_desc) * size_t(nchunk);
 
     auto *seg = reinterpret_cast<lora_seg_desc *>(base + h->seg_offset);
-    auto *blk = reinterpret_cast<int32_t *>(base + h->blk_offset);
+    auto *blk = reinterpret_cast<lora_blk_desc *>(base + h->blk_offset);
     auto *perm = reinterpret_cast<int32_t *>(base + h->perm_offset);
+    auto *chunks = reinterpret_cast<lora_chunk_desc *>(base + h->chunk_offset);
 
     // Prefix offsets (reusing count as the running write position), descriptors
     // and the block list.
-    int32_t s = 0, pos = 0, b = 0;
+    int32_t s = 0, pos = 0, b = 0, ch = 0;
     for (int32_t a = 0; a < n_adapters; ++a) {
         const int32_t c = count[size_t(a)];
         if (!c) continue;
@@ -240,15 +275,51 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
         d.scale = pool_alpha[a] / float(pool_rank[a]);
         d.blk0 = b;
         const int32_t nb = (c + LORA_PLAN_ROW_BLOCK - 1) / LORA_PLAN_ROW_BLOCK;
-        for (int32_t i = 0; i < nb; ++i) blk[b++] = s;
+        for (int32_t i = 0; i < nb; i += LORA_PLAN_CHUNK_BLOCKS, ++ch) {
+            lora_chunk_desc &k = chunks[ch];
+            std::memset(&k, 0, sizeof k);
+            k.A = d.A;
+            k.B = d.B;
+            k.scale = d.scale;
+            k.rank = d.rank;
+            k.p0 = pos + i * LORA_PLAN_ROW_BLOCK;
+            k.n = std::min(LORA_PLAN_CHUNK_ROWS, c - i * LORA_PLAN_ROW_BLOCK);
+            k.seg = s;
+            k.first_blk = b + i;
+            k.nblk = std::min(LORA_PLAN_CHUNK_BLOCKS, nb - i);
+            for (int32_t m = 0; m < LORA_PLAN_CHUNK_ROWS; ++m) k.rows[m] = -1;
+        }
+        for (int32_t i = 0; i < nb; ++i, ++b) {
+            lora_blk_desc &k = blk[b];
+            std::memset(&k, 0, sizeof k);
+            k.A = d.A;
+            k.B = d.B;
+            k.scale = d.scale;
+            k.rank = d.rank;
+            k.p0 = pos + i * LORA_PLAN_ROW_BLOCK;
+            k.n = std::min(LORA_PLAN_ROW_BLOCK, c - i * LORA_PLAN_ROW_BLOCK);
+            k.seg = s;
+            for (int32_t m = 0; m < LORA_PLAN_ROW_BLOCK; ++m) k.rows[m] = -1;
+        }
         count[size_t(a)] = pos;
         pos += c;
         ++s;
     }
-    // Stable scatter: tokens in their original order.
+    // Stable scatter: tokens in their original order; each lands in its
+    // block's row list too (block of sorted position p is blk0 + (p - start) / 16).
     for (int32_t t = 0; t < T; ++t) {
         const int32_t a = ids[t];
-        if (a >= 0) perm[count[size_t(a)]++] = t;
+        if (a < 0) continue;
+        const int32_t p = count[size_t(a)]++;
+        perm[p] = t;
+    }
+    for (int32_t si = 0, c0 = 0; si < S; ++si) {
+        const lora_seg_desc &d = seg[si];
+        for (int32_t q = 0; q < d.len; ++q) {
+            blk[d.blk0 + q / LORA_PLAN_ROW_BLOCK].rows[q % LORA_PLAN_ROW_BLOCK] = perm[d.start + q];
+            chunks[c0 + q / LORA_PLAN_CHUNK_ROWS].rows[q % LORA_PLAN_CHUNK_ROWS] = perm[d.start + q];
+        }
+        c0 += (d.len + LORA_PLAN_CHUNK_ROWS - 1) / LORA_PLAN_CHUNK_ROWS;
     }
     h->magic = LORA_PLAN_MAGIC;
     return LORA_OK;
@@ -302,9 +373,59 @@ int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv, const
     if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
     // B rows are r_s elements long: vector loads of 4 elements need r % 4 == 0 for
     // every segment; decided per segment on the device, so pass true here.
+    if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
     ExpandArgs ea{};
     if ((st = make_expand_args(dtype, v, ldv, h->max_rank, y, ldy, d_out, true, &ea))) return st;
     return launch_sgmv_expand(static_cast<hipStream_t>(stream), ea, PlanView{h, static_cast<const char *>(plan_dev)});
+}
+
+int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
+              const void *plan_dev, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    if (h->num_sorted == 0) return LORA_OK;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
+    const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, h->max_rank, &sa))) return st;
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
+        return st;
+    return launch_sgmv(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, static_cast<const char *>(plan_dev)}, ws);
+}
+
+int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in, const int32_t *ids_dev,
+              const uint64_t *pool_A_dev, const uint64_t *pool_B_dev, const int32_t *pool_rank_dev,
+              const float *pool_alpha_dev, int32_t n_adapters, int32_t max_rank, void *y, int64_t ldy, int32_t d_out,
+              void *ws, size_t ws_bytes)
+{
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (T < 0 || T > 65536) return fail(LORA_ERR_ARG, "T %d outside [0, 65536]", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return fail(LORA_ERR_RANK, "max_rank %d outside [1, 256]", max_rank);
+    if (T == 0) return LORA_OK;
+    if (!ids_dev || !pool_A_dev || !pool_B_dev || !pool_rank_dev || !pool_alpha_dev)
+        return fail(LORA_ERR_ARG, "device tables are NULL");
+    const size_t need = combined_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const int64_t ldw = (max_rank + 3) / 4 * 4;
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, max_rank, &sa))) return st;
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_bgmv(static_cast<hipStream_t>(stream), sa, ea, T, ids_dev, pool_A_dev, pool_B_dev, pool_rank_dev,
+                       pool_alpha_dev, n_adapters, max_rank, ws);
 }
 
 int lora_bgmv_shrink(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,

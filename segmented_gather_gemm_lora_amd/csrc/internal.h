@@ -1,6 +1,7 @@
 // Internal declarations shared by the host shim and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -50,11 +51,41 @@ int launch_bgmv_shrink(hipStream_t s, const ShrinkArgs &a, int32_t T, const int3
 int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int32_t *ids,
                        const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                        int32_t n_adapters, int32_t max_rank);
+int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws);
+int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                int32_t n_adapters, int32_t max_rank, void *ws);
+// Workspace of the combined calls: fp32 partial sums of the shrink over d_in slices.
+size_t combined_workspace_bytes(int32_t rows, int32_t d_in, int32_t max_rank);
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
                         const PlanView &p, void *ws, size_t ws_bytes);
 
 size_t fused_workspace_bytes(int32_t T, int32_t max_rank);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-thread request to time the next launches (lora_profile_launches).
+struct LaunchEvents {
+    void **start = nullptr;
+    void **stop = nullptr;
+    int count = 0;
+    int next = 0;
+};
+LaunchEvents &launch_events();
+
+// Every kernel launch of the library goes through here, so a pending timing
+// request attaches its events to the kernel's own start and end.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args)
+{
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    LaunchEvents &le = launch_events();
+    if (le.next < le.count) {
+        e0 = static_cast<hipEvent_t>(le.start[le.next]);
+        e1 = static_cast<hipEvent_t>(le.stop[le.next]);
+        ++le.next;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(shm), s, e0, e1, 0, static_cast<KArgs>(args)...);
+}
 
 } // namespace lora

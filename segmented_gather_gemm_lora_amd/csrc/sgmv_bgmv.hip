@@ -9,18 +9,25 @@
 // is read once per segment and reused for all of the segment's rows.
 //
 // Work unit: a block of up to 16 rows that share one adapter (a plan block, or
-// a group of decode tokens with the same id).  16 rows is the M of the
-// 16x16 MFMA tiles used by both kernels:
+// a group of decode tokens with the same id).  16 rows is the M of the 16x16
+// MFMA tiles used by both kernels:
 //
-//  * shrink: D[token, rank] += X[token, k] * A[rank, k], bf16 operands via
-//    v_mfma_f32_16x16x32_bf16 (fp32 inputs via v_mfma_f32_16x16x4_f32).  Every
-//    lane loads 64 contiguous bytes of its token row and of its A row per step,
-//    so both operands come straight from global memory with 16-byte loads.  The
-//    waves of a workgroup split d_in and are summed in LDS in a fixed order.
-//  * expand: D[column, token] += B[column, j] * v[token, j] with the fp32 MFMA
-//    (v stays fp32, B is widened exactly).  Output columns are assigned to MFMA
-//    rows so that every lane ends up owning 16 consecutive columns of one
-//    token: y is read and written with 16-byte accesses, once.
+//  * shrink: D[token, rank] += X[token, k] * A[rank, k] on
+//    v_mfma_f32_16x16x32_bf16 (fp32 inputs: v_mfma_f32_16x16x4_f32).  Operands
+//    come straight from global memory with 16-byte loads; each load
+//    instruction reads 64 contiguous bytes of every token row (and of every A
+//    row) of the block, and a wave issues the loads of all of its k-steps
+//    before the first MFMA.  A workgroup covers one slice of d_in;
+//    its waves are summed in LDS in a fixed order.  With several slices the
+//    slice results are fp32 partial sums, added in slice order by the expand.
+//  * expand: D[column, token] += B[column, j] * v[token, j] on the fp32 MFMA
+//    (v stays fp32; bf16 B is widened exactly).  Output columns are assigned to
+//    MFMA rows so that each lane owns 16 consecutive columns of one token: y is
+//    prefetched at the start and written once, with 16-byte accesses.
+//
+// Latency: every load a workgroup needs depends on at most one earlier load
+// (the block descriptor, or the decode ids), so a kernel costs about two
+// memory round trips plus its streaming time.
 #include "internal.h"
 
 namespace lora {
@@ -32,10 +39,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = LORA_PLAN_ROW_BLOCK; // rows per block (MFMA M)
-constexpr int kExpandThreads = 256;       // 4 waves x 64 output columns
-constexpr int kExpandCols = 256;          // output columns per workgroup
+constexpr int kExpandCols = 256;          // output columns per expand workgroup (4 waves x 64)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Adapter addresses come from descriptors and pool tables, so the compiler
+// cannot tell that they point to global memory and would use flat loads (which
+// also occupy the LDS/scalar counter and force extra waits).  Say so.
+template <typename T> using global_ptr = const __attribute__((address_space(1))) T *;
+template <typename T> __device__ __forceinline__ global_ptr<T> as_global(const void *p)
+{
+    return (global_ptr<T>)(p);
+}
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
@@ -46,420 +61,626 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
     return u >> 16;
 }
 
-// Rows of one block: x/y row (original token), v row, count.  Lives in LDS.
-struct BlockRows {
-    int xrow[kRows]; // -1 beyond n
-    int vrow[kRows];
-    int n;
-    int next; // BGMV: next position to scan
+// ----------------------------------------------------------------------------
+// Operand fragments.  bf16: one step = 4 lane groups x 32 elements of k; a
+// lane holds 4 fragments of 8.  fp32: one step = 4 lane groups x 16 elements;
+// a lane holds 4 fragments of 4.  Any assignment of k to (lane group, element)
+// is valid as long as x and A use the same one.
+// ----------------------------------------------------------------------------
+template <int DT> struct Frag;
+template <> struct Frag<LORA_BF16> {
+    using T = uint16_t;
+    using V = bf16x8;
+    static constexpr int kPerLane = 32; // elements of k per lane per step
+    static constexpr int kStep = 128;
+    static constexpr int kVec = 8;
+};
+template <> struct Frag<LORA_F32> {
+    using T = float;
+    using V = floatx4;
+    static constexpr int kPerLane = 16;
+    static constexpr int kStep = 64;
+    static constexpr int kVec = 4;
 };
 
-// ----------------------------------------------------------------------------
-// Shrink of one block: v[vrow[m], j] = sum_k x[xrow[m], k] * A[j, k], j < r.
-// W waves split d_in; partial tiles are summed over waves in LDS (wave order).
-// ----------------------------------------------------------------------------
-template <bool VEC>
-__device__ __forceinline__ bf16x8 frag_bf16(const uint16_t *row, int k, int d_in, bool ok)
+// Loads are never skipped by a branch: a branch around a load makes the
+// compiler wait for that load at the join, which serialises every load of the
+// wave.  Out-of-range fragments read a clamped in-range address and are then
+// zeroed with a select.
+template <int DT, bool VEC>
+__device__ __forceinline__ typename Frag<DT>::V load_frag(global_ptr<typename Frag<DT>::T> row, int k, int k_end)
 {
+    using F = Frag<DT>;
+    typename F::V f;
     if (VEC) {
-        if (ok && k < d_in) return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + k));
-        return bf16x8{};
+        // k and k_end are multiples of kVec: the fragment is all in or all out.
+        const int kk = k < k_end ? k : k_end - F::kVec;
+        if constexpr (DT == LORA_BF16) f = __builtin_bit_cast(bf16x8, *(global_ptr<u32x4>)(row + kk));
+        else f = *(global_ptr<floatx4>)(row + kk);
+        if (k >= k_end) f = typename F::V{};
     } else {
-        bf16x8 f{};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (ok && k + e < d_in) f[e] = __builtin_bit_cast(__bf16, row[k + e]);
-        return f;
+        for (int e = 0; e < F::kVec; ++e) {
+            const int kk = k + e < k_end ? k + e : k_end - 1;
+            typename F::T val = row[kk];
+            if constexpr (DT == LORA_BF16) f[e] = k + e < k_end ? __builtin_bit_cast(__bf16, val) : __bf16(0.f);
+            else f[e] = k + e < k_end ? val : 0.f;
+        }
+    }
+    return f;
+}
+
+template <int DT>
+__device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, const typename Frag<DT>::V &b, floatx4 acc)
+{
+    if constexpr (DT == LORA_BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+        return acc;
     }
 }
 
-template <bool VEC>
-__device__ __forceinline__ floatx4 frag_f32(const float *row, int k, int d_in, bool ok)
+// ----------------------------------------------------------------------------
+// Shrink of one block over k in [k_begin, k_end):
+//   out[orow(m), j] = sum_k x[xrow_m, k] * A[j, k]   (j < r, m < n)
+// W waves per workgroup; wave w takes chunks of NSTEP steps starting at
+// k_begin + (i * W + w) * NSTEP * kStep.  RT = rank tiles of 16 held at once.
+// Results of the W waves are added in wave order through LDS (`red`, W*RT*1 KB).
+// Output row of block row mm: orows[mm] if orows (LDS) is given, else orow0 + mm.
+// ----------------------------------------------------------------------------
+template <int DT, bool VEC, int W, int NSTEP, int RT>
+__device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xr, int xr0,
+                                             const void *__restrict__ Av, int d_in, int r, int k_begin, int k_end,
+                                             float *__restrict__ out, int64_t ldo, int orow0, const int *orows, int n,
+                                             float *red)
 {
-    if (VEC) {
-        if (ok && k < d_in) return *reinterpret_cast<const floatx4 *>(row + k);
-        return floatx4{};
-    } else {
-        floatx4 f{};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (ok && k + e < d_in) f[e] = row[k + e];
-        return f;
-    }
-}
-
-template <int DT, bool VEC, int W>
-__device__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int d_in, const void *__restrict__ Av,
-                             int r, float *__restrict__ v, int64_t ldv, const BlockRows &br, float *red)
-{
+    using F = Frag<DT>;
+    using T = typename F::T;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int xr = br.xrow[m];
-    const bool xok = xr >= 0;
+    // rows past n repeat the block's first row: their MFMA rows are never stored
+    const global_ptr<T> xrow = as_global<T>(xv) + int64_t(xr >= 0 ? xr : xr0) * ldx;
+    const global_ptr<T> A = as_global<T>(Av);
     const int ntiles = (r + 15) >> 4;
 
-    for (int rt0 = 0; rt0 < ntiles; rt0 += 4) {
-        floatx4 acc[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
-        if constexpr (DT == LORA_BF16) {
-            // K step per wave iteration: 4 lane groups x 32 elements.
-            const uint16_t *xrow = static_cast<const uint16_t *>(xv) + int64_t(xok ? xr : 0) * ldx;
-            const uint16_t *A = static_cast<const uint16_t *>(Av);
-            for (int kb = wave * 128; kb < d_in; kb += W * 128) {
-                const int k0 = kb + 32 * g;
-                bf16x8 xf[4];
+    for (int rt0 = 0; rt0 < ntiles; rt0 += RT) {
+        floatx4 acc[RT];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) xf[u] = frag_bf16<VEC>(xrow, k0 + 8 * u, d_in, xok);
+        for (int i = 0; i < RT; ++i) acc[i] = floatx4{};
+        // ranks past r repeat row r-1: their MFMA columns are never stored
+        global_ptr<T> arow[RT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (rt0 + i < ntiles) {
-                        const int j = 16 * (rt0 + i) + m;
-                        const uint16_t *arow = A + int64_t(j < r ? j : 0) * d_in;
+        for (int i = 0; i < RT; ++i) {
+            const int j = 16 * (rt0 + i) + m;
+            arow[i] = A + int64_t(j < r ? j : r - 1) * d_in;
+        }
+        for (int kb = k_begin + wave * NSTEP * F::kStep; kb < k_end; kb += W * NSTEP * F::kStep) {
+            typename F::V xf[NSTEP][4];
+            typename F::V af[NSTEP][RT][4];
+            // issue every load of this chunk first
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const bf16x8 af = frag_bf16<VEC>(arow, k0 + 8 * u, d_in, j < r);
-                            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u], af, acc[i], 0, 0, 0);
-                        }
-                    }
-                }
+            for (int s = 0; s < NSTEP; ++s) {
+                // fragment u of lane group g: k = kb + s*kStep + (4u + g)*kVec, so one
+                // load instruction covers 4*kVec contiguous elements of each row
+                const int k0 = kb + s * F::kStep + F::kVec * g;
+                // A rows first: their addresses are known before the token rows are
+#pragma unroll
+                for (int i = 0; i < RT; ++i)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) af[s][i][u] = load_frag<DT, VEC>(arow[i], k0 + 4 * F::kVec * u, k_end);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xf[s][u] = load_frag<DT, VEC>(xrow, k0 + 4 * F::kVec * u, k_end);
             }
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+                for (int i = 0; i < RT; ++i)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[i] = mfma_step<DT>(xf[s][u], af[s][i][u], acc[i]);
+        }
+        // lane l of tile i holds D[4*(l/16) + q][l%16] = (row in block, rank in tile)
+        if constexpr (W == 1) {
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int mm = 4 * g + q, j = 16 * (rt0 + i) + m;
+                    if (mm < n && j < r) out[int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j] = acc[i][q];
+                }
         } else {
-            // K step per wave iteration: 4 lane groups x 16 elements.
-            const float *xrow = static_cast<const float *>(xv) + int64_t(xok ? xr : 0) * ldx;
-            const float *A = static_cast<const float *>(Av);
-            for (int kb = wave * 64; kb < d_in; kb += W * 64) {
-                const int k0 = kb + 16 * g;
-                floatx4 xf[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) xf[u] = frag_f32<VEC>(xrow, k0 + 4 * u, d_in, xok);
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (rt0 + i < ntiles) {
-                        const int j = 16 * (rt0 + i) + m;
-                        const float *arow = A + int64_t(j < r ? j : 0) * d_in;
+                for (int q = 0; q < 4; ++q) red[((wave * RT + i) * 64 + lane) * 4 + q] = acc[i][q];
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < RT * 64 * 4; idx += W * 64) {
+                const int i = idx >> 8, l2 = (idx >> 2) & 63, q = idx & 3;
+                float sum = 0.f;
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const floatx4 af = frag_f32<VEC>(arow, k0 + 4 * u, d_in, j < r);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[u][e], af[e], acc[i], 0, 0, 0);
-                        }
-                    }
-                }
+                for (int w = 0; w < W; ++w) sum += red[((w * RT + i) * 64 + l2) * 4 + q];
+                const int mm = 4 * (l2 >> 4) + q, j = 16 * (rt0 + i) + (l2 & 15);
+                if (mm < n && j < r) out[int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j] = sum;
             }
+            __syncthreads();
         }
-        // Sum the W partial tiles in wave order; lane l of a tile holds
-        // D[4*(l/16) + q][l%16] = (row in block, rank in tile).
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) red[((wave * 4 + i) * 64 + lane) * 4 + q] = acc[i][q];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 4 * 64 * 4; idx += W * 64) {
-            const int i = idx >> 8, l2 = (idx >> 2) & 63, q = idx & 3;
-            if (rt0 + i < ntiles) {
-                float s = 0.f;
-#pragma unroll
-                for (int w = 0; w < W; ++w) s += red[((w * 4 + i) * 64 + l2) * 4 + q];
-                const int mm = 4 * (l2 >> 4) + q;
-                const int n = 16 * (rt0 + i) + (l2 & 15);
-                if (mm < br.n && n < r) v[int64_t(br.vrow[mm]) * ldv + n] = s;
-            }
-        }
-        __syncthreads();
     }
 }
 
-// ----------------------------------------------------------------------------
-// Expand of one block over this workgroup's 256 columns:
-//   y[xrow[m], n] += scale * sum_{j<r} v[vrow[m], j] * B[n, j].
-// MFMA rows are output columns, MFMA columns are the block's tokens.  Lane
-// (g = l/16, token = l%16) owns columns ncol0 + 16g .. +16 of its token.
-// ----------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ void load_b4(const void *Bv, int64_t off, bool vec, int jn, float *bf)
+// Output columns of a lane.  A lane (g = l/16) owns 16 columns of its row,
+// reached with 16-byte accesses ("instructions" s = 0 .. 16/E-1, E = elements
+// per 16 bytes).  Instruction s of lane group g covers columns
+// s*4E + g*E .. +E, so in every load/store instruction the 4 lanes of a row
+// touch 4E contiguous elements (64 bytes).  Accumulator element v = 4t + i of
+// the lane (MFMA tile t, D row 4g + i) belongs to instruction v / E, element
+// v % E; this also fixes which column MFMA row m = 4g' + i' of tile t stands for.
+template <int DT> struct Cols {
+    static constexpr int E = DT == LORA_BF16 ? 8 : 4;
+    // column offset (from the wave's first column) of accumulator element v of lane group g
+    static __device__ __forceinline__ int of(int g, int v) { return (v / E) * 4 * E + g * E + (v % E); }
+};
+
+// y tile of one lane: 16 elements (bf16 in 8 dwords, fp32 in 16), in
+// accumulator order (element v = 4t + i).
+template <int DT> struct YTile {
+    uint32_t w[DT == LORA_BF16 ? 8 : 16];
+};
+
+// VECY: 16-byte aligned rows and d_out % 16 == 0 (64-column waves never
+// straddle d_out partially within a 16-byte access).  Lanes of a wave past
+// d_out load from a clamped valid address; nothing is stored for them.
+template <int DT, bool VECY>
+__device__ __forceinline__ void y_load(const void *yv, int64_t row_off, int ncol0, int g, int d_out, YTile<DT> &t)
 {
-    // 4 consecutive elements of a B row starting at element `off`; jn = how many are valid.
+    constexpr int E = Cols<DT>::E;
     if constexpr (DT == LORA_BF16) {
-        const uint16_t *p = static_cast<const uint16_t *>(Bv) + off;
-        if (vec && jn >= 4) {
-            const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
-            bf[0] = bf16_to_f32(w[0] & 0xffffu);
-            bf[1] = bf16_to_f32(w[0] >> 16);
-            bf[2] = bf16_to_f32(w[1] & 0xffffu);
-            bf[3] = bf16_to_f32(w[1] >> 16);
-        } else {
+        const uint16_t *y = static_cast<const uint16_t *>(yv) + row_off;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bf[q] = q < jn ? bf16_to_f32(p[q]) : 0.f;
+        for (int sI = 0; sI < 16 / E; ++sI) {
+            const int c = ncol0 + Cols<DT>::of(g, sI * E);
+            if constexpr (VECY) {
+                const u32x4 q = *reinterpret_cast<const u32x4 *>(y + (c < d_out ? c : 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t.w[sI * 4 + e] = q[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c0 = min(c + 2 * e, d_out - 1), c1 = min(c + 2 * e + 1, d_out - 1);
+                    t.w[sI * 4 + e] = uint32_t(y[c0]) | (uint32_t(y[c1]) << 16);
+                }
+            }
         }
     } else {
-        const float *p = static_cast<const float *>(Bv) + off;
-        if (vec && jn >= 4) {
-            const floatx4 w = *reinterpret_cast<const floatx4 *>(p);
+        const float *y = static_cast<const float *>(yv) + row_off;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bf[q] = w[q];
-        } else {
+        for (int sI = 0; sI < 16 / E; ++sI) {
+            const int c = ncol0 + Cols<DT>::of(g, sI * E);
+            if constexpr (VECY) {
+                const u32x4 q = *reinterpret_cast<const u32x4 *>(y + (c < d_out ? c : 0));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bf[q] = q < jn ? p[q] : 0.f;
+                for (int e = 0; e < 4; ++e) t.w[sI * 4 + e] = q[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t.w[sI * 4 + e] = __float_as_uint(y[min(c + e, d_out - 1)]);
+            }
         }
     }
 }
 
-template <int DT>
-__device__ void expand_block(const float *__restrict__ v, int64_t ldv, const void *__restrict__ Bv, int r, float scale,
-                             void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg, const BlockRows &br,
-                             bool vec_b, bool vec_y)
+// y += scale * acc (accumulator element v = 4t + i, columns as in Cols), rounded once.
+template <int DT, bool VECY>
+__device__ __forceinline__ void y_store(void *yv, int64_t row_off, int ncol0, int g, int d_out, const YTile<DT> &t,
+                                        const floatx4 (&acc)[4], float scale)
+{
+    constexpr int E = Cols<DT>::E;
+    if constexpr (DT == LORA_BF16) {
+        uint16_t *y = static_cast<uint16_t *>(yv) + row_off;
+#pragma unroll
+        for (int sI = 0; sI < 16 / E; ++sI) {
+            const int c = ncol0 + Cols<DT>::of(g, sI * E);
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v0 = sI * E + 2 * e, v1 = v0 + 1;
+                const uint32_t w = t.w[sI * 4 + e];
+                const float f0 = __builtin_fmaf(scale, acc[v0 >> 2][v0 & 3], bf16_to_f32(w & 0xffffu));
+                const float f1 = __builtin_fmaf(scale, acc[v1 >> 2][v1 & 3], bf16_to_f32(w >> 16));
+                o[e] = f32_to_bf16(f0) | (f32_to_bf16(f1) << 16);
+            }
+            if constexpr (VECY) {
+                if (c < d_out) *reinterpret_cast<u32x4 *>(y + c) = u32x4{o[0], o[1], o[2], o[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (c + e < d_out) y[c + e] = uint16_t((o[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+        }
+    } else {
+        float *y = static_cast<float *>(yv) + row_off;
+#pragma unroll
+        for (int sI = 0; sI < 16 / E; ++sI) {
+            const int c = ncol0 + Cols<DT>::of(g, sI * E);
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = sI * E + e;
+                o[e] = __builtin_fmaf(scale, acc[v >> 2][v & 3], __uint_as_float(t.w[sI * 4 + e]));
+            }
+            if constexpr (VECY) {
+                if (c < d_out) *reinterpret_cast<floatx4 *>(y + c) = floatx4{o[0], o[1], o[2], o[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < d_out) y[c + e] = o[e];
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Expand of up to RB*16 rows that share one adapter, over this workgroup's 256
+// columns:  y[yrow, c] += scale * sum_{j<r} v[vrow, j] * B[c, j],  with v the
+// sum of `nsl` partial slices.
+//   * loads are issued in the order their results are needed (the memory
+//     counter retires them in order): row indices, v slices, B fragments, y;
+//   * the workgroup adds the v slices of its rows once, into LDS (vl, rows of
+//     ldl floats, zero beyond r), then every wave reads them from LDS;
+//   * MFMA rows are output columns, MFMA columns are the 16 rows of a block;
+//     lane (g = l/16, row m = l%16) owns 16 columns of its row (see Cols), and
+//     A-operand row m of column tile t stands for column
+//     ncol0 + Cols::of(m/4, 4t + m%4).
+// yrows may point to global or LDS memory; the v row of row q is vrow0 + q when
+// vrow0 >= 0, else yrows[q].  BV: r % 4 == 0 (4 ranks per load).
+// ----------------------------------------------------------------------------
+constexpr int kMaxSlices = 4;
+
+template <int DT, bool BV>
+__device__ __forceinline__ void load_bfrag(const void *Bv, int r, int j0, int ncol0, int m, int d_out,
+                                           float (&bf)[4][4])
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int ncol = ncol0 + Cols<DT>::of(m >> 2, 4 * t + (m & 3));
+        const bool cok = ncol < d_out;
+        const int64_t rowoff = int64_t(cok ? ncol : d_out - 1) * r;
+        if constexpr (BV) {
+            const bool ok = cok && j0 < r;
+            const int jj = j0 < r ? j0 : 0;
+            if constexpr (DT == LORA_BF16) {
+                const u32x2 q = *(global_ptr<u32x2>)(as_global<uint16_t>(Bv) + rowoff + jj);
+                bf[t][0] = ok ? bf16_to_f32(q[0] & 0xffffu) : 0.f;
+                bf[t][1] = ok ? bf16_to_f32(q[0] >> 16) : 0.f;
+                bf[t][2] = ok ? bf16_to_f32(q[1] & 0xffffu) : 0.f;
+                bf[t][3] = ok ? bf16_to_f32(q[1] >> 16) : 0.f;
+            } else {
+                const floatx4 q = *(global_ptr<floatx4>)(as_global<float>(Bv) + rowoff + jj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bf[t][e] = ok ? q[e] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + e;
+                const bool ok = cok && j < r;
+                const int jj = j < r ? j : r - 1;
+                float val;
+                if constexpr (DT == LORA_BF16) val = bf16_to_f32(as_global<uint16_t>(Bv)[rowoff + jj]);
+                else val = as_global<float>(Bv)[rowoff + jj];
+                bf[t][e] = ok ? val : 0.f;
+            }
+        }
+    }
+}
+
+// v rows of a block: VIND = indexed through yrows (BGMV: the token index),
+// else contiguous from vrow0 (SGMV: sorted positions).  UPT = float4 units of v
+// per thread (the launcher sizes it so that UPT*256 >= rows*ldl/4).  Split in a
+// load phase and a sum phase so that other loads can be issued in between.
+template <int UPT> struct VStage {
+    floatx4 w[UPT][kMaxSlices];
+    bool uok[UPT], vok[UPT];
+    int off[UPT];
+};
+
+template <bool BV, bool VIND, int UPT>
+__device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                             const int *yrows, int vrow0, int nrows, int r, int ldl, VStage<UPT> &st)
+{
+    const int q4 = ldl >> 2;
+    const int units = nrows * q4;
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const int u = threadIdx.x + k * int(blockDim.x);
+        st.uok[k] = u < units;
+        const int uu = st.uok[k] ? u : 0;
+        const int row = uu / q4, j = 4 * (uu - row * q4);
+        st.off[k] = row * ldl + j;
+        int vr;
+        if constexpr (VIND) vr = yrows[row]; // LDS
+        else vr = vrow0 + row;
+        st.vok[k] = st.uok[k] && vr >= 0 && j < r;
+        const float *p = v + int64_t(st.vok[k] ? vr : 0) * ldv + (j < r ? j : 0);
+#pragma unroll
+        for (int sl = 0; sl < kMaxSlices; ++sl) {
+            const float *ps = p + (sl < nsl ? sl : 0) * sl_stride;
+            if constexpr (BV) {
+                st.w[k][sl] = *reinterpret_cast<const floatx4 *>(ps);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.w[k][sl][e] = ps[(j + e < r ? e : 0)];
+            }
+        }
+    }
+}
+
+// LDS of an expand workgroup: RB*16 rows of ldl floats, then one spare float4
+// (at float offset `spare`) that absorbs the stores of units past the rows.
+template <bool BV, int UPT>
+__device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare, const VStage<UPT> &st, float *vl)
+{
+    const int q4 = ldl >> 2;
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        floatx4 acc4 = floatx4{};
+#pragma unroll
+        for (int sl = 0; sl < kMaxSlices; ++sl)
+            if (sl < nsl) acc4 += st.w[k][sl];
+        if constexpr (!BV) {
+            const int j = st.off[k] % ldl; // rank of the unit's first element
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e >= r) acc4[e] = 0.f;
+        }
+        if (!st.vok[k]) acc4 = floatx4{};
+        // units past the rows write a spare slot after them: no branch around the
+        // store, so the compiler keeps the loads where they were issued
+        const int dst = st.uok[k] ? st.off[k] : spare;
+        *reinterpret_cast<floatx4 *>(vl + dst) = acc4;
+    }
+    (void)q4;
+}
+
+template <int DT, int RB, bool VECY, bool BV, bool VIND, int UPT>
+__device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                                 const void *__restrict__ Bv, int r, float scale,
+                                                 void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
+                                                 const int *yrows, int vrow0, int nrows, float *vl, int ldl)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const bool tok_ok = m < br.n;
-    const int vr = br.vrow[m];
     const int ncol0 = ncol_wg + 64 * wave;
-    if (ncol0 >= d_out) return;
-    const bool bvec = vec_b && (r % 4 == 0);
 
-    floatx4 acc[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
+    // 1. row indices of the y tiles
+    int yr[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int row = 16 * i + m;
+        yr[i] = row < nrows ? yrows[row] : -1;
+    }
+    const int ysafe = yrows[0];
+    // 2. v slices, 3. B fragments of the first 16 ranks, 4. y tiles; then the v
+    // slices are added into LDS while B and y are still in flight
+    VStage<UPT> vst;
+    stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    float bf[4][4];
+    load_bfrag<DT, BV>(Bv, r, 4 * g, ncol0, m, d_out, bf);
+    YTile<DT> yt[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
+    stage_v_store<BV, UPT>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
+    __syncthreads();
+
+    floatx4 acc[RB][4];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{};
     const int nch = (r + 15) >> 4;
     for (int c = 0; c < nch; ++c) {
         const int j0 = 16 * c + 4 * g;
-        const int jn = r - j0; // valid ranks from j0 (may be <= 0)
-        float vf[4];
-        if (tok_ok && jn >= 4) {
-            const floatx4 w = *reinterpret_cast<const floatx4 *>(v + int64_t(vr) * ldv + j0);
+        if (c > 0) load_bfrag<DT, BV>(Bv, r, j0, ncol0, m, d_out, bf);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) vf[q] = w[q];
-        } else {
+        for (int i = 0; i < RB; ++i) {
+            if (16 * i >= nrows) break;
+            const int row = 16 * i + m;
+            floatx4 vf = *reinterpret_cast<const floatx4 *>(vl + (row < nrows ? row : 0) * ldl + (j0 < ldl ? j0 : 0));
+            if (row >= nrows || j0 >= ldl) vf = floatx4{};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) vf[q] = (tok_ok && q < jn) ? v[int64_t(vr) * ldv + j0 + q] : 0.f;
-        }
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int ncol = ncol0 + 16 * (m >> 2) + 4 * t + (m & 3);
-            float bf[4] = {0.f, 0.f, 0.f, 0.f};
-            if (ncol < d_out && jn > 0) load_b4<DT>(Bv, int64_t(ncol) * r + j0, bvec, jn, bf);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[q], vf[q], acc[t], 0, 0, 0);
+                for (int q = 0; q < 4; ++q)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[t][q], vf[q], acc[i][t], 0, 0, 0);
         }
     }
-    if (!tok_ok) return;
-    const int64_t yrow = int64_t(br.xrow[m]) * ldy;
-    const int cb = ncol0 + 16 * g;
-    if (cb >= d_out) return;
-    if constexpr (DT == LORA_BF16) {
-        uint16_t *y = static_cast<uint16_t *>(yv) + yrow + cb;
-        if (vec_y && cb + 16 <= d_out) {
-            u32x4 lo = *reinterpret_cast<const u32x4 *>(y);
-            u32x4 hi = *reinterpret_cast<const u32x4 *>(y + 8);
-            uint32_t in[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            uint32_t out[8];
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int e0 = 2 * w, e1 = 2 * w + 1; // column offsets 4t + i
-                const float f0 = __builtin_fmaf(scale, acc[e0 >> 2][e0 & 3], bf16_to_f32(in[w] & 0xffffu));
-                const float f1 = __builtin_fmaf(scale, acc[e1 >> 2][e1 & 3], bf16_to_f32(in[w] >> 16));
-                out[w] = f32_to_bf16(f0) | (f32_to_bf16(f1) << 16);
-            }
-            *reinterpret_cast<u32x4 *>(y) = u32x4{out[0], out[1], out[2], out[3]};
-            *reinterpret_cast<u32x4 *>(y + 8) = u32x4{out[4], out[5], out[6], out[7]};
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (cb + e < d_out) {
-                    const float f = __builtin_fmaf(scale, acc[e >> 2][e & 3], bf16_to_f32(y[e]));
-                    y[e] = uint16_t(f32_to_bf16(f));
-                }
-        }
+    for (int i = 0; i < RB; ++i)
+        if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc[i], scale);
+}
+
+template <int DT, int RB, bool VECY, bool VIND, int UPT>
+__device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                            const void *__restrict__ Bv, int r, float scale, void *__restrict__ yv,
+                                            int64_t ldy, int d_out, int ncol_wg, bool vec_b, const int *yrows,
+                                            int vrow0, int nrows, float *vl, int ldl)
+{
+    if (vec_b && (r & 3) == 0)
+        expand_rows_impl<DT, RB, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+                                                        yrows, vrow0, nrows, vl, ldl);
+    else
+        expand_rows_impl<DT, RB, VECY, false, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+                                                         yrows, vrow0, nrows, vl, ldl);
+}
+
+// ----------------------------------------------------------------------------
+// SGMV kernels.  Shrink: one workgroup per (plan block, d_in slice).  Expand:
+// one workgroup per (256 columns, plan block) or (256 columns, plan chunk).
+// ----------------------------------------------------------------------------
+template <int DT, bool VEC, int W, int NSTEP, int RT>
+__global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
+                                                             const lora_blk_desc *__restrict__ blks, int slice_len,
+                                                             float *__restrict__ out, int64_t ldo, int64_t sl_stride)
+{
+    __shared__ float red[W > 1 ? W * RT * 256 : 1];
+    const lora_blk_desc *bd = blks + blockIdx.x;
+    const int c = blockIdx.y;
+    const int xr = bd->rows[threadIdx.x & 15];
+    const int xr0 = bd->rows[0];
+    const int k_begin = c * slice_len;
+    const int k_end = min(d_in, k_begin + slice_len);
+    shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, xr0, reinterpret_cast<const void *>(bd->A), d_in, bd->rank,
+                                        k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red);
+}
+
+template <int DT, int RB, bool VECY, int UPT>
+__global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+                                                          int nsl, const void *__restrict__ descs,
+                                                          void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
+                                                          int ldl)
+{
+    extern __shared__ floatx4 vl4[];
+    if constexpr (RB == 1) {
+        const lora_blk_desc *d = static_cast<const lora_blk_desc *>(descs) + blockIdx.y;
+        expand_rows<DT, 1, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
+                                             d->scale, y,
+                                 ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0, d->n,
+                                 reinterpret_cast<float *>(vl4), ldl);
     } else {
-        float *y = static_cast<float *>(yv) + yrow + cb;
-        if (vec_y && cb + 16 <= d_out) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                floatx4 w = *reinterpret_cast<const floatx4 *>(y + 4 * t);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(scale, acc[t][i], w[i]);
-                *reinterpret_cast<floatx4 *>(y + 4 * t) = w;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (cb + e < d_out) y[e] = __builtin_fmaf(scale, acc[e >> 2][e & 3], y[e]);
-        }
+        const lora_chunk_desc *d = static_cast<const lora_chunk_desc *>(descs) + blockIdx.y;
+        expand_rows<DT, RB, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
+                                              d->scale, y,
+                                  ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0, d->n,
+                                  reinterpret_cast<float *>(vl4), ldl);
     }
 }
 
 // ----------------------------------------------------------------------------
-// Plan access.
+// BGMV: the block is found on the device from the ids.  Workgroup t serves the
+// tokens that share token t's adapter when t is the first of them (the
+// leader); the others exit.  Tokens are taken 16 at a time in token order
+// (pass p takes the group's members 16p .. 16p+15).
 // ----------------------------------------------------------------------------
-struct PlanPtrs {
-    const lora_seg_desc *seg;
-    const int32_t *blk;
-    const int32_t *perm;
+struct Group {
+    int rows[kRows]; // token indices, -1 past n
+    int n;
+    int total; // members of the group from the leader on
+    int leader;
 };
 
-__device__ __forceinline__ void plan_block_rows(const PlanPtrs &p, int b, lora_seg_desc &d, BlockRows &br)
+// All threads: scans ids for members of adapter a (from the leader t on) and
+// fills g.rows with those of rank [16*pass, 16*pass + 16).  Returns false if t
+// is not the first token with id a.  `cnt` is LDS scratch of one int per wave.
+__device__ bool bgmv_group(const int32_t *__restrict__ ids, int T, int t, int a, int pass, Group &grp, int *cnt,
+                           int id0)
 {
-    const int s = p.blk[b];
-    d = p.seg[s];
-    const int p0 = d.start + (b - d.blk0) * kRows;
-    const int n = min(kRows, d.start + d.len - p0);
-    if (threadIdx.x < kRows) {
-        const int mm = threadIdx.x;
-        br.xrow[mm] = mm < n ? p.perm[p0 + mm] : -1;
-        br.vrow[mm] = p0 + mm;
-    }
-    if (threadIdx.x == 0) br.n = n;
-}
-
-// ----------------------------------------------------------------------------
-// SGMV kernels.
-// ----------------------------------------------------------------------------
-template <int DT, bool VEC, int W>
-__global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
-                                                             PlanPtrs plan, float *__restrict__ v, int64_t ldv)
-{
-    __shared__ BlockRows br;
-    __shared__ float red[W * 4 * 64 * 4];
-    lora_seg_desc d;
-    plan_block_rows(plan, blockIdx.x, d, br);
-    __syncthreads();
-    shrink_block<DT, VEC, W>(x, ldx, d_in, reinterpret_cast<const void *>(d.A), d.rank, v, ldv, br, red);
-}
-
-template <int DT>
-__global__ __launch_bounds__(kExpandThreads) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv,
-                                                                     PlanPtrs plan, int nblk, int blocks_per_wg,
-                                                                     void *__restrict__ y, int64_t ldy, int d_out,
-                                                                     bool vec_b, bool vec_y)
-{
-    __shared__ BlockRows br;
-    const int b0 = blockIdx.y * blocks_per_wg;
-    const int b1 = min(nblk, b0 + blocks_per_wg);
-    const int ncol_wg = blockIdx.x * kExpandCols;
-    for (int b = b0; b < b1; ++b) {
-        lora_seg_desc d;
-        __syncthreads();
-        plan_block_rows(plan, b, d, br);
-        __syncthreads();
-        expand_block<DT>(v, ldv, reinterpret_cast<const void *>(d.B), d.rank, d.scale, y, ldy, d_out, ncol_wg, br,
-                         vec_b, vec_y);
-    }
-}
-
-// ----------------------------------------------------------------------------
-// BGMV: one workgroup per token; the first token of each adapter id (the
-// leader) handles every token with that id, 16 at a time, so each adapter is
-// read once per workgroup column; the other workgroups exit at once.
-// ----------------------------------------------------------------------------
-__device__ bool bgmv_is_leader(const int32_t *ids, int t, int a)
-{
-    for (int base = 0; base < t; base += blockDim.x) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int base_rank = 0;
+    bool leader = true;
+    for (int base = 0; base < T; base += blockDim.x) {
         const int tt = base + threadIdx.x;
-        const int hit = (tt < t && ids[tt] == a) ? 1 : 0;
-        if (__syncthreads_or(hit)) return false;
+        // id0 = ids[threadIdx.x], loaded by the caller at kernel entry
+        const int idv = base == 0 ? id0 : (tt < T ? ids[tt] : -2);
+        const bool hit = tt < T && idv == a;
+        if (__syncthreads_or(hit && tt < t)) {
+            leader = false;
+            break;
+        }
+        const bool mem = hit && tt >= t;
+        const uint64_t mask = __ballot(mem);
+        if (lane == 0) cnt[wave] = __popcll(mask);
+        __syncthreads();
+        int before = base_rank;
+        for (int w = 0; w < wave; ++w) before += cnt[w];
+        int chunk_total = 0;
+        for (int w = 0; w < nw; ++w) chunk_total += cnt[w];
+        const int rk = before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+        const int slot = rk - kRows * pass;
+        if (mem && slot >= 0 && slot < kRows) grp.rows[slot] = tt;
+        base_rank += chunk_total;
+        __syncthreads();
     }
+    if (!leader) return false;
+    const int n = min(kRows, max(0, base_rank - kRows * pass));
+    if (threadIdx.x < kRows && threadIdx.x >= n) grp.rows[threadIdx.x] = -1;
+    if (threadIdx.x == 0) {
+        grp.n = n;
+        grp.total = base_rank;
+    }
+    __syncthreads();
     return true;
 }
 
-// Wave 0 gathers up to 16 more tokens with id a, scanning from br.next.
-__device__ void bgmv_gather(const int32_t *ids, int T, int a, BlockRows &br)
-{
-    if ((threadIdx.x >> 6) == 0) {
-        const int lane = threadIdx.x & 63;
-        int pos = br.next, cnt = 0;
-        while (cnt < kRows && pos < T) {
-            const int tt = pos + lane;
-            const bool hit = tt < T && ids[tt] == a;
-            const uint64_t mask = __ballot(hit);
-            const int hits = __popcll(mask);
-            const int take = min(hits, kRows - cnt);
-            const int rk = __popcll(mask & ((uint64_t(1) << lane) - 1));
-            if (hit && rk < take) {
-                br.xrow[cnt + rk] = tt;
-                br.vrow[cnt + rk] = tt;
-            }
-            if (take < hits) {
-                uint64_t mm = mask;
-                for (int i = 0; i < take - 1; ++i) mm &= mm - 1;
-                pos += __builtin_ctzll(mm) + 1;
-                cnt += take;
-                break;
-            }
-            cnt += take;
-            pos += 64;
-        }
-        if (lane >= cnt && lane < kRows) br.xrow[lane] = -1;
-        if (lane == 0) {
-            br.n = cnt;
-            br.next = pos;
-        }
-    }
-}
-
-template <int DT, bool VEC, int W>
+// Which workgroup serves which tokens: SLOT = one workgroup per pool adapter
+// (blockIdx.x = adapter; its tokens are all tokens with that id), else one per
+// token (blockIdx.x = t; it serves its adapter's tokens when it is the first
+// of them).  The adapter tables are read in parallel with the ids scan.
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
 __global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in, int T,
                                                              const int32_t *__restrict__ ids,
                                                              const uint64_t *__restrict__ pool_A,
                                                              const int32_t *__restrict__ pool_rank, int n_adapters,
-                                                             int max_rank, float *__restrict__ v, int64_t ldv)
+                                                             int max_rank, int slice_len, float *__restrict__ out,
+                                                             int64_t ldo, int64_t sl_stride)
 {
-    __shared__ BlockRows br;
-    __shared__ float red[W * 4 * 64 * 4];
-    const int t = blockIdx.x;
-    const int a = ids[t];
+    __shared__ float red[W > 1 ? W * RT * 256 : 1];
+    __shared__ Group grp;
+    __shared__ int cnt[16];
+    const int c = blockIdx.y;
+    const int id0 = int(threadIdx.x) < T ? ids[threadIdx.x] : -2; // first chunk of the ids scan
+    const int t = SLOT ? 0 : int(blockIdx.x);
+    const int a = SLOT ? int(blockIdx.x) : ids[t];
     if (a < 0 || a >= n_adapters) return;
     const int r = pool_rank[a];
-    if (r < 1 || r > max_rank) return;
-    if (!bgmv_is_leader(ids, t, a)) return;
     const void *A = reinterpret_cast<const void *>(pool_A[a]);
-    if (threadIdx.x == 0) br.next = t;
-    __syncthreads();
-    for (;;) {
-        bgmv_gather(ids, T, a, br);
-        __syncthreads();
-        // Read the pass state before shrink_block's barriers: wave 0 rewrites br
-        // for the next pass only after every wave has passed them.
-        const int n = br.n;
-        const bool done = br.next >= T;
-        if (n == 0) break;
-        shrink_block<DT, VEC, W>(x, ldx, d_in, A, r, v, ldv, br, red);
-        if (done) break;
+    if (r < 1 || r > max_rank) return;
+    const int k_begin = c * slice_len;
+    const int k_end = min(d_in, k_begin + slice_len);
+    for (int pass = 0;; ++pass) {
+        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return;
+        const int n = grp.n, total = grp.total;
+        if (n == 0) return;
+        const int xr = grp.rows[threadIdx.x & 15];
+        shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end, out + c * sl_stride,
+                                            ldo, 0, grp.rows, n, red);
+        if (kRows * (pass + 1) >= total) break;
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kExpandThreads) void bgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int T,
-                                                                     const int32_t *__restrict__ ids,
-                                                                     const uint64_t *__restrict__ pool_B,
-                                                                     const int32_t *__restrict__ pool_rank,
-                                                                     const float *__restrict__ pool_alpha,
-                                                                     int n_adapters, int max_rank,
-                                                                     void *__restrict__ y, int64_t ldy, int d_out,
-                                                                     bool vec_b, bool vec_y)
+template <int DT, bool SLOT, bool VECY, int UPT>
+__global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+                                                          int nsl, int T, const int32_t *__restrict__ ids,
+                                                          const uint64_t *__restrict__ pool_B,
+                                                          const int32_t *__restrict__ pool_rank,
+                                                          const float *__restrict__ pool_alpha, int n_adapters,
+                                                          int max_rank, void *__restrict__ y, int64_t ldy, int d_out,
+                                                          bool vec_b, int ldl)
 {
-    __shared__ BlockRows br;
-    const int t = blockIdx.x;
-    const int a = ids[t];
+    extern __shared__ floatx4 vl4[];
+    __shared__ Group grp;
+    __shared__ int cnt[16];
+    const int id0 = int(threadIdx.x) < T ? ids[threadIdx.x] : -2;
+    const int t = SLOT ? 0 : int(blockIdx.x);
+    const int a = SLOT ? int(blockIdx.x) : ids[t];
     if (a < 0 || a >= n_adapters) return;
     const int r = pool_rank[a];
-    if (r < 1 || r > max_rank) return;
-    if (!bgmv_is_leader(ids, t, a)) return;
     const void *B = reinterpret_cast<const void *>(pool_B[a]);
-    const float scale = pool_alpha[a] / float(r);
-    const int ncol_wg = blockIdx.y * kExpandCols;
-    if (threadIdx.x == 0) br.next = t;
-    __syncthreads();
-    for (;;) {
-        bgmv_gather(ids, T, a, br);
-        __syncthreads();
-        if (br.n == 0) break;
-        expand_block<DT>(v, ldv, B, r, scale, y, ldy, d_out, ncol_wg, br, vec_b, vec_y);
-        const bool done = br.next >= T;
-        __syncthreads();
-        if (done) break;
+    const float alpha = pool_alpha[a];
+    if (r < 1 || r > max_rank) return;
+    const float scale = alpha / float(r);
+    for (int pass = 0;; ++pass) {
+        // bgmv_group starts with a barrier, so the previous pass is done with grp and vl
+        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return;
+        const int n = grp.n, total = grp.total;
+        if (n == 0) return;
+        expand_rows<DT, 1, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
+                                            blockIdx.y * kExpandCols, vec_b, grp.rows, -1, n,
+                                            reinterpret_cast<float *>(vl4), ldl);
+        if (kRows * (pass + 1) >= total) break;
     }
 }
 
 // ----------------------------------------------------------------------------
-// Launch helpers.
+// Launch configuration.
 // ----------------------------------------------------------------------------
 int check_launch(const char *what)
 {
@@ -468,97 +689,294 @@ int check_launch(const char *what)
     return LORA_OK;
 }
 
-PlanPtrs plan_ptrs(const PlanView &p)
+const lora_blk_desc *plan_blocks(const PlanView &p)
 {
-    PlanPtrs q;
-    q.seg = reinterpret_cast<const lora_seg_desc *>(p.dev + p.h->seg_offset);
-    q.blk = reinterpret_cast<const int32_t *>(p.dev + p.h->blk_offset);
-    q.perm = reinterpret_cast<const int32_t *>(p.dev + p.h->perm_offset);
-    return q;
+    return reinterpret_cast<const lora_blk_desc *>(p.dev + p.h->blk_offset);
 }
 
-template <int DT, bool VEC>
-void sgmv_shrink_dispatch(hipStream_t s, const ShrinkArgs &a, const PlanPtrs &q, int nblk)
+const lora_chunk_desc *plan_chunks(const PlanView &p)
 {
-    // Few blocks (decode-like plans): more waves per workgroup to keep enough
-    // loads in flight on the CUs that do get work.
-    if (nblk < 128)
-        sgmv_shrink_kernel<DT, VEC, 16><<<nblk, 16 * 64, 0, s>>>(a.x, a.ldx, a.d_in, q, a.v, a.ldv);
-    else
-        sgmv_shrink_kernel<DT, VEC, 4><<<nblk, 4 * 64, 0, s>>>(a.x, a.ldx, a.d_in, q, a.v, a.ldv);
+    return reinterpret_cast<const lora_chunk_desc *>(p.dev + p.h->chunk_offset);
 }
 
-template <int DT, bool VEC>
-void bgmv_shrink_dispatch(hipStream_t s, const ShrinkArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_A,
-                          const int32_t *pool_rank, int32_t n_adapters, int32_t max_rank)
+int rank_tiles(int max_rank) { return max_rank <= 16 ? 1 : (max_rank <= 32 ? 2 : 4); }
+
+// LDS row pitch (floats) of the staged v rows
+int lds_pitch(int max_rank) { return (max_rank + 3) / 4 * 4; }
+
+// Template dispatch over (dtype, vec, rank tiles) for a shrink launcher.
+template <template <int, bool, int> class L, typename... Args>
+void dispatch_shrink(int dtype, bool vec, int rt, Args &&...args)
 {
-    bgmv_shrink_kernel<DT, VEC, 16><<<T, 16 * 64, 0, s>>>(a.x, a.ldx, a.d_in, T, ids, pool_A, pool_rank, n_adapters,
-                                                          max_rank, a.v, a.ldv);
+    if (dtype == LORA_BF16) {
+        if (vec) {
+            if (rt == 1) L<LORA_BF16, true, 1>::run(args...);
+            else if (rt == 2) L<LORA_BF16, true, 2>::run(args...);
+            else L<LORA_BF16, true, 4>::run(args...);
+        } else {
+            if (rt == 1) L<LORA_BF16, false, 1>::run(args...);
+            else if (rt == 2) L<LORA_BF16, false, 2>::run(args...);
+            else L<LORA_BF16, false, 4>::run(args...);
+        }
+    } else {
+        if (vec) L<LORA_F32, true, 4>::run(args...);
+        else L<LORA_F32, false, 4>::run(args...);
+    }
+}
+
+// d_in slicing for the split shrink: enough workgroups to fill the chip, each
+// slice a whole number of 4-wave chunks, at most kMaxSlices slices.
+struct Split {
+    int kc, slice_len, nstep;
+};
+
+Split choose_split(int d_in, int units, int dtype)
+{
+    const int kstep = dtype == LORA_BF16 ? 128 : 64;
+    const int chunk = 4 * kstep; // one step per wave
+    const int max_kc = (d_in + chunk - 1) / chunk;
+    int kc = (1024 + units - 1) / (units < 1 ? 1 : units);
+    kc = kc < 1 ? 1 : (kc > max_kc ? max_kc : kc);
+    kc = kc > kMaxSlices ? kMaxSlices : kc;
+    int sl = (d_in + kc - 1) / kc;
+    sl = (sl + chunk - 1) / chunk * chunk;
+    kc = (d_in + sl - 1) / sl;
+    return Split{kc, sl, sl >= 2 * chunk ? 2 : 1};
+}
+
+size_t split_ws_bytes(int d_in, int rows, int max_rank)
+{
+    int kc = (d_in + 255) / 256;
+    kc = kc > kMaxSlices ? kMaxSlices : kc;
+    const size_t ld = size_t((max_rank + 3) / 4 * 4);
+    return size_t(kc) * size_t(rows) * ld * sizeof(float) + 256;
+}
+
+template <int DT, bool VEC, int RT> struct SgmvShrinkL {
+    static void run(hipStream_t s, const void *x, int64_t ldx, int d_in, const lora_blk_desc *blks, int nblk,
+                    int kc, int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride)
+    {
+        const dim3 grid(nblk, kc);
+        // register budget: 1024-thread workgroups have 128 VGPRs per lane, so
+        // hold two k-steps of fragments only for one rank tile
+        if (full)
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT>, grid, dim3(1024), 0, s, x, ldx, d_in,
+                          blks, slice_len, out, ldo, sl_stride);
+        else if (nstep == 2 && RT < 4)
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 2, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, slice_len,
+                          out, ldo, sl_stride);
+        else
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 1, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, slice_len,
+                          out, ldo, sl_stride);
+    }
+};
+
+template <int DT, bool VEC, int RT> struct BgmvShrinkL {
+    static void run(hipStream_t s, const void *x, int64_t ldx, int d_in, int T, const int32_t *ids,
+                    const uint64_t *pool_A, const int32_t *pool_rank, int n_adapters, int max_rank, bool slot, int kc,
+                    int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride)
+    {
+        const dim3 grid(slot ? n_adapters : T, kc);
+        if (slot) {
+            if (full)
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, true>, grid, dim3(1024), 0, s, x,
+                              ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo,
+                              sl_stride);
+            else if (nstep == 2 && RT < 4)
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, true>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
+                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+            else
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, true>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
+                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+        } else {
+            if (full)
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, false>, grid, dim3(1024), 0, s, x,
+                              ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo,
+                              sl_stride);
+            else if (nstep == 2 && RT < 4)
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, false>, grid, dim3(256), 0, s, x, ldx, d_in, T,
+                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+            else
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, false>, grid, dim3(256), 0, s, x, ldx, d_in, T,
+                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+        }
+    }
+};
+
+// One workgroup per pool adapter when the pool is not much larger than the
+// batch; else one per token.
+bool slot_major(int T, int n_adapters) { return n_adapters <= 2 * T; }
+
+// float4 units of staged v per thread for RB blocks of 16 rows at pitch ldl
+int units_per_thread(int rb, int ldl) { const int u = (rb * kRows * (ldl / 4) + 255) / 256; return u <= 1 ? 1 : (u <= 2 ? 2 : 4); }
+
+template <int DT, int RB, bool VECY>
+void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                    const void *descs, int ndesc, int ldl)
+{
+    const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
+    const size_t shm = (size_t(RB) * kRows * ldl + 4) * sizeof(float);
+    const dim3 grid(ncol, ndesc);
+    switch (units_per_thread(RB, ldl)) {
+    case 1:
+        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    case 2:
+        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    default:
+        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl);
+    }
+}
+
+template <int DT, int RB>
+void sgmv_expand_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv, int64_t sl_stride,
+                     int nsl, const void *descs, int ndesc, int ldl)
+{
+    if (vecy) sgmv_expand_go<DT, RB, true>(s, a, v, ldv, sl_stride, nsl, descs, ndesc, ldl);
+    else sgmv_expand_go<DT, RB, false>(s, a, v, ldv, sl_stride, nsl, descs, ndesc, ldl);
+}
+
+void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                        const PlanView &p)
+{
+    const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
+    const int ldl = lds_pitch(p.h->max_rank);
+    const bool vecy = a.vec_y && a.d_out % 16 == 0;
+    // chunks of up to 64 rows reuse B four times; use them when they still give
+    // enough workgroups and their staged v rows fit (64 rows x 64 ranks)
+    const bool chunked = p.h->num_chunks * ncol >= 1024 && ldl <= 64;
+    if (chunked) {
+        const void *d = plan_chunks(p);
+        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16, 4>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl);
+        else sgmv_expand_go2<LORA_F32, 4>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl);
+    } else {
+        const void *d = plan_blocks(p);
+        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16, 1>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
+        else sgmv_expand_go2<LORA_F32, 1>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
+    }
+}
+
+template <int DT, bool SLOT, bool VECY>
+void bgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                    int T, const int32_t *ids, const uint64_t *pool_B, const int32_t *pool_rank,
+                    const float *pool_alpha, int n_adapters, int max_rank)
+{
+    const dim3 grid(SLOT ? n_adapters : T, (a.d_out + kExpandCols - 1) / kExpandCols);
+    const int ldl = lds_pitch(max_rank);
+    const size_t shm = (size_t(kRows) * ldl + 4) * sizeof(float);
+    switch (units_per_thread(1, ldl)) {
+    case 1:
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    case 2:
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    default:
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+    }
+}
+
+void bgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                        int T, const int32_t *ids, const uint64_t *pool_B, const int32_t *pool_rank,
+                        const float *pool_alpha, int n_adapters, int max_rank)
+{
+    const bool slot = slot_major(T, n_adapters);
+    const bool vecy = a.vec_y && a.d_out % 16 == 0;
+#define LORA_BGMV_EXPAND(DT_, SLOT_, VECY_)                                                                            \
+    bgmv_expand_go<DT_, SLOT_, VECY_>(s, a, v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, \
+                                      max_rank)
+    if (a.dtype == LORA_BF16) {
+        if (slot) { if (vecy) LORA_BGMV_EXPAND(LORA_BF16, true, true); else LORA_BGMV_EXPAND(LORA_BF16, true, false); }
+        else { if (vecy) LORA_BGMV_EXPAND(LORA_BF16, false, true); else LORA_BGMV_EXPAND(LORA_BF16, false, false); }
+    } else {
+        if (slot) { if (vecy) LORA_BGMV_EXPAND(LORA_F32, true, true); else LORA_BGMV_EXPAND(LORA_F32, true, false); }
+        else { if (vecy) LORA_BGMV_EXPAND(LORA_F32, false, true); else LORA_BGMV_EXPAND(LORA_F32, false, false); }
+    }
+#undef LORA_BGMV_EXPAND
 }
 
 } // namespace
+
+size_t combined_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
+{
+    return split_ws_bytes(d_in, T, max_rank);
+}
 
 int launch_sgmv_shrink(hipStream_t s, const ShrinkArgs &a, const PlanView &p)
 {
     const int nblk = p.h->num_blocks;
     if (nblk == 0) return LORA_OK;
-    const PlanPtrs q = plan_ptrs(p);
-    if (a.dtype == LORA_BF16) {
-        if (a.vec) sgmv_shrink_dispatch<LORA_BF16, true>(s, a, q, nblk);
-        else sgmv_shrink_dispatch<LORA_BF16, false>(s, a, q, nblk);
-    } else {
-        if (a.vec) sgmv_shrink_dispatch<LORA_F32, true>(s, a, q, nblk);
-        else sgmv_shrink_dispatch<LORA_F32, false>(s, a, q, nblk);
-    }
+    dispatch_shrink<SgmvShrinkL>(a.dtype, a.vec, rank_tiles(p.h->max_rank), s, a.x, a.ldx, a.d_in, plan_blocks(p),
+                                 nblk, 1, a.d_in, 2, true, a.v, a.ldv, int64_t(0));
     return check_launch("sgmv_shrink");
 }
 
 int launch_sgmv_expand(hipStream_t s, const ExpandArgs &a, const PlanView &p)
 {
+    if (p.h->num_blocks == 0) return LORA_OK;
+    sgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, p);
+    return check_launch("sgmv_expand");
+}
+
+int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+{
     const int nblk = p.h->num_blocks;
     if (nblk == 0) return LORA_OK;
-    const PlanPtrs q = plan_ptrs(p);
-    const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
-    // Let a workgroup walk several consecutive blocks (B tile stays in L1/L2)
-    // while keeping at least ~1024 workgroups in flight.
-    int bpw = (nblk * ncol) / 1024;
-    bpw = bpw < 1 ? 1 : (bpw > 8 ? 8 : bpw);
-    const dim3 grid(ncol, (nblk + bpw - 1) / bpw);
-    if (a.dtype == LORA_BF16)
-        sgmv_expand_kernel<LORA_BF16><<<grid, kExpandThreads, 0, s>>>(a.v, a.ldv, q, nblk, bpw, a.y, a.ldy, a.d_out,
-                                                                     a.vec_b, a.vec_y);
-    else
-        sgmv_expand_kernel<LORA_F32><<<grid, kExpandThreads, 0, s>>>(a.v, a.ldv, q, nblk, bpw, a.y, a.ldy, a.d_out,
-                                                                    a.vec_b, a.vec_y);
-    return check_launch("sgmv_expand");
+    const Split sp = choose_split(sa.d_in, nblk, sa.dtype);
+    float *vp = static_cast<float *>(ws);
+    const int64_t ldw = (p.h->max_rank + 3) / 4 * 4;
+    const int64_t sl_stride = int64_t(p.h->num_sorted) * ldw;
+    dispatch_shrink<SgmvShrinkL>(sa.dtype, sa.vec, rank_tiles(p.h->max_rank), s, sa.x, sa.ldx, sa.d_in,
+                                 plan_blocks(p), nblk, sp.kc, sp.slice_len, sp.nstep, false, vp, ldw, sl_stride);
+    int st = check_launch("sgmv shrink");
+    if (st) return st;
+    sgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, p);
+    return check_launch("sgmv expand");
 }
 
 int launch_bgmv_shrink(hipStream_t s, const ShrinkArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_A,
                        const int32_t *pool_rank, int32_t n_adapters, int32_t max_rank)
 {
-    if (a.dtype == LORA_BF16) {
-        if (a.vec) bgmv_shrink_dispatch<LORA_BF16, true>(s, a, T, ids, pool_A, pool_rank, n_adapters, max_rank);
-        else bgmv_shrink_dispatch<LORA_BF16, false>(s, a, T, ids, pool_A, pool_rank, n_adapters, max_rank);
-    } else {
-        if (a.vec) bgmv_shrink_dispatch<LORA_F32, true>(s, a, T, ids, pool_A, pool_rank, n_adapters, max_rank);
-        else bgmv_shrink_dispatch<LORA_F32, false>(s, a, T, ids, pool_A, pool_rank, n_adapters, max_rank);
-    }
+    if (n_adapters == 0) return LORA_OK;
+    dispatch_shrink<BgmvShrinkL>(a.dtype, a.vec, rank_tiles(max_rank), s, a.x, a.ldx, a.d_in, T, ids, pool_A,
+                                 pool_rank, n_adapters, max_rank, slot_major(T, n_adapters), 1, a.d_in, 2, true, a.v,
+                                 a.ldv, int64_t(0));
     return check_launch("bgmv_shrink");
 }
 
 int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_B,
                        const int32_t *pool_rank, const float *pool_alpha, int32_t n_adapters, int32_t max_rank)
 {
-    const dim3 grid(T, (a.d_out + kExpandCols - 1) / kExpandCols);
-    if (a.dtype == LORA_BF16)
-        bgmv_expand_kernel<LORA_BF16><<<grid, kExpandThreads, 0, s>>>(a.v, a.ldv, T, ids, pool_B, pool_rank, pool_alpha,
-                                                                     n_adapters, max_rank, a.y, a.ldy, a.d_out,
-                                                                     a.vec_b, a.vec_y);
-    else
-        bgmv_expand_kernel<LORA_F32><<<grid, kExpandThreads, 0, s>>>(a.v, a.ldv, T, ids, pool_B, pool_rank, pool_alpha,
-                                                                    n_adapters, max_rank, a.y, a.ldy, a.d_out,
-                                                                    a.vec_b, a.vec_y);
+    if (n_adapters == 0) return LORA_OK;
+    bgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank);
     return check_launch("bgmv_expand");
+}
+
+int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                int32_t n_adapters, int32_t max_rank, void *ws)
+{
+    if (n_adapters == 0) return LORA_OK;
+    const bool slot = slot_major(T, n_adapters);
+    // units = expected groups: the pool size (slot-major) or T, both upper bounds
+    const Split sp = choose_split(sa.d_in, slot ? n_adapters : T, sa.dtype);
+    float *vp = static_cast<float *>(ws);
+    const int64_t ldw = (max_rank + 3) / 4 * 4;
+    const int64_t sl_stride = int64_t(T) * ldw;
+    dispatch_shrink<BgmvShrinkL>(sa.dtype, sa.vec, rank_tiles(max_rank), s, sa.x, sa.ldx, sa.d_in, T, ids, pool_A,
+                                 pool_rank, n_adapters, max_rank, slot, sp.kc, sp.slice_len, sp.nstep, false, vp, ldw,
+                                 sl_stride);
+    int st = check_launch("bgmv shrink");
+    if (st) return st;
+    bgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank);
+    return check_launch("bgmv expand");
 }
 
 } // namespace lora

@@ -98,6 +98,29 @@ class GpuCase:
         self.plan = plan
         return v.cpu().numpy().astype(np.float64), plan
 
+    def run(self, path, stream=None):
+        """path: sgmv / bgmv (one combined call) or sgmv_split / bgmv_split
+        (separate shrink and expand calls).  Returns (v or None, plan or None)."""
+        if path == "sgmv_split":
+            return self.run_sgmv(stream)
+        if path == "bgmv_split":
+            return self.run_bgmv(stream), None
+        torch = self.torch
+        p = self.prob
+        if path == "sgmv":
+            plan = B.Plan(max(p.T, 1)).build(p.ids, self.pool).upload(stream)
+            ws = B.workspace(B.LORA_OP_SGMV, max(p.T, 1), p.d_in, p.d_out, max(p.max_rank, 1))
+            B.sgmv(self.x, plan, self.y, ws, self.dt, stream=stream)
+            torch.cuda.synchronize()
+            self.plan = plan
+            return None, plan
+        if path == "bgmv":
+            ws = B.workspace(B.LORA_OP_BGMV, max(p.T, 1), p.d_in, p.d_out, max(p.max_rank, 1))
+            B.bgmv(self.x, self.ids_dev, self.pool, self.y, ws, self.dt, stream=stream)
+            torch.cuda.synchronize()
+            return None, None
+        raise ValueError(path)
+
     def run_bgmv(self, stream=None):
         torch = self.torch
         v = torch.full((max(self.prob.T, 1), self.ldv), float("nan"), device="cuda")

@@ -62,22 +62,16 @@ class HostPlan:
         return self.buf.ctypes.data
 
     def header(self):
-        b = self.buf.view(np.uint8)
-        i32 = b[:32].view(np.int32)
-        u64 = b[32:64].view(np.uint64)
-        return dict(magic=int(b[:4].view(np.uint32)[0]), T=int(i32[1]), Tp=int(i32[2]), S=int(i32[3]),
-                    nblk=int(i32[4]), max_rank=int(i32[5]), max_len=int(i32[6]), seg=int(u64[0]),
-                    blk=int(u64[1]), perm=int(u64[2]), used=int(u64[3]))
+        h = B.plan_header(self.buf.view(np.uint8))
+        return dict(magic=h["magic"], T=h["num_tokens"], Tp=h["num_sorted"], S=h["num_segments"],
+                    nblk=h["num_blocks"], max_rank=h["max_rank"], max_len=h["max_len"], seg=h["seg_offset"],
+                    blk=h["blk_offset"], perm=h["perm_offset"], used=h["bytes_used"], nchunk=h["num_chunks"],
+                    chunk=h["chunk_offset"])
 
     def arrays(self):
-        h = self.header()
-        b = self.buf.view(np.uint8)
-        desc = np.frombuffer(b[h["seg"]: h["seg"] + 40 * h["S"]].tobytes(), dtype=np.dtype([
-            ("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
-            ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")]))
-        blk = b[h["blk"]: h["blk"] + 4 * h["nblk"]].view(np.int32)
-        perm = b[h["perm"]: h["perm"] + 4 * h["Tp"]].view(np.int32)
-        return desc, blk, perm
+        h = B.plan_header(self.buf.view(np.uint8))
+        a = B.plan_arrays(self.buf.view(np.uint8), h)
+        return a["desc"], a["blocks"], a["perm"], a["chunks"]
 
 
 def make_tables(N, rng, ranks=None):
@@ -110,7 +104,7 @@ def test_plan_matches_oracle_segments(T, N, none_p, seed):
     assert st == 0, B.last_error()
     perm_o, indptr_o, adapter_o = oracle.segments(ids, N)
     h = plan.header()
-    desc, blk, perm = plan.arrays()
+    desc, blk, perm, chunks = plan.arrays()
     assert h["magic"] == B.PLAN_MAGIC and h["T"] == T and h["Tp"] == len(perm_o)
     assert h["S"] == len(adapter_o)
     assert np.array_equal(perm, perm_o)
@@ -124,7 +118,32 @@ def test_plan_matches_oracle_segments(T, N, none_p, seed):
     nb = (np.diff(indptr_o) + 15) // 16
     assert h["nblk"] == int(nb.sum())
     assert np.array_equal(desc["blk0"], np.concatenate([[0], np.cumsum(nb)[:-1]]).astype(np.int32) if len(nb) else [])
-    assert np.array_equal(blk, np.repeat(np.arange(len(nb)), nb))
+    # block descriptors: segment, adapter fields copied, 16-row windows of perm
+    seg_of_blk = np.repeat(np.arange(len(nb)), nb)
+    assert np.array_equal(blk["seg"], seg_of_blk)
+    assert h["blk"] % 128 == 0
+    for b, sgi in enumerate(seg_of_blk):
+        d = desc[sgi]
+        q0 = 16 * (b - d["blk0"])
+        n = min(16, d["len"] - q0)
+        assert blk["n"][b] == n and blk["p0"][b] == d["start"] + q0
+        assert blk["A"][b] == d["A"] and blk["B"][b] == d["B"] and blk["rank"][b] == d["rank"]
+        assert blk["scale"][b] == d["scale"]
+        assert blk["rows"][b][:n].tolist() == perm_o[d["start"] + q0: d["start"] + q0 + n].tolist()
+        assert (blk["rows"][b][n:] == -1).all()
+    # chunks: consecutive runs of up to 4 blocks (64 rows) inside one segment, covering every row once
+    want = [(si, int(d["blk0"]) + i, min(4, int(nbs) - i)) for si, (d, nbs) in enumerate(zip(desc, nb))
+            for i in range(0, int(nbs), 4)]
+    assert h["nchunk"] == len(want) and h["chunk"] % 64 == 0
+    for ch, (si, fb, cnt) in zip(chunks, want):
+        d = desc[si]
+        q0 = 16 * (fb - d["blk0"])
+        n = min(64, d["len"] - q0)
+        assert (ch["seg"], ch["first_blk"], ch["nblk"]) == (si, fb, cnt)
+        assert ch["n"] == n and ch["p0"] == d["start"] + q0 and ch["rank"] == d["rank"]
+        assert ch["A"] == d["A"] and ch["B"] == d["B"] and ch["scale"] == d["scale"]
+        assert ch["rows"][:n].tolist() == perm_o[d["start"] + q0: d["start"] + q0 + n].tolist()
+        assert (ch["rows"][n:] == -1).all()
     assert h["max_rank"] == (int(ranks[adapter_o].max()) if len(adapter_o) else 0)
     assert h["used"] <= plan.nbytes
 
@@ -225,6 +244,30 @@ def test_fused_argument_errors():
     assert f(None, 1, None, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -1
     need = B.lora_workspace_bytes(B.LORA_OP_FUSED, 8, 256, 256, 8)
     assert need >= 8 * 16 * 4
+
+
+def test_combined_argument_errors():
+    plan = _valid_plan()
+    sg = B.lora_sgmv
+    need = B.lora_workspace_bytes(B.LORA_OP_SGMV, 8, 256, 256, 8)
+    assert need >= 8 * 8 * 4
+    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need - 1) == -6
+    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, None, need) == -6
+    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX + 8, need) == -4
+    assert sg(None, 1, None, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need) == -1
+    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, None, 256, 256, FX, need) == -1
+    assert sg(None, 9, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need) == -5
+    empty = HostPlan(0)
+    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
+    assert sg(None, 1, None, 0, 0, empty.ptr, None, None, 0, 0, None, 0) == 0
+    bg = B.lora_bgmv
+    needb = B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, 4096, 4096, 16)
+    assert needb >= 64 * 16 * 4
+    assert bg(None, 1, 0, None, 0, 0, None, None, None, None, None, 0, 16, None, 0, 0, None, 0) == 0
+    assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 4096, 4096, FX, needb - 1) == -6
+    assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, None, FX, FX, 32, 16, FX, 4096, 4096, FX, needb) == -1
+    assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 300, FX, 4096, 4096, FX, needb) == -2
+    assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 100, 4096, FX, needb) == -1
 
 
 def test_workspace_bytes():

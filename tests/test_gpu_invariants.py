@@ -13,7 +13,7 @@ from segmented_gather_gemm_lora_amd import binding as B
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["sgmv", "bgmv"]
+PATHS = ["sgmv", "bgmv", "sgmv_split", "bgmv_split"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -24,7 +24,7 @@ def _gpu():
 
 def run(prob, path, y_init="stored"):
     c = GpuCase(prob, y_init=y_init)
-    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    c.run(path)
     return c
 
 
@@ -83,7 +83,9 @@ def test_zero_adapter_leaves_y_bitwise(dtype, which, path):
 @pytest.mark.parametrize("path", PATHS)
 def test_mixed_equals_per_request(path):
     """A batch of mixed adapters equals each adapter's tokens run alone
-    (decode workload; same kernels and split, so bitwise)."""
+    (decode workload).  The separate shrink/expand entries sum d_in the same
+    way whatever the batch, so they must agree bitwise; the combined calls
+    slice d_in by batch size, so they agree within the tolerance."""
     prob = make_config(2)
     say(f"case mixed-vs-alone {path}")
     full = bits(run(prob, path))
@@ -97,7 +99,10 @@ def test_mixed_equals_per_request(path):
         sub.x = prob.x[rows]
         sub.y_in = prob.y_in[rows]
         alone[rows] = bits(run(sub, path))
-    assert np.array_equal(full, alone)
+    if path.endswith("_split"):
+        assert np.array_equal(full, alone)
+    else:
+        assert_close(decode(full, "bf16"), decode(alone, "bf16"), "bf16", "mixed vs alone")
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -129,7 +134,7 @@ def test_scale_doubling_bitwise(dtype, path):
     assert np.abs(y1).max() > 0
 
 
-@pytest.mark.parametrize("path,k", [("sgmv", 3), ("sgmv", 4), ("bgmv", 2)])
+@pytest.mark.parametrize("path,k", [("sgmv", 3), ("sgmv", 4), ("bgmv", 2), ("sgmv_split", 3), ("bgmv_split", 2)])
 def test_determinism(path, k):
     prob = make_config(k)
     say(f"case determinism k={k} {path}")
@@ -158,10 +163,7 @@ def test_side_stream(path):
     c = GpuCase(prob)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        if path == "sgmv":
-            c.run_sgmv(stream=s)
-        else:
-            c.run_bgmv(stream=s)
+        c.run(path, stream=s)
     torch.cuda.synchronize()
     y_ref, _ = oracle.lora_forward(prob, nthreads=16)
     assert_close(c.y_out(), y_ref, "bf16", "side stream")

@@ -47,36 +47,38 @@ def check_case(prob, path, zero_base, key=None):
     say(f"case {prob.name} T={prob.T} d_in={prob.d_in} d_out={prob.d_out} dtype={prob.dtype} path={path} "
         f"zero_base={zero_base}")
     c = GpuCase(prob, y_init="zero" if zero_base else "stored")
-    if path == "sgmv":
-        v, plan = c.run_sgmv()
-        perm = plan.arrays()["perm"]
-        vrows = perm
-    else:
-        v = c.run_bgmv()
-        vrows = np.nonzero(prob.ids >= 0)[0]
+    v, plan = c.run(path)
     y = c.y_out()
     y_ref, v_ref = oracle_ref(key, prob, zero_base) if key else oracle.lora_forward(
         _with_zero_base(prob) if zero_base else prob, want_v=True, nthreads=16)
     worst = assert_close(y, y_ref, prob.dtype, f"{prob.name}/{path}/y")
+    none = np.nonzero(prob.ids < 0)[0]
+    if len(none):  # rows of tokens without an adapter are untouched (bitwise)
+        y0 = decode(c.y_host_in, prob.dtype)
+        assert np.array_equal(y[none], y0[none])
+    if v is None:
+        return worst
     # v: rows in sorted order (SGMV) or token order (BGMV)
-    vv = v[: len(vrows)] if path == "sgmv" else v[vrows]
-    tok = perm if path == "sgmv" else vrows
+    if path == "sgmv_split":
+        perm = plan.arrays()["perm"]
+        vv, tok = v[: len(perm)], perm
+    else:
+        tok = np.nonzero(prob.ids >= 0)[0]
+        vv = v[tok]
     ranks = prob.ranks[prob.ids[tok]] if len(tok) else np.zeros(0, dtype=np.int32)
     bound = v_bound(prob, tok, prob.ids[tok])
     for i, t in enumerate(tok):
         r = int(ranks[i])
         err = np.abs(vv[i, :r] - v_ref[t, :r])
         assert (err <= bound[i, :r] + 1e-6 * np.abs(v_ref[t, :r])).all(), (prob.name, path, "v", t)
-    # rows of tokens without an adapter are untouched (bitwise)
-    none = np.nonzero(prob.ids < 0)[0]
-    if len(none):
-        y0 = decode(c.y_host_in, prob.dtype)
-        assert np.array_equal(y[none], y0[none])
     return worst
 
 
+ALL_PATHS = ["sgmv", "bgmv", "sgmv_split", "bgmv_split"]
+
+
 @pytest.mark.parametrize("zero_base", [False, True], ids=["y_preset", "y_zero"])
-@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_named_workloads(k, path, zero_base):
     prob = make_config(k)
@@ -87,6 +89,7 @@ def test_named_workloads(k, path, zero_base):
 def test_named_workloads_other_seeds(k, seed):
     prob = make_config(k, seed=seed)
     check_case(prob, "sgmv" if k != 2 else "bgmv", False)
+    check_case(prob, "sgmv_split" if k != 2 else "bgmv_split", False)
 
 
 SHAPES = [
@@ -103,7 +106,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 def test_shapes(shape, path):
     name, dt, T, d_in, d_out, ranks, none_frac, seed = shape
@@ -120,14 +123,14 @@ def test_shapes(shape, path):
     check_case(prob, path, True)
 
 
-@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_all_tokens_without_adapter(dtype, path):
     prob = make_problem(name="none", dtype=dtype, ids=[-1] * 20, ranks=[4, 8], alphas=[1.0, 1.0], d_in=64, d_out=48,
                         seed=1)
     say(f"case all-none {dtype} {path}")
     c = GpuCase(prob)
-    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    c.run(path)
     assert np.array_equal(B_bits(c), prob.y_in)
 
 
@@ -152,19 +155,22 @@ def test_empty_batch(dtype, path):
     x = torch.zeros((0, 64), dtype=B.torch_dtype(dtype), device="cuda")
     y = torch.zeros((0, 48), dtype=B.torch_dtype(dtype), device="cuda")
     v = torch.zeros((1, 4), device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
     if path == "sgmv":
         plan = B.Plan(1).build(prob.ids, pool).upload()
         assert plan.header()["num_sorted"] == 0
         B.sgmv_shrink(x, plan, v, dtype)
         B.sgmv_expand(v, plan, y, dtype)
+        B.sgmv(x, plan, y, ws, dtype)
     else:
         ids = torch.zeros(0, dtype=torch.int32, device="cuda")
         B.bgmv_shrink(x, ids, pool, v, dtype)
         B.bgmv_expand(v, ids, pool, y, dtype)
+        B.bgmv(x, ids, pool, y, ws, dtype)
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_integer_bitwise(seed, dtype, path):
@@ -173,13 +179,13 @@ def test_integer_bitwise(seed, dtype, path):
     prob = make_integer_problem(seed=seed, dtype=dtype, T=40, d_in=16, d_out=16, n_adapters=3, none_frac=0.1)
     say(f"case integer seed={seed} {dtype} {path}")
     c = GpuCase(prob)
-    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    c.run(path)
     y = c.y_out()
     y_ref, _ = oracle.lora_forward(prob)
     assert np.array_equal(y, y_ref)
 
 
-@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_integer_bitwise_larger(dtype, path):
     """Larger integer case (d_in 200, ranks 1..4, d_out 333): fp32 sums are
@@ -189,7 +195,7 @@ def test_integer_bitwise_larger(dtype, path):
     prob = make_integer_problem(seed=11, dtype=dtype, T=70, d_in=200, d_out=333, n_adapters=5, none_frac=0.1)
     say(f"case integer-larger {dtype} {path}")
     c = GpuCase(prob)
-    c.run_sgmv() if path == "sgmv" else c.run_bgmv()
+    c.run(path)
     y_ref, _ = oracle.lora_forward(prob)
     from segmented_gather_gemm_lora_amd import binding as B
 
