@@ -162,6 +162,54 @@ def cpu_baseline(prob, budget_s):
             "sample": f"{desc} ({el:.1f} s, fp64, OpenMP over tokens)"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+KERNEL_SOURCES = {"fused": ["segmented_gather_gemm_lora_amd/csrc/fused.hip"]}
+COPY_CAL_BYTES = 256 << 20
+
+
+def kernel_source_digest(dominant):
+    """sha256 over the source files that define the kernel, so that recorded
+    counter figures are used only for the code they were taken on."""
+    import hashlib
+
+    files = KERNEL_SOURCES.get(dominant, ["segmented_gather_gemm_lora_amd/csrc/sgmv_bgmv.hip"])
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel, dominant):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE and WRITE_SIZE
+    counter runs recorded in profiles/hbm_traffic.md (each scaled by the
+    factor the same counter gives for a copy of known size), or None when no
+    figures exist or the kernel source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            line = next(l for l in fh if l.startswith("traffic-json: "))
+        rec = json.loads(line[len("traffic-json: "):])
+    except (OSError, StopIteration, ValueError):
+        return None
+    e = rec.get("entries", {}).get(f"{workload}/{kernel}")
+    if not e or e.get("source_sha256") != kernel_source_digest(dominant):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def copy_calibration(reps=8):
+    """Plain device-to-device copies of COPY_CAL_BYTES each: the known-size
+    kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +219,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain copies of a known size (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -186,6 +236,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        copy_calibration()
+        return
     B.load()
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
@@ -253,6 +306,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
     roof["kernel"] = {"shrink": f"{kind}_shrink_kernel", "expand": f"{kind}_expand_kernel",
                       "fused": "fused_linear"}[dominant]
+    roof["traffic"] = recorded_traffic(CONFIG_NAMES[k], roof["kernel"], dominant)
     roof["algorithmic_bytes_per_launch"] = round(dom_bytes)
     roof["avg_launch_us"] = round(dom_us, 3)
 
