@@ -88,10 +88,13 @@ typedef enum lora_dtype {
  * A plan lives in one contiguous buffer with the same layout on the host and
  * the device, so a single copy moves it:
  *
- *   [lora_plan_header][lora_seg_desc x S][lora_blk_desc x n_blocks][int32 perm x T']
- *   [lora_chunk_desc x n_chunks]
+ *   [lora_plan_header][lora_seg_desc x S][lora_blk_desc x n_blocks][int32 perm x T]
+ *   [lora_chunk_desc x n_chunks][int32 segidx x T']
  *
- * perm[p] is the original token index at sorted position p.  Segment s covers
+ * perm[p] is the original token index at sorted position p (p < T'); the
+ * tokens without an adapter follow in their original order (perm[T' .. T)),
+ * for the fused entry, which writes every row.  segidx[p] is the segment of
+ * sorted position p.  Segment s covers
  * sorted positions [start, start + len).  The block list cuts every segment
  * into blocks of LORA_PLAN_ROW_BLOCK rows (the last one ragged); segment s
  * owns blocks [blk0, blk0 + ceil(len/16)).  A block descriptor repeats what a
@@ -135,7 +138,8 @@ typedef struct lora_plan_header {
     uint64_t perm_offset; /* byte offset of perm */
     uint64_t bytes_used;  /* bytes from the start of the buffer that hold the plan */
     uint64_t chunk_offset; /* byte offset of the lora_chunk_desc array (64-byte aligned) */
-    uint64_t reserved[3];
+    uint64_t segidx_offset; /* byte offset of segidx (16-byte aligned) */
+    uint64_t reserved[2];
 } lora_plan_header; /* 96 bytes */
 
 /* A chunk is up to this many consecutive blocks of one segment (64 rows): the

@@ -333,7 +333,7 @@ def plan_header(h: np.ndarray) -> dict:
             "num_segments": int(i32[3]), "num_blocks": int(i32[4]), "max_rank": int(i32[5]),
             "max_len": int(i32[6]), "num_chunks": int(i32[7]), "seg_offset": int(u64[0]),
             "blk_offset": int(u64[1]), "perm_offset": int(u64[2]), "bytes_used": int(u64[3]),
-            "chunk_offset": int(u64[4])}
+            "chunk_offset": int(u64[4]), "segidx_offset": int(u64[5])}
 
 
 def plan_arrays(buf: np.ndarray, h: dict) -> dict:
@@ -343,7 +343,11 @@ def plan_arrays(buf: np.ndarray, h: dict) -> dict:
     seg = np.frombuffer(buf[so: so + SEG_DESC.itemsize * S].tobytes(), dtype=SEG_DESC)
     blk = np.frombuffer(buf[bo: bo + BLK_DESC.itemsize * nb].tobytes(), dtype=BLK_DESC)
     perm = buf[po: po + 4 * Tp].view(np.int32).copy()
-    out = {"desc": seg, "blocks": blk, "perm": perm}
+    rest = buf[po + 4 * Tp: po + 4 * h["num_tokens"]].view(np.int32).copy()
+    out = {"desc": seg, "blocks": blk, "perm": perm, "unadapted": rest}
+    if "segidx_offset" in h:
+        xo = h["segidx_offset"]
+        out["segidx"] = buf[xo: xo + 4 * Tp].view(np.int32).copy()
     if "chunk_offset" in h:
         co = h["chunk_offset"]
         out["chunks"] = np.frombuffer(buf[co: co + CHUNK_DESC.itemsize * h["num_chunks"]].tobytes(), dtype=CHUNK_DESC)

@@ -171,9 +171,10 @@ size_t lora_plan_bytes(int32_t capacity)
     if (capacity < 0) capacity = 0;
     const size_t c = size_t(capacity);
     // header, segment descriptors (S <= T), block descriptors (blocks <= T'),
-    // perm (T' <= T), alignment slack
+    // perm (T), chunk descriptors (chunks <= T'), segment index (T' <= T),
+    // alignment slack
     return sizeof(lora_plan_header) + sizeof(lora_seg_desc) * c + 128 + sizeof(lora_blk_desc) * c + 4 * c + 64 +
-           sizeof(lora_chunk_desc) * c + 16;
+           sizeof(lora_chunk_desc) * c + 4 * c + 16;
 }
 
 size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank)
@@ -184,7 +185,7 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_SGMV_EXPAND:
     case LORA_OP_BGMV_SHRINK:
     case LORA_OP_BGMV_EXPAND: return 0;
-    case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, max_rank < 1 ? 1 : max_rank);
+    case LORA_OP_FUSED:
     case LORA_OP_SGMV:
     case LORA_OP_BGMV:
         return combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
@@ -251,13 +252,15 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
     h->seg_offset = sizeof(lora_plan_header);
     h->blk_offset = (h->seg_offset + sizeof(lora_seg_desc) * size_t(S) + 127) & ~size_t(127);
     h->perm_offset = align16(h->blk_offset + sizeof(lora_blk_desc) * size_t(nblk));
-    h->chunk_offset = (h->perm_offset + 4 * size_t(sorted) + 63) & ~size_t(63);
-    h->bytes_used = h->chunk_offset + sizeof(lora_chunk_desc) * size_t(nchunk);
+    h->chunk_offset = (h->perm_offset + 4 * size_t(T) + 63) & ~size_t(63);
+    h->segidx_offset = align16(h->chunk_offset + sizeof(lora_chunk_desc) * size_t(nchunk));
+    h->bytes_used = h->segidx_offset + 4 * size_t(sorted);
 
     auto *seg = reinterpret_cast<lora_seg_desc *>(base + h->seg_offset);
     auto *blk = reinterpret_cast<lora_blk_desc *>(base + h->blk_offset);
     auto *perm = reinterpret_cast<int32_t *>(base + h->perm_offset);
     auto *chunks = reinterpret_cast<lora_chunk_desc *>(base + h->chunk_offset);
+    auto *segidx = reinterpret_cast<int32_t *>(base + h->segidx_offset);
 
     // Prefix offsets (reusing count as the running write position), descriptors
     // and the block list.
@@ -307,14 +310,19 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
     }
     // Stable scatter: tokens in their original order; each lands in its
     // block's row list too (block of sorted position p is blk0 + (p - start) / 16).
-    for (int32_t t = 0; t < T; ++t) {
+    // Tokens without an adapter follow in their original order (perm[T' .. T)).
+    for (int32_t t = 0, rest = sorted; t < T; ++t) {
         const int32_t a = ids[t];
-        if (a < 0) continue;
+        if (a < 0) {
+            perm[rest++] = t;
+            continue;
+        }
         const int32_t p = count[size_t(a)]++;
         perm[p] = t;
     }
     for (int32_t si = 0, c0 = 0; si < S; ++si) {
         const lora_seg_desc &d = seg[si];
+        for (int32_t q = 0; q < d.len; ++q) segidx[d.start + q] = si;
         for (int32_t q = 0; q < d.len; ++q) {
             blk[d.blk0 + q / LORA_PLAN_ROW_BLOCK].rows[q % LORA_PLAN_ROW_BLOCK] = perm[d.start + q];
             chunks[c0 + q / LORA_PLAN_CHUNK_ROWS].rows[q % LORA_PLAN_CHUNK_ROWS] = perm[d.start + q];
@@ -487,8 +495,8 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     if (ldx < d_in || ldy < d_out) return fail(LORA_ERR_ARG, "row pitch smaller than the row");
     if (!aligned16(x) || !aligned16(W0) || !aligned16(y) || (ldx * 2) % 16 || (ldy * 2) % 16 || (d_in * 2) % 16)
         return fail(LORA_ERR_ALIGN, "fused entry needs 16-byte aligned x, W0, y rows and d_in %% 8 == 0");
-    if (h->num_sorted > 0 && !plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
-    const size_t need = fused_workspace_bytes(T, h->max_rank < 1 ? 1 : h->max_rank);
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    const size_t need = combined_workspace_bytes(T, d_in, h->max_rank < 1 ? 1 : h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     ShrinkArgs sa{};
@@ -505,7 +513,7 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     ea.vec_b = true;
     ea.vec_y = true;
     return launch_fused_linear(static_cast<hipStream_t>(stream), sa, W0, ea,
-                               PlanView{h, static_cast<const char *>(plan_dev)}, ws, ws_bytes);
+                               PlanView{h, static_cast<const char *>(plan_dev)}, ws);
 }
 
 } // extern "C"

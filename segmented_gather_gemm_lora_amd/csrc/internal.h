@@ -55,12 +55,16 @@ int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                 int32_t n_adapters, int32_t max_rank, void *ws);
-// Workspace of the combined calls: fp32 partial sums of the shrink over d_in slices.
+// Workspace of the combined calls and of the fused entry: fp32 partial sums of
+// the shrink over d_in slices.
 size_t combined_workspace_bytes(int32_t rows, int32_t d_in, int32_t max_rank);
+// SGMV shrink of every plan row into slice partials: ws[c * sl_stride + p * ldw + j]
+// for slice c < *nsl, sorted position p, rank j < r (ranks r .. ldw-1 are not
+// written).  ldw = round4(max_rank), sl_stride = T' * ldw.
+int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw,
+                             int64_t *sl_stride, int *nsl);
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
-                        const PlanView &p, void *ws, size_t ws_bytes);
-
-size_t fused_workspace_bytes(int32_t T, int32_t max_rank);
+                        const PlanView &p, void *ws);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

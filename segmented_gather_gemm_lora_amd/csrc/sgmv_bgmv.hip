@@ -925,19 +925,29 @@ int launch_sgmv_expand(hipStream_t s, const ExpandArgs &a, const PlanView &p)
     return check_launch("sgmv_expand");
 }
 
-int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw,
+                             int64_t *sl_stride, int *nsl)
 {
     const int nblk = p.h->num_blocks;
-    if (nblk == 0) return LORA_OK;
     const Split sp = choose_split(sa.d_in, nblk, sa.dtype);
-    float *vp = static_cast<float *>(ws);
-    const int64_t ldw = (p.h->max_rank + 3) / 4 * 4;
-    const int64_t sl_stride = int64_t(p.h->num_sorted) * ldw;
+    *ldw = (p.h->max_rank + 3) / 4 * 4;
+    *sl_stride = int64_t(p.h->num_sorted) * *ldw;
+    *nsl = sp.kc;
+    if (nblk == 0) return LORA_OK;
     dispatch_shrink<SgmvShrinkL>(sa.dtype, sa.vec, rank_tiles(p.h->max_rank), s, sa.x, sa.ldx, sa.d_in,
-                                 plan_blocks(p), nblk, sp.kc, sp.slice_len, sp.nstep, false, vp, ldw, sl_stride);
-    int st = check_launch("sgmv shrink");
+                                 plan_blocks(p), nblk, sp.kc, sp.slice_len, sp.nstep, false, ws, *ldw, *sl_stride);
+    return check_launch("sgmv shrink");
+}
+
+int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+{
+    if (p.h->num_blocks == 0) return LORA_OK;
+    float *vp = static_cast<float *>(ws);
+    int64_t ldw = 0, sl_stride = 0;
+    int nsl = 0;
+    int st = launch_sgmv_shrink_split(s, sa, p, vp, &ldw, &sl_stride, &nsl);
     if (st) return st;
-    sgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, p);
+    sgmv_expand_launch(s, ea, vp, ldw, sl_stride, nsl, p);
     return check_launch("sgmv expand");
 }
 

@@ -73,6 +73,11 @@ class HostPlan:
         a = B.plan_arrays(self.buf.view(np.uint8), h)
         return a["desc"], a["blocks"], a["perm"], a["chunks"]
 
+    def tail(self):
+        h = B.plan_header(self.buf.view(np.uint8))
+        a = B.plan_arrays(self.buf.view(np.uint8), h)
+        return a["unadapted"], a["segidx"], h
+
 
 def make_tables(N, rng, ranks=None):
     if ranks is None:
@@ -146,6 +151,12 @@ def test_plan_matches_oracle_segments(T, N, none_p, seed):
         assert (ch["rows"][n:] == -1).all()
     assert h["max_rank"] == (int(ranks[adapter_o].max()) if len(adapter_o) else 0)
     assert h["used"] <= plan.nbytes
+    # tokens without an adapter, in order, after the sorted ones; segment of each sorted position
+    rest, segidx, hh = plan.tail()
+    assert np.array_equal(rest, np.nonzero(ids < 0)[0])
+    assert np.array_equal(segidx, np.repeat(np.arange(len(adapter_o)), np.diff(indptr_o)))
+    assert hh["segidx_offset"] % 16 == 0 and hh["segidx_offset"] >= hh["chunk_offset"] + 320 * h["nchunk"]
+    assert hh["bytes_used"] == hh["segidx_offset"] + 4 * h["Tp"]
 
 
 def test_plan_errors():
