@@ -307,7 +307,7 @@ def main():
 
     # ---- per-kernel durations: HIP events attached to each kernel's own start
     # and end (hipExtLaunchKernelGGL), on the stream the kernels run on
-    names = ["shrink", "fused"] if kind == "fused" else ["shrink", "expand"]
+    names = ["shrink", "prep", "fused"] if kind == "fused" else ["shrink", "expand"]
     nk = len(names)
     K2 = max(L, min(K, 20 * L))
     timer = B.KernelTimer(K2 * nk)

@@ -185,7 +185,7 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_SGMV_EXPAND:
     case LORA_OP_BGMV_SHRINK:
     case LORA_OP_BGMV_EXPAND: return 0;
-    case LORA_OP_FUSED:
+    case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     case LORA_OP_SGMV:
     case LORA_OP_BGMV:
         return combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
@@ -496,7 +496,7 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     if (!aligned16(x) || !aligned16(W0) || !aligned16(y) || (ldx * 2) % 16 || (ldy * 2) % 16 || (d_in * 2) % 16)
         return fail(LORA_ERR_ALIGN, "fused entry needs 16-byte aligned x, W0, y rows and d_in %% 8 == 0");
     if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
-    const size_t need = combined_workspace_bytes(T, d_in, h->max_rank < 1 ? 1 : h->max_rank);
+    const size_t need = fused_workspace_bytes(T, d_in, h->max_rank < 1 ? 1 : h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     ShrinkArgs sa{};

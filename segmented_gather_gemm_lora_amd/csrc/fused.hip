@@ -5,27 +5,32 @@
 // correction; "Multi-LoRA Serving in Production ..." (llms.blog), section
 // "Mathematical Formulation and the Batching Challenge", layer equation).
 //
-// Two launches:
+// Three launches:
 //  1. the SGMV shrink of the plan writes v = x A_s (fp32 slice partials) into
 //     the workspace, rows in sorted order;
-//  2. one GEMM over the plan's rows (sorted adapted tokens, then the tokens
+//  2. a small pass sums the slices, scales by scale_s and splits each value
+//     into two bf16 halves (hi = bf16(v), lo = bf16(v - hi)), stored in the
+//     order the MFMA fragments read them;
+//  3. one GEMM over the plan's rows (sorted adapted tokens, then the tokens
 //     without an adapter) computes the base product on bf16 MFMA
 //     (v_mfma_f32_16x16x32_bf16) and adds the correction as extra
 //     contraction steps of the same accumulators: for each segment that meets
 //     a wave's rows, the A operand is B_s (output column c, ranks j) and the B
-//     operand is scale_s * v (zero on rows outside the segment).  v is fp32, so
-//     it enters as two bf16 halves (hi = bf16(v), lo = bf16(v - hi)) that
-//     share the B_s fragment: one 32-deep step covers 16 ranks.
+//     operand is the split scale_s * v (zero on rows outside the segment); the
+//     two halves share the B_s fragment, so one 32-deep step covers 16 ranks.
 //
-// GEMM tiling: a workgroup computes 192 output columns x 256 plan rows with 8
-// waves (2 along columns x 4 along rows, 96 x 64 each); k advances 64 per
-// stage through a double-buffered LDS tile (x rows gathered through perm, W0
-// rows contiguous), with the next stage's global loads in flight during the
-// current stage's MFMAs.  MFMA rows are output columns, MFMA columns are
-// tokens, and the column order inside a wave tile is permuted so that every
-// lane ends up with 24 consecutive columns of one token: y is written with
-// 16-byte stores.  Workgroups are numbered so that the tiles that share W0
-// column slabs run on the same XCD (its own L2).
+// GEMM tiling: a workgroup computes 192 output columns x 256 plan rows with 4
+// waves (2 x 2, 96 columns x 128 rows each, accumulators in AGPRs).  k
+// advances 32 per stage through a ring of kStages LDS stages filled by
+// direct global-to-LDS loads (global_load_lds_dwordx4), issued kStages - 1
+// stages ahead so that several HBM round trips are in flight per CU while
+// MFMAs run.  A stage holds rows of 64 bytes (4 units of 16 bytes); unit u of
+// row r sits in slot u ^ swz(r), so the 16 rows a fragment read touches fall
+// in distinct LDS banks.  MFMA rows are output columns, MFMA columns are
+// tokens, and the W0 rows are placed in LDS in the order that gives every lane
+// 24 consecutive output columns of one token: y is written with 16-byte
+// stores.  Workgroups are numbered so that the tiles that share W0 column
+// slabs run on the same XCD (its own L2).
 #include "internal.h"
 
 namespace lora {
@@ -38,21 +43,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> using gptr = const __attribute__((address_space(1))) T *;
 template <typename T> __device__ __forceinline__ gptr<T> as_global(const void *p) { return (gptr<T>)(p); }
 
-constexpr int kBN = 192;               // output columns per workgroup
-constexpr int kBM = 256;               // plan rows per workgroup
-constexpr int kBK = 64;                // k per stage
-constexpr int kPitch = kBK + 8;        // LDS row pitch in bf16 (144 bytes)
-constexpr int kThreads = 512;          // 8 waves
-constexpr int kWN = 96, kWM = 64;      // wave tile
-constexpr int kTN = kWN / 16;          // MFMA tiles along columns (6)
-constexpr int kTM = kWM / 16;          // MFMA tiles along rows (4)
-constexpr int kLdsW = kBN * kPitch;    // elements of the W0 tile per stage
-constexpr int kLdsX = kBM * kPitch;    // elements of the x tile per stage
-constexpr int kStage = kLdsW + kLdsX;
-constexpr int kWLoads = kBN * kBK / 8 / kThreads; // 16-byte chunks per thread and stage (3)
-constexpr int kXLoads = kBM * kBK / 8 / kThreads; // (4)
-static_assert(kWLoads * kThreads * 8 == kBN * kBK && kXLoads * kThreads * 8 == kBM * kBK, "tile / thread split");
-static_assert(2 * kStage * 2 <= 160 * 1024, "LDS budget");
+constexpr int kBN = 192;                 // output columns per workgroup
+constexpr int kBM = 256;                 // plan rows per workgroup
+constexpr int kBK = 32;                  // k per stage
+constexpr int kStages = 5;               // LDS ring depth
+constexpr int kThreads = 256;            // 4 waves
+constexpr int kWN = 96, kWM = 128;       // wave tile
+constexpr int kTN = kWN / 16;            // MFMA tiles along columns (6)
+constexpr int kTM = kWM / 16;            // MFMA tiles along rows (8)
+constexpr int kRowBytes = kBK * 2;       // 64
+constexpr int kWBytes = kBN * kRowBytes; // W0 part of a stage
+constexpr int kXBytes = kBM * kRowBytes; // x part of a stage
+constexpr int kStageBytes = kWBytes + kXBytes;
+constexpr int kWDma = kWBytes / 1024 / 4; // 1 KB direct loads per wave and stage (3)
+constexpr int kXDma = kXBytes / 1024 / 4; // (4)
+constexpr int kDma = kWDma + kXDma;
+constexpr int kMaxSlicesFused = 4; // bound on the shrink's d_in slices
+static_assert(kWDma * 4 * 1024 == kWBytes && kXDma * 4 * 1024 == kXBytes, "tile / wave split");
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
@@ -67,6 +76,31 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 // then holds columns 24 g + 4 j + q (q < 4), i.e. 24 consecutive columns.
 __device__ __forceinline__ int wave_col(int m, int j) { return (m >> 2) * 24 + 4 * j + (m & 3); }
 
+// Slot of 16-byte unit u in LDS row r is u ^ swz(r), so that the 8
+// consecutive rows of a quarter-wave fragment read fall in 8 distinct 16-byte
+// bank groups (the fastest of the patterns measured on gfx950).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8).  Written through the builtin, so that the compiler's
+// own wait insertion knows about them.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// 16 bytes per lane from global memory to LDS at m0 + 16 * lane.  The
+// compiler does not see this write to LDS; the kernel waits for it with an
+// explicit vmcnt before the barrier that publishes the stage.  dma16s: the
+// address is a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_byte)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16s(const void *base, uint32_t off, uint32_t lds_byte)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_byte)
+                 : "memory", "m0");
+}
+
 struct FusedArgs {
     const uint16_t *x;
     int64_t ldx;
@@ -77,90 +111,184 @@ struct FusedArgs {
     const int32_t *segidx;    // [T'] sorted position -> segment
     const lora_seg_desc *seg; // [S]
     int T, Tp;
-    const float *v; // shrink partials: v[c * sl_stride + p * ldw + j]
-    int64_t ldw, sl_stride;
-    int nsl;
+    const uint16_t *vh; // split scaled v rows (fused_prep_kernel)
+    int64_t ldh;
     uint16_t *y;
     int64_t ldy;
     int tiles_m, tiles_n;
+    int off32; // byte offsets into x and W0 fit in 32 bits
 };
 
-// Correction of one segment for this wave's rows: for every 16 ranks, one
-// 32-deep MFMA step per tile with A = B_s rows and B = scale * v split into
-// bf16 halves (lane groups 0,1: hi of ranks 0-7 / 8-15; groups 2,3: lo).
-__device__ __forceinline__ void lora_segment(const FusedArgs &a, int s, int pw0, int cw0, int lane,
-                                             floatx4 (&acc)[kTN][kTM])
+// v of sorted row p, scaled and split, for the fused GEMM: for every 16 ranks
+// (chunk c) 32 bf16 at vh[p * ldh + 32 c]: hi of ranks 16c .. 16c+15, then lo
+// of the same ranks; ranks past r are zero.  One thread per 8 ranks of a row.
+__global__ __launch_bounds__(256) void fused_prep_kernel(const float *__restrict__ v, int64_t ldw, int64_t sl_stride,
+                                                         int nsl, const int32_t *__restrict__ segidx,
+                                                         const lora_seg_desc *__restrict__ seg, int Tp, int units,
+                                                         uint16_t *__restrict__ vh, int64_t ldh)
+{
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int p = int(idx / units), u = int(idx % units);
+    if (p >= Tp) return;
+    // the v loads do not wait for the segment lookup: ranks past r (not
+    // written by the shrink, any bits) are replaced by zero afterwards
+    const int j = 8 * u;
+    const int jl = j + 4 < ldw ? j + 4 : 0, jh = j < ldw ? j : 0;
+    floatx4 f[kMaxSlicesFused][2];
+#pragma unroll
+    for (int c = 0; c < kMaxSlicesFused; ++c) {
+        const float *row = v + (c < nsl ? c : 0) * sl_stride + int64_t(p) * ldw;
+        f[c][0] = *reinterpret_cast<const floatx4 *>(row + jh);
+        f[c][1] = *reinterpret_cast<const floatx4 *>(row + jl);
+    }
+    const int s = segidx[p];
+    const int r = seg[s].rank;
+    const float scale = seg[s].scale;
+    float val[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < kMaxSlicesFused; ++c)
+            if (c < nsl) sum += f[c][e >> 2][e & 3];
+        val[e] = j + e < r ? sum * scale : 0.f;
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        uint32_t h2[2], l2[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            h2[q] = f32_to_bf16(val[e + q]);
+            l2[q] = f32_to_bf16(val[e + q] - bf16_to_f32(h2[q]));
+        }
+        hi[e / 2] = h2[0] | (h2[1] << 16);
+        lo[e / 2] = l2[0] | (l2[1] << 16);
+    }
+    uint16_t *dst = vh + int64_t(p) * ldh + 32 * (u >> 1) + 8 * (u & 1);
+    *reinterpret_cast<u32x4 *>(dst) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+}
+
+// Operands of one correction step: 16 ranks (from j0) of segment s for this
+// wave's rows and columns.  A = B_s rows (lane groups 0, 2: ranks j0 .. j0+7,
+// groups 1, 3: j0+8 .. j0+15), B = the split v (groups 0, 1: hi, 2, 3: lo),
+// zero on rows outside the segment.
+struct LoraStep {
+    bf16x8 bf[kTN];
+    bf16x8 vf[kTM];
+};
+
+struct SegInfo {
+    gptr<uint16_t> B;
+    int r, p_begin, p_end;
+};
+
+__device__ __forceinline__ SegInfo seg_info(const FusedArgs &a, int s)
+{
+    const lora_seg_desc *d = a.seg + s;
+    return SegInfo{as_global<uint16_t>(reinterpret_cast<const void *>(d->B)), d->rank, d->start, d->start + d->len};
+}
+
+// VECB: every rank of the plan is a multiple of 8, so B_s rows are 16-byte
+// aligned and 8 ranks are one load.
+template <bool VECB>
+__device__ __forceinline__ void lora_load(const FusedArgs &a, const SegInfo &sg, int j0, int pw0, int cw0, int lane,
+                                          LoraStep &f)
 {
     const int m = lane & 15, g = lane >> 4;
-    const gptr<lora_seg_desc> d = (gptr<lora_seg_desc>)(a.seg + s);
-    const gptr<uint16_t> B = as_global<uint16_t>(reinterpret_cast<const void *>(d->B));
-    const int r = d->rank, p_begin = d->start, p_end = d->start + d->len;
-    const float scale = d->scale;
-    const bool vec = (r & 7) == 0;
-    for (int j0 = 0; j0 < r; j0 += 16) {
-        const int jj = j0 + 8 * (g & 1);
-        // A operand: B_s[c, jj .. jj+7] for the 6 column tiles
-        bf16x8 bf[kTN];
+    const int r = sg.r;
+    const int jj = j0 + 8 * (g & 1);
 #pragma unroll
-        for (int t = 0; t < kTN; ++t) {
-            int c = cw0 + wave_col(m, t);
-            c = c < a.d_out ? c : a.d_out - 1;
-            const gptr<uint16_t> row = B + int64_t(c) * r;
-            if (vec) {
-                const int jc = jj < r ? jj : 0;
-                u32x4 u = *(gptr<u32x4>)(row + jc);
-                if (jj >= r) u = u32x4{};
-                bf[t] = __builtin_bit_cast(bf16x8, u);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = jj + e;
-                    const uint16_t h = row[j < r ? j : r - 1];
-                    bf[t][e] = __builtin_bit_cast(__bf16, j < r ? h : uint16_t(0));
-                }
-            }
-        }
-        // B operand: scale * v[p, jj .. jj+7], summed over slices, hi or lo half
-        bf16x8 vf[kTM];
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-            const int p = pw0 + 16 * i + m;
-            const bool in = p >= p_begin && p < p_end;
-            const int pc = in ? p : p_begin;
-            float vv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[e] = 0.f;
-            for (int c = 0; c < a.nsl; ++c) {
-                const gptr<float> vrow = as_global<float>(a.v) + c * a.sl_stride + int64_t(pc) * a.ldw;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int j = jj + 4 * h;
-                    floatx4 f = *(gptr<floatx4>)(vrow + (j < a.ldw ? j : 0));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) vv[4 * h + e] += f[e];
-                }
-            }
+    for (int t = 0; t < kTN; ++t) {
+        int c = cw0 + wave_col(m, t);
+        c = c < a.d_out ? c : a.d_out - 1;
+        const gptr<uint16_t> row = sg.B + int64_t(c) * r;
+        if (VECB) {
+            const int jc = jj < r ? jj : 0;
+            u32x4 u = *(gptr<u32x4>)(row + jc);
+            if (jj >= r) u = u32x4{};
+            f.bf[t] = __builtin_bit_cast(bf16x8, u);
+        } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float val = (in && jj + e < r) ? vv[e] * scale : 0.f;
-                const uint32_t hi = f32_to_bf16(val);
-                const uint32_t part = (g >> 1) ? f32_to_bf16(val - bf16_to_f32(hi)) : hi;
-                vf[i][e] = __builtin_bit_cast(__bf16, uint16_t(part));
+                const int j = jj + e;
+                const uint16_t h = row[j < r ? j : r - 1];
+                f.bf[t][e] = __builtin_bit_cast(__bf16, j < r ? h : uint16_t(0));
             }
         }
+    }
 #pragma unroll
-        for (int t = 0; t < kTN; ++t)
-#pragma unroll
-            for (int i = 0; i < kTM; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[t], vf[i], acc[t][i], 0, 0, 0);
+    for (int i = 0; i < kTM; ++i) {
+        const int p = pw0 + 16 * i + m;
+        const bool in = p >= sg.p_begin && p < sg.p_end;
+        const int pc = in ? p : sg.p_begin;
+        u32x4 u = *(gptr<u32x4>)(as_global<uint16_t>(a.vh) + int64_t(pc) * a.ldh + 2 * j0 + 8 * g);
+        if (!in) u = u32x4{};
+        f.vf[i] = __builtin_bit_cast(bf16x8, u);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void fused_linear_kernel(FusedArgs a)
+__device__ __forceinline__ void lora_mma(const LoraStep &f, floatx4 (&acc)[kTN][kTM])
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int t = 0; t < kTN; ++t)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.bf[t], f.vf[i], acc[t][i], 0, 0, 0);
+}
+
+// Correction of segments s0 .. s1 (wave-uniform) for this wave's rows, one
+// 16-rank step at a time.  With VECB the operands of the next step are loaded
+// before the MFMAs of the current one; otherwise (ranks that are not
+// multiples of 8, element loads) the steps run one after the other.
+template <bool VECB>
+__device__ __forceinline__ void lora_correction(const FusedArgs &a, int s0, int s1, int pw0, int cw0, int lane,
+                                                floatx4 (&acc)[kTN][kTM])
+{
+    if (!VECB) {
+        for (int s = s0; s <= s1; ++s) {
+            const SegInfo sg = seg_info(a, s);
+            for (int j0 = 0; j0 < sg.r; j0 += 16) {
+                LoraStep f;
+                lora_load<false>(a, sg, j0, pw0, cw0, lane, f);
+                lora_mma(f, acc);
+            }
+        }
+        return;
+    }
+    int s = s0, j0 = 0;
+    SegInfo cur = seg_info(a, s);
+    LoraStep f0, f1;
+    lora_load<true>(a, cur, j0, pw0, cw0, lane, f0);
+    for (;;) {
+        int ns = s, nj = j0 + 16;
+        if (nj >= cur.r) {
+            ns = s + 1;
+            nj = 0;
+        }
+        const bool more = ns <= s1;
+        // past the last step the current step is loaded again (unused), which
+        // keeps the loads unconditional
+        const SegInfo nxt = more ? seg_info(a, ns) : cur;
+        lora_load<true>(a, nxt, more ? nj : j0, pw0, cw0, lane, f1);
+        lora_mma(f0, acc);
+        if (!more) break;
+        f0 = f1;
+        cur = nxt;
+        s = ns;
+        j0 = nj;
+    }
+}
+
+template <bool VECB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_linear_kernel(FusedArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, g = lane >> 4;
-    const int wn = wave >> 2, wm = wave & 3; // wave position: column half, row quarter
+    const int wn = wave >> 1, wm = wave & 1; // wave position: column half, row half
+    const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char *)(lds)));
 
     // XCD-aware numbering: consecutive workgroups go to different XCDs, so
     // give each XCD a contiguous run of tiles (row tiles fastest).
@@ -170,61 +298,70 @@ __global__ __launch_bounds__(kThreads) void fused_linear_kernel(FusedArgs a)
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int m0 = tm * kBM, n0 = tn * kBN;
 
-    // global -> LDS assignment: chunk q = tid + 512 i covers row q / 8, k chunk q % 8
-    const int kc = tid & 7;
-    gptr<uint16_t> wrow[kWLoads];
+    // Direct loads: lane `lane` of this wave's load j fills 16-byte unit
+    // (wave * n + j) * 64 + lane of the W0 or x part of a stage, i.e. LDS row
+    // u / 4, slot u % 4, which holds k unit (u % 4) ^ swz(row).  Per lane:
+    // the byte offset of that unit in stage 0 (row start + 16 * unit) and the
+    // unit's first k.
+    uint32_t woff32[kWDma], xoff32[kXDma];
+    int wk[kWDma], xk[kXDma];
 #pragma unroll
-    for (int i = 0; i < kWLoads; ++i) {
-        int c = n0 + (tid >> 3) + 64 * i;
+    for (int j = 0; j < kWDma; ++j) {
+        const int u = (wave * kWDma + j) * 64 + lane, rho = u >> 2;
+        wk[j] = 8 * ((u & 3) ^ swz(rho));
+        const int rp = rho % kWN;
+        int c = n0 + (rho / kWN) * kWN + wave_col(rp & 15, rp >> 4);
         c = c < a.d_out ? c : a.d_out - 1;
-        wrow[i] = as_global<uint16_t>(a.W0) + int64_t(c) * a.d_in;
+        woff32[j] = uint32_t((int64_t(c) * a.d_in + wk[j]) * 2);
     }
-    gptr<uint16_t> xrow[kXLoads];
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-        int p = m0 + (tid >> 3) + 64 * i;
+    for (int j = 0; j < kXDma; ++j) {
+        const int u = (wave * kXDma + j) * 64 + lane, row = u >> 2;
+        xk[j] = 8 * ((u & 3) ^ swz(row));
+        int p = m0 + row;
         p = p < a.T ? p : a.T - 1;
-        xrow[i] = as_global<uint16_t>(a.x) + int64_t(as_global<int32_t>(a.perm)[p]) * a.ldx;
+        xoff32[j] = uint32_t((int64_t(as_global<int32_t>(a.perm)[p]) * a.ldx + xk[j]) * 2);
     }
-    // output rows of this lane (token tile i: plan row m0 + 64 wm + 16 i + m)
+    const int nk = (a.d_in + kBK - 1) / kBK;
+    // stage kt into ring slot kt % kStages.  A full stage adds kt * 64 bytes
+    // to the uniform bases; in a partial last stage, k units past d_in read
+    // the row's first unit (d_in % 8 == 0) and are zeroed when the fragments
+    // are read.
+    auto issue = [&](int kt) {
+        const uint32_t base = lds0 + uint32_t((kt % kStages) * kStageBytes);
+        if (a.off32 && (kt + 1) * kBK <= a.d_in) {
+            const char *wb = reinterpret_cast<const char *>(a.W0) + int64_t(kt) * kRowBytes;
+            const char *xb = reinterpret_cast<const char *>(a.x) + int64_t(kt) * kRowBytes;
+#pragma unroll
+            for (int j = 0; j < kWDma; ++j) dma16s(wb, woff32[j], base + uint32_t((wave * kWDma + j) * 1024));
+#pragma unroll
+            for (int j = 0; j < kXDma; ++j)
+                dma16s(xb, xoff32[j], base + uint32_t(kWBytes + (wave * kXDma + j) * 1024));
+        } else {
+#pragma unroll
+            for (int j = 0; j < kWDma; ++j) {
+                const int k = kt * kBK + wk[j];
+                const char *row = reinterpret_cast<const char *>(a.W0) + woff32[j] - 2 * wk[j];
+                dma16(row + 2 * (k < a.d_in ? k : 0), base + uint32_t((wave * kWDma + j) * 1024));
+            }
+#pragma unroll
+            for (int j = 0; j < kXDma; ++j) {
+                const int k = kt * kBK + xk[j];
+                const char *row = reinterpret_cast<const char *>(a.x) + xoff32[j] - 2 * xk[j];
+                dma16(row + 2 * (k < a.d_in ? k : 0), base + uint32_t(kWBytes + (wave * kXDma + j) * 1024));
+            }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1);
+
+    // output rows of this lane (token tile i: plan row m0 + 128 wm + 16 i + m)
     int yrow[kTM];
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
         const int p = m0 + kWM * wm + 16 * i + m;
         yrow[i] = p < a.T ? as_global<int32_t>(a.perm)[p] : -1;
     }
-
-    const int nk = (a.d_in + kBK - 1) / kBK;
-    u32x4 rw[kWLoads], rx[kXLoads];
-    auto gload = [&](int kt) {
-        // d_in % 8 == 0: a 16-byte chunk is all in or all out; an out chunk
-        // reads the row's first chunk and is zeroed
-        const int k = kt * kBK + 8 * kc;
-        const bool in = k < a.d_in;
-        const int off = in ? k : 0;
-#pragma unroll
-        for (int i = 0; i < kWLoads; ++i) {
-            rw[i] = *(gptr<u32x4>)(wrow[i] + off);
-            if (!in) rw[i] = u32x4{};
-        }
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            rx[i] = *(gptr<u32x4>)(xrow[i] + off);
-            if (!in) rx[i] = u32x4{};
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint16_t *w = lds + buf * kStage;
-        uint16_t *xs = w + kLdsW;
-#pragma unroll
-        for (int i = 0; i < kWLoads; ++i)
-            *reinterpret_cast<u32x4 *>(w + ((tid >> 3) + 64 * i) * kPitch + 8 * kc) = rw[i];
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i)
-            *reinterpret_cast<u32x4 *>(xs + ((tid >> 3) + 64 * i) * kPitch + 8 * kc) = rx[i];
-    };
-
-    gload(0);
 
     floatx4 acc[kTN][kTM];
 #pragma unroll
@@ -237,45 +374,66 @@ __global__ __launch_bounds__(kThreads) void fused_linear_kernel(FusedArgs a)
     const int cw0 = n0 + kWN * wn;
     if (pw0 < a.Tp) {
         const int plast = (pw0 + kWM < a.Tp ? pw0 + kWM : a.Tp) - 1;
-        const int s0 = as_global<int32_t>(a.segidx)[pw0];
-        const int s1 = as_global<int32_t>(a.segidx)[plast];
-        for (int s = s0; s <= s1; ++s) lora_segment(a, s, pw0, cw0, lane, acc);
+        const int s0 = __builtin_amdgcn_readfirstlane(a.segidx[pw0]);
+        const int s1 = __builtin_amdgcn_readfirstlane(a.segidx[plast]);
+        lora_correction<VECB>(a, s0, s1, pw0, cw0, lane, acc);
     }
 
-    lstore(0);
-    __syncthreads();
-
-    // fragment rows in LDS
-    int wr[kTN], xr[kTM];
+    // fragment byte offsets inside a stage
+    uint32_t woff[kTN], xoff[kTM];
 #pragma unroll
-    for (int t = 0; t < kTN; ++t) wr[t] = (kWN * wn + wave_col(m, t)) * kPitch + 8 * g;
+    for (int t = 0; t < kTN; ++t) {
+        const int rho = kWN * wn + 16 * t + m;
+        woff[t] = uint32_t(rho * kRowBytes + ((g ^ swz(rho)) << 4));
+    }
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) xr[i] = (kWM * wm + 16 * i + m) * kPitch + 8 * g;
+    for (int i = 0; i < kTM; ++i) {
+        const int row = kWM * wm + 16 * i + m;
+        xoff[i] = uint32_t(kWBytes + row * kRowBytes + ((g ^ swz(row)) << 4));
+    }
 
+    // Fragments of stage kt sit in registers while stage kt + 1 is read from
+    // LDS and its MFMAs run; the ring then holds stages kt + 1 .. kt + 4.
+    auto read_frags = [&](int kt, bf16x8 (&wf)[kTN], bf16x8 (&xf)[kTM]) {
+        const char *st = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+        for (int t = 0; t < kTN; ++t) wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + woff[t]));
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) xf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + xoff[i]));
+        if (kt * kBK + 8 * g >= a.d_in) {
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) xf[i] = bf16x8{};
+        }
+    };
+    bf16x8 wc[kTN], xc[kTM], wn_[kTN], xn[kTM];
+    // Drain every load issued so far (the first stages and the correction's
+    // operands): the compiler then knows that no load of its own is pending
+    // in the loop, and inserts no wait there that would also wait for the
+    // direct loads in flight.  The barrier publishes every wave's stage 0.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, wc, xc);
     for (int kt = 0; kt < nk; ++kt) {
-        // next stage in flight (the last iteration re-reads the last stage
-        // into the idle buffer, which keeps the loads unconditional)
-        gload(kt + 1 < nk ? kt + 1 : kt);
-        const uint16_t *w = lds + (kt & 1) * kStage;
-        const uint16_t *xs = w + kLdsW;
+        // stage kt + 1 complete (stages kt + 2, kt + 3 may be outstanding);
+        // after the barrier every wave is past its reads of stage kt, so the
+        // slot of stage kt - 1 is free for stage kt + 4
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
+        __builtin_amdgcn_s_barrier();
+        const int nxt = kt + kStages - 1;
+        issue(nxt < nk ? nxt : nk - 1);
+        read_frags(kt + 1 < nk ? kt + 1 : kt, wn_, xn);
 #pragma unroll
-        for (int s = 0; s < kBK / 32; ++s) {
-            bf16x8 wf[kTN], xf[kTM];
-#pragma unroll
-            for (int t = 0; t < kTN; ++t)
-                wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(w + wr[t] + 32 * s));
+        for (int t = 0; t < kTN; ++t)
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
-                xf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + xr[i] + 32 * s));
+                acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[t], xc[i], acc[t][i], 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < kTN; ++t)
+        for (int t = 0; t < kTN; ++t) wc[t] = wn_[t];
 #pragma unroll
-                for (int i = 0; i < kTM; ++i)
-                    acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[t], xf[i], acc[t][i], 0, 0, 0);
-        }
-        lstore((kt + 1) & 1);
-        __syncthreads();
+        for (int i = 0; i < kTM; ++i) xc[i] = xn[i];
     }
+    // no direct load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
     // y[token, cw0 + 24 g + 4 t + q] = acc[t][i][q]
     const int c0 = cw0 + 24 * g;
@@ -307,6 +465,19 @@ __global__ __launch_bounds__(kThreads) void fused_linear_kernel(FusedArgs a)
 
 } // namespace
 
+// Workspace: the shrink's slice partials, then the split v rows
+// ([T'][2 * round16(max_rank)] bf16).
+static int64_t vh_pitch(int32_t max_rank) { return 2 * int64_t((max_rank + 15) / 16 * 16); }
+static size_t vh_offset(int32_t T, int32_t d_in, int32_t max_rank)
+{
+    return (combined_workspace_bytes(T, d_in, max_rank) + 255) / 256 * 256;
+}
+
+size_t fused_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
+{
+    return vh_offset(T, d_in, max_rank) + size_t(T) * size_t(vh_pitch(max_rank)) * 2 + 256;
+}
+
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
                         const PlanView &p, void *ws)
 {
@@ -317,6 +488,21 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     int nsl = 0;
     int st = launch_sgmv_shrink_split(s, sa, p, v, &ldw, &sl_stride, &nsl);
     if (st) return st;
+    const int Tp = p.h->num_sorted;
+    const int max_rank = p.h->max_rank < 1 ? 1 : p.h->max_rank;
+    uint16_t *vh = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + vh_offset(T, sa.d_in, max_rank));
+    const int64_t ldh = vh_pitch(max_rank);
+    const int32_t *segidx = reinterpret_cast<const int32_t *>(p.dev + p.h->segidx_offset);
+    const lora_seg_desc *segs = reinterpret_cast<const lora_seg_desc *>(p.dev + p.h->seg_offset);
+    if (nsl > kMaxSlicesFused) return fail(LORA_ERR_ARG, "fused layer: %d d_in slices > %d", nsl, kMaxSlicesFused);
+    if (Tp > 0) {
+        const int units = int(ldh / 16);
+        const int64_t threads = int64_t(Tp) * units;
+        launch_kernel(fused_prep_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, v, ldw, sl_stride,
+                      nsl, segidx, segs, Tp, units, vh, ldh);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(LORA_ERR_HIP, "fused layer prep launch: %s", hipGetErrorString(e));
+    }
     FusedArgs a{};
     a.x = static_cast<const uint16_t *>(sa.x);
     a.ldx = sa.ldx;
@@ -324,21 +510,27 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     a.W0 = static_cast<const uint16_t *>(W0);
     a.d_out = ea.d_out;
     a.perm = reinterpret_cast<const int32_t *>(p.dev + p.h->perm_offset);
-    a.segidx = reinterpret_cast<const int32_t *>(p.dev + p.h->segidx_offset);
-    a.seg = reinterpret_cast<const lora_seg_desc *>(p.dev + p.h->seg_offset);
+    a.segidx = segidx;
+    a.seg = segs;
     a.T = T;
     a.Tp = p.h->num_sorted;
-    a.v = v;
-    a.ldw = ldw;
-    a.sl_stride = sl_stride;
-    a.nsl = nsl;
+    a.vh = vh;
+    a.ldh = ldh;
     a.y = static_cast<uint16_t *>(ea.y);
     a.ldy = ea.ldy;
+    // 32-bit byte offsets hold every x row and W0 row start plus one row
+    a.off32 = (int64_t(T) * sa.ldx + sa.d_in) * 2 < (int64_t(1) << 32) &&
+              (int64_t(ea.d_out) * sa.d_in + sa.d_in) * 2 < (int64_t(1) << 32);
     a.tiles_m = (T + kBM - 1) / kBM;
     a.tiles_n = (ea.d_out + kBN - 1) / kBN;
     const int64_t nwg = int64_t(a.tiles_m) * a.tiles_n;
     if (nwg > (int64_t(1) << 31) - 1) return fail(LORA_ERR_ARG, "fused layer: too many tiles");
-    launch_kernel(fused_linear_kernel, dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+    bool vecb = true;
+    const lora_seg_desc *hseg = reinterpret_cast<const lora_seg_desc *>(reinterpret_cast<const char *>(p.h) +
+                                                                        p.h->seg_offset);
+    for (int i = 0; i < p.h->num_segments; ++i) vecb = vecb && (hseg[i].rank & 7) == 0;
+    if (vecb) launch_kernel(fused_linear_kernel<true>, dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+    else launch_kernel(fused_linear_kernel<false>, dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(LORA_ERR_HIP, "fused layer launch: %s", hipGetErrorString(e));
     return LORA_OK;

@@ -65,6 +65,7 @@ int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView
                              int64_t *sl_stride, int *nsl);
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
                         const PlanView &p, void *ws);
+size_t fused_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
