@@ -65,10 +65,15 @@ static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays a (quiet) NaN
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// two fp32 -> packed bf16 (lo in bits 15:0), one conversion instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -81,24 +86,25 @@ __device__ __forceinline__ int wave_col(int m, int j) { return (m >> 2) * 24 + 4
 // bank groups (the fastest of the patterns measured on gfx950).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8).  Written through the builtin, so that the compiler's
+// s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt in 6:4, lgkmcnt in 11:8).  Written through the builtin, so that the compiler's
 // own wait insertion knows about them.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // 16 bytes per lane from global memory to LDS at m0 + 16 * lane.  The
 // compiler does not see this write to LDS; the kernel waits for it with an
 // explicit vmcnt before the barrier that publishes the stage.  dma16s: the
-// address is a wave-uniform base plus a 32-bit per-lane byte offset.
+// address is a wave-uniform base plus a 32-bit per-lane byte offset.  m0 is
+// a reserved register (never allocated by the compiler) and no other code in
+// these kernels reads it.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_byte)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte) : "memory");
 }
 __device__ __forceinline__ void dma16s(const void *base, uint32_t off, uint32_t lds_byte)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_byte)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 struct FusedArgs {
@@ -445,8 +451,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             uint32_t pk[12];
 #pragma unroll
             for (int t = 0; t < kTN; ++t) {
-                pk[2 * t] = f32_to_bf16(acc[t][i][0]) | (f32_to_bf16(acc[t][i][1]) << 16);
-                pk[2 * t + 1] = f32_to_bf16(acc[t][i][2]) | (f32_to_bf16(acc[t][i][3]) << 16);
+                pk[2 * t] = pack_bf16x2(acc[t][i][0], acc[t][i][1]);
+                pk[2 * t + 1] = pack_bf16x2(acc[t][i][2], acc[t][i][3]);
             }
 #pragma unroll
             for (int u = 0; u < 3; ++u)

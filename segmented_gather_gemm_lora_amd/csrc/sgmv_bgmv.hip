@@ -52,13 +52,13 @@ template <typename T> __device__ __forceinline__ global_ptr<T> as_global(const v
     return (global_ptr<T>)(p);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+// two fp32 -> packed bf16 (lo in bits 15:0) with one v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays a (quiet) NaN
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // ----------------------------------------------------------------------------
@@ -71,14 +71,12 @@ template <int DT> struct Frag;
 template <> struct Frag<LORA_BF16> {
     using T = uint16_t;
     using V = bf16x8;
-    static constexpr int kPerLane = 32; // elements of k per lane per step
     static constexpr int kStep = 128;
     static constexpr int kVec = 8;
 };
 template <> struct Frag<LORA_F32> {
     using T = float;
     using V = floatx4;
-    static constexpr int kPerLane = 16;
     static constexpr int kStep = 64;
     static constexpr int kVec = 4;
 };
@@ -286,7 +284,7 @@ __device__ __forceinline__ void y_store(void *yv, int64_t row_off, int ncol0, in
                 const uint32_t w = t.w[sI * 4 + e];
                 const float f0 = __builtin_fmaf(scale, acc[v0 >> 2][v0 & 3], bf16_to_f32(w & 0xffffu));
                 const float f1 = __builtin_fmaf(scale, acc[v1 >> 2][v1 & 3], bf16_to_f32(w >> 16));
-                o[e] = f32_to_bf16(f0) | (f32_to_bf16(f1) << 16);
+                o[e] = pack_bf16x2(f0, f1);
             }
             if constexpr (VECY) {
                 if (c < d_out) *reinterpret_cast<u32x4 *>(y + c) = u32x4{o[0], o[1], o[2], o[3]};
