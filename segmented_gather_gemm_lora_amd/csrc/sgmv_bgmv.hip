@@ -510,18 +510,85 @@ __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t
                                                          yrows, vrow0, nrows, vl, ldl);
 }
 
+// Expand of one plan chunk (up to 64 rows of one segment) over this
+// workgroup's 256 columns.  Every y tile of the chunk is loaded up front, into
+// registers of its own (registers that hold store data are never reloaded:
+// that would wait for the store to finish); then the blocks are computed and
+// stored one at a time, with only one block's accumulators live.  The B
+// fragments of all NCH * 16 ranks stay in registers for the whole chunk.
+template <int DT, bool VECY, bool BV, int NCH, int UPT>
+__device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                                  const void *__restrict__ Bv, int r, float scale,
+                                                  void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
+                                                  const int *yrows, int vrow0, int nrows, float *vl, int ldl)
+{
+    constexpr int RB = LORA_PLAN_CHUNK_BLOCKS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int ncol0 = ncol_wg + 64 * wave;
+
+    int yr[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int row = 16 * i + m;
+        yr[i] = row < nrows ? yrows[row] : -1;
+    }
+    const int ysafe = yrows[0];
+    VStage<UPT> vst;
+    stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    float bf[NCH][4][4];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) load_bfrag<DT, BV>(Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
+    // rows past the chunk read the first row again (never stored)
+    YTile<DT> yt[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
+    stage_v_store<BV, UPT>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
+    __syncthreads();
+
+    const int nblk = (nrows + kRows - 1) / kRows;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        if (i >= nblk) break;
+        floatx4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = floatx4{};
+        const int row = 16 * i + m;
+        const float *vrow = vl + (row < nrows ? row : 0) * ldl;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j0 = 16 * c + 4 * g;
+            floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
+            if (row >= nrows || j0 >= ldl) vf = floatx4{};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[c][t][q], vf[q], acc[t], 0, 0, 0);
+        }
+        if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc, scale);
+    }
+}
+
 // ----------------------------------------------------------------------------
 // SGMV kernels.  Shrink: one workgroup per (plan block, d_in slice).  Expand:
 // one workgroup per (256 columns, plan block) or (256 columns, plan chunk).
 // ----------------------------------------------------------------------------
 template <int DT, bool VEC, int W, int NSTEP, int RT>
 __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
-                                                             const lora_blk_desc *__restrict__ blks, int slice_len,
-                                                             float *__restrict__ out, int64_t ldo, int64_t sl_stride)
+                                                             const lora_blk_desc *__restrict__ blks, int nblk, int kc,
+                                                             int slice_len, float *__restrict__ out, int64_t ldo,
+                                                             int64_t sl_stride)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
-    const lora_blk_desc *bd = blks + blockIdx.x;
-    const int c = blockIdx.y;
+    // Workgroup b runs on XCD b % 8.  Give each XCD a contiguous run of
+    // (block, slice) items, blocks fastest, so that the blocks of a segment
+    // share one L2 and its A slice is fetched into few L2s.
+    const int total = nblk * kc, per = (total + 7) >> 3;
+    const int item = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+    if (item >= total) return;
+    const lora_blk_desc *bd = blks + item % nblk;
+    const int c = item / nblk;
     const int xr = bd->rows[threadIdx.x & 15];
     const int xr0 = bd->rows[0];
     const int k_begin = c * slice_len;
@@ -530,26 +597,37 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restr
                                         k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red);
 }
 
-template <int DT, int RB, bool VECY, int UPT>
+template <int DT, bool VECY, int UPT>
 __global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
-                                                          int nsl, const void *__restrict__ descs,
+                                                          int nsl, const lora_blk_desc *__restrict__ blks,
                                                           void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
                                                           int ldl)
 {
     extern __shared__ floatx4 vl4[];
-    if constexpr (RB == 1) {
-        const lora_blk_desc *d = static_cast<const lora_blk_desc *>(descs) + blockIdx.y;
-        expand_rows<DT, 1, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
-                                             d->scale, y,
-                                 ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0, d->n,
-                                 reinterpret_cast<float *>(vl4), ldl);
-    } else {
-        const lora_chunk_desc *d = static_cast<const lora_chunk_desc *>(descs) + blockIdx.y;
-        expand_rows<DT, RB, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
-                                              d->scale, y,
-                                  ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0, d->n,
-                                  reinterpret_cast<float *>(vl4), ldl);
-    }
+    const lora_blk_desc *d = blks + blockIdx.y;
+    expand_rows<DT, 1, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
+                                         d->scale, y, ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0,
+                                         d->n, reinterpret_cast<float *>(vl4), ldl);
+}
+
+template <int DT, bool VECY, int NCH, int UPT>
+__global__ __launch_bounds__(256) void sgmv_expand_chunk_kernel(const float *__restrict__ v, int64_t ldv,
+                                                                int64_t sl_stride, int nsl,
+                                                                const lora_chunk_desc *__restrict__ chunks,
+                                                                void *__restrict__ y, int64_t ldy, int d_out,
+                                                                bool vec_b, int ldl)
+{
+    extern __shared__ floatx4 vl4[];
+    const lora_chunk_desc *d = chunks + blockIdx.y;
+    const int r = d->rank;
+    const void *B = reinterpret_cast<const void *>(d->B);
+    float *vl = reinterpret_cast<float *>(vl4);
+    if (vec_b && (r & 3) == 0)
+        expand_chunk_impl<DT, VECY, true, NCH, UPT>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
+                                                    blockIdx.x * kExpandCols, d->rows, d->p0, d->n, vl, ldl);
+    else
+        expand_chunk_impl<DT, VECY, false, NCH, UPT>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
+                                                     blockIdx.x * kExpandCols, d->rows, d->p0, d->n, vl, ldl);
 }
 
 // ----------------------------------------------------------------------------
@@ -754,18 +832,18 @@ template <int DT, bool VEC, int RT> struct SgmvShrinkL {
     static void run(hipStream_t s, const void *x, int64_t ldx, int d_in, const lora_blk_desc *blks, int nblk,
                     int kc, int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride)
     {
-        const dim3 grid(nblk, kc);
+        const dim3 grid(unsigned((int64_t(nblk) * kc + 7) / 8 * 8));
         // register budget: 1024-thread workgroups have 128 VGPRs per lane, so
         // hold two k-steps of fragments only for one rank tile
         if (full)
             launch_kernel(sgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT>, grid, dim3(1024), 0, s, x, ldx, d_in,
-                          blks, slice_len, out, ldo, sl_stride);
+                          blks, nblk, kc, slice_len, out, ldo, sl_stride);
         else if (nstep == 2 && RT < 4)
-            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 2, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, slice_len,
-                          out, ldo, sl_stride);
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 2, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
+                          slice_len, out, ldo, sl_stride);
         else
-            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 1, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, slice_len,
-                          out, ldo, sl_stride);
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 1, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
+                          slice_len, out, ldo, sl_stride);
     }
 };
 
@@ -808,34 +886,71 @@ bool slot_major(int T, int n_adapters) { return n_adapters <= 2 * T; }
 // float4 units of staged v per thread for RB blocks of 16 rows at pitch ldl
 int units_per_thread(int rb, int ldl) { const int u = (rb * kRows * (ldl / 4) + 255) / 256; return u <= 1 ? 1 : (u <= 2 ? 2 : 4); }
 
-template <int DT, int RB, bool VECY>
+template <int DT, bool VECY>
 void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
-                    const void *descs, int ndesc, int ldl)
+                    const lora_blk_desc *blks, int nblk, int ldl)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
-    const size_t shm = (size_t(RB) * kRows * ldl + 4) * sizeof(float);
-    const dim3 grid(ncol, ndesc);
-    switch (units_per_thread(RB, ldl)) {
+    const size_t shm = (size_t(kRows) * ldl + 4) * sizeof(float);
+    const dim3 grid(ncol, nblk);
+    switch (units_per_thread(1, ldl)) {
     case 1:
-        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl);
         break;
     case 2:
-        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl);
         break;
     default:
-        launch_kernel(sgmv_expand_kernel<DT, RB, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, descs, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl);
     }
 }
 
-template <int DT, int RB>
-void sgmv_expand_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv, int64_t sl_stride,
-                     int nsl, const void *descs, int ndesc, int ldl)
+template <int DT, bool VECY, int NCH>
+void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                          const lora_chunk_desc *chunks, int nchunk, int ldl)
 {
-    if (vecy) sgmv_expand_go<DT, RB, true>(s, a, v, ldv, sl_stride, nsl, descs, ndesc, ldl);
-    else sgmv_expand_go<DT, RB, false>(s, a, v, ldv, sl_stride, nsl, descs, ndesc, ldl);
+    const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
+    const size_t shm = (size_t(LORA_PLAN_CHUNK_ROWS) * ldl + 4) * sizeof(float);
+    const dim3 grid(ncol, nchunk);
+    switch (units_per_thread(LORA_PLAN_CHUNK_BLOCKS, ldl)) {
+    case 1:
+        launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
+                      chunks, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    case 2:
+        launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
+                      chunks, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        break;
+    default:
+        launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
+                      chunks, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+    }
+}
+
+template <int DT>
+void sgmv_expand_chunk_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv,
+                           int64_t sl_stride, int nsl, const lora_chunk_desc *chunks, int nchunk, int ldl, int max_rank)
+{
+    // chunked launches need ldl <= 32: at most two 16-rank steps
+    const int nch = (max_rank + 15) / 16;
+    if (vecy) {
+        if (nch <= 1) sgmv_expand_chunk_go<DT, true, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+        else sgmv_expand_chunk_go<DT, true, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+    } else {
+        if (nch <= 1) sgmv_expand_chunk_go<DT, false, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+        else sgmv_expand_chunk_go<DT, false, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+    }
+}
+
+template <int DT>
+void sgmv_expand_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv, int64_t sl_stride,
+                     int nsl, const lora_blk_desc *blks, int nblk, int ldl)
+{
+    if (vecy) sgmv_expand_go<DT, true>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl);
+    else sgmv_expand_go<DT, false>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl);
 }
 
 void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
@@ -845,16 +960,20 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     const int ldl = lds_pitch(p.h->max_rank);
     const bool vecy = a.vec_y && a.d_out % 16 == 0;
     // chunks of up to 64 rows reuse B four times; use them when they still give
-    // enough workgroups and their staged v rows fit (64 rows x 64 ranks)
-    const bool chunked = p.h->num_chunks * ncol >= 1024 && ldl <= 64;
+    // enough workgroups and the B fragments of every rank fit in registers
+    // next to four y tiles (ranks <= 32; larger ranks lose more to occupancy
+    // than they gain from B reuse)
+    const bool chunked = p.h->num_chunks * ncol >= 1024 && ldl <= 32;
     if (chunked) {
-        const void *d = plan_chunks(p);
-        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16, 4>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl);
-        else sgmv_expand_go2<LORA_F32, 4>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl);
+        const lora_chunk_desc *d = plan_chunks(p);
+        if (a.dtype == LORA_BF16)
+            sgmv_expand_chunk_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank);
+        else
+            sgmv_expand_chunk_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank);
     } else {
-        const void *d = plan_blocks(p);
-        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16, 1>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
-        else sgmv_expand_go2<LORA_F32, 1>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
+        const lora_blk_desc *d = plan_blocks(p);
+        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
+        else sgmv_expand_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
     }
 }
 
