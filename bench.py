@@ -205,21 +205,22 @@ def kernel_source_digest(dominant):
     return h.hexdigest()
 
 
-def recorded_traffic(workload, kernel, dominant):
-    """HBM bytes per launch of `kernel` from the FETCH_SIZE and WRITE_SIZE
-    counter runs recorded in profiles/hbm_traffic.md (each scaled by the
-    factor the same counter gives for a copy of known size), or None when no
+def recorded_traffic(workload, role):
+    """HBM bytes per launch of the workload's `role` kernel (shrink, expand,
+    fused) from the FETCH_SIZE and WRITE_SIZE counter runs recorded in
+    profiles/hbm_traffic.md (each scaled by the factor the same counter gives
+    for a copy of known size), with the kernel's name; (None, None) when no
     figures exist or the kernel source has changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             line = next(l for l in fh if l.startswith("traffic-json: "))
         rec = json.loads(line[len("traffic-json: "):])
     except (OSError, StopIteration, ValueError):
-        return None
-    e = rec.get("entries", {}).get(f"{workload}/{kernel}")
-    if not e or e.get("source_sha256") != kernel_source_digest(dominant):
-        return None
-    return e.get("bytes_per_launch")
+        return None, None
+    e = rec.get("entries", {}).get(f"{workload}/{role}")
+    if not e or e.get("source_sha256") != kernel_source_digest(role):
+        return None, None
+    return e.get("bytes_per_launch"), e.get("kernel")
 
 
 def copy_calibration(reps=8):
@@ -333,9 +334,9 @@ def main():
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-    roof["kernel"] = {"shrink": f"{kind}_shrink_kernel", "expand": f"{kind}_expand_kernel",
-                      "fused": "fused_linear_kernel"}[dominant]
-    roof["traffic"] = recorded_traffic(CONFIG_NAMES[k], roof["kernel"], dominant)
+    traffic, kname = recorded_traffic(CONFIG_NAMES[k], dominant)
+    roof["traffic"] = traffic
+    roof["kernel"] = kname or {"shrink": f"{kind}_shrink", "expand": f"{kind}_expand", "fused": "fused_linear"}[dominant]
     roof["algorithmic_bytes_per_launch"] = round(dom_bytes)
     roof["avg_launch_us"] = round(dom_us, 3)
 
