@@ -47,19 +47,24 @@ constexpr int kBN = 192;                 // output columns per workgroup
 constexpr int kBM = 256;                 // plan rows per workgroup
 constexpr int kBK = 32;                  // k per stage
 constexpr int kStages = 5;               // LDS ring depth
-constexpr int kThreads = 256;            // 4 waves
-constexpr int kWN = 96, kWM = 128;       // wave tile
+constexpr int kThreads = 512;            // 8 waves, 2 per SIMD
+constexpr int kWaves = kThreads / 64;
+constexpr int kWN = 96, kWM = 64;        // wave tile: 2 x 4 waves cover 192 x 256
 constexpr int kTN = kWN / 16;            // MFMA tiles along columns (6)
-constexpr int kTM = kWM / 16;            // MFMA tiles along rows (8)
+constexpr int kTM = kWM / 16;            // MFMA tiles along rows (4)
 constexpr int kRowBytes = kBK * 2;       // 64
 constexpr int kWBytes = kBN * kRowBytes; // W0 part of a stage
 constexpr int kXBytes = kBM * kRowBytes; // x part of a stage
 constexpr int kStageBytes = kWBytes + kXBytes;
-constexpr int kWDma = kWBytes / 1024 / 4; // 1 KB direct loads per wave and stage (3)
-constexpr int kXDma = kXBytes / 1024 / 4; // (4)
+// 1 KB direct loads per stage: W0 part 12, split 2/1 over the waves (waves
+// below kWExtra take one more); x part 16, two per wave
+constexpr int kWInst = kWBytes / 1024, kXInst = kXBytes / 1024;
+constexpr int kWBase = kWInst / kWaves, kWExtra = kWInst % kWaves;
+constexpr int kWDma = kWBase + (kWExtra ? 1 : 0); // most W0 loads of a wave
+constexpr int kXDma = kXInst / kWaves;
 constexpr int kDma = kWDma + kXDma;
 constexpr int kMaxSlicesFused = 4; // bound on the shrink's d_in slices
-static_assert(kWDma * 4 * 1024 == kWBytes && kXDma * 4 * 1024 == kXBytes, "tile / wave split");
+static_assert(kXDma * kWaves == kXInst && kWBase >= 1, "tile / wave split");
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
 static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
 
@@ -287,13 +292,13 @@ __device__ __forceinline__ void lora_correction(const FusedArgs &a, int s0, int 
 }
 
 template <bool VECB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fused_linear_kernel(FusedArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_linear_kernel(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, g = lane >> 4;
-    const int wn = wave >> 1, wm = wave & 1; // wave position: column half, row half
+    const int wn = wave >> 2, wm = wave & 3; // wave position: column half, row quarter
     const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) char *)(lds)));
 
     // XCD-aware numbering: consecutive workgroups go to different XCDs, so
@@ -304,16 +309,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int m0 = tm * kBM, n0 = tn * kBN;
 
-    // Direct loads: lane `lane` of this wave's load j fills 16-byte unit
-    // (wave * n + j) * 64 + lane of the W0 or x part of a stage, i.e. LDS row
-    // u / 4, slot u % 4, which holds k unit (u % 4) ^ swz(row).  Per lane:
-    // the byte offset of that unit in stage 0 (row start + 16 * unit) and the
-    // unit's first k.
+    // Direct loads: lane `lane` of load instruction i fills 16-byte unit
+    // 64 i + lane of the W0 or x part of a stage, i.e. LDS row u / 4, slot
+    // u % 4, which holds k unit (u % 4) ^ swz(row).  This wave issues W0
+    // instructions wi0 .. wi0 + nw - 1 and x instructions kXDma * wave + j.
+    // Per lane: the byte offset of the unit in stage 0 (row start + 16 *
+    // unit) and the unit's first k.
+    const int nw = kWBase + (wave < kWExtra ? 1 : 0);
+    const int wi0 = wave * kWBase + (wave < kWExtra ? wave : kWExtra);
     uint32_t woff32[kWDma], xoff32[kXDma];
     int wk[kWDma], xk[kXDma];
 #pragma unroll
     for (int j = 0; j < kWDma; ++j) {
-        const int u = (wave * kWDma + j) * 64 + lane, rho = u >> 2;
+        const int u = ((j < nw ? wi0 + j : wi0)) * 64 + lane, rho = u >> 2;
         wk[j] = 8 * ((u & 3) ^ swz(rho));
         const int rp = rho % kWN;
         int c = n0 + (rho / kWN) * kWN + wave_col(rp & 15, rp >> 4);
@@ -339,7 +347,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const char *wb = reinterpret_cast<const char *>(a.W0) + int64_t(kt) * kRowBytes;
             const char *xb = reinterpret_cast<const char *>(a.x) + int64_t(kt) * kRowBytes;
 #pragma unroll
-            for (int j = 0; j < kWDma; ++j) dma16s(wb, woff32[j], base + uint32_t((wave * kWDma + j) * 1024));
+            for (int j = 0; j < kWDma; ++j)
+                if (j < nw) dma16s(wb, woff32[j], base + uint32_t((wi0 + j) * 1024));
 #pragma unroll
             for (int j = 0; j < kXDma; ++j)
                 dma16s(xb, xoff32[j], base + uint32_t(kWBytes + (wave * kXDma + j) * 1024));
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int j = 0; j < kWDma; ++j) {
                 const int k = kt * kBK + wk[j];
                 const char *row = reinterpret_cast<const char *>(a.W0) + woff32[j] - 2 * wk[j];
-                dma16(row + 2 * (k < a.d_in ? k : 0), base + uint32_t((wave * kWDma + j) * 1024));
+                if (j < nw) dma16(row + 2 * (k < a.d_in ? k : 0), base + uint32_t((wi0 + j) * 1024));
             }
 #pragma unroll
             for (int j = 0; j < kXDma; ++j) {
@@ -423,7 +432,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // stage kt + 1 complete (stages kt + 2, kt + 3 may be outstanding);
         // after the barrier every wave is past its reads of stage kt, so the
         // slot of stage kt - 1 is free for stage kt + 4
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
+        if (nw == kWDma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((kDma - 1) * (kStages - 3)));
         __builtin_amdgcn_s_barrier();
         const int nxt = kt + kStages - 1;
         issue(nxt < nk ? nxt : nk - 1);
