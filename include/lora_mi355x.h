@@ -312,6 +312,10 @@ const char *lora_last_error(void);
  * Errors: LORA_ERR_ARG (negative count, NULL array or event). */
 int lora_profile_launches(void **start_events, void **stop_events, int32_t count);
 
+/* Number of events of the current lora_profile_launches request that kernels
+ * have taken so far on this thread (how many kernels a call enqueued). */
+int32_t lora_profile_launches_used(void);
+
 /* Library version string. */
 const char *lora_version(void);
 

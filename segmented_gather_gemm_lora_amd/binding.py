@@ -41,7 +41,7 @@ EXPORTS = [
     "lora_plan_bytes", "lora_build_plan", "lora_plan_upload", "lora_sgmv_shrink",
     "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
-    "lora_version", "lora_profile_launches",
+    "lora_version", "lora_profile_launches", "lora_profile_launches_used",
 ]
 
 PLAN_HEADER_BYTES = 96
@@ -81,6 +81,7 @@ _SIGS = {
     "lora_last_error": (ctypes.c_char_p, []),
     "lora_version": (ctypes.c_char_p, []),
     "lora_profile_launches": (ctypes.c_int, [_vp, _vp, _i32]),
+    "lora_profile_launches_used": (ctypes.c_int32, []),
 }
 
 
@@ -217,6 +218,11 @@ class KernelTimer:
 
     def disarm(self):
         _check(lora_profile_launches(None, None, 0), "lora_profile_launches")
+
+    @staticmethod
+    def used() -> int:
+        """Launches that took events since the last arm()."""
+        return int(load().lora_profile_launches_used())
 
     def elapsed_us(self, i: int) -> float:
         hip = KernelTimer._hip

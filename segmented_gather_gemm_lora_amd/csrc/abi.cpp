@@ -140,6 +140,8 @@ int lora_profile_launches(void **start_events, void **stop_events, int32_t count
     return LORA_OK;
 }
 
+int32_t lora_profile_launches_used(void) { return launch_events().next; }
+
 const char *lora_version(void) { return "lora_mi355x 0.1.0 (gfx950)"; }
 
 const char *lora_last_error(void) { return g_last_error; }
