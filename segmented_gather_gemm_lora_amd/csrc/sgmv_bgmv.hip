@@ -516,13 +516,12 @@ __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t
 // that would wait for the store to finish); then the blocks are computed and
 // stored one at a time, with only one block's accumulators live.  The B
 // fragments of all NCH * 16 ranks stay in registers for the whole chunk.
-template <int DT, bool VECY, bool BV, int NCH, int UPT>
+template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB>
 __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                   const void *__restrict__ Bv, int r, float scale,
                                                   void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
                                                   const int *yrows, int vrow0, int nrows, float *vl, int ldl)
 {
-    constexpr int RB = LORA_PLAN_CHUNK_BLOCKS;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int ncol0 = ncol_wg + 64 * wave;
@@ -610,6 +609,9 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restric
                                          d->n, reinterpret_cast<float *>(vl4), ldl);
 }
 
+// 16-row blocks one workgroup takes from a chunk (a divisor of the chunk's
+// LORA_PLAN_CHUNK_BLOCKS; 2 and 4 measure the same on the prefill workload)
+constexpr int kChunkRB = LORA_PLAN_CHUNK_BLOCKS;
 template <int DT, bool VECY, int NCH, int UPT>
 __global__ __launch_bounds__(256) void sgmv_expand_chunk_kernel(const float *__restrict__ v, int64_t ldv,
                                                                 int64_t sl_stride, int nsl,
@@ -618,16 +620,23 @@ __global__ __launch_bounds__(256) void sgmv_expand_chunk_kernel(const float *__r
                                                                 bool vec_b, int ldl)
 {
     extern __shared__ floatx4 vl4[];
-    const lora_chunk_desc *d = chunks + blockIdx.y;
+    constexpr int parts = LORA_PLAN_CHUNK_BLOCKS / kChunkRB;
+    const lora_chunk_desc *d = chunks + blockIdx.y / parts;
+    const int part = int(blockIdx.y % parts);
+    const int q0 = part * kChunkRB * kRows;
+    const int n = d->n - q0;
+    if (n <= 0) return;
     const int r = d->rank;
     const void *B = reinterpret_cast<const void *>(d->B);
     float *vl = reinterpret_cast<float *>(vl4);
     if (vec_b && (r & 3) == 0)
-        expand_chunk_impl<DT, VECY, true, NCH, UPT>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
-                                                    blockIdx.x * kExpandCols, d->rows, d->p0, d->n, vl, ldl);
+        expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
+                                                              blockIdx.x * kExpandCols, d->rows + q0, d->p0 + q0,
+                                                              n < kChunkRB * kRows ? n : kChunkRB * kRows, vl, ldl);
     else
-        expand_chunk_impl<DT, VECY, false, NCH, UPT>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
-                                                     blockIdx.x * kExpandCols, d->rows, d->p0, d->n, vl, ldl);
+        expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
+                                                               blockIdx.x * kExpandCols, d->rows + q0, d->p0 + q0,
+                                                               n < kChunkRB * kRows ? n : kChunkRB * kRows, vl, ldl);
 }
 
 // ----------------------------------------------------------------------------
@@ -913,9 +922,9 @@ void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, in
                           const lora_chunk_desc *chunks, int nchunk, int ldl)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
-    const size_t shm = (size_t(LORA_PLAN_CHUNK_ROWS) * ldl + 4) * sizeof(float);
-    const dim3 grid(ncol, nchunk);
-    switch (units_per_thread(LORA_PLAN_CHUNK_BLOCKS, ldl)) {
+    const size_t shm = (size_t(kChunkRB * kRows) * ldl + 4) * sizeof(float);
+    const dim3 grid(ncol, nchunk * (LORA_PLAN_CHUNK_BLOCKS / kChunkRB));
+    switch (units_per_thread(kChunkRB, ldl)) {
     case 1:
         launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
                       chunks, a.y, a.ldy, a.d_out, a.vec_b, ldl);

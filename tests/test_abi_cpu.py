@@ -285,3 +285,21 @@ def test_workspace_bytes():
     for op in (0, 1, 2, 3):
         assert B.lora_workspace_bytes(op, 4096, 4096, 4096, 16) == 0
     assert B.lora_workspace_bytes(99, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
+
+
+def test_header_is_a_c_abi(tmp_path):
+    """tests/c/abi_c_check.c, built as C99 with gcc against the header and
+    linked with the library, runs the host-only entry points."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lib = B.lib_path()
+    exe = str(tmp_path / "abi_c_check")
+    src = os.path.join(ROOT, "tests", "c", "abi_c_check.c")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src, "-o", exe, lib,
+                    "-Wl,-rpath," + os.path.dirname(lib)], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True)
+    assert out.stdout.strip() == "ok"
