@@ -9,8 +9,9 @@
 // is read once per segment and reused for all of the segment's rows.
 //
 // Work unit: a block of up to 16 rows that share one adapter (a plan block, or
-// a group of decode tokens with the same id).  16 rows is the M of the 16x16
-// MFMA tiles used by both kernels:
+// a group of decode tokens with the same id); the SGMV expand of ranks <= 32
+// takes plan chunks of up to four blocks, so that each B tile serves 64 rows.
+// 16 rows is the M of the 16x16 MFMA tiles used by both kernels:
 //
 //  * shrink: D[token, rank] += X[token, k] * A[rank, k] on
 //    v_mfma_f32_16x16x32_bf16 (fp32 inputs: v_mfma_f32_16x16x4_f32).  Operands
@@ -20,10 +21,13 @@
 //    before the first MFMA.  A workgroup covers one slice of d_in;
 //    its waves are summed in LDS in a fixed order.  With several slices the
 //    slice results are fp32 partial sums, added in slice order by the expand.
+//    Each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of
+//    blocks, so the A slice of a segment is fetched into few L2s.
 //  * expand: D[column, token] += B[column, j] * v[token, j] on the fp32 MFMA
 //    (v stays fp32; bf16 B is widened exactly).  Output columns are assigned to
 //    MFMA rows so that each lane owns 16 consecutive columns of one token: y is
-//    prefetched at the start and written once, with 16-byte accesses.
+//    prefetched at the start and written once, with 16-byte accesses, rounded
+//    to bf16 with v_cvt_pk_bf16_f32.
 //
 // Latency: every load a workgroup needs depends on at most one earlier load
 // (the block descriptor, or the decode ids), so a kernel costs about two
@@ -317,9 +321,9 @@ __device__ __forceinline__ void y_store(void *yv, int64_t row_off, int ncol0, in
 }
 
 // ----------------------------------------------------------------------------
-// Expand of up to RB*16 rows that share one adapter, over this workgroup's 256
-// columns:  y[yrow, c] += scale * sum_{j<r} v[vrow, j] * B[c, j],  with v the
-// sum of `nsl` partial slices.
+// Expand of one block (up to 16 rows that share one adapter) over this
+// workgroup's 256 columns:  y[yrow, c] += scale * sum_{j<r} v[vrow, j] * B[c, j],
+// with v the sum of `nsl` partial slices.
 //   * loads are issued in the order their results are needed (the memory
 //     counter retires them in order): row indices, v slices, B fragments, y;
 //   * the workgroup adds the v slices of its rows once, into LDS (vl, rows of
@@ -412,7 +416,7 @@ __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_
     }
 }
 
-// LDS of an expand workgroup: RB*16 rows of ldl floats, then one spare float4
+// LDS of an expand workgroup: its rows (16 or 64) of ldl floats, then one spare float4
 // (at float offset `spare`) that absorbs the stores of units past the rows.
 template <bool BV, int UPT>
 __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare, const VStage<UPT> &st, float *vl)
@@ -439,7 +443,7 @@ __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare
     (void)q4;
 }
 
-template <int DT, int RB, bool VECY, bool BV, bool VIND, int UPT>
+template <int DT, bool VECY, bool BV, bool VIND, int UPT>
 __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                  const void *__restrict__ Bv, int r, float scale,
                                                  void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
@@ -449,64 +453,48 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     const int m = lane & 15, g = lane >> 4;
     const int ncol0 = ncol_wg + 64 * wave;
 
-    // 1. row indices of the y tiles
-    int yr[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        const int row = 16 * i + m;
-        yr[i] = row < nrows ? yrows[row] : -1;
-    }
+    // 1. row index of this lane's y row
+    const int yr = m < nrows ? yrows[m] : -1;
     const int ysafe = yrows[0];
-    // 2. v slices, 3. B fragments of the first 16 ranks, 4. y tiles; then the v
-    // slices are added into LDS while B and y are still in flight
+    // 2. v slices, 3. B fragments of the first 16 ranks, 4. the y tile; then the
+    // v slices are added into LDS while B and y are still in flight
     VStage<UPT> vst;
     stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[4][4];
     load_bfrag<DT, BV>(Bv, r, 4 * g, ncol0, m, d_out, bf);
-    YTile<DT> yt[RB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
-    stage_v_store<BV, UPT>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
+    YTile<DT> yt;
+    y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
+    stage_v_store<BV, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
     __syncthreads();
 
-    floatx4 acc[RB][4];
+    floatx4 acc[4];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{};
+    for (int t = 0; t < 4; ++t) acc[t] = floatx4{};
     const int nch = (r + 15) >> 4;
     for (int c = 0; c < nch; ++c) {
         const int j0 = 16 * c + 4 * g;
         if (c > 0) load_bfrag<DT, BV>(Bv, r, j0, ncol0, m, d_out, bf);
+        floatx4 vf = *reinterpret_cast<const floatx4 *>(vl + (m < nrows ? m : 0) * ldl + (j0 < ldl ? j0 : 0));
+        if (m >= nrows || j0 >= ldl) vf = floatx4{};
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (16 * i >= nrows) break;
-            const int row = 16 * i + m;
-            floatx4 vf = *reinterpret_cast<const floatx4 *>(vl + (row < nrows ? row : 0) * ldl + (j0 < ldl ? j0 : 0));
-            if (row >= nrows || j0 >= ldl) vf = floatx4{};
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[t][q], vf[q], acc[i][t], 0, 0, 0);
-        }
+            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[t][q], vf[q], acc[t], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-        if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc[i], scale);
+    if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
 }
 
-template <int DT, int RB, bool VECY, bool VIND, int UPT>
+template <int DT, bool VECY, bool VIND, int UPT>
 __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                             const void *__restrict__ Bv, int r, float scale, void *__restrict__ yv,
                                             int64_t ldy, int d_out, int ncol_wg, bool vec_b, const int *yrows,
                                             int vrow0, int nrows, float *vl, int ldl)
 {
     if (vec_b && (r & 3) == 0)
-        expand_rows_impl<DT, RB, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+        expand_rows_impl<DT, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
                                                         yrows, vrow0, nrows, vl, ldl);
     else
-        expand_rows_impl<DT, RB, VECY, false, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+        expand_rows_impl<DT, VECY, false, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
                                                          yrows, vrow0, nrows, vl, ldl);
 }
 
@@ -604,7 +592,7 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restric
 {
     extern __shared__ floatx4 vl4[];
     const lora_blk_desc *d = blks + blockIdx.y;
-    expand_rows<DT, 1, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
+    expand_rows<DT, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
                                          d->scale, y, ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0,
                                          d->n, reinterpret_cast<float *>(vl4), ldl);
 }
@@ -757,7 +745,7 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restric
         if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return;
         const int n = grp.n, total = grp.total;
         if (n == 0) return;
-        expand_rows<DT, 1, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
+        expand_rows<DT, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
                                             blockIdx.y * kExpandCols, vec_b, grp.rows, -1, n,
                                             reinterpret_cast<float *>(vl4), ldl);
         if (kRows * (pass + 1) >= total) break;

@@ -167,3 +167,33 @@ def test_side_stream(path):
     torch.cuda.synchronize()
     y_ref, _ = oracle.lora_forward(prob, nthreads=16)
     assert_close(c.y_out(), y_ref, "bf16", "side stream")
+
+
+def test_launch_counts():
+    """The combined calls enqueue exactly the kernels they document: SGMV and
+    BGMV one shrink and one expand, the fused layer shrink, split and GEMM."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob = make_config(2)
+    c = GpuCase(prob)
+    say("case launch counts")
+    timer = B.KernelTimer(8)
+    for path, want in (("sgmv", 2), ("bgmv", 2)):
+        timer.arm(0, 8)
+        c.run(path)
+        assert B.KernelTimer.used() == want, path
+        timer.disarm()
+    fused = make_problem(name="fused_count", dtype="bf16", ids=[0, 1, -1, 0], ranks=[8, 16], alphas=[16.0, 32.0],
+                         d_in=64, d_out=64, seed=3, w0_std=0.05)
+    pool = B.DevicePool.from_problem(fused)
+    plan = B.Plan(4).build(fused.ids, pool).upload()
+    ws = B.workspace(B.LORA_OP_FUSED, 4, 64, 64, 16)
+    y = torch.empty((4, 64), dtype=torch.bfloat16, device="cuda")
+    timer.arm(0, 8)
+    B.fused_linear(B.to_device(fused.x, "bf16"), B.to_device(fused.W0, "bf16"), plan, y, ws, "bf16")
+    assert B.KernelTimer.used() == 3
+    timer.disarm()
+    torch.cuda.synchronize()
+    timer.close()
