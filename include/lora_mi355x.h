@@ -268,9 +268,18 @@ int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, in
  * ("Multi-LoRA Serving" (fp-ai-systems.pages.dev), section "Serving it: batch
  * across adapters": one shared matmul for all requests plus a per-request
  * low-rank correction; "Multi-LoRA Serving in Production ...", layer equation).
- * Tokens without an adapter get x W0 only.  W0 is [d_out, d_in], bf16 only.
- * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_FUSED, T, d_in, d_out, max_rank).
- * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */
+ * Tokens without an adapter get x W0 only.  bf16 only; W0 is [d_out, d_in]
+ * with row pitch d_in.  x, W0, y and the workspace must be 16-byte aligned,
+ * ldx and ldy multiples of 8 elements and d_in a multiple of 8 (d_out is
+ * free).  Enqueues three kernels: the SGMV shrink into the workspace, a pass
+ * that writes scale_s * v as two bf16 halves (hi + lo, 16 significant bits),
+ * and one GEMM over the plan's rows whose bf16 MFMA accumulators also take the
+ * correction (fp32 accumulation, one rounding to bf16).  The plan must come
+ * from the same batch (its perm also lists the tokens without an adapter).
+ * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_FUSED, T, d_in, d_out, max_rank)
+ * (the shrink's slice partials plus T * 2 * round16(max_rank) bf16).
+ * Errors: as lora_sgmv_shrink; LORA_ERR_DTYPE for fp32; LORA_ERR_ALIGN for
+ * the alignment rules above; LORA_ERR_WORKSPACE. */
 int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
                       const void *W0, int32_t d_out,
                       const void *plan_host, const void *plan_dev,
