@@ -367,8 +367,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
     };
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1);
 
     // output rows of this lane (token tile i: plan row m0 + 128 wm + 16 i + m)
     int yrow[kTM];
@@ -384,7 +382,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < kTM; ++i) acc[t][i] = floatx4{};
 
-    // correction of the segments that meet this wave's rows (sorted rows only)
+    // correction of the segments that meet this wave's rows (sorted rows
+    // only), before the first direct loads go out, so that its loads do not
+    // queue behind them
     const int pw0 = m0 + kWM * wm;
     const int cw0 = n0 + kWN * wn;
     if (pw0 < a.Tp) {
@@ -393,6 +393,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int s1 = __builtin_amdgcn_readfirstlane(a.segidx[plast]);
         lora_correction<VECB>(a, s0, s1, pw0, cw0, lane, acc);
     }
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1);
 
     // fragment byte offsets inside a stage
     uint32_t woff[kTN], xoff[kTM];
