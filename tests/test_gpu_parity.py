@@ -204,3 +204,19 @@ def test_integer_bitwise_larger(dtype, path):
         assert np.array_equal(bits, f32_to_bf16_bits(y_ref.astype(np.float32)))
     else:
         assert np.array_equal(bits, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("path", ["bgmv", "bgmv_split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,n_pool", [(8, 50), (40, 200), (3, 1000)])
+def test_bgmv_large_pool(T, n_pool, dtype, path):
+    """Pools larger than twice the batch take the leader-token grid (one
+    workgroup per token; the first token of each adapter serves its group)."""
+    rng = np.random.default_rng(T * 7 + n_pool)
+    ranks = rng.choice([4, 8, 16, 24], n_pool).tolist()
+    ids = rng.integers(0, min(n_pool, 6), T).astype(np.int32)  # repeats: groups of several tokens
+    ids[rng.random(T) < 0.2] = -1
+    prob = make_problem(name=f"pool{n_pool}", dtype=dtype, ids=ids, ranks=ranks, alphas=[2.0 * r for r in ranks],
+                        d_in=256, d_out=320, seed=T + n_pool, a_std=0.05, b_std=0.05)
+    check_case(prob, path, False)
+    check_case(prob, path, True)
