@@ -193,8 +193,10 @@ int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_byte
  *     v[p, j] = sum_k x[perm[p], k] * A_s[j, k]    for j < r_s,
  * for every sorted position p of segment s.  v rows are in sorted order; the
  * columns j >= r_s of a row are left untouched.  Overwrites v.
- *   plan_host / plan_dev  the same plan, on the host (read for the launch
- *                         geometry) and on the device (read by the kernels)
+ *   plan_host / plan_dev  the same plan, on the host (read during the call for
+ *                         the launch geometry, and by the expand for the chunk
+ *                         descriptors it passes in the kernel arguments) and on
+ *                         the device (read by the kernels)
  *   v                     device fp32 [header.num_sorted, ldv], ldv >= max_rank,
  *                         ldv a multiple of 4
  * Errors: LORA_ERR_ARG, LORA_ERR_DTYPE, LORA_ERR_RANK, LORA_ERR_ALIGN,

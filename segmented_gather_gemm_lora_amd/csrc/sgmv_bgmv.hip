@@ -34,6 +34,8 @@
 // memory round trips plus its streaming time.
 #include "internal.h"
 
+#include <cstring>
+
 namespace lora {
 namespace {
 
@@ -504,11 +506,13 @@ __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t
 // that would wait for the store to finish); then the blocks are computed and
 // stored one at a time, with only one block's accumulators live.  The B
 // fragments of all NCH * 16 ranks stay in registers for the whole chunk.
-template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB>
+// CONTIG: the rows are the consecutive tokens ybase, ybase + 1, ... (yrows unused)
+template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB, bool CONTIG = false>
 __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                   const void *__restrict__ Bv, int r, float scale,
                                                   void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
-                                                  const int *yrows, int vrow0, int nrows, float *vl, int ldl)
+                                                  const int *yrows, int vrow0, int nrows, float *vl, int ldl,
+                                                  int ybase = 0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -518,9 +522,10 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
         const int row = 16 * i + m;
-        yr[i] = row < nrows ? yrows[row] : -1;
+        if constexpr (CONTIG) yr[i] = row < nrows ? ybase + row : -1;
+        else yr[i] = row < nrows ? yrows[row] : -1;
     }
-    const int ysafe = yrows[0];
+    const int ysafe = CONTIG ? ybase : yrows[0];
     VStage<UPT> vst;
     stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[NCH][4][4];
@@ -625,6 +630,61 @@ __global__ __launch_bounds__(256) void sgmv_expand_chunk_kernel(const float *__r
         expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, d->scale, y, ldy, d_out,
                                                                blockIdx.x * kExpandCols, d->rows + q0, d->p0 + q0,
                                                                n < kChunkRB * kRows ? n : kChunkRB * kRows, vl, ldl);
+}
+
+// Chunk descriptors passed in the kernel arguments: a workgroup's descriptor
+// then arrives with the other arguments instead of one dependent load later.
+struct ChunkArg {
+    uint64_t B;
+    float scale;
+    int32_t rank;
+    int32_t n;
+    int32_t p0;
+    int32_t row0; // token of the first row when the rows are consecutive tokens, else -1
+    int32_t pad;
+};
+static_assert(sizeof(ChunkArg) == 32, "one 8-dword scalar load per descriptor");
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+constexpr int kArgChunks = 112; // 3.5 KB of the 4 KB argument space
+struct ChunkArgs {
+    u32x8 c[kArgChunks]; // ChunkArg bits
+};
+
+template <int DT, bool VECY, int NCH, int UPT>
+__global__ __launch_bounds__(256) void sgmv_expand_chunk_arg_kernel(const float *__restrict__ v, int64_t ldv,
+                                                                    int64_t sl_stride, int nsl,
+                                                                    const lora_chunk_desc *__restrict__ chunks,
+                                                                    void *__restrict__ y, int64_t ldy, int d_out,
+                                                                    int vec_b, int ldl, const ChunkArgs tab)
+{
+    static_assert(kChunkRB == LORA_PLAN_CHUNK_BLOCKS, "one workgroup per chunk");
+    extern __shared__ floatx4 vl4[];
+    // the descriptor is read first, so that its load and those of the other
+    // arguments share one round trip
+    const u32x8 w = tab.c[blockIdx.y];
+    const uint64_t Bp = uint64_t(w[0]) | (uint64_t(w[1]) << 32);
+    const float scale = __uint_as_float(w[2]);
+    const int r = int(w[3]), n = int(w[4]), p0 = int(w[5]), row0 = int(w[6]);
+    __builtin_amdgcn_sched_barrier(0);
+    const void *B = reinterpret_cast<const void *>(Bp);
+    float *vl = reinterpret_cast<float *>(vl4);
+    const int ncw = blockIdx.x * kExpandCols;
+    const int *rows = chunks[blockIdx.y].rows;
+    if (vec_b && (r & 3) == 0) {
+        if (row0 >= 0)
+            expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB, true>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
+                                                                        d_out, ncw, rows, p0, n, vl, ldl, row0);
+        else
+            expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
+                                                                  ncw, rows, p0, n, vl, ldl);
+    } else {
+        if (row0 >= 0)
+            expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB, true>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
+                                                                         d_out, ncw, rows, p0, n, vl, ldl, row0);
+        else
+            expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
+                                                                   d_out, ncw, rows, p0, n, vl, ldl);
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -772,6 +832,12 @@ const lora_chunk_desc *plan_chunks(const PlanView &p)
     return reinterpret_cast<const lora_chunk_desc *>(p.dev + p.h->chunk_offset);
 }
 
+// the same chunk descriptors in the host copy of the plan
+const lora_chunk_desc *plan_chunks_host(const PlanView &p)
+{
+    return reinterpret_cast<const lora_chunk_desc *>(reinterpret_cast<const char *>(p.h) + p.h->chunk_offset);
+}
+
 int rank_tiles(int max_rank) { return max_rank <= 16 ? 1 : (max_rank <= 32 ? 2 : 4); }
 
 // LDS row pitch (floats) of the staged v rows
@@ -907,11 +973,37 @@ void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t 
 
 template <int DT, bool VECY, int NCH>
 void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
-                          const lora_chunk_desc *chunks, int nchunk, int ldl)
+                          const lora_chunk_desc *chunks, int nchunk, int ldl, const lora_chunk_desc *host_chunks)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const size_t shm = (size_t(kChunkRB * kRows) * ldl + 4) * sizeof(float);
     const dim3 grid(ncol, nchunk * (LORA_PLAN_CHUNK_BLOCKS / kChunkRB));
+    if (nchunk <= kArgChunks) {
+        ChunkArgs tab;
+        for (int i = 0; i < nchunk; ++i) {
+            const lora_chunk_desc &c = host_chunks[i];
+            bool consecutive = true;
+            const int nr = c.n < LORA_PLAN_CHUNK_ROWS ? c.n : LORA_PLAN_CHUNK_ROWS;
+            for (int q = 1; q < nr; ++q) consecutive = consecutive && c.rows[q] == c.rows[0] + q;
+            const ChunkArg ca{c.B, c.scale, c.rank, c.n, c.p0, consecutive ? c.rows[0] : -1, 0};
+            std::memcpy(&tab.c[i], &ca, sizeof(ca));
+        }
+        std::memset(&tab.c[nchunk], 0, sizeof(ChunkArg) * size_t(kArgChunks - nchunk));
+        switch (units_per_thread(kChunkRB, ldl)) {
+        case 1:
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+            break;
+        case 2:
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+            break;
+        default:
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+        }
+        return;
+    }
     switch (units_per_thread(kChunkRB, ldl)) {
     case 1:
         launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
@@ -929,16 +1021,17 @@ void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, in
 
 template <int DT>
 void sgmv_expand_chunk_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv,
-                           int64_t sl_stride, int nsl, const lora_chunk_desc *chunks, int nchunk, int ldl, int max_rank)
+                           int64_t sl_stride, int nsl, const lora_chunk_desc *chunks, int nchunk, int ldl, int max_rank,
+                           const lora_chunk_desc *host_chunks)
 {
     // chunked launches need ldl <= 32: at most two 16-rank steps
     const int nch = (max_rank + 15) / 16;
     if (vecy) {
-        if (nch <= 1) sgmv_expand_chunk_go<DT, true, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
-        else sgmv_expand_chunk_go<DT, true, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+        if (nch <= 1) sgmv_expand_chunk_go<DT, true, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
+        else sgmv_expand_chunk_go<DT, true, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
     } else {
-        if (nch <= 1) sgmv_expand_chunk_go<DT, false, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
-        else sgmv_expand_chunk_go<DT, false, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl);
+        if (nch <= 1) sgmv_expand_chunk_go<DT, false, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
+        else sgmv_expand_chunk_go<DT, false, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
     }
 }
 
@@ -964,9 +1057,11 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     if (chunked) {
         const lora_chunk_desc *d = plan_chunks(p);
         if (a.dtype == LORA_BF16)
-            sgmv_expand_chunk_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank);
+            sgmv_expand_chunk_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank,
+                                             plan_chunks_host(p));
         else
-            sgmv_expand_chunk_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank);
+            sgmv_expand_chunk_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank,
+                                             plan_chunks_host(p));
     } else {
         const lora_blk_desc *d = plan_blocks(p);
         if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);

@@ -123,6 +123,87 @@ def test_shapes(shape, path):
     check_case(prob, path, True)
 
 
+LONG_SEGMENT_SHAPES = [
+    # name, segment lengths, ranks, d_in, d_out, shuffled token order, none_frac, seed
+    # d_in 4608 is split into 3 slices of 1536 (a ragged last 512 of each)
+    ("mixed_lengths", [145, 40, 16, 130], [16, 5, 1, 13], 4608, 384, True, 0.05, 21),
+    ("d_in_8192", [200, 300], [16, 8], 8192, 256, False, 0.0, 22),
+    ("short_d_in", [100, 70], [12, 16], 200, 100, True, 0.0, 23),
+    ("prefill_like", [900, 37, 1500, 611], [16, 16, 16, 16], 4096, 4096, False, 0.0, 24),
+]
+
+
+def segmented_problem(name, lens, ranks, d_in, d_out, shuffled, none_frac, seed):
+    """Segments of the given lengths (adapter i for segment i), in token order,
+    shuffled so that every segment's rows are gathered (True), or with only the
+    tokens after the first segment shuffled ("tail")."""
+    rng = np.random.default_rng(seed)
+    ids = np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+    if shuffled == "tail":
+        ids[lens[0]:] = rng.permutation(ids[lens[0]:])
+    elif shuffled:
+        ids = rng.permutation(ids).astype(np.int32)
+    ids[rng.random(len(ids)) < none_frac] = -1
+    return make_problem(name=name, dtype="bf16", ids=ids, ranks=ranks, alphas=[2.0 * r for r in ranks], d_in=d_in,
+                        d_out=d_out, seed=seed, a_std=0.05, b_std=0.05)
+
+
+@pytest.mark.parametrize("shape", LONG_SEGMENT_SHAPES, ids=[s[0] for s in LONG_SEGMENT_SHAPES])
+def test_long_segment_shapes(shape):
+    prob = segmented_problem(*shape)
+    check_case(prob, "sgmv", False)
+    check_case(prob, "sgmv", True)
+
+
+def test_long_segment_integer_bitwise():
+    """Entries in {-1,0,1}, scale 1, two long segments over d_in 4608 (three
+    slices): fp32 sums are exact, so the bf16 output equals the exact integer
+    result rounded once."""
+    from lora_workloads import f32_to_bf16_bits
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob = make_integer_problem(seed=31, dtype="bf16", T=300, d_in=4608, d_out=200, n_adapters=2, ranks=[3, 4],
+                                none_frac=0.05)
+    say("case long-segment integer")
+    c = GpuCase(prob)
+    c.run("sgmv")
+    y_ref, _ = oracle.lora_forward(prob)
+    assert np.array_equal(B.to_host_bits(c.y, "bf16"), f32_to_bf16_bits(y_ref.astype(np.float32)))
+
+
+ARG_TABLE_CHUNKS = 112  # chunk descriptors the chunked expand takes in its kernel arguments
+
+
+def chunked_expand(plan, d_out):
+    """Whether the SGMV expand runs on 64-row chunks (chunks x 256-column tiles
+    >= 1024 and max rank <= 32), and whether its chunk table fits in the kernel
+    arguments."""
+    h = plan.header()
+    ncol = (d_out + 255) // 256
+    return h["num_chunks"] * ncol >= 1024 and h["max_rank"] <= 32, h["num_chunks"] <= ARG_TABLE_CHUNKS
+
+
+CHUNK_EXPAND_SHAPES = [
+    # name, segment lengths, ranks, d_in, d_out, shuffled, none_frac, seed, expected table use
+    # every chunk gathered (rows not consecutive)
+    ("gathered_rows", [700, 500, 600, 248], [16, 8, 4, 12], 256, 8192, True, 0.0, 41, True),
+    # consecutive chunks next to gathered ones, ranks up to 32 (two 16-rank steps)
+    ("mixed_rows", [1100, 300, 300, 300], [32, 16, 24, 8], 256, 8192, "tail", 0.0, 42, True),
+    # more chunks than the argument table holds: descriptors read from the plan
+    ("table_overflow", [5000, 3000], [16, 8], 256, 4096, False, 0.02, 43, False),
+]
+
+
+@pytest.mark.parametrize("shape", CHUNK_EXPAND_SHAPES, ids=[s[0] for s in CHUNK_EXPAND_SHAPES])
+def test_chunk_expand_shapes(shape):
+    *args, table = shape
+    prob = segmented_problem(*args)
+    _, plan = GpuCase(prob).run("sgmv")
+    assert chunked_expand(plan, prob.d_out) == (True, table), "shape no longer reaches the intended expand"
+    check_case(prob, "sgmv", False)
+    check_case(prob, "sgmv_split", True)
+
+
 @pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_all_tokens_without_adapter(dtype, path):
