@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
-    python bench.py [--config decode|prefill|hetero|fused|tiny] [--steps K] [--warmup W]
+    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv] [--steps K] [--warmup W]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
 every token (BGMV for the decode workload, SGMV from a prebuilt plan for the
@@ -112,6 +112,162 @@ class Instance:
             B.bgmv(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
         else:
             B.sgmv(self.x, self.plan, self.y, self.ws, self.dt)
+
+
+class GroupedInstance:
+    """One layer's q, k, v decode inputs (shared x, own adapters and outputs)
+    for the grouped call, and the same work as separate single calls."""
+
+    def __init__(self, probs):
+        import torch
+
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        self.probs = probs
+        self.pools = [B.DevicePool.from_problem(p) for p in probs]
+        self.x = B.to_device(probs[0].x, probs[0].dtype)
+        self.ys = [B.to_device(p.y_base(), p.dtype) for p in probs]
+        self.ids = torch.from_numpy(np.ascontiguousarray(probs[0].ids, dtype=np.int32)).cuda()
+        self.xs = [self.x] * len(probs)
+        self.projs = B.proj_array(self.xs, self.pools, self.ys)
+        self.ws = B.bgmv_grouped_workspace(probs[0].T, self.projs)
+        self.ws1 = [B.workspace(B.LORA_OP_BGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
+
+    def step(self):
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        B.bgmv_grouped(self.xs, self.ids, self.pools, self.ys, self.ws, self.probs[0].dtype, projs=self.projs)
+
+    def step_separate(self):
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        for p, prob in enumerate(self.probs):
+            B.bgmv(self.x, self.ids, self.pools[p], self.ys[p], self.ws1[p], prob.dtype)
+
+
+def grouped_bytes(probs):
+    """Algorithmic bytes of one grouped step: the shared x once, each
+    projection's distinct adapters' A and B once, each y read and written once."""
+    per = [algorithmic_bytes(p) for p in probs]
+    x_bytes = probs[0].T * probs[0].d_in * probs[0].esize
+    shrink = x_bytes + sum(a["shrink"] - x_bytes for a in per)
+    expand = sum(a["expand"] for a in per)
+    return {"shrink": shrink, "expand": expand, "total": shrink + expand}
+
+
+def time_steps(step, K, stream):
+    import torch
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / K, time.perf_counter() - t0
+
+
+def grouped_main(args):
+    """The q, k, v decode projections in one grouped shrink + expand (two
+    launches), with the same work as three single BGMV calls timed beside it."""
+    import torch
+
+    import oracle
+    from lora_workloads import QKV_NAME, make_decode_qkv
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    probs0 = make_decode_qkv()
+    ab0 = grouped_bytes(probs0)
+    L = args.rotation or rotation_count(ab0["total"])
+    print(f"[bench] {QKV_NAME}: T={probs0[0].T} d_in={probs0[0].d_in} d_out={[p.d_out for p in probs0]} "
+          f"rotation={L} bytes/layer={ab0['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
+    insts = [GroupedInstance(probs0)] + [GroupedInstance(make_decode_qkv(seed=2000 + i)) for i in range(1, L)]
+    ab_all = [grouped_bytes(g.probs) for g in insts]
+    bytes_step = float(np.mean([a["total"] for a in ab_all]))
+    T = probs0[0].T
+    K = args.steps if args.steps is not None else 20 * L
+    W = args.warmup if args.warmup is not None else 10 * L
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        insts[i % L].step()
+        insts[i % L].step_separate()
+    torch.cuda.synchronize()
+    ms_step, t_wall = time_steps(lambda i: insts[i % L].step(), K, stream)
+    ms_sep, _ = time_steps(lambda i: insts[i % L].step_separate(), K, stream)
+
+    probe = B.KernelTimer(8)
+    probe.arm(0, 8)
+    insts[0].step()
+    used = B.KernelTimer.used()
+    probe.disarm()
+    torch.cuda.synchronize()
+    probe.close()
+    names = ["shrink", "expand"]
+    assert used == 2, used
+    K2 = max(L, min(K, 20 * L))
+    timer = B.KernelTimer(K2 * 2)
+    for i in range(K2):
+        timer.arm(i * 2, 2)
+        insts[i % L].step()
+    timer.disarm()
+    torch.cuda.synchronize()
+    per_kernel_us = {n: float(np.mean([timer.elapsed_us(i * 2 + j) for i in range(K2)])) for j, n in enumerate(names)}
+    timer.close()
+    dominant = max(names, key=lambda n: per_kernel_us[n])
+    dom_bytes = float(np.mean([a[dominant] for a in ab_all]))
+    dom_us = per_kernel_us[dominant]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic, kname = recorded_traffic(QKV_NAME, dominant)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": kname or f"bgmv_{dominant}_grouped_kernel", "algorithmic_bytes_per_launch": round(dom_bytes),
+            "avg_launch_us": round(dom_us, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        oracle.build(force=False)
+        cores = max(1, min(16, os.cpu_count() or 1))
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            for p in probs0:
+                oracle.lora_forward(p, nthreads=cores)
+            reps += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": reps * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"{reps} full q/k/v layers of {T} tokens ({el:.1f} s, fp64, OpenMP over tokens)"}
+
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": probs0[0].dtype,
+        "data": "synthetic",
+        "config": {"workload": QKV_NAME, "T": T, "d_in": probs0[0].d_in, "d_out": [p.d_out for p in probs0],
+                   "ranks": [16], "pool_adapters": probs0[0].n_adapters,
+                   "distinct_adapters": int(len(probs0[0].distinct_adapters())), "rotated_instances": L,
+                   "path": "bgmv_grouped"},
+        "achieved_GBps": round(gbps, 1),
+        "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": round(bytes_step),
+        "per_kernel_us": {n: round(v, 3) for n, v in per_kernel_us.items()},
+        "separate_calls_ms_per_step": round(ms_sep, 6),
+        "separate_calls": "the same q, k, v work as three lora_bgmv calls (six launches)",
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
 
 
 def base_gemm_reference_us(inst, reps=50):
@@ -241,7 +397,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", choices=sorted(CONFIG_OF), default="decode")
+    ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv"], default="decode")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
@@ -266,6 +422,9 @@ def main():
         copy_calibration()
         return
     B.load()
+    if args.config == "decode_qkv":
+        grouped_main(args)
+        return
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
 

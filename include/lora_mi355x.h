@@ -264,6 +264,46 @@ int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, in
               int32_t n_adapters, int32_t max_rank,
               void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------ grouped BGMV
+ * Several projections of a layer in one shrink launch and one expand launch,
+ * after the pages' grouped invocation that serves every active adapter of all
+ * projections at once instead of one launch per projection ("Multi-LoRA
+ * Serving in Production ...", section "Ragged Batching and FlashInfer Grouped
+ * GEMM"; the per-launch cost it removes is in section "Kernel Architectures:
+ * SGMV, MBGMV, and Grouped GEMMs").  Every projection p applies
+ *     y_p[t, :] += (alpha_{i,p} / r_{i,p}) (x_p[t, :] A_{i,p}) B_{i,p},  i = ids[t],
+ * with one adapter id per token for all projections and its own x, y, sizes
+ * and adapter tables.  Projections whose inputs are the same tensor (q, k, v;
+ * gate, up) may pass the same x.  Each projection gives the same result as a
+ * lora_bgmv call with its arguments (same d_in split and summation order). */
+#define LORA_MAX_PROJ 8 /* projections per grouped call */
+
+typedef struct lora_proj {
+    const void *x;              /* device [T, ldx] of the call's dtype */
+    void *y;                    /* device [T, ldy]; the y of two projections share no element */
+    const uint64_t *pool_A_dev; /* [n_adapters] device addresses of A_{i,p}, [r, d_in] */
+    const uint64_t *pool_B_dev; /* [n_adapters] device addresses of B_{i,p}, [d_out, r] */
+    const int32_t *pool_rank_dev; /* [n_adapters] device r_{i,p} */
+    const float *pool_alpha_dev;  /* [n_adapters] device alpha_{i,p} */
+    int64_t ldx, ldy;
+    int32_t d_in, d_out;
+    int32_t max_rank;           /* upper bound of the projection's ranks, [1, 256] */
+    int32_t reserved;           /* 0 */
+} lora_proj;
+
+/* Workspace bytes of lora_bgmv_grouped for T tokens and these projections
+ * (host array of n_proj, 1 <= n_proj <= LORA_MAX_PROJ); 0 if the arguments
+ * are invalid. */
+size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj);
+
+/*   ids_dev  [T] device int32, -1 = none; n_adapters entries in every table
+ *   projs    host array of n_proj projections (read during the call)
+ *   ws       device, 16-byte aligned, >= lora_bgmv_grouped_workspace_bytes
+ * Errors: LORA_ERR_ARG (also: two projections with the same y), LORA_ERR_DTYPE,
+ * LORA_ERR_RANK, LORA_ERR_ALIGN, LORA_ERR_WORKSPACE, LORA_ERR_HIP. */
+int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev, int32_t n_adapters,
+                      const lora_proj *projs, int32_t n_proj, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------ fused layer
  * The whole adapted layer: the shared base product once for every token plus
  * each token's correction, y = x W0 + scale_s (x A_s) B_s, overwriting y

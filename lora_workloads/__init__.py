@@ -13,6 +13,8 @@ from .synth import (  # noqa: F401
     make_config,
     make_problem,
     make_integer_problem,
+    make_decode_qkv,
+    QKV_NAME,
     CONFIG_NAMES,
     zipf_probs,
 )

@@ -311,6 +311,28 @@ def make_config(k: int, seed: Optional[int] = None) -> LoraProblem:
     raise ValueError(f"unknown config {k}")
 
 
+QKV_NAME = "decode_qkv_grouped_bf16"
+
+
+def make_decode_qkv(seed: int = 2, d_outs: Sequence[int] = (4096, 1024, 1024)) -> list:
+    """The q, k and v projections of one decode batch, for the grouped call: the
+    decode workload's 64 tokens, ids (uniform over a pool of 32 adapters of rank
+    16, alpha 32) and value distributions, d_in 4096, d_out 4096 / 1024 / 1024
+    (grouped-query attention with a quarter of the heads for k and v).  One id
+    per token for all three projections; x is shared (the same array object);
+    every projection has its own adapters (A, B) and base output."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, 32, 64).astype(np.int32)
+    probs = []
+    for p, d_out in enumerate(d_outs):
+        prob = make_problem(name=f"{QKV_NAME}/{'qkv'[p] if p < 3 else p}", dtype="bf16", ids=ids, ranks=[16] * 32,
+                            alphas=[32.0] * 32, d_in=4096, d_out=d_out, seed=seed, rng=rng)
+        if p > 0:
+            prob.x = probs[0].x
+        probs.append(prob)
+    return probs
+
+
 def make_integer_problem(
     *, seed: int, dtype: str, T: int, d_in: int, d_out: int, n_adapters: int,
     ranks: Optional[Sequence[int]] = None, with_w0: bool = False, none_frac: float = 0.0,

@@ -41,8 +41,10 @@ EXPORTS = [
     "lora_plan_bytes", "lora_build_plan", "lora_plan_upload", "lora_sgmv_shrink",
     "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
-    "lora_version", "lora_profile_launches", "lora_profile_launches_used",
+    "lora_version", "lora_profile_launches", "lora_profile_launches_used", "lora_bgmv_grouped",
+    "lora_bgmv_grouped_workspace_bytes",
 ]
+MAX_PROJ = 8
 
 PLAN_HEADER_BYTES = 96
 CHUNK_BLOCKS = 4
@@ -82,7 +84,20 @@ _SIGS = {
     "lora_version": (ctypes.c_char_p, []),
     "lora_profile_launches": (ctypes.c_int, [_vp, _vp, _i32]),
     "lora_profile_launches_used": (ctypes.c_int32, []),
+    "lora_bgmv_grouped": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _sz]),
+    "lora_bgmv_grouped_workspace_bytes": (_sz, [_i32, _vp, _i32]),
 }
+
+
+class LoraProj(ctypes.Structure):
+    """struct lora_proj: one projection of a grouped BGMV call."""
+
+    _fields_ = [("x", _vp), ("y", _vp), ("pool_A_dev", _vp), ("pool_B_dev", _vp), ("pool_rank_dev", _vp),
+                ("pool_alpha_dev", _vp), ("ldx", _i64), ("ldy", _i64), ("d_in", _i32), ("d_out", _i32),
+                ("max_rank", _i32), ("reserved", _i32)]
+
+
+assert ctypes.sizeof(LoraProj) == 80
 
 
 def lib_path() -> str:
@@ -175,6 +190,14 @@ def lora_bgmv_expand(stream, dtype, T, v, ldv, ids, pool_B, pool_rank, pool_alph
                      y, ldy, d_out, ws, ws_bytes) -> int:
     return int(load().lora_bgmv_expand(stream, dtype, T, v, ldv, ids, pool_B, pool_rank, pool_alpha,
                                        n_adapters, max_rank, y, ldy, d_out, ws, ws_bytes))
+
+
+def lora_bgmv_grouped(stream, dtype, T, ids, n_adapters, projs, n_proj, ws, ws_bytes) -> int:
+    return int(load().lora_bgmv_grouped(stream, dtype, T, ids, n_adapters, projs, n_proj, ws, ws_bytes))
+
+
+def lora_bgmv_grouped_workspace_bytes(T, projs, n_proj) -> int:
+    return int(load().lora_bgmv_grouped_workspace_bytes(T, projs, n_proj))
 
 
 def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy, ws, ws_bytes) -> int:
@@ -427,6 +450,41 @@ def bgmv(x, ids_dev, pool: DevicePool, y, ws, dtype: str, max_rank: Optional[int
                      _ptr(pool.alpha_dev), pool.n_adapters, max_rank or pool.max_rank, _ptr(y), y.stride(0),
                      y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_bgmv")
+
+
+def proj_array(xs, pools, ys, max_ranks=None):
+    """Host array of struct lora_proj for projections (xs[p], pools[p], ys[p])."""
+    n = len(xs)
+    arr = (LoraProj * n)()
+    for p in range(n):
+        x, pool, y = xs[p], pools[p], ys[p]
+        arr[p] = LoraProj(_ptr(x), _ptr(y), _ptr(pool.addr_A_dev), _ptr(pool.addr_B_dev), _ptr(pool.rank_dev),
+                          _ptr(pool.alpha_dev), x.stride(0), y.stride(0), x.shape[1], y.shape[1],
+                          int(max_ranks[p]) if max_ranks is not None else max(pool.max_rank, 1), 0)
+    return arr
+
+
+def bgmv_grouped_workspace(T: int, projs, device="cuda"):
+    torch = _torch()
+    nbytes = lora_bgmv_grouped_workspace_bytes(T, ctypes.cast(projs, _vp), len(projs))
+    if nbytes == 0 and T > 0:
+        raise ValueError("invalid projections for a grouped workspace")
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def bgmv_grouped(xs, ids_dev, pools, ys, ws, dtype: str, max_ranks=None, stream=None, projs=None):
+    """Decode for several projections in one shrink and one expand launch:
+    ys[p][t] += scale (xs[p][t] A_{ids[t],p}) B_{ids[t],p}.  All pools share the
+    adapter numbering of ids_dev."""
+    n_adapters = pools[0].n_adapters
+    if any(p.n_adapters != n_adapters for p in pools):
+        raise ValueError("every projection's pool must number the same adapters as ids_dev")
+    if projs is None:
+        projs = proj_array(xs, pools, ys, max_ranks)
+    T = xs[0].shape[0]
+    _check(lora_bgmv_grouped(_stream_handle(stream), DTYPES[dtype], T, _ptr(ids_dev), n_adapters,
+                             ctypes.cast(projs, _vp), len(projs), _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_bgmv_grouped")
 
 
 def bgmv_shrink(x, ids_dev, pool: DevicePool, v, dtype: str, max_rank: Optional[int] = None, stream=None):

@@ -438,6 +438,61 @@ int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, in
                        pool_alpha_dev, n_adapters, max_rank, ws);
 }
 
+size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj)
+{
+    if (T < 0 || !projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;
+    size_t total = 0;
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_proj &q = projs[p];
+        if (q.max_rank < 1 || q.max_rank > LORA_MAX_RANK) return 0;
+        total += grouped_region_bytes(T, q.d_in < 1 ? 1 : q.d_in, q.max_rank);
+    }
+    return total;
+}
+
+int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev, int32_t n_adapters,
+                      const lora_proj *projs, int32_t n_proj, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (T < 0 || T > 65536) return fail(LORA_ERR_ARG, "T %d outside [0, 65536]", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (!projs) return fail(LORA_ERR_ARG, "projs is NULL");
+    if (n_proj < 1 || n_proj > LORA_MAX_PROJ)
+        return fail(LORA_ERR_ARG, "n_proj %d outside [1, %d]", n_proj, LORA_MAX_PROJ);
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_proj &q = projs[p];
+        if (q.max_rank < 1 || q.max_rank > LORA_MAX_RANK)
+            return fail(LORA_ERR_RANK, "projection %d: max_rank %d outside [1, 256]", p, q.max_rank);
+        if (!q.pool_A_dev || !q.pool_B_dev || !q.pool_rank_dev || !q.pool_alpha_dev)
+            return fail(LORA_ERR_ARG, "projection %d: device tables are NULL", p);
+        for (int o = 0; o < p; ++o)
+            if (projs[o].y == q.y) return fail(LORA_ERR_ARG, "projections %d and %d write the same y", o, p);
+    }
+    if (T == 0) return LORA_OK;
+    if (!ids_dev) return fail(LORA_ERR_ARG, "ids_dev is NULL");
+    const size_t need = lora_bgmv_grouped_workspace_bytes(T, projs, n_proj);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    GroupedProj gp[LORA_MAX_PROJ];
+    char *region = static_cast<char *>(ws);
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_proj &q = projs[p];
+        const int64_t ldw = (q.max_rank + 3) / 4 * 4;
+        float *v = reinterpret_cast<float *>(region);
+        if ((st = make_shrink_args(dtype, q.x, q.ldx, q.d_in, v, ldw, q.max_rank, &gp[p].sa))) return st;
+        if ((st = make_expand_args(dtype, v, ldw, q.max_rank, q.y, q.ldy, q.d_out, true, &gp[p].ea))) return st;
+        gp[p].pool_A = q.pool_A_dev;
+        gp[p].pool_B = q.pool_B_dev;
+        gp[p].pool_rank = q.pool_rank_dev;
+        gp[p].pool_alpha = q.pool_alpha_dev;
+        gp[p].max_rank = q.max_rank;
+        region += grouped_region_bytes(T, q.d_in, q.max_rank);
+    }
+    return launch_bgmv_grouped(static_cast<hipStream_t>(stream), T, ids_dev, n_adapters, gp, n_proj);
+}
+
 int lora_bgmv_shrink(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
                      const int32_t *ids_dev, const uint64_t *pool_A_dev, const int32_t *pool_rank_dev,
                      int32_t n_adapters, int32_t max_rank, float *v, int64_t ldv, void *ws, size_t ws_bytes)

@@ -55,6 +55,22 @@ int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                 int32_t n_adapters, int32_t max_rank, void *ws);
+// One projection of a grouped BGMV call: its shrink (x, d_in, v = its
+// workspace region) and expand (y, d_out) arguments and its adapter tables.
+struct GroupedProj {
+    ShrinkArgs sa;
+    ExpandArgs ea;
+    const uint64_t *pool_A;
+    const uint64_t *pool_B;
+    const int32_t *pool_rank;
+    const float *pool_alpha;
+    int32_t max_rank;
+};
+int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
+                        int n);
+// Bytes of one projection's region in a grouped workspace (256-byte multiple).
+size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank);
+
 // Workspace of the combined calls and of the fused entry: fp32 partial sums of
 // the shrink over d_in slices.
 size_t combined_workspace_bytes(int32_t rows, int32_t d_in, int32_t max_rank);

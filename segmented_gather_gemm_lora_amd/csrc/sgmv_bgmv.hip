@@ -748,12 +748,11 @@ __device__ bool bgmv_group(const int32_t *__restrict__ ids, int T, int t, int a,
 // token (blockIdx.x = t; it serves its adapter's tokens when it is the first
 // of them).  The adapter tables are read in parallel with the ids scan.
 template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
-__global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in, int T,
-                                                             const int32_t *__restrict__ ids,
-                                                             const uint64_t *__restrict__ pool_A,
-                                                             const int32_t *__restrict__ pool_rank, int n_adapters,
-                                                             int max_rank, int slice_len, float *__restrict__ out,
-                                                             int64_t ldo, int64_t sl_stride)
+__device__ __forceinline__ void bgmv_shrink_body(const void *__restrict__ x, int64_t ldx, int d_in, int T,
+                                                 const int32_t *__restrict__ ids, const uint64_t *__restrict__ pool_A,
+                                                 const int32_t *__restrict__ pool_rank, int n_adapters, int max_rank,
+                                                 int slice_len, float *__restrict__ out, int64_t ldo,
+                                                 int64_t sl_stride)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     __shared__ Group grp;
@@ -779,14 +778,25 @@ __global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restr
     }
 }
 
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
+__global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in, int T,
+                                                             const int32_t *__restrict__ ids,
+                                                             const uint64_t *__restrict__ pool_A,
+                                                             const int32_t *__restrict__ pool_rank, int n_adapters,
+                                                             int max_rank, int slice_len, float *__restrict__ out,
+                                                             int64_t ldo, int64_t sl_stride)
+{
+    bgmv_shrink_body<DT, VEC, W, NSTEP, RT, SLOT>(x, ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank,
+                                                  slice_len, out, ldo, sl_stride);
+}
+
 template <int DT, bool SLOT, bool VECY, int UPT>
-__global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
-                                                          int nsl, int T, const int32_t *__restrict__ ids,
-                                                          const uint64_t *__restrict__ pool_B,
-                                                          const int32_t *__restrict__ pool_rank,
-                                                          const float *__restrict__ pool_alpha, int n_adapters,
-                                                          int max_rank, void *__restrict__ y, int64_t ldy, int d_out,
-                                                          bool vec_b, int ldl)
+__device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                                 int T, const int32_t *__restrict__ ids,
+                                                 const uint64_t *__restrict__ pool_B,
+                                                 const int32_t *__restrict__ pool_rank,
+                                                 const float *__restrict__ pool_alpha, int n_adapters, int max_rank,
+                                                 void *__restrict__ y, int64_t ldy, int d_out, bool vec_b, int ldl)
 {
     extern __shared__ floatx4 vl4[];
     __shared__ Group grp;
@@ -810,6 +820,70 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restric
                                             reinterpret_cast<float *>(vl4), ldl);
         if (kRows * (pass + 1) >= total) break;
     }
+}
+
+template <int DT, bool SLOT, bool VECY, int UPT>
+__global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+                                                          int nsl, int T, const int32_t *__restrict__ ids,
+                                                          const uint64_t *__restrict__ pool_B,
+                                                          const int32_t *__restrict__ pool_rank,
+                                                          const float *__restrict__ pool_alpha, int n_adapters,
+                                                          int max_rank, void *__restrict__ y, int64_t ldy, int d_out,
+                                                          bool vec_b, int ldl)
+{
+    bgmv_expand_body<DT, SLOT, VECY, UPT>(v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters,
+                                          max_rank, y, ldy, d_out, vec_b, ldl);
+}
+
+// ----------------------------------------------------------------------------
+// Grouped BGMV: several projections of a layer, each with its own x, y, sizes
+// and adapter tables but one adapter id per token for all of them, in one
+// shrink launch and one expand launch.  blockIdx.z is the projection; its
+// arguments come from a table in the kernel arguments.  Workgroups past a
+// projection's own d_in slices or column tiles exit at once.
+// ----------------------------------------------------------------------------
+struct GShrink {
+    const void *x;
+    const uint64_t *pool_A;
+    const int32_t *pool_rank;
+    float *out;
+    int64_t ldx, ldo, sl_stride;
+    int32_t d_in, max_rank, slice_len, kc;
+};
+struct GShrinkTable {
+    GShrink p[LORA_MAX_PROJ];
+};
+struct GExpand {
+    const float *v;
+    const uint64_t *pool_B;
+    const int32_t *pool_rank;
+    const float *pool_alpha;
+    void *y;
+    int64_t ldv, sl_stride, ldy;
+    int32_t nsl, max_rank, d_out, ldl, ncol, vec_b;
+};
+struct GExpandTable {
+    GExpand p[LORA_MAX_PROJ];
+};
+
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
+__global__ __launch_bounds__(W * 64) void bgmv_shrink_grouped_kernel(int T, const int32_t *__restrict__ ids,
+                                                                     int n_adapters, const GShrinkTable tab)
+{
+    const GShrink &P = tab.p[blockIdx.z];
+    if (int(blockIdx.y) >= P.kc) return;
+    bgmv_shrink_body<DT, VEC, W, NSTEP, RT, SLOT>(P.x, P.ldx, P.d_in, T, ids, P.pool_A, P.pool_rank, n_adapters,
+                                                  P.max_rank, P.slice_len, P.out, P.ldo, P.sl_stride);
+}
+
+template <int DT, bool SLOT, bool VECY, int UPT>
+__global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const int32_t *__restrict__ ids,
+                                                                  int n_adapters, const GExpandTable tab)
+{
+    const GExpand &P = tab.p[blockIdx.z];
+    if (int(blockIdx.y) >= P.ncol) return;
+    bgmv_expand_body<DT, SLOT, VECY, UPT>(P.v, P.ldv, P.sl_stride, P.nsl, T, ids, P.pool_B, P.pool_rank, P.pool_alpha,
+                                          n_adapters, P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl);
 }
 
 // ----------------------------------------------------------------------------
@@ -938,6 +1012,28 @@ template <int DT, bool VEC, int RT> struct BgmvShrinkL {
             else
                 launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, false>, grid, dim3(256), 0, s, x, ldx, d_in, T,
                               ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+        }
+    }
+};
+
+template <int DT, bool VEC, int RT> struct BgmvShrinkGroupedL {
+    static void run(hipStream_t s, dim3 grid, int T, const int32_t *ids, int n_adapters, bool slot, bool two,
+                    const GShrinkTable &tab)
+    {
+        if (slot) {
+            if (two && RT < 4)
+                launch_kernel(bgmv_shrink_grouped_kernel<DT, VEC, 4, 2, RT, true>, grid, dim3(256), 0, s, T, ids,
+                              n_adapters, tab);
+            else
+                launch_kernel(bgmv_shrink_grouped_kernel<DT, VEC, 4, 1, RT, true>, grid, dim3(256), 0, s, T, ids,
+                              n_adapters, tab);
+        } else {
+            if (two && RT < 4)
+                launch_kernel(bgmv_shrink_grouped_kernel<DT, VEC, 4, 2, RT, false>, grid, dim3(256), 0, s, T, ids,
+                              n_adapters, tab);
+            else
+                launch_kernel(bgmv_shrink_grouped_kernel<DT, VEC, 4, 1, RT, false>, grid, dim3(256), 0, s, T, ids,
+                              n_adapters, tab);
         }
     }
 };
@@ -1111,6 +1207,17 @@ void bgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
 #undef LORA_BGMV_EXPAND
 }
 
+template <int DT, bool SLOT, bool VECY>
+void bgmv_expand_grouped_go(hipStream_t s, dim3 grid, size_t shm, int upt, int T, const int32_t *ids, int n_adapters,
+                            const GExpandTable &tab)
+{
+    switch (upt) {
+    case 1: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 1>, grid, dim3(256), shm, s, T, ids, n_adapters, tab); break;
+    case 2: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 2>, grid, dim3(256), shm, s, T, ids, n_adapters, tab); break;
+    default: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 4>, grid, dim3(256), shm, s, T, ids, n_adapters, tab);
+    }
+}
+
 } // namespace
 
 size_t combined_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
@@ -1196,6 +1303,62 @@ int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32
     if (st) return st;
     bgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank);
     return check_launch("bgmv expand");
+}
+
+size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank)
+{
+    return (combined_workspace_bytes(T, d_in, max_rank) + 255) / 256 * 256;
+}
+
+int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
+                        int n)
+{
+    if (n_adapters == 0 || n == 0) return LORA_OK;
+    const int dtype = pr[0].sa.dtype;
+    const bool slot = slot_major(T, n_adapters);
+    GShrinkTable stab{};
+    GExpandTable etab{};
+    // template choices shared by all projections: the most general one
+    bool vec = true, vecy = true, two = true;
+    int rt = 1, kc_max = 1, ncol_max = 1, ldl_max = 4;
+    for (int p = 0; p < n; ++p) {
+        const GroupedProj &g = pr[p];
+        // the same split as a single lora_bgmv call of this projection
+        const Split sp = choose_split(g.sa.d_in, slot ? n_adapters : T, dtype);
+        const int64_t ldw = (g.max_rank + 3) / 4 * 4;
+        const int64_t sl_stride = int64_t(T) * ldw;
+        const int ldl = lds_pitch(g.max_rank);
+        const int ncol = (g.ea.d_out + kExpandCols - 1) / kExpandCols;
+        stab.p[p] = GShrink{g.sa.x, g.pool_A, g.pool_rank, g.sa.v, g.sa.ldx, ldw, sl_stride, g.sa.d_in, g.max_rank,
+                            sp.slice_len, sp.kc};
+        etab.p[p] = GExpand{g.sa.v, g.pool_B, g.pool_rank, g.pool_alpha, g.ea.y, ldw, sl_stride, g.ea.ldy, sp.kc,
+                            g.max_rank, g.ea.d_out, ldl, ncol, g.ea.vec_b ? 1 : 0};
+        vec = vec && g.sa.vec;
+        vecy = vecy && g.ea.vec_y && g.ea.d_out % 16 == 0;
+        two = two && sp.nstep == 2;
+        rt = rt > rank_tiles(g.max_rank) ? rt : rank_tiles(g.max_rank);
+        kc_max = kc_max > sp.kc ? kc_max : sp.kc;
+        ncol_max = ncol_max > ncol ? ncol_max : ncol;
+        ldl_max = ldl_max > ldl ? ldl_max : ldl;
+    }
+    const unsigned groups = unsigned(slot ? n_adapters : T);
+    dispatch_shrink<BgmvShrinkGroupedL>(dtype, vec, rt, s, dim3(groups, kc_max, n), T, ids, n_adapters, slot, two,
+                                        stab);
+    int st = check_launch("bgmv grouped shrink");
+    if (st) return st;
+    const dim3 egrid(groups, ncol_max, n);
+    const size_t shm = (size_t(kRows) * ldl_max + 4) * sizeof(float);
+    const int upt = units_per_thread(1, ldl_max);
+#define LORA_BGMV_GEXPAND(DT_, SLOT_, VECY_) bgmv_expand_grouped_go<DT_, SLOT_, VECY_>(s, egrid, shm, upt, T, ids, n_adapters, etab)
+    if (dtype == LORA_BF16) {
+        if (slot) { if (vecy) LORA_BGMV_GEXPAND(LORA_BF16, true, true); else LORA_BGMV_GEXPAND(LORA_BF16, true, false); }
+        else { if (vecy) LORA_BGMV_GEXPAND(LORA_BF16, false, true); else LORA_BGMV_GEXPAND(LORA_BF16, false, false); }
+    } else {
+        if (slot) { if (vecy) LORA_BGMV_GEXPAND(LORA_F32, true, true); else LORA_BGMV_GEXPAND(LORA_F32, true, false); }
+        else { if (vecy) LORA_BGMV_GEXPAND(LORA_F32, false, true); else LORA_BGMV_GEXPAND(LORA_F32, false, false); }
+    }
+#undef LORA_BGMV_GEXPAND
+    return check_launch("bgmv grouped expand");
 }
 
 } // namespace lora

@@ -56,6 +56,40 @@ int main(void)
     CHECK(lora_build_plan(2, bad, N, pool_A, pool_B, rank, alpha, plan, bytes) == LORA_ERR_ADAPTER_ID);
     CHECK(lora_build_plan(T, ids, N, pool_A, pool_B, rank, alpha, plan, 16) == LORA_ERR_WORKSPACE);
     CHECK(lora_profile_launches(NULL, NULL, -1) == LORA_ERR_ARG);
+
+    /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection regions;
+     * malformed calls are rejected on the host */
+    lora_proj pr[2];
+    memset(pr, 0, sizeof(pr));
+    for (int p = 0; p < 2; ++p) {
+        pr[p].x = (const void *)0x7f1000000000ull;
+        pr[p].y = (void *)(0x7f2000000000ull + 0x100000ull * (uint64_t)p);
+        pr[p].pool_A_dev = (const uint64_t *)0x7f3000000000ull;
+        pr[p].pool_B_dev = (const uint64_t *)0x7f3000001000ull;
+        pr[p].pool_rank_dev = (const int32_t *)0x7f3000002000ull;
+        pr[p].pool_alpha_dev = (const float *)0x7f3000003000ull;
+        pr[p].ldx = 4096;
+        pr[p].ldy = 1024;
+        pr[p].d_in = 4096;
+        pr[p].d_out = 1024;
+        pr[p].max_rank = p == 0 ? 16 : 64;
+    }
+    const size_t r0 = lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 16);
+    const size_t r1 = lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 64);
+    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == (r0 + 255) / 256 * 256 + (r1 + 255) / 256 * 256);
+    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 0) == 0);
+    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, LORA_MAX_PROJ + 1) == 0);
+    CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, NULL, 4, pr, LORA_MAX_PROJ + 1, NULL, 0) == LORA_ERR_ARG);
+    CHECK(lora_bgmv_grouped(NULL, 7, 64, NULL, 4, pr, 2, NULL, 0) == LORA_ERR_DTYPE);
+    pr[1].max_rank = 300;
+    CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, NULL, 4, pr, 2, NULL, 0) == LORA_ERR_RANK);
+    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == 0);
+    pr[1].max_rank = 64;
+    pr[1].y = pr[0].y;
+    CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, NULL, 4, pr, 2, NULL, 0) == LORA_ERR_ARG);
+    pr[1].y = (void *)0x7f2000100000ull;
+    CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, (const int32_t *)0x7f4000000000ull, 4, pr, 2, NULL, 0) ==
+          LORA_ERR_WORKSPACE);
     CHECK(lora_profile_launches(NULL, NULL, 0) == LORA_OK && lora_profile_launches_used() == 0);
     free(plan);
     printf("ok\n");

@@ -281,6 +281,38 @@ def test_combined_argument_errors():
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 100, 4096, FX, needb) == -1
 
 
+def test_grouped_bgmv_host_checks():
+    """Grouped BGMV: the workspace is the sum of the projections' 256-byte
+    rounded regions, and malformed calls are rejected before any GPU work."""
+    import ctypes as C
+
+    projs = (B.LoraProj * 3)()
+    for p, (d_in, d_out, r) in enumerate([(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)]):
+        projs[p] = B.LoraProj(FX, FX + 0x100000 * (p + 1), FX, FX, FX, FX, d_in, d_out, d_in, d_out, r, 0)
+    want = sum((B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, d_in, d_out, r) + 255) // 256 * 256
+               for d_in, d_out, r in [(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)])
+    ptr = C.cast(projs, C.c_void_p)
+    assert B.lora_bgmv_grouped_workspace_bytes(64, ptr, 3) == want
+    assert B.lora_bgmv_grouped_workspace_bytes(64, ptr, 0) == 0
+    assert B.lora_bgmv_grouped_workspace_bytes(64, None, 3) == 0
+    g = B.lora_bgmv_grouped
+    assert g(None, 1, 64, FX, 32, ptr, 9, FX, want) == -1          # too many projections
+    assert g(None, 1, 64, FX, 32, None, 3, FX, want) == -1         # no projections
+    assert g(None, 1, -1, FX, 32, ptr, 3, FX, want) == -1          # negative T
+    assert g(None, 1, 64, FX, 32, ptr, 3, FX, want - 16) == -6     # workspace too small
+    assert g(None, 1, 64, None, 32, ptr, 3, FX, want) == -1        # no ids
+    assert g(None, 1, 64, FX, 32, ptr, 3, FX + 4, want) == -4      # misaligned workspace
+    projs[2].max_rank = 0
+    assert g(None, 1, 64, FX, 32, ptr, 3, FX, want) == -2
+    projs[2].max_rank = 64
+    projs[1].y = projs[0].y
+    assert g(None, 1, 64, FX, 32, ptr, 3, FX, want) == -1          # two projections write one y
+    projs[1].y = FX + 0x200000
+    projs[1].d_in = 0
+    assert g(None, 1, 64, FX, 32, ptr, 3, FX, want) == -1          # d_in < 1
+    assert g(None, 1, 0, FX, 32, ptr, 3, None, 0) in (0, -1)       # T = 0: nothing to do (or the d_in error)
+
+
 def test_workspace_bytes():
     for op in (0, 1, 2, 3):
         assert B.lora_workspace_bytes(op, 4096, 4096, 4096, 16) == 0
