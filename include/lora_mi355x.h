@@ -304,6 +304,92 @@ size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int3
 int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev, int32_t n_adapters,
                       const lora_proj *projs, int32_t n_proj, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------ adapter residency
+ * The GPU and host tiers of the pages' adapter storage ("Multi-LoRA Serving:
+ * Many Adapters on One GPU" (gpusmith.com), section "Swap latency and cache
+ * policy"; "Multi-LoRA Serving in Production ..." (llms.blog), sections
+ * "Tiered Storage Hierarchy and Asynchronous Streaming" and "Eviction and
+ * Replacement Policies"): adapters live in pinned host memory and are copied
+ * into HBM on a copy stream when a batch needs them; when HBM is full the
+ * least recently used adapter that is neither pinned nor in the batch is
+ * evicted.
+ *
+ * The cache manages a caller-owned device buffer: the first
+ * lora_cache_table_bytes(n_adapters) bytes hold the device tables the kernels
+ * read (pool_A, pool_B, rank, alpha, indexed by adapter id; zero for an adapter
+ * that is not resident), the rest holds adapter extents (A [r, d_in] then
+ * B [d_out, r], 256-byte aligned, not padded to a maximum rank).  One cache
+ * serves one projection shape (d_in, d_out) and dtype.  It never allocates
+ * device memory; it allocates a few pinned host staging buffers and events.
+ * Not thread-safe: one host thread drives a cache.
+ */
+typedef struct lora_cache lora_cache;
+
+#define LORA_CACHE_DRY 1u /* placement and statistics only: no GPU call, no copy (host-side tests) */
+
+typedef struct lora_cache_stats {
+    int64_t batches;        /* lora_cache_prepare calls that succeeded */
+    int64_t hits;           /* adapters of a batch that were already resident */
+    int64_t misses;         /* adapters copied in */
+    int64_t evictions;
+    int64_t bytes_copied;   /* adapter bytes copied host -> device */
+    int64_t resident_bytes; /* bytes of the extents resident now */
+    int32_t resident;       /* adapters resident now */
+    int32_t reserved;
+} lora_cache_stats;
+
+typedef struct lora_cache_view {
+    const uint64_t *pool_A_dev; /* device tables [n_adapters], for the BGMV calls */
+    const uint64_t *pool_B_dev;
+    const int32_t *rank_dev;
+    const float *alpha_dev;
+    const uint64_t *pool_A_host; /* host mirrors, current after the last prepare: the */
+    const uint64_t *pool_B_host; /* inputs of lora_build_plan for the batch */
+    const int32_t *rank_host;
+    const float *alpha_host;
+    int32_t n_adapters;
+    int32_t max_rank; /* largest registered rank */
+} lora_cache_view;
+
+/* Bytes at the start of the device buffer that hold the tables. */
+size_t lora_cache_table_bytes(int32_t n_adapters);
+
+/* dev_buf: device memory, 256-byte aligned, dev_bytes > table bytes; it must
+ * outlive the cache.  flags: 0 or LORA_CACHE_DRY.  Zeroes the tables (a
+ * synchronous hipMemset) unless dry.
+ * Errors: LORA_ERR_ARG, LORA_ERR_DTYPE, LORA_ERR_ALIGN, LORA_ERR_WORKSPACE, LORA_ERR_HIP. */
+int lora_cache_create(void *dev_buf, size_t dev_bytes, int32_t n_adapters, int dtype, int32_t d_in,
+                      int32_t d_out, unsigned flags, lora_cache **out);
+
+/* Waits for the cache's own staging copies, then frees its host resources. */
+void lora_cache_destroy(lora_cache *cache);
+
+/* Host copy of adapter `adapter`: A_host [rank, d_in], B_host [d_out, rank]
+ * row-major of the cache's dtype; pinned memory (hipHostMalloc) for copies that
+ * overlap compute.  The memory must stay valid while the adapter may be loaded.
+ * Errors: LORA_ERR_ARG (also: adapter resident), LORA_ERR_ADAPTER_ID, LORA_ERR_RANK. */
+int lora_cache_register(lora_cache *cache, int32_t adapter, const void *A_host, const void *B_host,
+                        int32_t rank, float alpha);
+
+/* A pinned adapter is never evicted (the pages' priority tiers). */
+int lora_cache_pin(lora_cache *cache, int32_t adapter, int pinned);
+
+/* Make every adapter of a batch (ids_host [T], -1 = none) resident before the
+ * work enqueued next on compute_stream.  Copies of missing adapters and the
+ * table update are enqueued on copy_stream, after the compute work that last
+ * read any space they reuse; compute_stream then waits for them (only when a
+ * copy was needed).  No host synchronisation.  Build the batch's plan from the
+ * view's host mirrors after this call.
+ * Errors: LORA_ERR_ARG, LORA_ERR_ADAPTER_ID (id out of range or not
+ * registered), LORA_ERR_WORKSPACE (the batch does not fit, or the free space is
+ * too fragmented once every evictable adapter is gone), LORA_ERR_HIP.  After an
+ * error the batch must not run; the cache stays consistent. */
+int lora_cache_prepare(lora_cache *cache, const int32_t *ids_host, int32_t T, void *copy_stream,
+                       void *compute_stream);
+
+int lora_cache_view_get(const lora_cache *cache, lora_cache_view *out);
+int lora_cache_stats_get(const lora_cache *cache, lora_cache_stats *out);
+
 /* ------------------------------------------------------------------ fused layer
  * The whole adapted layer: the shared base product once for every token plus
  * each token's correction, y = x W0 + scale_s (x A_s) B_s, overwriting y

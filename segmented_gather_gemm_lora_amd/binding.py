@@ -42,8 +42,10 @@ EXPORTS = [
     "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
     "lora_version", "lora_profile_launches", "lora_profile_launches_used", "lora_bgmv_grouped",
-    "lora_bgmv_grouped_workspace_bytes",
+    "lora_bgmv_grouped_workspace_bytes", "lora_cache_table_bytes", "lora_cache_create", "lora_cache_destroy",
+    "lora_cache_register", "lora_cache_pin", "lora_cache_prepare", "lora_cache_view_get", "lora_cache_stats_get",
 ]
+LORA_CACHE_DRY = 1
 MAX_PROJ = 8
 
 PLAN_HEADER_BYTES = 96
@@ -86,7 +88,33 @@ _SIGS = {
     "lora_profile_launches_used": (ctypes.c_int32, []),
     "lora_bgmv_grouped": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i32, _vp, _i32, _vp, _sz]),
     "lora_bgmv_grouped_workspace_bytes": (_sz, [_i32, _vp, _i32]),
+    "lora_cache_table_bytes": (_sz, [_i32]),
+    "lora_cache_create": (ctypes.c_int, [_vp, _sz, _i32, ctypes.c_int, _i32, _i32, ctypes.c_uint, _vp]),
+    "lora_cache_destroy": (None, [_vp]),
+    "lora_cache_register": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, ctypes.c_float]),
+    "lora_cache_pin": (ctypes.c_int, [_vp, _i32, ctypes.c_int]),
+    "lora_cache_prepare": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+    "lora_cache_view_get": (ctypes.c_int, [_vp, _vp]),
+    "lora_cache_stats_get": (ctypes.c_int, [_vp, _vp]),
 }
+
+
+class CacheStats(ctypes.Structure):
+    """struct lora_cache_stats."""
+
+    _fields_ = [("batches", _i64), ("hits", _i64), ("misses", _i64), ("evictions", _i64), ("bytes_copied", _i64),
+                ("resident_bytes", _i64), ("resident", _i32), ("reserved", _i32)]
+
+
+class CacheView(ctypes.Structure):
+    """struct lora_cache_view."""
+
+    _fields_ = [("pool_A_dev", _vp), ("pool_B_dev", _vp), ("rank_dev", _vp), ("alpha_dev", _vp),
+                ("pool_A_host", _vp), ("pool_B_host", _vp), ("rank_host", _vp), ("alpha_host", _vp),
+                ("n_adapters", _i32), ("max_rank", _i32)]
+
+
+assert ctypes.sizeof(CacheStats) == 56 and ctypes.sizeof(CacheView) == 72
 
 
 class LoraProj(ctypes.Structure):
@@ -198,6 +226,102 @@ def lora_bgmv_grouped(stream, dtype, T, ids, n_adapters, projs, n_proj, ws, ws_b
 
 def lora_bgmv_grouped_workspace_bytes(T, projs, n_proj) -> int:
     return int(load().lora_bgmv_grouped_workspace_bytes(T, projs, n_proj))
+
+
+class _Raw:
+    """A raw device address where the calls expect a tensor."""
+
+    def __init__(self, addr):
+        self.addr = int(addr or 0)
+
+    def data_ptr(self) -> int:
+        return self.addr
+
+
+class AdapterCache:
+    """Residency cache over a device buffer (lora_cache_*): adapters registered
+    from pinned host memory are copied in on a copy stream when a batch needs
+    them, least recently used ones evicted.  dev_buf: a uint8 device tensor (or
+    an int address when dry).  `pool()` gives the tables in the form the
+    SGMV/BGMV calls take."""
+
+    def __init__(self, dev_buf, n_adapters: int, dtype: str, d_in: int, d_out: int, dry: bool = False):
+        lib = load()
+        self._buf = dev_buf  # keeps the device memory alive
+        addr = dev_buf if isinstance(dev_buf, int) else _ptr(dev_buf)
+        nbytes = self.dry_bytes if isinstance(dev_buf, int) else dev_buf.numel()
+        h = ctypes.c_void_p()
+        _check(lib.lora_cache_create(addr, nbytes, n_adapters, DTYPES[dtype], d_in, d_out,
+                                     LORA_CACHE_DRY if dry else 0, ctypes.byref(h)), "lora_cache_create")
+        self.h, self.n_adapters, self.dtype, self.d_in, self.d_out = h, n_adapters, dtype, d_in, d_out
+        self.dry = dry
+        self._host = {}
+
+    dry_bytes = 0
+
+    @classmethod
+    def dry_run(cls, nbytes: int, n_adapters: int, dtype: str, d_in: int, d_out: int):
+        """A placement-only cache over a fake 256-byte aligned address range."""
+        obj = cls.__new__(cls)
+        obj.dry_bytes = nbytes
+        cls.__init__(obj, 0x7F0000000000, n_adapters, dtype, d_in, d_out, dry=True)
+        return obj
+
+    def close(self):
+        if getattr(self, "h", None) is not None and self.h.value:
+            load().lora_cache_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def register(self, adapter: int, A_host, B_host, rank: int, alpha: float):
+        """A_host / B_host: host arrays or tensors (pinned for overlapped copies),
+        kept referenced by the cache object."""
+        self._host[adapter] = (A_host, B_host)
+        pa = A_host.ctypes.data if isinstance(A_host, np.ndarray) else A_host.data_ptr()
+        pb = B_host.ctypes.data if isinstance(B_host, np.ndarray) else B_host.data_ptr()
+        _check(load().lora_cache_register(self.h, adapter, pa, pb, rank, alpha), "lora_cache_register")
+
+    def pin(self, adapter: int, pinned: bool = True):
+        _check(load().lora_cache_pin(self.h, adapter, int(pinned)), "lora_cache_pin")
+
+    def prepare(self, ids, copy_stream=None, compute_stream=None):
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        streams = (None, None) if self.dry else (_stream_handle(copy_stream), _stream_handle(compute_stream))
+        _check(load().lora_cache_prepare(self.h, ids.ctypes.data if ids.size else None, ids.shape[0], *streams),
+               "lora_cache_prepare")
+
+    def stats(self) -> dict:
+        st = CacheStats()
+        _check(load().lora_cache_stats_get(self.h, ctypes.byref(st)), "lora_cache_stats_get")
+        return {f: getattr(st, f) for f, _ in CacheStats._fields_ if f != "reserved"}
+
+    def view(self) -> CacheView:
+        v = CacheView()
+        _check(load().lora_cache_view_get(self.h, ctypes.byref(v)), "lora_cache_view_get")
+        return v
+
+    def pool(self) -> "DevicePool":
+        """The current tables as a DevicePool: host mirrors for lora_build_plan,
+        device tables for the BGMV calls.  Valid until the next prepare."""
+        v = self.view()
+        A, Bt, r, a = self.host_tables()
+        return DevicePool(storage=self._buf, n_adapters=self.n_adapters, dtype=self.dtype, d_in=self.d_in,
+                          d_out=self.d_out, addr_A=A, addr_B=Bt, rank=r, alpha=a, addr_A_dev=_Raw(v.pool_A_dev),
+                          addr_B_dev=_Raw(v.pool_B_dev), rank_dev=_Raw(v.rank_dev), alpha_dev=_Raw(v.alpha_dev))
+
+    def host_tables(self):
+        """Copies of the host mirrors: (A addresses, B addresses, ranks, alphas)."""
+        v, n = self.view(), self.n_adapters
+        A = np.ctypeslib.as_array(ctypes.cast(v.pool_A_host, ctypes.POINTER(ctypes.c_uint64)), (n,)).copy()
+        Bt = np.ctypeslib.as_array(ctypes.cast(v.pool_B_host, ctypes.POINTER(ctypes.c_uint64)), (n,)).copy()
+        r = np.ctypeslib.as_array(ctypes.cast(v.rank_host, ctypes.POINTER(ctypes.c_int32)), (n,)).copy()
+        a = np.ctypeslib.as_array(ctypes.cast(v.alpha_host, ctypes.POINTER(ctypes.c_float)), (n,)).copy()
+        return A, Bt, r, a
 
 
 def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy, ws, ws_bytes) -> int:
