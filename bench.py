@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
-    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv] [--steps K] [--warmup W]
+    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|decode_cache] [--steps K] [--warmup W]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
 every token (BGMV for the decode workload, SGMV from a prebuilt plan for the
@@ -270,6 +270,119 @@ def grouped_main(args):
     print(json.dumps(out))
 
 
+def cache_main(args):
+    """Decode batches whose adapters come through the residency cache: 256
+    adapters of rank 16 in pinned host memory, Zipf(1.1) popularity, a cache
+    of 64 adapters; a step is lora_cache_prepare (copies of missing adapters on
+    a copy stream) + one BGMV call.  The same batches with every adapter
+    resident are timed beside it."""
+    import torch
+
+    import oracle
+    from lora_workloads import CACHE_NAME, make_decode_registry
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob, batches = make_decode_registry()
+    n, T, slots = prob.n_adapters, prob.T, 64
+    nb = len(batches)
+    print(f"[bench] {CACHE_NAME}: T={T} registry={n} cache={slots} adapters, {nb} batches", file=sys.stderr,
+          flush=True)
+    ext = lambda r: (r * prob.d_in * 2 + 255) // 256 * 256 + (prob.d_out * r * 2 + 255) // 256 * 256  # noqa: E731
+    buf = torch.zeros(B.load().lora_cache_table_bytes(n) + slots * ext(16), dtype=torch.uint8, device="cuda")
+    cache = B.AdapterCache(buf, n, "bf16", prob.d_in, prob.d_out)
+    for a in range(n):
+        r = int(prob.ranks[a])
+        A = torch.from_numpy(prob.pool[prob.a_off[a]: prob.a_off[a] + r * prob.d_in].copy()).pin_memory()
+        Bm = torch.from_numpy(prob.pool[prob.b_off[a]: prob.b_off[a] + prob.d_out * r].copy()).pin_memory()
+        cache.register(a, A, Bm, r, float(prob.alphas[a]))
+    resident = B.DevicePool.from_problem(prob)
+    x = B.to_device(prob.x, "bf16")
+    y = B.to_device(prob.y_base(), "bf16")
+    ids_dev = [torch.from_numpy(b).cuda() for b in batches]
+    ws = B.workspace(B.LORA_OP_BGMV, T, prob.d_in, prob.d_out, 16)
+    copy_stream = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+    cache.prepare(batches[0], copy_stream, stream)
+    cpool = cache.pool()  # device tables keep their addresses; host mirrors are not needed for BGMV
+
+    def step_cache(i):
+        cache.prepare(batches[i % nb], copy_stream, stream)
+        B.bgmv(x, ids_dev[i % nb], cpool, y, ws, "bf16", max_rank=16)
+
+    def step_resident(i):
+        B.bgmv(x, ids_dev[i % nb], resident, y, ws, "bf16", max_rank=16)
+
+    K = args.steps if args.steps is not None else 4 * nb
+    W = args.warmup if args.warmup is not None else nb
+    for i in range(W):
+        step_cache(i)
+        step_resident(i)
+    torch.cuda.synchronize()
+    s0 = cache.stats()
+    ms_cache, t_wall = time_steps(step_cache, K, stream)
+    s1 = cache.stats()
+    ms_res, _ = time_steps(step_resident, K, stream)
+    misses = (s1["misses"] - s0["misses"]) / K
+    h2d = (s1["bytes_copied"] - s0["bytes_copied"]) / K
+    hits = (s1["hits"] - s0["hits"]) / K
+
+    timer = B.KernelTimer(2 * nb)
+    for i in range(nb):
+        timer.arm(2 * i, 2)
+        step_cache(i)
+    timer.disarm()
+    torch.cuda.synchronize()
+    per_kernel_us = {nm: float(np.mean([timer.elapsed_us(2 * i + j) for i in range(nb)]))
+                     for j, nm in enumerate(["shrink", "expand"])}
+    timer.close()
+    dominant = max(per_kernel_us, key=per_kernel_us.get)
+    dom_bytes = float(np.mean([algorithmic_bytes(dataclasses_replace_ids(prob, b))[dominant] for b in batches]))
+    achieved = dom_bytes / (per_kernel_us[dominant] * 1e-6) / 1e9
+    traffic, kname = recorded_traffic(CACHE_NAME, dominant)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": kname or f"bgmv_{dominant}", "algorithmic_bytes_per_launch": round(dom_bytes),
+            "avg_launch_us": round(per_kernel_us[dominant], 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(prob, args.cpu_budget)
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_cache * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_cache, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CACHE_NAME, "T": T, "d_in": prob.d_in, "d_out": prob.d_out, "ranks": [16],
+                   "registry_adapters": n, "cache_adapters": slots, "popularity": "zipf 1.1", "batches": nb,
+                   "path": "lora_cache_prepare + bgmv"},
+        "resident_ms_per_step": round(ms_res, 6),
+        "resident": "the same batches with all 256 adapters resident (no cache)",
+        "misses_per_step": round(misses, 2),
+        "hits_per_step": round(hits, 2),
+        "h2d_bytes_per_step": round(h2d),
+        "h2d_GBps_over_step": round(h2d / (ms_cache * 1e-3) / 1e9, 2),
+        "per_kernel_us": {nm: round(v, 3) for nm, v in per_kernel_us.items()},
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    cache.close()
+    print(json.dumps(out))
+
+
+def dataclasses_replace_ids(prob, ids):
+    import dataclasses
+
+    return dataclasses.replace(prob, ids=np.asarray(ids, dtype=np.int32))
+
+
 def base_gemm_reference_us(inst, reps=50):
     """Average time of torch.matmul for the base product alone (same shape,
     bf16): the vendor-library figure the fused kernel is compared with."""
@@ -397,7 +510,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv"], default="decode")
+    ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv", "decode_cache"], default="decode")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
@@ -424,6 +537,9 @@ def main():
     B.load()
     if args.config == "decode_qkv":
         grouped_main(args)
+        return
+    if args.config == "decode_cache":
+        cache_main(args)
         return
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]

@@ -333,6 +333,23 @@ def make_decode_qkv(seed: int = 2, d_outs: Sequence[int] = (4096, 1024, 1024)) -
     return probs
 
 
+CACHE_NAME = "decode_cache_bf16"
+
+
+def make_decode_registry(seed: int = 2, n_adapters: int = 256, n_batches: int = 64):
+    """Decode batches over an adapter registry larger than HBM is given for it:
+    n_adapters adapters of rank 16 (alpha 32, d 4096 -> 4096, values as in the
+    decode workload), and n_batches id lists of 64 tokens drawn from a
+    Zipf(1.1) popularity over the registry (the pages' benchmark protocol).
+    Returns (problem holding every adapter and batch 0's tokens, [ids per batch])."""
+    rng = np.random.default_rng(seed)
+    P = zipf_probs(n_adapters, 1.1)
+    batches = [rng.choice(n_adapters, size=64, p=P).astype(np.int32) for _ in range(n_batches)]
+    prob = make_problem(name=CACHE_NAME, dtype="bf16", ids=batches[0], ranks=[16] * n_adapters,
+                        alphas=[32.0] * n_adapters, d_in=4096, d_out=4096, seed=seed, rng=rng)
+    return prob, batches
+
+
 def make_integer_problem(
     *, seed: int, dtype: str, T: int, d_in: int, d_out: int, n_adapters: int,
     ranks: Optional[Sequence[int]] = None, with_w0: bool = False, none_frac: float = 0.0,

@@ -26,6 +26,12 @@
 //  * The batch's copies and the table update go to the copy stream, whose
 //    completion event the compute stream then waits for.  Batches that need no
 //    copy add no wait.
+//
+// The copies are one gather-copy kernel per batch: its workgroups read the
+// registered pinned host memory over PCIe and write the extents, 64 KB each,
+// so a batch of many small adapters costs one launch instead of two copy
+// commands per adapter.  Host memory that the device cannot address directly
+// (not pinned, or mapped at another address) is copied with hipMemcpyAsync.
 #include <algorithm>
 #include <cstring>
 #include <vector>
@@ -48,6 +54,7 @@ struct Extent {
 struct AdapterRec {
     const void *A_host = nullptr;
     const void *B_host = nullptr;
+    bool direct = false; // A_host and B_host are pinned and mapped at the same address on the device
     int32_t rank = 0;
     float alpha = 0.f;
     bool registered = false;
@@ -57,6 +64,72 @@ struct AdapterRec {
     int64_t last_use = -1;   // batch index
     int64_t mark = -1;       // prepare call that last listed it (duplicate filter)
 };
+
+// One gather-copy launch: entries (source, destination, bytes), each cut
+// into kCopyChunk-byte pieces, one workgroup per piece.
+constexpr int kCopyEntries = 96;
+constexpr uint64_t kCopyChunk = 64u << 10;
+struct CopyEntry {
+    const uint8_t *src;
+    uint8_t *dst;
+    uint64_t bytes;
+};
+struct CopyList {
+    CopyEntry e[kCopyEntries];
+    int32_t first[kCopyEntries + 1]; // first piece of entry i; first[n] = pieces in all
+    int32_t n;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void cache_copy_kernel(const CopyList L)
+{
+    // the entry of this piece: the last i with first[i] <= blockIdx.x
+    const int b = int(blockIdx.x);
+    int lo = 0, hi = L.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (L.first[mid] <= b) lo = mid;
+        else hi = mid - 1;
+    }
+    const uint8_t *src = L.e[lo].src;
+    uint8_t *dst = L.e[lo].dst;
+    const uint64_t off0 = uint64_t(b - L.first[lo]) * kCopyChunk;
+    const uint64_t end = L.e[lo].bytes < off0 + kCopyChunk ? L.e[lo].bytes : off0 + kCopyChunk;
+    const uint64_t tid = threadIdx.x;
+    uint64_t tail = off0;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0) {
+        // 16-byte pieces, four in flight per thread
+        const uint64_t vend = off0 + ((end - off0) & ~uint64_t(15));
+        for (uint64_t base = off0; base < vend; base += 4 * 4096) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint64_t o = base + uint64_t(u) * 4096 + 16 * tid;
+                if (o < vend) v[u] = *reinterpret_cast<const u32x4 *>(src + o);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint64_t o = base + uint64_t(u) * 4096 + 16 * tid;
+                if (o < vend) *reinterpret_cast<u32x4 *>(dst + o) = v[u];
+            }
+        }
+        tail = vend;
+    }
+    for (uint64_t o = tail + tid; o < end; o += 256) dst[o] = src[o];
+}
+
+// Pinned host memory that the device reads at the same address.
+bool device_readable(const void *p)
+{
+    hipPointerAttribute_t at{};
+    const hipError_t e = hipPointerGetAttributes(&at, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError(); // a pageable pointer is not an error of the next call
+        return false;
+    }
+    return at.type == hipMemoryTypeHost && at.devicePointer != nullptr && at.devicePointer == at.hostPointer;
+}
 
 } // namespace
 } // namespace lora
@@ -73,6 +146,7 @@ struct lora_cache {
     std::vector<int32_t> tr;
     std::vector<float> ta;
     void *stage[lora::kStageRing] = {};
+    bool stage_direct = false;
     hipEvent_t stage_ev[lora::kStageRing] = {};
     bool stage_busy[lora::kStageRing] = {};
     int stage_next = 0;
@@ -198,6 +272,10 @@ int lora_cache_create(void *dev_buf, size_t dev_bytes, int32_t n_adapters, int d
         for (int i = 0; i < kEventRing && e == hipSuccess; ++i)
             e = hipEventCreateWithFlags(&c->batch_ev[i], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&c->copy_ev, hipEventDisableTiming);
+        if (e == hipSuccess) {
+            c->stage_direct = true;
+            for (int i = 0; i < kStageRing; ++i) c->stage_direct = c->stage_direct && device_readable(c->stage[i]);
+        }
         // tables start out all zero (no adapter resident)
         if (e == hipSuccess) e = hipMemset(c->dev, 0, tab);
         if (e != hipSuccess) {
@@ -240,6 +318,7 @@ int lora_cache_register(lora_cache *c, int32_t adapter, const void *A_host, cons
     if (r.resident) return fail(LORA_ERR_ARG, "adapter %d is resident; it cannot be registered again", adapter);
     r.A_host = A_host;
     r.B_host = B_host;
+    r.direct = !c->dry && device_readable(A_host) && device_readable(B_host);
     r.rank = rank;
     r.alpha = alpha;
     r.registered = true;
@@ -355,14 +434,39 @@ int lora_cache_prepare(lora_cache *c, const int32_t *ids_host, int32_t T, void *
                                  : start_ev;
         e = hipStreamWaitEvent(xs, w, 0);
     }
+    CopyList L{};
+    int32_t pieces = 0;
+    auto flush = [&]() -> hipError_t {
+        if (L.n == 0) return hipSuccess;
+        L.first[L.n] = pieces;
+        hipLaunchKernelGGL(cache_copy_kernel, dim3(unsigned(pieces)), dim3(256), 0, xs, L);
+        const hipError_t le = hipGetLastError();
+        L.n = 0;
+        pieces = 0;
+        return le;
+    };
+    auto add = [&](const void *src, void *dst, uint64_t bytes) -> hipError_t {
+        hipError_t fe = hipSuccess;
+        if (L.n == kCopyEntries) fe = flush();
+        L.e[L.n] = CopyEntry{static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), bytes};
+        L.first[L.n] = pieces;
+        pieces += int32_t((bytes + kCopyChunk - 1) / kCopyChunk);
+        ++L.n;
+        return fe;
+    };
     for (size_t i = 0; i < loads.size() && e == hipSuccess; ++i) {
         const AdapterRec &r = c->ad[size_t(loads[i])];
         const size_t a_bytes = size_t(r.rank) * size_t(c->d_in) * size_t(c->es);
         const size_t b_bytes = size_t(c->d_out) * size_t(r.rank) * size_t(c->es);
         char *dst = c->dev + c->tab_bytes + r.off;
-        e = hipMemcpyAsync(dst, r.A_host, a_bytes, hipMemcpyHostToDevice, xs);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst + round_up(a_bytes, kAlign), r.B_host, b_bytes,
-                                                hipMemcpyHostToDevice, xs);
+        if (r.direct) {
+            e = add(r.A_host, dst, a_bytes);
+            if (e == hipSuccess) e = add(r.B_host, dst + round_up(a_bytes, kAlign), b_bytes);
+        } else {
+            e = hipMemcpyAsync(dst, r.A_host, a_bytes, hipMemcpyHostToDevice, xs);
+            if (e == hipSuccess) e = hipMemcpyAsync(dst + round_up(a_bytes, kAlign), r.B_host, b_bytes,
+                                                    hipMemcpyHostToDevice, xs);
+        }
         c->st.bytes_copied += int64_t(a_bytes + b_bytes);
     }
     // tables: staged in pinned memory (a ring, so that a buffer is rewritten
@@ -378,7 +482,13 @@ int lora_cache_prepare(lora_cache *c, const int32_t *ids_host, int32_t T, void *
             std::memcpy(p + 8 * n, c->tB.data(), 8 * n);
             std::memcpy(p + 16 * n, c->tr.data(), 4 * n);
             std::memcpy(p + 20 * n, c->ta.data(), 4 * n);
-            e = hipMemcpyAsync(c->dev, p, 24 * n, hipMemcpyHostToDevice, xs);
+            if (c->stage_direct) {
+                e = add(p, c->dev, 24 * n);
+                if (e == hipSuccess) e = flush();
+            } else {
+                e = flush();
+                if (e == hipSuccess) e = hipMemcpyAsync(c->dev, p, 24 * n, hipMemcpyHostToDevice, xs);
+            }
         }
         if (e == hipSuccess) e = hipEventRecord(c->stage_ev[s], xs);
         if (e == hipSuccess) c->stage_busy[s] = true;

@@ -32,9 +32,11 @@ def up(v):
     return (v + 255) // 256 * 256
 
 
-def setup_cache(ranks, cache_units, seed):
-    """A master problem holding every adapter, pinned host copies of each, and
-    a cache with room for about `cache_units` adapters of the largest rank."""
+def setup_cache(ranks, cache_units, seed, pageable=()):
+    """A master problem holding every adapter, pinned host copies of each (plain
+    pageable numpy arrays for the adapters in `pageable`, which the cache copies
+    with hipMemcpyAsync instead of its copy kernel), and a cache with room for
+    about `cache_units` adapters of the largest rank."""
     import torch
 
     from segmented_gather_gemm_lora_amd import binding as B
@@ -47,8 +49,10 @@ def setup_cache(ranks, cache_units, seed):
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     cache = B.AdapterCache(buf, n, "bf16", D_IN, D_OUT)
     for a, r in enumerate(ranks):
-        A = torch.from_numpy(master.pool[master.a_off[a]: master.a_off[a] + r * D_IN].copy()).pin_memory()
-        Bm = torch.from_numpy(master.pool[master.b_off[a]: master.b_off[a] + D_OUT * r].copy()).pin_memory()
+        A = master.pool[master.a_off[a]: master.a_off[a] + r * D_IN].copy()
+        Bm = master.pool[master.b_off[a]: master.b_off[a] + D_OUT * r].copy()
+        if a not in pageable:
+            A, Bm = torch.from_numpy(A).pin_memory(), torch.from_numpy(Bm).pin_memory()
         cache.register(a, A, Bm, r, float(master.alphas[a]))
     return master, cache
 
@@ -70,7 +74,7 @@ def test_batches_through_a_small_cache(path):
     from segmented_gather_gemm_lora_amd import binding as B
 
     ranks = [8, 16, 32, 4, 16, 64, 8, 16, 32, 12, 16, 24]
-    master, cache = setup_cache(ranks, cache_units=3, seed=7)
+    master, cache = setup_cache(ranks, cache_units=3, seed=7, pageable=(3, 9))
     copy_stream = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
     rng = np.random.default_rng(11)
