@@ -390,6 +390,84 @@ int lora_cache_prepare(lora_cache *cache, const int32_t *ids_host, int32_t T, vo
 int lora_cache_view_get(const lora_cache *cache, lora_cache_view *out);
 int lora_cache_stats_get(const lora_cache *cache, lora_cache_stats *out);
 
+/* ------------------------------------------------------------ paged adapter storage
+ * The pages' unified paging ("Multi-LoRA Serving in Production ..."
+ * (llms.blog), section "Unified Paged Memory"; "Multi-LoRA serving: the single
+ * translator with a thousand glossaries" (blog.lo0.es), section "Operational
+ * pitfalls", on memory fragmentation): adapter matrices are cut into fixed-size pages held in
+ * non-contiguous frames of one device pool, and a page table per matrix maps
+ * its logical pages to frames, so adapters of any rank come and go without
+ * fragmenting HBM.
+ *
+ * Layout.  `pages` is a caller-owned device buffer of n_frames * page_bytes
+ * bytes, 16-byte aligned; page_bytes is a power of two in [64, 2^24] (the
+ * pages name 16 KB and 64 KB).  A matrix of `bytes` bytes (A_i [r_i, d_in] or
+ * B_i [d_out, r_i], row-major, as in the dense pool) occupies
+ * lora_pages_needed(bytes, page_bytes) frames; its page table is a device
+ * int32 array whose entry p is the frame of logical page p, so byte b of the
+ * matrix lives at pages + table[b / page_bytes] * page_bytes + b % page_bytes.
+ * Each page table must start on a 16-byte boundary.  Frame numbers are device
+ * data: that every entry is in [0, n_frames) is a precondition (like the BGMV
+ * ids); the kernels do not check it.
+ *
+ * The paged calls take the same plans and tables as the dense ones, with the
+ * address of each adapter's A and B page tables where the dense pool has the
+ * address of A and B.  They run the same kernels with the element address
+ * looked up through the page table, so for the same inputs they return the
+ * same bits as lora_sgmv / lora_bgmv. */
+
+/* Frames a matrix of `bytes` bytes needs: ceil(bytes / page_bytes); -1 if
+ * bytes < 0 or page_bytes is not a power of two in [64, 2^24]. */
+int64_t lora_pages_needed(int64_t bytes, int64_t page_bytes);
+
+/* Host allocator of the frames of one pool: a free list, so any request for at
+ * most lora_page_alloc_free_count() frames succeeds whatever the order of
+ * earlier allocations and frees (no fragmentation).  Frames come back in the
+ * order they were freed last-in first-out.  Host memory only; not
+ * thread-safe: one thread drives an allocator. */
+typedef struct lora_page_alloc lora_page_alloc;
+
+/* n_frames in [1, 2^31 - 1].  Errors: LORA_ERR_ARG. */
+int lora_page_alloc_create(int32_t n_frames, lora_page_alloc **out);
+void lora_page_alloc_destroy(lora_page_alloc *alloc);
+
+/* Takes n frames into frames_out (host int32 [n]), all or nothing.
+ * Errors: LORA_ERR_ARG (n < 0, NULL), LORA_ERR_WORKSPACE (fewer than n free). */
+int lora_page_alloc_take(lora_page_alloc *alloc, int32_t n, int32_t *frames_out);
+
+/* Returns n frames (host int32 [n]) to the free list, all or nothing.
+ * Errors: LORA_ERR_ARG (a frame out of range, not taken, or repeated). */
+int lora_page_alloc_give(lora_page_alloc *alloc, const int32_t *frames, int32_t n);
+
+/* Free frames now; -1 for NULL. */
+int32_t lora_page_alloc_free_count(const lora_page_alloc *alloc);
+
+/* Copies `bytes` bytes of a matrix from src (device memory, or host memory
+ * the device can read, 16-byte aligned) into its frames:
+ * logical page p goes to pages + table_dev[p] * page_bytes.  One kernel on
+ * `stream`.  table_dev: device int32 [lora_pages_needed(bytes, page_bytes)].
+ * Errors: LORA_ERR_ARG, LORA_ERR_ALIGN, LORA_ERR_HIP. */
+int lora_pages_write(void *stream, void *pages, int64_t page_bytes, const int32_t *table_dev,
+                     const void *src, int64_t bytes);
+
+/* lora_sgmv over paged adapters: the plan was built (lora_build_plan) with
+ * pool_A[i] / pool_B[i] = device addresses of adapter i's A and B page tables.
+ * Errors: as lora_sgmv, plus LORA_ERR_ARG / LORA_ERR_ALIGN for pages or
+ * page_bytes. */
+int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
+                    const void *plan_host, const void *plan_dev, const void *pages, int64_t page_bytes,
+                    void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
+/* lora_bgmv over paged adapters: pool_A_dev[i] / pool_B_dev[i] are the
+ * device addresses of adapter i's A and B page tables.
+ * Errors: as lora_bgmv, plus LORA_ERR_ARG / LORA_ERR_ALIGN for pages or
+ * page_bytes. */
+int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+                    const int32_t *ids_dev, const uint64_t *pool_A_dev, const uint64_t *pool_B_dev,
+                    const int32_t *pool_rank_dev, const float *pool_alpha_dev,
+                    int32_t n_adapters, int32_t max_rank, const void *pages, int64_t page_bytes,
+                    void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------ fused layer
  * The whole adapted layer: the shared base product once for every token plus
  * each token's correction, y = x W0 + scale_s (x A_s) B_s, overwriting y

@@ -44,6 +44,8 @@ EXPORTS = [
     "lora_version", "lora_profile_launches", "lora_profile_launches_used", "lora_bgmv_grouped",
     "lora_bgmv_grouped_workspace_bytes", "lora_cache_table_bytes", "lora_cache_create", "lora_cache_destroy",
     "lora_cache_register", "lora_cache_pin", "lora_cache_prepare", "lora_cache_view_get", "lora_cache_stats_get",
+    "lora_pages_needed", "lora_page_alloc_create", "lora_page_alloc_destroy", "lora_page_alloc_take",
+    "lora_page_alloc_give", "lora_page_alloc_free_count", "lora_pages_write", "lora_sgmv_paged", "lora_bgmv_paged",
 ]
 LORA_CACHE_DRY = 1
 MAX_PROJ = 8
@@ -96,6 +98,17 @@ _SIGS = {
     "lora_cache_prepare": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
     "lora_cache_view_get": (ctypes.c_int, [_vp, _vp]),
     "lora_cache_stats_get": (ctypes.c_int, [_vp, _vp]),
+    "lora_pages_needed": (_i64, [_i64, _i64]),
+    "lora_page_alloc_create": (ctypes.c_int, [_i32, _vp]),
+    "lora_page_alloc_destroy": (None, [_vp]),
+    "lora_page_alloc_take": (ctypes.c_int, [_vp, _i32, _vp]),
+    "lora_page_alloc_give": (ctypes.c_int, [_vp, _vp, _i32]),
+    "lora_page_alloc_free_count": (_i32, [_vp]),
+    "lora_pages_write": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64]),
+    "lora_sgmv_paged": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32,
+                                       _vp, _sz]),
+    "lora_bgmv_paged": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                                       _i32, _vp, _i64, _vp, _i64, _i32, _vp, _sz]),
 }
 
 
@@ -468,6 +481,129 @@ class DevicePool:
         return p
 
 
+class PageAlloc:
+    """The library's frame allocator of one page pool (host side)."""
+
+    def __init__(self, n_frames: int):
+        self._h = ctypes.c_void_p()
+        _check(load().lora_page_alloc_create(int(n_frames), ctypes.byref(self._h)), "lora_page_alloc_create")
+        self.n_frames = int(n_frames)
+
+    def take(self, n: int) -> np.ndarray:
+        out = np.zeros(max(int(n), 1), dtype=np.int32)
+        _check(load().lora_page_alloc_take(self._h, int(n), out.ctypes.data), "lora_page_alloc_take")
+        return out[: int(n)]
+
+    def give(self, frames) -> None:
+        f = np.ascontiguousarray(frames, dtype=np.int32)
+        _check(load().lora_page_alloc_give(self._h, f.ctypes.data, int(f.size)), "lora_page_alloc_give")
+
+    @property
+    def free(self) -> int:
+        return int(load().lora_page_alloc_free_count(self._h))
+
+    def close(self):
+        if self._h:
+            load().lora_page_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lora_pages_needed(nbytes: int, page_bytes: int) -> int:
+    return int(load().lora_pages_needed(int(nbytes), int(page_bytes)))
+
+
+@dataclass
+class PagedPool:
+    """Adapters held in fixed-size pages of one device pool, each matrix behind
+    a device page table (int32 frames).  addr_A / addr_B hold the addresses of
+    the page tables, so a Plan builds from this pool as from a DevicePool."""
+
+    pages: object  # device uint8 [n_frames * page_bytes]
+    page_bytes: int
+    tables: object  # device int32: every page table, each 16-byte aligned
+    table_host: np.ndarray
+    frames_A: list  # host int32 frames of each adapter's A
+    frames_B: list
+    alloc: PageAlloc
+    n_adapters: int
+    dtype: str
+    d_in: int
+    d_out: int
+    addr_A: np.ndarray
+    addr_B: np.ndarray
+    rank: np.ndarray
+    alpha: np.ndarray
+    addr_A_dev: object = None
+    addr_B_dev: object = None
+    rank_dev: object = None
+    alpha_dev: object = None
+
+    @property
+    def max_rank(self) -> int:
+        return int(self.rank.max()) if self.rank.size else 0
+
+    @classmethod
+    def from_problem(cls, prob, page_bytes: int = 16384, shuffle_seed: Optional[int] = 0, spare_frames: int = 0,
+                     device="cuda", stream=None) -> "PagedPool":
+        """Allocates frames for every adapter of `prob` and writes A_i and B_i
+        into them with lora_pages_write.  shuffle_seed: frames are first taken
+        and given back in a seeded random order, so each matrix lands in
+        scattered frames (None: ascending frames)."""
+        torch = _torch()
+        es = prob.esize
+        ranks = np.ascontiguousarray(prob.ranks, dtype=np.int32)
+        nA = [lora_pages_needed(int(r) * prob.d_in * es, page_bytes) for r in ranks]
+        nB = [lora_pages_needed(prob.d_out * int(r) * es, page_bytes) for r in ranks]
+        if min(nA + nB, default=0) < 0:
+            raise ValueError(f"page_bytes {page_bytes} is not a power of two in [64, 2^24]")
+        n_frames = int(sum(nA) + sum(nB) + spare_frames)
+        alloc = PageAlloc(max(n_frames, 1))
+        if shuffle_seed is not None and n_frames > 0:
+            all_frames = alloc.take(n_frames)
+            alloc.give(np.random.default_rng(shuffle_seed).permutation(all_frames))
+        frames_A = [alloc.take(n) for n in nA]
+        frames_B = [alloc.take(n) for n in nB]
+        # page tables, each starting on a 16-byte boundary
+        offs_A, offs_B, parts, pos = [], [], [], 0
+        for fa, fb in zip(frames_A, frames_B):
+            for f, offs in ((fa, offs_A), (fb, offs_B)):
+                offs.append(pos)
+                pad = (-len(f)) % 4
+                parts.append(np.concatenate([f, np.zeros(pad, dtype=np.int32)]))
+                pos += len(f) + pad
+        table_host = np.concatenate(parts) if parts else np.zeros(4, dtype=np.int32)
+        tables = torch.from_numpy(table_host).to(device)
+        base = tables.data_ptr()
+        addr_A = np.array([base + 4 * o for o in offs_A], dtype=np.uint64)
+        addr_B = np.array([base + 4 * o for o in offs_B], dtype=np.uint64)
+        pages = torch.empty(max(n_frames, 1) * page_bytes, dtype=torch.uint8, device=device)
+        dense = to_device(prob.pool, prob.dtype, device)
+        sbase = dense.data_ptr()
+        st = _stream_handle(stream)
+        for i, r in enumerate(ranks):
+            for off, nbytes, addr in ((int(prob.a_off[i]), int(r) * prob.d_in * es, addr_A[i]),
+                                      (int(prob.b_off[i]), prob.d_out * int(r) * es, addr_B[i])):
+                _check(load().lora_pages_write(st, pages.data_ptr(), page_bytes, int(addr), sbase + off * es,
+                                               nbytes), "lora_pages_write")
+        torch.cuda.synchronize()
+        del dense
+        alpha = np.ascontiguousarray(prob.alphas, dtype=np.float32)
+        p = cls(pages=pages, page_bytes=int(page_bytes), tables=tables, table_host=table_host, frames_A=frames_A,
+                frames_B=frames_B, alloc=alloc, n_adapters=prob.n_adapters, dtype=prob.dtype, d_in=prob.d_in,
+                d_out=prob.d_out, addr_A=addr_A, addr_B=addr_B, rank=ranks, alpha=alpha)
+        p.addr_A_dev = torch.from_numpy(addr_A.view(np.int64)).to(device)
+        p.addr_B_dev = torch.from_numpy(addr_B.view(np.int64)).to(device)
+        p.rank_dev = torch.from_numpy(ranks).to(device)
+        p.alpha_dev = torch.from_numpy(alpha).to(device)
+        return p
+
+
 SEG_DESC = np.dtype([("A", "<u8"), ("B", "<u8"), ("start", "<i4"), ("len", "<i4"), ("rank", "<i4"),
                      ("adapter", "<i4"), ("scale", "<f4"), ("blk0", "<i4")])
 BLK_DESC = np.dtype([("A", "<u8"), ("B", "<u8"), ("scale", "<f4"), ("rank", "<i4"), ("n", "<i4"), ("p0", "<i4"),
@@ -574,6 +710,24 @@ def bgmv(x, ids_dev, pool: DevicePool, y, ws, dtype: str, max_rank: Optional[int
                      _ptr(pool.alpha_dev), pool.n_adapters, max_rank or pool.max_rank, _ptr(y), y.stride(0),
                      y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_bgmv")
+
+
+def sgmv_paged(x, plan: Plan, pool: PagedPool, y, ws, dtype: str, stream=None):
+    """lora_sgmv over paged adapters (plan built from the PagedPool)."""
+    _check(load().lora_sgmv_paged(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
+                                  plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(pool.pages), pool.page_bytes,
+                                  _ptr(y), y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_sgmv_paged")
+
+
+def bgmv_paged(x, ids_dev, pool: PagedPool, y, ws, dtype: str, max_rank: Optional[int] = None, stream=None):
+    """lora_bgmv over paged adapters."""
+    _check(load().lora_bgmv_paged(_stream_handle(stream), DTYPES[dtype], x.shape[0], _ptr(x), x.stride(0),
+                                  x.shape[1], _ptr(ids_dev), _ptr(pool.addr_A_dev), _ptr(pool.addr_B_dev),
+                                  _ptr(pool.rank_dev), _ptr(pool.alpha_dev), pool.n_adapters,
+                                  max_rank or pool.max_rank, _ptr(pool.pages), pool.page_bytes, _ptr(y), y.stride(0),
+                                  y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_bgmv_paged")
 
 
 def proj_array(xs, pools, ys, max_ranks=None):

@@ -438,6 +438,75 @@ int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, in
                        pool_alpha_dev, n_adapters, max_rank, ws);
 }
 
+// pages / page_bytes of the paged calls; *shift = log2(page_bytes).
+static int check_pages(const void *pages, int64_t page_bytes, int *shift)
+{
+    if (!pages) return fail(LORA_ERR_ARG, "pages is NULL");
+    if (!aligned16(pages)) return fail(LORA_ERR_ALIGN, "pages is not 16-byte aligned");
+    if (lora_pages_needed(0, page_bytes) < 0)
+        return fail(LORA_ERR_ARG, "page_bytes %lld is not a power of two in [64, 2^24]", (long long)page_bytes);
+    int sh = 0;
+    while ((int64_t(1) << sh) < page_bytes) ++sh;
+    *shift = sh;
+    return LORA_OK;
+}
+
+int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
+                    const void *plan_dev, const void *pages, int64_t page_bytes, void *y, int64_t ldy,
+                    int32_t d_out, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(plan_host, &h);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    int shift = 0;
+    if ((st = check_pages(pages, page_bytes, &shift))) return st;
+    if (h->num_sorted == 0) return LORA_OK;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
+    const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, h->max_rank, &sa))) return st;
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
+        return st;
+    return launch_sgmv_paged(static_cast<hipStream_t>(stream), sa, ea,
+                             PlanView{h, static_cast<const char *>(plan_dev)}, ws, pages, shift);
+}
+
+int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+                    const int32_t *ids_dev, const uint64_t *pool_A_dev, const uint64_t *pool_B_dev,
+                    const int32_t *pool_rank_dev, const float *pool_alpha_dev, int32_t n_adapters,
+                    int32_t max_rank, const void *pages, int64_t page_bytes, void *y, int64_t ldy, int32_t d_out,
+                    void *ws, size_t ws_bytes)
+{
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    int shift = 0;
+    if ((st = check_pages(pages, page_bytes, &shift))) return st;
+    if (T < 0 || T > 65536) return fail(LORA_ERR_ARG, "T %d outside [0, 65536]", T);
+    if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return fail(LORA_ERR_RANK, "max_rank %d outside [1, 256]", max_rank);
+    if (T == 0) return LORA_OK;
+    if (!ids_dev || !pool_A_dev || !pool_B_dev || !pool_rank_dev || !pool_alpha_dev)
+        return fail(LORA_ERR_ARG, "device tables are NULL");
+    const size_t need = combined_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const int64_t ldw = (max_rank + 3) / 4 * 4;
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, max_rank, &sa))) return st;
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_bgmv_paged(static_cast<hipStream_t>(stream), sa, ea, T, ids_dev, pool_A_dev, pool_B_dev,
+                             pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, ws, pages, shift);
+}
+
 size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj)
 {
     if (T < 0 || !projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;

@@ -55,6 +55,15 @@ int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                 int32_t n_adapters, int32_t max_rank, void *ws);
+// The combined SGMV / BGMV calls over paged adapter storage: the adapter
+// table entries (plan descriptors, pool_A / pool_B) are int32 page tables of
+// frames in `pages`, pages of 2^page_shift bytes.
+int launch_sgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws,
+                      const void *pages, int page_shift);
+int launch_bgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                      const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank,
+                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, const void *pages,
+                      int page_shift);
 // One projection of a grouped BGMV call: its shrink (x, d_in, v = its
 // workspace region) and expand (y, d_out) arguments and its adapter tables.
 struct GroupedProj {

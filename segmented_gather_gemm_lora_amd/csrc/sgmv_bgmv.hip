@@ -35,6 +35,7 @@
 #include "internal.h"
 
 #include <cstring>
+#include <type_traits>
 
 namespace lora {
 namespace {
@@ -66,6 +67,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(uint32_t, v);
 }
+
+// Where adapter elements live.  The kernels address A_i and B_i as element
+// offsets from the adapter's table entry:
+//  * DenseMem: the entry is the matrix's address, element e at entry + e;
+//  * PagedMem: paged adapter storage ("Multi-LoRA Serving in Production ..."
+//    (llms.blog), section "Unified Paged Memory"): the matrix is cut into pages
+//    of 2^shift bytes held in non-contiguous frames of one pool; the entry is
+//    the matrix's page table (int32 frame per logical page), and byte b of the
+//    matrix lives at pool + frame[b >> shift] * 2^shift + (b mod 2^shift).
+//    Vector loads never straddle a page: their offsets are multiples of their
+//    size and pages are powers of two of at least 64 bytes.
+struct DenseMem {
+    template <typename T> __device__ __forceinline__ global_ptr<T> at(const void *base, int64_t e) const
+    {
+        return as_global<T>(base) + e;
+    }
+};
+struct PagedMem {
+    const char *pool;
+    int shift;
+    template <typename T> __device__ __forceinline__ global_ptr<T> at(const void *frames, int64_t e) const
+    {
+        const int64_t b = e * int64_t(sizeof(T));
+        const int64_t f = as_global<int32_t>(frames)[b >> shift];
+        return (global_ptr<T>)(as_global<char>(pool) + ((f << shift) | (b & ((int64_t(1) << shift) - 1))));
+    }
+};
 
 // ----------------------------------------------------------------------------
 // Operand fragments.  bf16: one step = 4 lane groups x 32 elements of k; a
@@ -114,6 +142,36 @@ __device__ __forceinline__ typename Frag<DT>::V load_frag(global_ptr<typename Fr
     return f;
 }
 
+// load_frag of row `rowoff` (an element offset) of an adapter matrix held as `mem` says.
+template <int DT, bool VEC, class M>
+__device__ __forceinline__ typename Frag<DT>::V load_frag_m(const M &mem, const void *base, int64_t rowoff, int k,
+                                                            int k_end)
+{
+    using F = Frag<DT>;
+    using T = typename F::T;
+    if constexpr (std::is_same_v<M, DenseMem>) {
+        return load_frag<DT, VEC>(mem.template at<T>(base, rowoff), k, k_end);
+    } else {
+        typename F::V f;
+        if (VEC) {
+            const int kk = k < k_end ? k : k_end - F::kVec;
+            if constexpr (DT == LORA_BF16)
+                f = __builtin_bit_cast(bf16x8, *(global_ptr<u32x4>)(mem.template at<T>(base, rowoff + kk)));
+            else f = *(global_ptr<floatx4>)(mem.template at<T>(base, rowoff + kk));
+            if (k >= k_end) f = typename F::V{};
+        } else {
+#pragma unroll
+            for (int e = 0; e < F::kVec; ++e) {
+                const int kk = k + e < k_end ? k + e : k_end - 1;
+                const T val = *mem.template at<T>(base, rowoff + kk);
+                if constexpr (DT == LORA_BF16) f[e] = k + e < k_end ? __builtin_bit_cast(__bf16, val) : __bf16(0.f);
+                else f[e] = k + e < k_end ? val : 0.f;
+            }
+        }
+        return f;
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, const typename Frag<DT>::V &b, floatx4 acc)
 {
@@ -134,11 +192,11 @@ __device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, cons
 // Results of the W waves are added in wave order through LDS (`red`, W*RT*1 KB).
 // Output row of block row mm: orows[mm] if orows (LDS) is given, else orow0 + mm.
 // ----------------------------------------------------------------------------
-template <int DT, bool VEC, int W, int NSTEP, int RT>
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem>
 __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xr, int xr0,
                                              const void *__restrict__ Av, int d_in, int r, int k_begin, int k_end,
                                              float *__restrict__ out, int64_t ldo, int orow0, const int *orows, int n,
-                                             float *red)
+                                             float *red, const M &mem = M{})
 {
     using F = Frag<DT>;
     using T = typename F::T;
@@ -146,7 +204,6 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
     const int m = lane & 15, g = lane >> 4;
     // rows past n repeat the block's first row: their MFMA rows are never stored
     const global_ptr<T> xrow = as_global<T>(xv) + int64_t(xr >= 0 ? xr : xr0) * ldx;
-    const global_ptr<T> A = as_global<T>(Av);
     const int ntiles = (r + 15) >> 4;
 
     for (int rt0 = 0; rt0 < ntiles; rt0 += RT) {
@@ -154,11 +211,11 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
         for (int i = 0; i < RT; ++i) acc[i] = floatx4{};
         // ranks past r repeat row r-1: their MFMA columns are never stored
-        global_ptr<T> arow[RT];
+        int64_t aoff[RT];
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             const int j = 16 * (rt0 + i) + m;
-            arow[i] = A + int64_t(j < r ? j : r - 1) * d_in;
+            aoff[i] = int64_t(j < r ? j : r - 1) * d_in;
         }
         for (int kb = k_begin + wave * NSTEP * F::kStep; kb < k_end; kb += W * NSTEP * F::kStep) {
             typename F::V xf[NSTEP][4];
@@ -173,7 +230,8 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
                 for (int i = 0; i < RT; ++i)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) af[s][i][u] = load_frag<DT, VEC>(arow[i], k0 + 4 * F::kVec * u, k_end);
+                    for (int u = 0; u < 4; ++u)
+                        af[s][i][u] = load_frag_m<DT, VEC>(mem, Av, aoff[i], k0 + 4 * F::kVec * u, k_end);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) xf[s][u] = load_frag<DT, VEC>(xrow, k0 + 4 * F::kVec * u, k_end);
             }
@@ -339,8 +397,8 @@ __device__ __forceinline__ void y_store(void *yv, int64_t row_off, int ncol0, in
 // ----------------------------------------------------------------------------
 constexpr int kMaxSlices = 4;
 
-template <int DT, bool BV>
-__device__ __forceinline__ void load_bfrag(const void *Bv, int r, int j0, int ncol0, int m, int d_out,
+template <int DT, bool BV, class M>
+__device__ __forceinline__ void load_bfrag(const M &mem, const void *Bv, int r, int j0, int ncol0, int m, int d_out,
                                            float (&bf)[4][4])
 {
 #pragma unroll
@@ -352,13 +410,13 @@ __device__ __forceinline__ void load_bfrag(const void *Bv, int r, int j0, int nc
             const bool ok = cok && j0 < r;
             const int jj = j0 < r ? j0 : 0;
             if constexpr (DT == LORA_BF16) {
-                const u32x2 q = *(global_ptr<u32x2>)(as_global<uint16_t>(Bv) + rowoff + jj);
+                const u32x2 q = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + jj));
                 bf[t][0] = ok ? bf16_to_f32(q[0] & 0xffffu) : 0.f;
                 bf[t][1] = ok ? bf16_to_f32(q[0] >> 16) : 0.f;
                 bf[t][2] = ok ? bf16_to_f32(q[1] & 0xffffu) : 0.f;
                 bf[t][3] = ok ? bf16_to_f32(q[1] >> 16) : 0.f;
             } else {
-                const floatx4 q = *(global_ptr<floatx4>)(as_global<float>(Bv) + rowoff + jj);
+                const floatx4 q = *(global_ptr<floatx4>)(mem.template at<float>(Bv, rowoff + jj));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bf[t][e] = ok ? q[e] : 0.f;
             }
@@ -369,8 +427,8 @@ __device__ __forceinline__ void load_bfrag(const void *Bv, int r, int j0, int nc
                 const bool ok = cok && j < r;
                 const int jj = j < r ? j : r - 1;
                 float val;
-                if constexpr (DT == LORA_BF16) val = bf16_to_f32(as_global<uint16_t>(Bv)[rowoff + jj]);
-                else val = as_global<float>(Bv)[rowoff + jj];
+                if constexpr (DT == LORA_BF16) val = bf16_to_f32(*mem.template at<uint16_t>(Bv, rowoff + jj));
+                else val = *mem.template at<float>(Bv, rowoff + jj);
                 bf[t][e] = ok ? val : 0.f;
             }
         }
@@ -445,11 +503,12 @@ __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare
     (void)q4;
 }
 
-template <int DT, bool VECY, bool BV, bool VIND, int UPT>
+template <int DT, bool VECY, bool BV, bool VIND, int UPT, class M>
 __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                  const void *__restrict__ Bv, int r, float scale,
                                                  void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
-                                                 const int *yrows, int vrow0, int nrows, float *vl, int ldl)
+                                                 const int *yrows, int vrow0, int nrows, float *vl, int ldl,
+                                                 const M &mem)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -463,7 +522,7 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     VStage<UPT> vst;
     stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[4][4];
-    load_bfrag<DT, BV>(Bv, r, 4 * g, ncol0, m, d_out, bf);
+    load_bfrag<DT, BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, bf);
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
     stage_v_store<BV, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
@@ -475,7 +534,7 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     const int nch = (r + 15) >> 4;
     for (int c = 0; c < nch; ++c) {
         const int j0 = 16 * c + 4 * g;
-        if (c > 0) load_bfrag<DT, BV>(Bv, r, j0, ncol0, m, d_out, bf);
+        if (c > 0) load_bfrag<DT, BV>(mem, Bv, r, j0, ncol0, m, d_out, bf);
         floatx4 vf = *reinterpret_cast<const floatx4 *>(vl + (m < nrows ? m : 0) * ldl + (j0 < ldl ? j0 : 0));
         if (m >= nrows || j0 >= ldl) vf = floatx4{};
 #pragma unroll
@@ -486,18 +545,18 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
 }
 
-template <int DT, bool VECY, bool VIND, int UPT>
+template <int DT, bool VECY, bool VIND, int UPT, class M = DenseMem>
 __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                             const void *__restrict__ Bv, int r, float scale, void *__restrict__ yv,
                                             int64_t ldy, int d_out, int ncol_wg, bool vec_b, const int *yrows,
-                                            int vrow0, int nrows, float *vl, int ldl)
+                                            int vrow0, int nrows, float *vl, int ldl, const M &mem = M{})
 {
     if (vec_b && (r & 3) == 0)
         expand_rows_impl<DT, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                        yrows, vrow0, nrows, vl, ldl);
+                                                        yrows, vrow0, nrows, vl, ldl, mem);
     else
         expand_rows_impl<DT, VECY, false, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                         yrows, vrow0, nrows, vl, ldl);
+                                                         yrows, vrow0, nrows, vl, ldl, mem);
 }
 
 // Expand of one plan chunk (up to 64 rows of one segment) over this
@@ -507,12 +566,12 @@ __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t
 // stored one at a time, with only one block's accumulators live.  The B
 // fragments of all NCH * 16 ranks stay in registers for the whole chunk.
 // CONTIG: the rows are the consecutive tokens ybase, ybase + 1, ... (yrows unused)
-template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB, bool CONTIG = false>
+template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB, bool CONTIG = false, class M = DenseMem>
 __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                   const void *__restrict__ Bv, int r, float scale,
                                                   void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
                                                   const int *yrows, int vrow0, int nrows, float *vl, int ldl,
-                                                  int ybase = 0)
+                                                  int ybase = 0, const M &mem = M{})
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -530,7 +589,7 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
     stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[NCH][4][4];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) load_bfrag<DT, BV>(Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
+    for (int c = 0; c < NCH; ++c) load_bfrag<DT, BV>(mem, Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
     // rows past the chunk read the first row again (never stored)
     YTile<DT> yt[RB];
 #pragma unroll
@@ -566,11 +625,11 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
 // SGMV kernels.  Shrink: one workgroup per (plan block, d_in slice).  Expand:
 // one workgroup per (256 columns, plan block) or (256 columns, plan chunk).
 // ----------------------------------------------------------------------------
-template <int DT, bool VEC, int W, int NSTEP, int RT>
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
 __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
                                                              const lora_blk_desc *__restrict__ blks, int nblk, int kc,
                                                              int slice_len, float *__restrict__ out, int64_t ldo,
-                                                             int64_t sl_stride)
+                                                             int64_t sl_stride, const M mem)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     // Workgroup b runs on XCD b % 8.  Give each XCD a contiguous run of
@@ -586,20 +645,20 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restr
     const int k_begin = c * slice_len;
     const int k_end = min(d_in, k_begin + slice_len);
     shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, xr0, reinterpret_cast<const void *>(bd->A), d_in, bd->rank,
-                                        k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red);
+                                        k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red, mem);
 }
 
-template <int DT, bool VECY, int UPT>
+template <int DT, bool VECY, int UPT, class M>
 __global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                           int nsl, const lora_blk_desc *__restrict__ blks,
                                                           void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
-                                                          int ldl)
+                                                          int ldl, const M mem)
 {
     extern __shared__ floatx4 vl4[];
     const lora_blk_desc *d = blks + blockIdx.y;
     expand_rows<DT, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
                                          d->scale, y, ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0,
-                                         d->n, reinterpret_cast<float *>(vl4), ldl);
+                                         d->n, reinterpret_cast<float *>(vl4), ldl, mem);
 }
 
 // 16-row blocks one workgroup takes from a chunk (a divisor of the chunk's
@@ -650,12 +709,13 @@ struct ChunkArgs {
     u32x8 c[kArgChunks]; // ChunkArg bits
 };
 
-template <int DT, bool VECY, int NCH, int UPT>
+template <int DT, bool VECY, int NCH, int UPT, class M>
 __global__ __launch_bounds__(256) void sgmv_expand_chunk_arg_kernel(const float *__restrict__ v, int64_t ldv,
                                                                     int64_t sl_stride, int nsl,
                                                                     const lora_chunk_desc *__restrict__ chunks,
                                                                     void *__restrict__ y, int64_t ldy, int d_out,
-                                                                    int vec_b, int ldl, const ChunkArgs tab)
+                                                                    int vec_b, int ldl, const ChunkArgs tab,
+                                                                    const M mem)
 {
     static_assert(kChunkRB == LORA_PLAN_CHUNK_BLOCKS, "one workgroup per chunk");
     extern __shared__ floatx4 vl4[];
@@ -673,17 +733,17 @@ __global__ __launch_bounds__(256) void sgmv_expand_chunk_arg_kernel(const float 
     if (vec_b && (r & 3) == 0) {
         if (row0 >= 0)
             expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB, true>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
-                                                                        d_out, ncw, rows, p0, n, vl, ldl, row0);
+                                                                        d_out, ncw, rows, p0, n, vl, ldl, row0, mem);
         else
             expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
-                                                                  ncw, rows, p0, n, vl, ldl);
+                                                                  ncw, rows, p0, n, vl, ldl, 0, mem);
     } else {
         if (row0 >= 0)
             expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB, true>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
-                                                                         d_out, ncw, rows, p0, n, vl, ldl, row0);
+                                                                         d_out, ncw, rows, p0, n, vl, ldl, row0, mem);
         else
             expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
-                                                                   d_out, ncw, rows, p0, n, vl, ldl);
+                                                                   d_out, ncw, rows, p0, n, vl, ldl, 0, mem);
     }
 }
 
@@ -747,12 +807,12 @@ __device__ bool bgmv_group(const int32_t *__restrict__ ids, int T, int t, int a,
 // (blockIdx.x = adapter; its tokens are all tokens with that id), else one per
 // token (blockIdx.x = t; it serves its adapter's tokens when it is the first
 // of them).  The adapter tables are read in parallel with the ids scan.
-template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M = DenseMem>
 __device__ __forceinline__ void bgmv_shrink_body(const void *__restrict__ x, int64_t ldx, int d_in, int T,
                                                  const int32_t *__restrict__ ids, const uint64_t *__restrict__ pool_A,
                                                  const int32_t *__restrict__ pool_rank, int n_adapters, int max_rank,
                                                  int slice_len, float *__restrict__ out, int64_t ldo,
-                                                 int64_t sl_stride)
+                                                 int64_t sl_stride, const M &mem = M{})
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     __shared__ Group grp;
@@ -773,30 +833,31 @@ __device__ __forceinline__ void bgmv_shrink_body(const void *__restrict__ x, int
         if (n == 0) return;
         const int xr = grp.rows[threadIdx.x & 15];
         shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end, out + c * sl_stride,
-                                            ldo, 0, grp.rows, n, red);
+                                            ldo, 0, grp.rows, n, red, mem);
         if (kRows * (pass + 1) >= total) break;
     }
 }
 
-template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT>
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M>
 __global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in, int T,
                                                              const int32_t *__restrict__ ids,
                                                              const uint64_t *__restrict__ pool_A,
                                                              const int32_t *__restrict__ pool_rank, int n_adapters,
                                                              int max_rank, int slice_len, float *__restrict__ out,
-                                                             int64_t ldo, int64_t sl_stride)
+                                                             int64_t ldo, int64_t sl_stride, const M mem)
 {
     bgmv_shrink_body<DT, VEC, W, NSTEP, RT, SLOT>(x, ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank,
-                                                  slice_len, out, ldo, sl_stride);
+                                                  slice_len, out, ldo, sl_stride, mem);
 }
 
-template <int DT, bool SLOT, bool VECY, int UPT>
+template <int DT, bool SLOT, bool VECY, int UPT, class M = DenseMem>
 __device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                  int T, const int32_t *__restrict__ ids,
                                                  const uint64_t *__restrict__ pool_B,
                                                  const int32_t *__restrict__ pool_rank,
                                                  const float *__restrict__ pool_alpha, int n_adapters, int max_rank,
-                                                 void *__restrict__ y, int64_t ldy, int d_out, bool vec_b, int ldl)
+                                                 void *__restrict__ y, int64_t ldy, int d_out, bool vec_b, int ldl,
+                                                 const M &mem = M{})
 {
     extern __shared__ floatx4 vl4[];
     __shared__ Group grp;
@@ -817,22 +878,22 @@ __device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, in
         if (n == 0) return;
         expand_rows<DT, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
                                             blockIdx.y * kExpandCols, vec_b, grp.rows, -1, n,
-                                            reinterpret_cast<float *>(vl4), ldl);
+                                            reinterpret_cast<float *>(vl4), ldl, mem);
         if (kRows * (pass + 1) >= total) break;
     }
 }
 
-template <int DT, bool SLOT, bool VECY, int UPT>
+template <int DT, bool SLOT, bool VECY, int UPT, class M>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                           int nsl, int T, const int32_t *__restrict__ ids,
                                                           const uint64_t *__restrict__ pool_B,
                                                           const int32_t *__restrict__ pool_rank,
                                                           const float *__restrict__ pool_alpha, int n_adapters,
                                                           int max_rank, void *__restrict__ y, int64_t ldy, int d_out,
-                                                          bool vec_b, int ldl)
+                                                          bool vec_b, int ldl, const M mem)
 {
     bgmv_expand_body<DT, SLOT, VECY, UPT>(v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters,
-                                          max_rank, y, ldy, d_out, vec_b, ldl);
+                                          max_rank, y, ldy, d_out, vec_b, ldl, mem);
 }
 
 // ----------------------------------------------------------------------------
@@ -966,52 +1027,55 @@ size_t split_ws_bytes(int d_in, int rows, int max_rank)
 }
 
 template <int DT, bool VEC, int RT> struct SgmvShrinkL {
+    template <class M>
     static void run(hipStream_t s, const void *x, int64_t ldx, int d_in, const lora_blk_desc *blks, int nblk,
-                    int kc, int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride)
+                    int kc, int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride,
+                    const M &mem)
     {
         const dim3 grid(unsigned((int64_t(nblk) * kc + 7) / 8 * 8));
         // register budget: 1024-thread workgroups have 128 VGPRs per lane, so
         // hold two k-steps of fragments only for one rank tile
         if (full)
-            launch_kernel(sgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT>, grid, dim3(1024), 0, s, x, ldx, d_in,
-                          blks, nblk, kc, slice_len, out, ldo, sl_stride);
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, M>, grid, dim3(1024), 0, s, x, ldx, d_in,
+                          blks, nblk, kc, slice_len, out, ldo, sl_stride, mem);
         else if (nstep == 2 && RT < 4)
-            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 2, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
-                          slice_len, out, ldo, sl_stride);
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 2, RT, M>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
+                          slice_len, out, ldo, sl_stride, mem);
         else
-            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 1, RT>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
-                          slice_len, out, ldo, sl_stride);
+            launch_kernel(sgmv_shrink_kernel<DT, VEC, 4, 1, RT, M>, grid, dim3(256), 0, s, x, ldx, d_in, blks, nblk, kc,
+                          slice_len, out, ldo, sl_stride, mem);
     }
 };
 
 template <int DT, bool VEC, int RT> struct BgmvShrinkL {
+    template <class M>
     static void run(hipStream_t s, const void *x, int64_t ldx, int d_in, int T, const int32_t *ids,
                     const uint64_t *pool_A, const int32_t *pool_rank, int n_adapters, int max_rank, bool slot, int kc,
-                    int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride)
+                    int slice_len, int nstep, bool full, float *out, int64_t ldo, int64_t sl_stride, const M &mem)
     {
         const dim3 grid(slot ? n_adapters : T, kc);
         if (slot) {
             if (full)
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, true>, grid, dim3(1024), 0, s, x,
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, true, M>, grid, dim3(1024), 0, s, x,
                               ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo,
-                              sl_stride);
+                              sl_stride, mem);
             else if (nstep == 2 && RT < 4)
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, true>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
-                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, true, M>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
+                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride, mem);
             else
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, true>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
-                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, true, M>, grid, dim3(256), 0, s, x, ldx, d_in, T, ids,
+                              pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride, mem);
         } else {
             if (full)
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, false>, grid, dim3(1024), 0, s, x,
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 16, RT == 1 ? 2 : 1, RT, false, M>, grid, dim3(1024), 0, s, x,
                               ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo,
-                              sl_stride);
+                              sl_stride, mem);
             else if (nstep == 2 && RT < 4)
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, false>, grid, dim3(256), 0, s, x, ldx, d_in, T,
-                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 2, RT, false, M>, grid, dim3(256), 0, s, x, ldx, d_in, T,
+                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride, mem);
             else
-                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, false>, grid, dim3(256), 0, s, x, ldx, d_in, T,
-                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride);
+                launch_kernel(bgmv_shrink_kernel<DT, VEC, 4, 1, RT, false, M>, grid, dim3(256), 0, s, x, ldx, d_in, T,
+                              ids, pool_A, pool_rank, n_adapters, max_rank, slice_len, out, ldo, sl_stride, mem);
         }
     }
 };
@@ -1045,31 +1109,32 @@ bool slot_major(int T, int n_adapters) { return n_adapters <= 2 * T; }
 // float4 units of staged v per thread for RB blocks of 16 rows at pitch ldl
 int units_per_thread(int rb, int ldl) { const int u = (rb * kRows * (ldl / 4) + 255) / 256; return u <= 1 ? 1 : (u <= 2 ? 2 : 4); }
 
-template <int DT, bool VECY>
+template <int DT, bool VECY, class M>
 void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
-                    const lora_blk_desc *blks, int nblk, int ldl)
+                    const lora_blk_desc *blks, int nblk, int ldl, const M &mem)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const size_t shm = (size_t(kRows) * ldl + 4) * sizeof(float);
     const dim3 grid(ncol, nblk);
     switch (units_per_thread(1, ldl)) {
     case 1:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
-                      a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 1, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     case 2:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
-                      a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 2, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     default:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
-                      a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 4, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+                      a.ldy, a.d_out, a.vec_b, ldl, mem);
     }
 }
 
-template <int DT, bool VECY, int NCH>
+template <int DT, bool VECY, int NCH, class M>
 void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
-                          const lora_chunk_desc *chunks, int nchunk, int ldl, const lora_chunk_desc *host_chunks)
+                          const lora_chunk_desc *chunks, int nchunk, int ldl, const lora_chunk_desc *host_chunks,
+                          const M &mem)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const size_t shm = (size_t(kChunkRB * kRows) * ldl + 4) * sizeof(float);
@@ -1087,20 +1152,22 @@ void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, in
         std::memset(&tab.c[nchunk], 0, sizeof(ChunkArg) * size_t(kArgChunks - nchunk));
         switch (units_per_thread(kChunkRB, ldl)) {
         case 1:
-            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride,
-                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 1, M>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab, mem);
             break;
         case 2:
-            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride,
-                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 2, M>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab, mem);
             break;
         default:
-            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride,
-                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab);
+            launch_kernel(sgmv_expand_chunk_arg_kernel<DT, VECY, NCH, 4, M>, grid, dim3(256), shm, s, v, ldv, sl_stride,
+                          nsl, chunks, a.y, a.ldy, a.d_out, int(a.vec_b), ldl, tab, mem);
         }
         return;
     }
-    switch (units_per_thread(kChunkRB, ldl)) {
+    // paged launches take chunks only through the argument table (the
+    // launcher sends larger plans to the block kernel)
+    if constexpr (std::is_same_v<M, DenseMem>) switch (units_per_thread(kChunkRB, ldl)) {
     case 1:
         launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
                       chunks, a.y, a.ldy, a.d_out, a.vec_b, ldl);
@@ -1115,32 +1182,33 @@ void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, in
     }
 }
 
-template <int DT>
+template <int DT, class M>
 void sgmv_expand_chunk_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv,
                            int64_t sl_stride, int nsl, const lora_chunk_desc *chunks, int nchunk, int ldl, int max_rank,
-                           const lora_chunk_desc *host_chunks)
+                           const lora_chunk_desc *host_chunks, const M &mem)
 {
     // chunked launches need ldl <= 32: at most two 16-rank steps
     const int nch = (max_rank + 15) / 16;
     if (vecy) {
-        if (nch <= 1) sgmv_expand_chunk_go<DT, true, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
-        else sgmv_expand_chunk_go<DT, true, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
+        if (nch <= 1) sgmv_expand_chunk_go<DT, true, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks, mem);
+        else sgmv_expand_chunk_go<DT, true, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks, mem);
     } else {
-        if (nch <= 1) sgmv_expand_chunk_go<DT, false, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
-        else sgmv_expand_chunk_go<DT, false, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks);
+        if (nch <= 1) sgmv_expand_chunk_go<DT, false, 1>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks, mem);
+        else sgmv_expand_chunk_go<DT, false, 2>(s, a, v, ldv, sl_stride, nsl, chunks, nchunk, ldl, host_chunks, mem);
     }
 }
 
-template <int DT>
+template <int DT, class M>
 void sgmv_expand_go2(hipStream_t s, const ExpandArgs &a, bool vecy, const float *v, int64_t ldv, int64_t sl_stride,
-                     int nsl, const lora_blk_desc *blks, int nblk, int ldl)
+                     int nsl, const lora_blk_desc *blks, int nblk, int ldl, const M &mem)
 {
-    if (vecy) sgmv_expand_go<DT, true>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl);
-    else sgmv_expand_go<DT, false>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl);
+    if (vecy) sgmv_expand_go<DT, true>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
+    else sgmv_expand_go<DT, false>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
 }
 
+template <class M>
 void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
-                        const PlanView &p)
+                        const PlanView &p, const M &mem)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const int ldl = lds_pitch(p.h->max_rank);
@@ -1149,54 +1217,56 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     // enough workgroups and the B fragments of every rank fit in registers
     // next to four y tiles (ranks <= 32; larger ranks lose more to occupancy
     // than they gain from B reuse)
-    const bool chunked = p.h->num_chunks * ncol >= 1024 && ldl <= 32;
+    const bool chunked = p.h->num_chunks * ncol >= 1024 && ldl <= 32 &&
+                         (std::is_same_v<M, DenseMem> || p.h->num_chunks <= kArgChunks);
     if (chunked) {
         const lora_chunk_desc *d = plan_chunks(p);
         if (a.dtype == LORA_BF16)
             sgmv_expand_chunk_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank,
-                                             plan_chunks_host(p));
+                                             plan_chunks_host(p), mem);
         else
             sgmv_expand_chunk_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_chunks, ldl, p.h->max_rank,
-                                             plan_chunks_host(p));
+                                             plan_chunks_host(p), mem);
     } else {
         const lora_blk_desc *d = plan_blocks(p);
-        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
-        else sgmv_expand_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl);
+        if (a.dtype == LORA_BF16) sgmv_expand_go2<LORA_BF16>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl, mem);
+        else sgmv_expand_go2<LORA_F32>(s, a, vecy, v, ldv, sl_stride, nsl, d, p.h->num_blocks, ldl, mem);
     }
 }
 
-template <int DT, bool SLOT, bool VECY>
+template <int DT, bool SLOT, bool VECY, class M>
 void bgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
                     int T, const int32_t *ids, const uint64_t *pool_B, const int32_t *pool_rank,
-                    const float *pool_alpha, int n_adapters, int max_rank)
+                    const float *pool_alpha, int n_adapters, int max_rank, const M &mem)
 {
     const dim3 grid(SLOT ? n_adapters : T, (a.d_out + kExpandCols - 1) / kExpandCols);
     const int ldl = lds_pitch(max_rank);
     const size_t shm = (size_t(kRows) * ldl + 4) * sizeof(float);
     switch (units_per_thread(1, ldl)) {
     case 1:
-        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
-                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 1, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     case 2:
-        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 2>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
-                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 2, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     default:
-        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 4>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
-                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl);
+        launch_kernel(bgmv_expand_kernel<DT, SLOT, VECY, 4, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, T, ids,
+                      pool_B, pool_rank, pool_alpha, n_adapters, max_rank, a.y, a.ldy, a.d_out, a.vec_b, ldl, mem);
     }
 }
 
+template <class M>
 void bgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
                         int T, const int32_t *ids, const uint64_t *pool_B, const int32_t *pool_rank,
-                        const float *pool_alpha, int n_adapters, int max_rank)
+                        const float *pool_alpha, int n_adapters, int max_rank, const M &mem)
 {
     const bool slot = slot_major(T, n_adapters);
     const bool vecy = a.vec_y && a.d_out % 16 == 0;
 #define LORA_BGMV_EXPAND(DT_, SLOT_, VECY_)                                                                            \
     bgmv_expand_go<DT_, SLOT_, VECY_>(s, a, v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, \
-                                      max_rank)
+                                      max_rank, mem)
     if (a.dtype == LORA_BF16) {
         if (slot) { if (vecy) LORA_BGMV_EXPAND(LORA_BF16, true, true); else LORA_BGMV_EXPAND(LORA_BF16, true, false); }
         else { if (vecy) LORA_BGMV_EXPAND(LORA_BF16, false, true); else LORA_BGMV_EXPAND(LORA_BF16, false, false); }
@@ -1230,19 +1300,21 @@ int launch_sgmv_shrink(hipStream_t s, const ShrinkArgs &a, const PlanView &p)
     const int nblk = p.h->num_blocks;
     if (nblk == 0) return LORA_OK;
     dispatch_shrink<SgmvShrinkL>(a.dtype, a.vec, rank_tiles(p.h->max_rank), s, a.x, a.ldx, a.d_in, plan_blocks(p),
-                                 nblk, 1, a.d_in, 2, true, a.v, a.ldv, int64_t(0));
+                                 nblk, 1, a.d_in, 2, true, a.v, a.ldv, int64_t(0), DenseMem{});
     return check_launch("sgmv_shrink");
 }
 
 int launch_sgmv_expand(hipStream_t s, const ExpandArgs &a, const PlanView &p)
 {
     if (p.h->num_blocks == 0) return LORA_OK;
-    sgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, p);
+    sgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, p, DenseMem{});
     return check_launch("sgmv_expand");
 }
 
-int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw,
-                             int64_t *sl_stride, int *nsl)
+namespace {
+template <class M>
+int shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw, int64_t *sl_stride,
+                 int *nsl, const M &mem)
 {
     const int nblk = p.h->num_blocks;
     const Split sp = choose_split(sa.d_in, nblk, sa.dtype);
@@ -1251,43 +1323,28 @@ int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView
     *nsl = sp.kc;
     if (nblk == 0) return LORA_OK;
     dispatch_shrink<SgmvShrinkL>(sa.dtype, sa.vec, rank_tiles(p.h->max_rank), s, sa.x, sa.ldx, sa.d_in,
-                                 plan_blocks(p), nblk, sp.kc, sp.slice_len, sp.nstep, false, ws, *ldw, *sl_stride);
+                                 plan_blocks(p), nblk, sp.kc, sp.slice_len, sp.nstep, false, ws, *ldw, *sl_stride,
+                                 mem);
     return check_launch("sgmv shrink");
 }
 
-int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+template <class M>
+int sgmv_combined(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws, const M &mem)
 {
     if (p.h->num_blocks == 0) return LORA_OK;
     float *vp = static_cast<float *>(ws);
     int64_t ldw = 0, sl_stride = 0;
     int nsl = 0;
-    int st = launch_sgmv_shrink_split(s, sa, p, vp, &ldw, &sl_stride, &nsl);
+    int st = shrink_split(s, sa, p, vp, &ldw, &sl_stride, &nsl, mem);
     if (st) return st;
-    sgmv_expand_launch(s, ea, vp, ldw, sl_stride, nsl, p);
+    sgmv_expand_launch(s, ea, vp, ldw, sl_stride, nsl, p, mem);
     return check_launch("sgmv expand");
 }
 
-int launch_bgmv_shrink(hipStream_t s, const ShrinkArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_A,
-                       const int32_t *pool_rank, int32_t n_adapters, int32_t max_rank)
-{
-    if (n_adapters == 0) return LORA_OK;
-    dispatch_shrink<BgmvShrinkL>(a.dtype, a.vec, rank_tiles(max_rank), s, a.x, a.ldx, a.d_in, T, ids, pool_A,
-                                 pool_rank, n_adapters, max_rank, slot_major(T, n_adapters), 1, a.d_in, 2, true, a.v,
-                                 a.ldv, int64_t(0));
-    return check_launch("bgmv_shrink");
-}
-
-int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_B,
-                       const int32_t *pool_rank, const float *pool_alpha, int32_t n_adapters, int32_t max_rank)
-{
-    if (n_adapters == 0) return LORA_OK;
-    bgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank);
-    return check_launch("bgmv_expand");
-}
-
-int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
-                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
-                int32_t n_adapters, int32_t max_rank, void *ws)
+template <class M>
+int bgmv_combined(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                  const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                  int32_t n_adapters, int32_t max_rank, void *ws, const M &mem)
 {
     if (n_adapters == 0) return LORA_OK;
     const bool slot = slot_major(T, n_adapters);
@@ -1298,11 +1355,66 @@ int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32
     const int64_t sl_stride = int64_t(T) * ldw;
     dispatch_shrink<BgmvShrinkL>(sa.dtype, sa.vec, rank_tiles(max_rank), s, sa.x, sa.ldx, sa.d_in, T, ids, pool_A,
                                  pool_rank, n_adapters, max_rank, slot, sp.kc, sp.slice_len, sp.nstep, false, vp, ldw,
-                                 sl_stride);
+                                 sl_stride, mem);
     int st = check_launch("bgmv shrink");
     if (st) return st;
-    bgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank);
+    bgmv_expand_launch(s, ea, vp, ldw, sl_stride, sp.kc, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank,
+                       mem);
     return check_launch("bgmv expand");
+}
+} // namespace
+
+int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw,
+                             int64_t *sl_stride, int *nsl)
+{
+    return shrink_split(s, sa, p, ws, ldw, sl_stride, nsl, DenseMem{});
+}
+
+int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+{
+    return sgmv_combined(s, sa, ea, p, ws, DenseMem{});
+}
+
+int launch_sgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws,
+                      const void *pages, int page_shift)
+{
+    return sgmv_combined(s, sa, ea, p, ws, PagedMem{static_cast<const char *>(pages), page_shift});
+}
+
+int launch_bgmv_shrink(hipStream_t s, const ShrinkArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_A,
+                       const int32_t *pool_rank, int32_t n_adapters, int32_t max_rank)
+{
+    if (n_adapters == 0) return LORA_OK;
+    dispatch_shrink<BgmvShrinkL>(a.dtype, a.vec, rank_tiles(max_rank), s, a.x, a.ldx, a.d_in, T, ids, pool_A,
+                                 pool_rank, n_adapters, max_rank, slot_major(T, n_adapters), 1, a.d_in, 2, true, a.v,
+                                 a.ldv, int64_t(0), DenseMem{});
+    return check_launch("bgmv_shrink");
+}
+
+int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int32_t *ids, const uint64_t *pool_B,
+                       const int32_t *pool_rank, const float *pool_alpha, int32_t n_adapters, int32_t max_rank)
+{
+    if (n_adapters == 0) return LORA_OK;
+    bgmv_expand_launch(s, a, a.v, a.ldv, 0, 1, T, ids, pool_B, pool_rank, pool_alpha, n_adapters, max_rank,
+                       DenseMem{});
+    return check_launch("bgmv_expand");
+}
+
+int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                int32_t n_adapters, int32_t max_rank, void *ws)
+{
+    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
+                         DenseMem{});
+}
+
+int launch_bgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                      const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank,
+                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, const void *pages,
+                      int page_shift)
+{
+    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
+                         PagedMem{static_cast<const char *>(pages), page_shift});
 }
 
 size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank)

@@ -91,6 +91,18 @@ int main(void)
     CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, (const int32_t *)0x7f4000000000ull, 4, pr, 2, NULL, 0) ==
           LORA_ERR_WORKSPACE);
     CHECK(lora_profile_launches(NULL, NULL, 0) == LORA_OK && lora_profile_launches_used() == 0);
+
+    /* paged storage, host side: page counts and the frame allocator */
+    CHECK(lora_pages_needed(16 * 4096 * 2, 16384) == 8);
+    CHECK(lora_pages_needed(1, 48) == -1);
+    lora_page_alloc *pa = NULL;
+    CHECK(lora_page_alloc_create(6, &pa) == LORA_OK && lora_page_alloc_free_count(pa) == 6);
+    int32_t fr[6];
+    CHECK(lora_page_alloc_take(pa, 4, fr) == LORA_OK && fr[0] == 0 && fr[3] == 3);
+    CHECK(lora_page_alloc_take(pa, 3, fr + 4) == LORA_ERR_WORKSPACE);
+    CHECK(lora_page_alloc_give(pa, fr + 1, 2) == LORA_OK && lora_page_alloc_free_count(pa) == 4);
+    CHECK(lora_page_alloc_give(pa, fr + 1, 1) == LORA_ERR_ARG);
+    lora_page_alloc_destroy(pa);
     free(plan);
     printf("ok\n");
     return 0;
