@@ -2,6 +2,7 @@
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
     python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|decode_cache] [--steps K] [--warmup W]
+                    [--paged PAGE_BYTES]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
 every token (BGMV for the decode workload, SGMV from a prebuilt plan for the
@@ -74,7 +75,7 @@ def algorithmic_flops(prob, part="total"):
 class Instance:
     """One layer's worth of device-resident inputs."""
 
-    def __init__(self, prob, kind):
+    def __init__(self, prob, kind, page_bytes=0, seed=0):
         import torch
 
         from segmented_gather_gemm_lora_amd import binding as B
@@ -82,7 +83,12 @@ class Instance:
         self.prob = prob
         self.kind = kind
         self.dt = prob.dtype
-        self.pool = B.DevicePool.from_problem(prob)
+        self.page_bytes = page_bytes
+        if page_bytes:
+            # adapters in scattered frames of a page pool (seeded frame order)
+            self.pool = B.PagedPool.from_problem(prob, page_bytes=page_bytes, shuffle_seed=seed)
+        else:
+            self.pool = B.DevicePool.from_problem(prob)
         self.x = B.to_device(prob.x, self.dt)
         self.y = B.to_device(prob.y_base(), self.dt)
         self.ids = torch.from_numpy(np.ascontiguousarray(prob.ids, dtype=np.int32)).cuda()
@@ -109,7 +115,12 @@ class Instance:
         if self.kind == "fused":
             self.fused()
         elif self.kind == "bgmv":
-            B.bgmv(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
+            if self.page_bytes:
+                B.bgmv_paged(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
+            else:
+                B.bgmv(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
+        elif self.page_bytes:
+            B.sgmv_paged(self.x, self.plan, self.pool, self.y, self.ws, self.dt)
         else:
             B.sgmv(self.x, self.plan, self.y, self.ws, self.dt)
 
@@ -514,6 +525,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_BYTES",
+                    help="adapters in a page pool of this page size (decode, prefill, hetero); 0 = dense pool")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain copies of a known size (counter calibration) and exit")
     args = ap.parse_args()
@@ -543,15 +556,19 @@ def main():
         return
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
+    page = args.paged
+    if page and kind == "fused":
+        print("--paged applies to the SGMV/BGMV workloads, not the fused layer", file=sys.stderr)
+        sys.exit(2)
 
     prob0 = make_config(k)
     ab = algorithmic_bytes(prob0)
     L = args.rotation or rotation_count(ab["total"])
     print(f"[bench] {CONFIG_NAMES[k]}: T={prob0.T} d_in={prob0.d_in} d_out={prob0.d_out} rotation={L} "
           f"bytes/layer={ab['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
-    insts = [Instance(prob0, kind)]
+    insts = [Instance(prob0, kind, page, seed=0)]
     for i in range(1, L):
-        insts.append(Instance(make_config(k, seed=1000 * k + i), kind))
+        insts.append(Instance(make_config(k, seed=1000 * k + i), kind, page, seed=i))
     # every instance has its own distinct-adapter count; average the algorithmic bytes
     ab_all = [algorithmic_bytes(inst.prob) for inst in insts]
     bytes_step = float(np.mean([a["total"] for a in ab_all]))
@@ -627,7 +644,7 @@ def main():
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-    traffic, kname = recorded_traffic(CONFIG_NAMES[k], dominant)
+    traffic, kname = recorded_traffic(CONFIG_NAMES[k] + (f"_paged{page}" if page else ""), dominant)
     roof["traffic"] = traffic
     roof["kernel"] = kname or {"shrink": f"{kind}_shrink", "expand": f"{kind}_expand", "fused": "fused_linear",
                                kind: f"{kind}_onepass"}[dominant]
@@ -662,7 +679,7 @@ def main():
         "config": {"workload": CONFIG_NAMES[k], "T": T, "d_in": prob0.d_in, "d_out": prob0.d_out,
                    "ranks": sorted(set(int(r) for r in prob0.ranks)), "pool_adapters": prob0.n_adapters,
                    "distinct_adapters": int(len(prob0.distinct_adapters())), "rotated_instances": L,
-                   "path": kind},
+                   "path": kind + ("_paged" if page else ""), **({"page_bytes": page} if page else {})},
         "achieved_GBps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": round(bytes_step),
