@@ -304,6 +304,40 @@ size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int3
 int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev, int32_t n_adapters,
                       const lora_proj *projs, int32_t n_proj, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------ grouped SGMV
+ * The prefill form of the grouped invocation (same sections as grouped BGMV):
+ * several projections of a layer, each with its own plan, x, y and sizes, in
+ * one shrink launch and one expand launch.  Each projection's plan is built
+ * (lora_build_plan) from the batch's ids with that projection's adapter
+ * tables, so every projection applies
+ *     y_p[t, :] += (alpha_{i,p} / r_{i,p}) (x_p[t, :] A_{i,p}) B_{i,p},  i = ids[t].
+ * Projections whose inputs are the same tensor (q, k, v; gate, up) may pass the
+ * same x.  The expand always takes the 16-row block form; a projection's
+ * result equals that of a lora_sgmv call that takes the same kernel variants
+ * (block expand, same d_in split), and is within the stated tolerance of the
+ * exact result in every case. */
+typedef struct lora_sgmv_proj {
+    const void *x;          /* device [T, ldx] of the call's dtype */
+    void *y;                /* device [T, ldy]; the y of two projections share no element */
+    const void *plan_host;  /* this projection's plan (host copy) */
+    const void *plan_dev;   /* and its device copy (lora_plan_upload) */
+    int64_t ldx, ldy;
+    int32_t d_in, d_out;
+} lora_sgmv_proj;
+
+/* Workspace bytes of lora_sgmv_grouped for these projections (host array of
+ * n_proj, 1 <= n_proj <= LORA_MAX_PROJ, plans already built); 0 if the
+ * arguments are invalid. */
+size_t lora_sgmv_grouped_workspace_bytes(const lora_sgmv_proj *projs, int32_t n_proj);
+
+/*   projs    host array of n_proj projections (read during the call)
+ *   ws       device, 16-byte aligned, >= lora_sgmv_grouped_workspace_bytes
+ * Projections whose plan has no adapted token are skipped.
+ * Errors: LORA_ERR_ARG (also: two projections with the same y), LORA_ERR_DTYPE,
+ * LORA_ERR_RANK, LORA_ERR_ALIGN, LORA_ERR_PLAN, LORA_ERR_WORKSPACE, LORA_ERR_HIP. */
+int lora_sgmv_grouped(void *stream, int dtype, const lora_sgmv_proj *projs, int32_t n_proj, void *ws,
+                      size_t ws_bytes);
+
 /* ------------------------------------------------------------ adapter residency
  * The GPU and host tiers of the pages' adapter storage ("Multi-LoRA Serving:
  * Many Adapters on One GPU" (gpusmith.com), section "Swap latency and cache

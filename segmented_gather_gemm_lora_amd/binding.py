@@ -46,6 +46,7 @@ EXPORTS = [
     "lora_cache_register", "lora_cache_pin", "lora_cache_prepare", "lora_cache_view_get", "lora_cache_stats_get",
     "lora_pages_needed", "lora_page_alloc_create", "lora_page_alloc_destroy", "lora_page_alloc_take",
     "lora_page_alloc_give", "lora_page_alloc_free_count", "lora_pages_write", "lora_sgmv_paged", "lora_bgmv_paged",
+    "lora_sgmv_grouped", "lora_sgmv_grouped_workspace_bytes",
 ]
 LORA_CACHE_DRY = 1
 MAX_PROJ = 8
@@ -99,6 +100,8 @@ _SIGS = {
     "lora_cache_view_get": (ctypes.c_int, [_vp, _vp]),
     "lora_cache_stats_get": (ctypes.c_int, [_vp, _vp]),
     "lora_pages_needed": (_i64, [_i64, _i64]),
+    "lora_sgmv_grouped": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _sz]),
+    "lora_sgmv_grouped_workspace_bytes": (_sz, [_vp, _i32]),
     "lora_page_alloc_create": (ctypes.c_int, [_i32, _vp]),
     "lora_page_alloc_destroy": (None, [_vp]),
     "lora_page_alloc_take": (ctypes.c_int, [_vp, _i32, _vp]),
@@ -139,6 +142,16 @@ class LoraProj(ctypes.Structure):
 
 
 assert ctypes.sizeof(LoraProj) == 80
+
+
+class LoraSgmvProj(ctypes.Structure):
+    """struct lora_sgmv_proj: one projection of a grouped SGMV call."""
+
+    _fields_ = [("x", _vp), ("y", _vp), ("plan_host", _vp), ("plan_dev", _vp), ("ldx", _i64), ("ldy", _i64),
+                ("d_in", _i32), ("d_out", _i32)]
+
+
+assert ctypes.sizeof(LoraSgmvProj) == 56
 
 
 def lib_path() -> str:
@@ -728,6 +741,34 @@ def bgmv_paged(x, ids_dev, pool: PagedPool, y, ws, dtype: str, max_rank: Optiona
                                   max_rank or pool.max_rank, _ptr(pool.pages), pool.page_bytes, _ptr(y), y.stride(0),
                                   y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_bgmv_paged")
+
+
+def sgmv_proj_array(xs, plans, ys):
+    """Host array of struct lora_sgmv_proj for projections (xs[p], plans[p], ys[p])."""
+    arr = (LoraSgmvProj * len(xs))()
+    for p, (x, plan, y) in enumerate(zip(xs, plans, ys)):
+        arr[p] = LoraSgmvProj(_ptr(x), _ptr(y), plan.host.data_ptr(), plan.dev.data_ptr(), x.stride(0), y.stride(0),
+                              x.shape[1], y.shape[1])
+    return arr
+
+
+def sgmv_grouped_workspace(plans_or_projs, xs=None, ys=None, device="cuda"):
+    """A device workspace for lora_sgmv_grouped (uint8 tensor)."""
+    torch = _torch()
+    projs = plans_or_projs if xs is None else sgmv_proj_array(xs, plans_or_projs, ys)
+    n = int(load().lora_sgmv_grouped_workspace_bytes(projs, len(projs)))
+    if n == 0:
+        raise LoraError(-1, "lora_sgmv_grouped_workspace_bytes", "invalid projections")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sgmv_grouped(xs, plans, ys, ws, dtype: str, stream=None, projs=None):
+    """Prefill correction of several projections in one shrink and one expand
+    launch: projection p applies plans[p] (built from the batch's ids with its
+    own adapter tables) to xs[p] and accumulates into ys[p]."""
+    projs = projs if projs is not None else sgmv_proj_array(xs, plans, ys)
+    _check(load().lora_sgmv_grouped(_stream_handle(stream), DTYPES[dtype], projs, len(projs), _ptr(ws),
+                                    ws.numel() * ws.element_size()), "lora_sgmv_grouped")
 
 
 def proj_array(xs, pools, ys, max_ranks=None):

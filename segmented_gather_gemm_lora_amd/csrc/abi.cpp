@@ -507,6 +507,69 @@ int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t l
                              pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, ws, pages, shift);
 }
 
+size_t lora_sgmv_grouped_workspace_bytes(const lora_sgmv_proj *projs, int32_t n_proj)
+{
+    if (!projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;
+    size_t total = 0;
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_plan_header *h = nullptr;
+        if (check_plan(projs[p].plan_host, &h)) return 0;
+        clear_error();
+        total += grouped_region_bytes(h->num_sorted, projs[p].d_in < 1 ? 1 : projs[p].d_in,
+                                      h->max_rank < 1 ? 1 : h->max_rank);
+    }
+    return total;
+}
+
+int lora_sgmv_grouped(void *stream, int dtype, const lora_sgmv_proj *projs, int32_t n_proj, void *ws,
+                      size_t ws_bytes)
+{
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (!projs) return fail(LORA_ERR_ARG, "projs is NULL");
+    if (n_proj < 1 || n_proj > LORA_MAX_PROJ)
+        return fail(LORA_ERR_ARG, "n_proj %d outside [1, %d]", n_proj, LORA_MAX_PROJ);
+    GroupedSgmv g[LORA_MAX_PROJ];
+    size_t need = 0;
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_sgmv_proj &q = projs[p];
+        const lora_plan_header *h = nullptr;
+        if ((st = check_plan(q.plan_host, &h))) return st;
+        for (int o = 0; o < p; ++o)
+            if (projs[o].y == q.y) return fail(LORA_ERR_ARG, "projections %d and %d write the same y", o, p);
+        g[p].plan = PlanView{h, static_cast<const char *>(q.plan_dev)};
+        g[p].ws = nullptr;
+        if (h->num_sorted == 0) {
+            g[p].sa = ShrinkArgs{};
+            g[p].ea = ExpandArgs{};
+            continue;
+        }
+        if (!q.plan_dev) return fail(LORA_ERR_ARG, "projection %d: plan_dev is NULL", p);
+        if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "projection %d: plan has %d blocks", p, h->num_blocks);
+        need += grouped_region_bytes(h->num_sorted, q.d_in < 1 ? 1 : q.d_in, h->max_rank);
+    }
+    if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    char *wp = static_cast<char *>(ws);
+    for (int p = 0; p < n_proj; ++p) {
+        const lora_sgmv_proj &q = projs[p];
+        const lora_plan_header *h = g[p].plan.h;
+        if (h->num_sorted == 0) continue;
+        const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+        float *v = reinterpret_cast<float *>(wp);
+        if ((st = make_shrink_args(dtype, q.x, q.ldx, q.d_in, v, ldw, h->max_rank, &g[p].sa)) ||
+            (st = make_expand_args(dtype, v, ldw, h->max_rank, q.y, q.ldy, q.d_out, true, &g[p].ea))) {
+            char msg[192];
+            snprintf(msg, sizeof msg, "%s", lora_last_error()); // fail() rewrites the message buffer
+            return fail(st, "projection %d: %s", p, msg);
+        }
+        g[p].ws = v;
+        wp += grouped_region_bytes(h->num_sorted, q.d_in < 1 ? 1 : q.d_in, h->max_rank);
+    }
+    return launch_sgmv_grouped(static_cast<hipStream_t>(stream), g, n_proj);
+}
+
 size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj)
 {
     if (T < 0 || !projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;

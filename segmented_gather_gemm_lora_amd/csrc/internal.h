@@ -77,6 +77,15 @@ struct GroupedProj {
 };
 int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
                         int n);
+// One projection of a grouped SGMV call: its plan, shrink and expand
+// arguments, and its workspace region (the fp32 slice partials of v).
+struct GroupedSgmv {
+    ShrinkArgs sa;
+    ExpandArgs ea;
+    PlanView plan;
+    float *ws;
+};
+int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n);
 // Bytes of one projection's region in a grouped workspace (256-byte multiple).
 size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank);
 

@@ -625,18 +625,20 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
 // SGMV kernels.  Shrink: one workgroup per (plan block, d_in slice).  Expand:
 // one workgroup per (256 columns, plan block) or (256 columns, plan chunk).
 // ----------------------------------------------------------------------------
+// Item b of a shrink launch (b = the workgroup's index along x).
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
-__global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
-                                                             const lora_blk_desc *__restrict__ blks, int nblk, int kc,
-                                                             int slice_len, float *__restrict__ out, int64_t ldo,
-                                                             int64_t sl_stride, const M mem)
+__device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int64_t ldx, int d_in,
+                                                 const lora_blk_desc *__restrict__ blks, int nblk, int kc,
+                                                 int slice_len, float *__restrict__ out, int64_t ldo,
+                                                 int64_t sl_stride, unsigned b, const M &mem)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     // Workgroup b runs on XCD b % 8.  Give each XCD a contiguous run of
     // (block, slice) items, blocks fastest, so that the blocks of a segment
     // share one L2 and its A slice is fetched into few L2s.
     const int total = nblk * kc, per = (total + 7) >> 3;
-    const int item = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+    if (int(b >> 3) >= per) return;
+    const int item = int(b & 7) * per + int(b >> 3);
     if (item >= total) return;
     const lora_blk_desc *bd = blks + item % nblk;
     const int c = item / nblk;
@@ -648,8 +650,18 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restr
                                         k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red, mem);
 }
 
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
+__global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
+                                                             const lora_blk_desc *__restrict__ blks, int nblk, int kc,
+                                                             int slice_len, float *__restrict__ out, int64_t ldo,
+                                                             int64_t sl_stride, const M mem)
+{
+    sgmv_shrink_item<DT, VEC, W, NSTEP, RT>(x, ldx, d_in, blks, nblk, kc, slice_len, out, ldo, sl_stride, blockIdx.x,
+                                            mem);
+}
+
 template <int DT, bool VECY, int UPT, class M>
-__global__ __launch_bounds__(256) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                           int nsl, const lora_blk_desc *__restrict__ blks,
                                                           void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
                                                           int ldl, const M mem)
@@ -948,6 +960,56 @@ __global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const i
 }
 
 // ----------------------------------------------------------------------------
+// Grouped SGMV: several projections of a layer, each with its own plan (the
+// batch's segments with the projection's adapter tables), x, y and sizes, in
+// one shrink launch and one expand launch.  blockIdx.z is the projection, its
+// arguments come from a table in the kernel arguments; workgroups past a
+// projection's own items, blocks or column tiles exit at once.  The bodies are
+// the single-call kernels' (the expand the 16-row block form).
+// ----------------------------------------------------------------------------
+struct SGShrink {
+    const void *x;
+    const lora_blk_desc *blks;
+    float *out;
+    int64_t ldx, ldo, sl_stride;
+    int32_t d_in, nblk, kc, slice_len;
+};
+struct SGShrinkTable {
+    SGShrink p[LORA_MAX_PROJ];
+};
+struct SGExpand {
+    const float *v;
+    const lora_blk_desc *blks;
+    void *y;
+    int64_t ldv, sl_stride, ldy;
+    int32_t nsl, nblk, d_out, ncol, ldl, vec_b;
+};
+struct SGExpandTable {
+    SGExpand p[LORA_MAX_PROJ];
+};
+
+template <int DT, bool VEC, int W, int NSTEP, int RT>
+__global__ __launch_bounds__(W * 64) void sgmv_shrink_grouped_kernel(const SGShrinkTable tab)
+{
+    const SGShrink &P = tab.p[blockIdx.z];
+    sgmv_shrink_item<DT, VEC, W, NSTEP, RT>(P.x, P.ldx, P.d_in, P.blks, P.nblk, P.kc, P.slice_len, P.out, P.ldo,
+                                            P.sl_stride, blockIdx.x, DenseMem{});
+}
+
+template <int DT, bool VECY, int UPT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sgmv_expand_grouped_kernel(
+    const SGExpandTable tab)
+{
+    extern __shared__ floatx4 vl4[];
+    const SGExpand &P = tab.p[blockIdx.z];
+    if (int(blockIdx.y) >= P.nblk || int(blockIdx.x) >= P.ncol) return;
+    const lora_blk_desc *d = P.blks + blockIdx.y;
+    expand_rows<DT, VECY, false, UPT>(P.v, P.ldv, P.sl_stride, P.nsl, reinterpret_cast<const void *>(d->B), d->rank,
+                                      d->scale, P.y, P.ldy, P.d_out, blockIdx.x * kExpandCols, P.vec_b != 0, d->rows,
+                                      d->p0, d->n, reinterpret_cast<float *>(vl4), P.ldl);
+}
+
+// ----------------------------------------------------------------------------
 // Launch configuration.
 // ----------------------------------------------------------------------------
 int check_launch(const char *what)
@@ -1099,6 +1161,16 @@ template <int DT, bool VEC, int RT> struct BgmvShrinkGroupedL {
                 launch_kernel(bgmv_shrink_grouped_kernel<DT, VEC, 4, 1, RT, false>, grid, dim3(256), 0, s, T, ids,
                               n_adapters, tab);
         }
+    }
+};
+
+template <int DT, bool VEC, int RT> struct SgmvShrinkGroupedL {
+    static void run(hipStream_t s, dim3 grid, bool two, const SGShrinkTable &tab)
+    {
+        if (two && RT < 4)
+            launch_kernel(sgmv_shrink_grouped_kernel<DT, VEC, 4, 2, RT>, grid, dim3(256), 0, s, tab);
+        else
+            launch_kernel(sgmv_shrink_grouped_kernel<DT, VEC, 4, 1, RT>, grid, dim3(256), 0, s, tab);
     }
 };
 
@@ -1471,6 +1543,63 @@ int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_
     }
 #undef LORA_BGMV_GEXPAND
     return check_launch("bgmv grouped expand");
+}
+
+int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n)
+{
+    SGShrinkTable stab{};
+    SGExpandTable etab{};
+    int m = 0, dtype = -1;
+    // template choices shared by all projections: the most general one
+    bool vec = true, vecy = true, two = true;
+    int rt = 1, gx = 8, nblk_max = 1, ncol_max = 1, ldl_max = 4;
+    for (int p = 0; p < n; ++p) {
+        const GroupedSgmv &g = pr[p];
+        const lora_plan_header *h = g.plan.h;
+        if (h->num_blocks == 0) continue; // nothing to do for this projection
+        dtype = g.sa.dtype;
+        // the same split as a single lora_sgmv call of this projection
+        const Split sp = choose_split(g.sa.d_in, h->num_blocks, dtype);
+        const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+        const int64_t sl_stride = int64_t(h->num_sorted) * ldw;
+        const int ldl = lds_pitch(h->max_rank);
+        const int ncol = (g.ea.d_out + kExpandCols - 1) / kExpandCols;
+        const lora_blk_desc *blks = plan_blocks(g.plan);
+        stab.p[m] = SGShrink{g.sa.x, blks, g.ws, g.sa.ldx, ldw, sl_stride, g.sa.d_in, h->num_blocks, sp.kc,
+                             sp.slice_len};
+        etab.p[m] = SGExpand{g.ws, blks, g.ea.y, ldw, sl_stride, g.ea.ldy, sp.kc, h->num_blocks, g.ea.d_out, ncol,
+                             ldl, g.ea.vec_b ? 1 : 0};
+        ++m;
+        vec = vec && g.sa.vec;
+        vecy = vecy && g.ea.vec_y && g.ea.d_out % 16 == 0;
+        two = two && sp.nstep == 2;
+        rt = rt > rank_tiles(h->max_rank) ? rt : rank_tiles(h->max_rank);
+        const int items = (h->num_blocks * sp.kc + 7) / 8 * 8;
+        gx = gx > items ? gx : items;
+        nblk_max = nblk_max > h->num_blocks ? nblk_max : h->num_blocks;
+        ncol_max = ncol_max > ncol ? ncol_max : ncol;
+        ldl_max = ldl_max > ldl ? ldl_max : ldl;
+    }
+    if (m == 0) return LORA_OK;
+    dispatch_shrink<SgmvShrinkGroupedL>(dtype, vec, rt, s, dim3(unsigned(gx), 1, unsigned(m)), two, stab);
+    int st = check_launch("sgmv grouped shrink");
+    if (st) return st;
+    const dim3 egrid(static_cast<unsigned>(ncol_max), static_cast<unsigned>(nblk_max), static_cast<unsigned>(m));
+    const size_t shm = (size_t(kRows) * ldl_max + 4) * sizeof(float);
+    const int upt = units_per_thread(1, ldl_max);
+#define LORA_SGMV_GEXPAND(DT_, VECY_)                                                                                  \
+    switch (upt) {                                                                                                     \
+    case 1: launch_kernel(sgmv_expand_grouped_kernel<DT_, VECY_, 1>, egrid, dim3(256), shm, s, etab); break;          \
+    case 2: launch_kernel(sgmv_expand_grouped_kernel<DT_, VECY_, 2>, egrid, dim3(256), shm, s, etab); break;          \
+    default: launch_kernel(sgmv_expand_grouped_kernel<DT_, VECY_, 4>, egrid, dim3(256), shm, s, etab);                \
+    }
+    if (dtype == LORA_BF16) {
+        if (vecy) { LORA_SGMV_GEXPAND(LORA_BF16, true) } else { LORA_SGMV_GEXPAND(LORA_BF16, false) }
+    } else {
+        if (vecy) { LORA_SGMV_GEXPAND(LORA_F32, true) } else { LORA_SGMV_GEXPAND(LORA_F32, false) }
+    }
+#undef LORA_SGMV_GEXPAND
+    return check_launch("sgmv grouped expand");
 }
 
 } // namespace lora

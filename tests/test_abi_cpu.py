@@ -335,3 +335,32 @@ def test_header_is_a_c_abi(tmp_path):
                     "-Wl,-rpath," + os.path.dirname(lib)], check=True)
     out = subprocess.run([exe], check=True, capture_output=True, text=True)
     assert out.stdout.strip() == "ok"
+
+
+def test_grouped_sgmv_host_checks():
+    """Grouped SGMV: workspace = the projections' 256-byte rounded regions;
+    malformed calls are rejected before any GPU work."""
+    L = B.load()
+    plan = _valid_plan()  # T = 8, max rank 8
+    projs = (B.LoraSgmvProj * 2)()
+    for p in range(2):
+        projs[p] = B.LoraSgmvProj(FX, FX + 0x100000 * (p + 1), plan.ptr, FX, 256, 256, 256, 256)
+    one = B.lora_workspace_bytes(B.LORA_OP_SGMV, 8, 256, 256, 8)
+    need = L.lora_sgmv_grouped_workspace_bytes(projs, 2)
+    assert need == 2 * ((one + 255) // 256 * 256)
+    assert L.lora_sgmv_grouped_workspace_bytes(projs, 0) == 0
+    assert L.lora_sgmv_grouped_workspace_bytes(projs, 9) == 0
+    g = L.lora_sgmv_grouped
+    assert g(None, 1, projs, 2, FX, need - 1) == -6
+    assert g(None, 1, projs, 2, FX + 8, need) == -4
+    assert g(None, 1, projs, 0, FX, need) == -1
+    assert g(None, 1, None, 2, FX, need) == -1
+    assert g(None, 9, projs, 2, FX, need) == -5
+    projs[1].y = projs[0].y
+    assert g(None, 1, projs, 2, FX, need) == -1          # same y twice
+    projs[1].y = FX + 0x300000
+    projs[1].x = None
+    assert g(None, 1, projs, 2, FX, need) == -1          # NULL x
+    projs[1].x = FX
+    projs[1].plan_host = None
+    assert g(None, 1, projs, 2, FX, need) != 0           # no plan
