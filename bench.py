@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
-    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|decode_cache] [--steps K] [--warmup W]
+    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|prefill_qkv|decode_cache]
+                    [--steps K] [--warmup W]
                     [--paged PAGE_BYTES]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
@@ -126,14 +127,16 @@ class Instance:
 
 
 class GroupedInstance:
-    """One layer's q, k, v decode inputs (shared x, own adapters and outputs)
-    for the grouped call, and the same work as separate single calls."""
+    """One layer's q, k, v inputs (shared x, own adapters and outputs) for the
+    grouped call (BGMV for decode, SGMV from per-projection plans for
+    prefill), and the same work as separate single calls."""
 
-    def __init__(self, probs):
+    def __init__(self, probs, sgmv=False):
         import torch
 
         from segmented_gather_gemm_lora_amd import binding as B
 
+        self.sgmv = sgmv
         self.probs = probs
         self.pools = [B.DevicePool.from_problem(p) for p in probs]
         self.x = B.to_device(probs[0].x, probs[0].dtype)
@@ -143,17 +146,28 @@ class GroupedInstance:
         self.projs = B.proj_array(self.xs, self.pools, self.ys)
         self.ws = B.bgmv_grouped_workspace(probs[0].T, self.projs)
         self.ws1 = [B.workspace(B.LORA_OP_BGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
+        if sgmv:
+            self.plans = [B.Plan(p.T).build(p.ids, pool).upload() for p, pool in zip(probs, self.pools)]
+            self.sprojs = B.sgmv_proj_array(self.xs, self.plans, self.ys)
+            self.ws = B.sgmv_grouped_workspace(self.sprojs)
+            self.ws1 = [B.workspace(B.LORA_OP_SGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
 
     def step(self):
         from segmented_gather_gemm_lora_amd import binding as B
 
-        B.bgmv_grouped(self.xs, self.ids, self.pools, self.ys, self.ws, self.probs[0].dtype, projs=self.projs)
+        if self.sgmv:
+            B.sgmv_grouped(self.xs, self.plans, self.ys, self.ws, self.probs[0].dtype, projs=self.sprojs)
+        else:
+            B.bgmv_grouped(self.xs, self.ids, self.pools, self.ys, self.ws, self.probs[0].dtype, projs=self.projs)
 
     def step_separate(self):
         from segmented_gather_gemm_lora_amd import binding as B
 
         for p, prob in enumerate(self.probs):
-            B.bgmv(self.x, self.ids, self.pools[p], self.ys[p], self.ws1[p], prob.dtype)
+            if self.sgmv:
+                B.sgmv(self.x, self.plans[p], self.ys[p], self.ws1[p], prob.dtype)
+            else:
+                B.bgmv(self.x, self.ids, self.pools[p], self.ys[p], self.ws1[p], prob.dtype)
 
 
 def grouped_bytes(probs):
@@ -181,21 +195,25 @@ def time_steps(step, K, stream):
     return ev0.elapsed_time(ev1) / K, time.perf_counter() - t0
 
 
-def grouped_main(args):
-    """The q, k, v decode projections in one grouped shrink + expand (two
-    launches), with the same work as three single BGMV calls timed beside it."""
+def grouped_main(args, sgmv=False):
+    """The q, k, v projections in one grouped shrink + expand (two launches),
+    with the same work as three single calls timed beside it: decode (BGMV)
+    or, with sgmv, prefill (SGMV from per-projection plans)."""
     import torch
 
     import oracle
-    from lora_workloads import QKV_NAME, make_decode_qkv
+    from lora_workloads import PREFILL_QKV_NAME, QKV_NAME, make_decode_qkv, make_prefill_qkv
     from segmented_gather_gemm_lora_amd import binding as B
 
-    probs0 = make_decode_qkv()
+    make = make_prefill_qkv if sgmv else make_decode_qkv
+    name = PREFILL_QKV_NAME if sgmv else QKV_NAME
+    kind = "sgmv" if sgmv else "bgmv"
+    probs0 = make()
     ab0 = grouped_bytes(probs0)
     L = args.rotation or rotation_count(ab0["total"])
-    print(f"[bench] {QKV_NAME}: T={probs0[0].T} d_in={probs0[0].d_in} d_out={[p.d_out for p in probs0]} "
+    print(f"[bench] {name}: T={probs0[0].T} d_in={probs0[0].d_in} d_out={[p.d_out for p in probs0]} "
           f"rotation={L} bytes/layer={ab0['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
-    insts = [GroupedInstance(probs0)] + [GroupedInstance(make_decode_qkv(seed=2000 + i)) for i in range(1, L)]
+    insts = [GroupedInstance(probs0, sgmv)] + [GroupedInstance(make(seed=2000 + i), sgmv) for i in range(1, L)]
     ab_all = [grouped_bytes(g.probs) for g in insts]
     bytes_step = float(np.mean([a["total"] for a in ab_all]))
     T = probs0[0].T
@@ -231,10 +249,10 @@ def grouped_main(args):
     dom_bytes = float(np.mean([a[dominant] for a in ab_all]))
     dom_us = per_kernel_us[dominant]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic, kname = recorded_traffic(QKV_NAME, dominant)
+    traffic, kname = recorded_traffic(name, dominant)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": kname or f"bgmv_{dominant}_grouped_kernel", "algorithmic_bytes_per_launch": round(dom_bytes),
+            "kernel": kname or f"{kind}_{dominant}_grouped_kernel", "algorithmic_bytes_per_launch": round(dom_bytes),
             "avg_launch_us": round(dom_us, 3)}
 
     cpu = None
@@ -264,16 +282,16 @@ def grouped_main(args):
         "vs_baseline": None,
         "dtype": probs0[0].dtype,
         "data": "synthetic",
-        "config": {"workload": QKV_NAME, "T": T, "d_in": probs0[0].d_in, "d_out": [p.d_out for p in probs0],
+        "config": {"workload": name, "T": T, "d_in": probs0[0].d_in, "d_out": [p.d_out for p in probs0],
                    "ranks": [16], "pool_adapters": probs0[0].n_adapters,
                    "distinct_adapters": int(len(probs0[0].distinct_adapters())), "rotated_instances": L,
-                   "path": "bgmv_grouped"},
+                   "path": f"{kind}_grouped"},
         "achieved_GBps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": round(bytes_step),
         "per_kernel_us": {n: round(v, 3) for n, v in per_kernel_us.items()},
         "separate_calls_ms_per_step": round(ms_sep, 6),
-        "separate_calls": "the same q, k, v work as three lora_bgmv calls (six launches)",
+        "separate_calls": f"the same q, k, v work as three lora_{kind} calls (six launches)",
         "wall_s_timed": round(t_wall, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -521,7 +539,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv", "decode_cache"], default="decode")
+    ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv", "prefill_qkv", "decode_cache"],
+                    default="decode")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
@@ -548,8 +567,8 @@ def main():
         copy_calibration()
         return
     B.load()
-    if args.config == "decode_qkv":
-        grouped_main(args)
+    if args.config in ("decode_qkv", "prefill_qkv"):
+        grouped_main(args, sgmv=args.config == "prefill_qkv")
         return
     if args.config == "decode_cache":
         cache_main(args)

@@ -14,6 +14,8 @@ from .synth import (  # noqa: F401
     make_problem,
     make_integer_problem,
     make_decode_qkv,
+    make_prefill_qkv,
+    PREFILL_QKV_NAME,
     make_decode_registry,
     CACHE_NAME,
     QKV_NAME,

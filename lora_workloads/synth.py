@@ -333,6 +333,27 @@ def make_decode_qkv(seed: int = 2, d_outs: Sequence[int] = (4096, 1024, 1024)) -
     return probs
 
 
+PREFILL_QKV_NAME = "prefill_qkv_grouped_bf16"
+
+
+def make_prefill_qkv(seed: int = 3, d_outs: Sequence[int] = (4096, 1024, 1024)) -> list:
+    """The q, k and v projections of one prefill batch, for the grouped SGMV
+    call: the prefill workload's 4096 tokens in 16 Dirichlet(1) segments over
+    a pool of 16 rank-16 adapters (alpha 32), d_in 4096, d_out 4096 / 1024 /
+    1024.  One id per token for all three projections; x is shared (the same
+    array object); every projection has its own adapters and base output."""
+    ids = make_config(3, seed=seed).ids
+    rng = np.random.default_rng(seed + 7)
+    probs = []
+    for p, d_out in enumerate(d_outs):
+        prob = make_problem(name=f"{PREFILL_QKV_NAME}/{'qkv'[p] if p < 3 else p}", dtype="bf16", ids=ids,
+                            ranks=[16] * 16, alphas=[32.0] * 16, d_in=4096, d_out=d_out, seed=seed, rng=rng)
+        if p > 0:
+            prob.x = probs[0].x
+        probs.append(prob)
+    return probs
+
+
 CACHE_NAME = "decode_cache_bf16"
 
 

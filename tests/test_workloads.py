@@ -67,3 +67,17 @@ def test_fused_config_structure():
     assert c5.n_adapters == 200 and len(c5.meta["resident_ids"]) == 200
     drawn = set(c5.meta["request_adapter"])
     assert drawn <= set(c5.meta["resident_ids"])
+
+
+def test_prefill_qkv_structure():
+    """q, k, v of the prefill batch: the prefill workload's ids for all three,
+    one shared x, own adapters and outputs, seeded."""
+    from lora_workloads import make_config, make_prefill_qkv
+
+    a, b = make_prefill_qkv(), make_prefill_qkv()
+    assert [p.d_out for p in a] == [4096, 1024, 1024]
+    assert all(np.array_equal(p.ids, make_config(3).ids) for p in a)
+    assert a[1].x is a[0].x and a[2].x is a[0].x
+    assert not np.array_equal(a[0].pool[:1000], a[1].pool[:1000])
+    for p, q in zip(a, b):
+        assert np.array_equal(p.pool, q.pool) and np.array_equal(p.x, q.x)
