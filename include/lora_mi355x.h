@@ -312,10 +312,12 @@ int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev
  * tables, so every projection applies
  *     y_p[t, :] += (alpha_{i,p} / r_{i,p}) (x_p[t, :] A_{i,p}) B_{i,p},  i = ids[t].
  * Projections whose inputs are the same tensor (q, k, v; gate, up) may pass the
- * same x.  The expand always takes the 16-row block form; a projection's
- * result equals that of a lora_sgmv call that takes the same kernel variants
- * (block expand, same d_in split), and is within the stated tolerance of the
- * exact result in every case. */
+ * same x.  The expand takes the 64-row chunk form when every projection's
+ * ranks are <= 32 and the projections together give at least 1024 (chunk,
+ * 256-column tile) items, else the 16-row block form; a projection's result
+ * equals that of a lora_sgmv call that takes the same kernel variants (same
+ * expand form and d_in split), and is within the stated tolerance of the exact
+ * result in every case. */
 typedef struct lora_sgmv_proj {
     const void *x;          /* device [T, ldx] of the call's dtype */
     void *y;                /* device [T, ldy]; the y of two projections share no element */

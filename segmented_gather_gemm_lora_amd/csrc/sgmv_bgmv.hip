@@ -964,8 +964,9 @@ __global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const i
 // batch's segments with the projection's adapter tables), x, y and sizes, in
 // one shrink launch and one expand launch.  blockIdx.z is the projection, its
 // arguments come from a table in the kernel arguments; workgroups past a
-// projection's own items, blocks or column tiles exit at once.  The bodies are
-// the single-call kernels' (the expand the 16-row block form).
+// projection's own items, blocks, chunks or column tiles exit at once.  The
+// bodies are the single-call kernels' (the expand in the 64-row chunk form or
+// the 16-row block form, chosen for the whole launch).
 // ----------------------------------------------------------------------------
 struct SGShrink {
     const void *x;
@@ -980,9 +981,11 @@ struct SGShrinkTable {
 struct SGExpand {
     const float *v;
     const lora_blk_desc *blks;
+    const lora_chunk_desc *chunks;
     void *y;
     int64_t ldv, sl_stride, ldy;
-    int32_t nsl, nblk, d_out, ncol, ldl, vec_b;
+    int32_t nsl, nblk, nchunk, d_out, ncol, ldl, vec_b;
+    int32_t item0; // chunk expand: first item of this projection in the flat grid
 };
 struct SGExpandTable {
     SGExpand p[LORA_MAX_PROJ];
@@ -994,6 +997,36 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_grouped_kernel(const SGShr
     const SGShrink &P = tab.p[blockIdx.z];
     sgmv_shrink_item<DT, VEC, W, NSTEP, RT>(P.x, P.ldx, P.d_in, P.blks, P.nblk, P.kc, P.slice_len, P.out, P.ldo,
                                             P.sl_stride, blockIdx.x, DenseMem{});
+}
+
+// One flat grid of (projection, chunk, column tile) items, column tiles
+// fastest, projections in order: no workgroup is idle when the projections
+// have different widths.
+template <int DT, bool VECY, int NCH, int UPT>
+__global__ __launch_bounds__(256) void sgmv_expand_chunk_grouped_kernel(const SGExpandTable tab, int n_proj)
+{
+    extern __shared__ floatx4 vl4[];
+    const int b = int(blockIdx.x);
+    int p = 0;
+    for (int q = 1; q < n_proj; ++q)
+        if (b >= tab.p[q].item0) p = q;
+    const SGExpand &P = tab.p[p];
+    const int local = b - P.item0;
+    const int ci = local / P.ncol, col = local - ci * P.ncol;
+    if (ci >= P.nchunk) return;
+    const lora_chunk_desc *d = P.chunks + ci;
+    const int r = d->rank;
+    const int n = d->n < kChunkRB * kRows ? d->n : kChunkRB * kRows;
+    const void *B = reinterpret_cast<const void *>(d->B);
+    float *vl = reinterpret_cast<float *>(vl4);
+    if (P.vec_b && (r & 3) == 0)
+        expand_chunk_impl<DT, VECY, true, NCH, UPT, kChunkRB>(P.v, P.ldv, P.sl_stride, P.nsl, B, r, d->scale, P.y,
+                                                              P.ldy, P.d_out, col * kExpandCols, d->rows, d->p0, n,
+                                                              vl, P.ldl);
+    else
+        expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(P.v, P.ldv, P.sl_stride, P.nsl, B, r, d->scale, P.y,
+                                                               P.ldy, P.d_out, col * kExpandCols, d->rows, d->p0, n,
+                                                               vl, P.ldl);
 }
 
 template <int DT, bool VECY, int UPT>
@@ -1552,7 +1585,8 @@ int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n)
     int m = 0, dtype = -1;
     // template choices shared by all projections: the most general one
     bool vec = true, vecy = true, two = true;
-    int rt = 1, gx = 8, nblk_max = 1, ncol_max = 1, ldl_max = 4;
+    int rt = 1, gx = 8, nblk_max = 1, nchunk_max = 1, ncol_max = 1, ldl_max = 4, rank_max = 1;
+    int64_t chunk_items = 0;
     for (int p = 0; p < n; ++p) {
         const GroupedSgmv &g = pr[p];
         const lora_plan_header *h = g.plan.h;
@@ -1567,8 +1601,8 @@ int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n)
         const lora_blk_desc *blks = plan_blocks(g.plan);
         stab.p[m] = SGShrink{g.sa.x, blks, g.ws, g.sa.ldx, ldw, sl_stride, g.sa.d_in, h->num_blocks, sp.kc,
                              sp.slice_len};
-        etab.p[m] = SGExpand{g.ws, blks, g.ea.y, ldw, sl_stride, g.ea.ldy, sp.kc, h->num_blocks, g.ea.d_out, ncol,
-                             ldl, g.ea.vec_b ? 1 : 0};
+        etab.p[m] = SGExpand{g.ws, blks, plan_chunks(g.plan), g.ea.y, ldw, sl_stride, g.ea.ldy, sp.kc, h->num_blocks,
+                             h->num_chunks, g.ea.d_out, ncol, ldl, g.ea.vec_b ? 1 : 0, int32_t(chunk_items)};
         ++m;
         vec = vec && g.sa.vec;
         vecy = vecy && g.ea.vec_y && g.ea.d_out % 16 == 0;
@@ -1577,6 +1611,9 @@ int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n)
         const int items = (h->num_blocks * sp.kc + 7) / 8 * 8;
         gx = gx > items ? gx : items;
         nblk_max = nblk_max > h->num_blocks ? nblk_max : h->num_blocks;
+        nchunk_max = nchunk_max > h->num_chunks ? nchunk_max : h->num_chunks;
+        rank_max = rank_max > h->max_rank ? rank_max : h->max_rank;
+        chunk_items += int64_t(h->num_chunks) * ncol;
         ncol_max = ncol_max > ncol ? ncol_max : ncol;
         ldl_max = ldl_max > ldl ? ldl_max : ldl;
     }
@@ -1584,6 +1621,30 @@ int launch_sgmv_grouped(hipStream_t s, const GroupedSgmv *pr, int n)
     dispatch_shrink<SgmvShrinkGroupedL>(dtype, vec, rt, s, dim3(unsigned(gx), 1, unsigned(m)), two, stab);
     int st = check_launch("sgmv grouped shrink");
     if (st) return st;
+    // the single call's path choice over all projections together: 64-row
+    // chunks (B reused by four blocks) when every rank fits the chunk kernel's
+    // registers and there are enough (chunk, column tile) items
+    if (ldl_max <= 32 && chunk_items >= 1024) {
+        const dim3 cgrid(static_cast<unsigned>(chunk_items));
+        const size_t cshm = (size_t(kChunkRB * kRows) * ldl_max + 4) * sizeof(float);
+        const int cupt = units_per_thread(kChunkRB, ldl_max);
+        const bool two_steps = rank_max > 16;
+#define LORA_SGMV_GCHUNK(DT_, VECY_, NCH_)                                                                             \
+    switch (cupt) {                                                                                                    \
+    case 1: launch_kernel(sgmv_expand_chunk_grouped_kernel<DT_, VECY_, NCH_, 1>, cgrid, dim3(256), cshm, s, etab, m); break; \
+    case 2: launch_kernel(sgmv_expand_chunk_grouped_kernel<DT_, VECY_, NCH_, 2>, cgrid, dim3(256), cshm, s, etab, m); break; \
+    default: launch_kernel(sgmv_expand_chunk_grouped_kernel<DT_, VECY_, NCH_, 4>, cgrid, dim3(256), cshm, s, etab, m);     \
+    }
+        if (dtype == LORA_BF16) {
+            if (vecy) { if (two_steps) { LORA_SGMV_GCHUNK(LORA_BF16, true, 2) } else { LORA_SGMV_GCHUNK(LORA_BF16, true, 1) } }
+            else { if (two_steps) { LORA_SGMV_GCHUNK(LORA_BF16, false, 2) } else { LORA_SGMV_GCHUNK(LORA_BF16, false, 1) } }
+        } else {
+            if (vecy) { if (two_steps) { LORA_SGMV_GCHUNK(LORA_F32, true, 2) } else { LORA_SGMV_GCHUNK(LORA_F32, true, 1) } }
+            else { if (two_steps) { LORA_SGMV_GCHUNK(LORA_F32, false, 2) } else { LORA_SGMV_GCHUNK(LORA_F32, false, 1) } }
+        }
+#undef LORA_SGMV_GCHUNK
+        return check_launch("sgmv grouped chunk expand");
+    }
     const dim3 egrid(static_cast<unsigned>(ncol_max), static_cast<unsigned>(nblk_max), static_cast<unsigned>(m));
     const size_t shm = (size_t(kRows) * ldl_max + 4) * sizeof(float);
     const int upt = units_per_thread(1, ldl_max);

@@ -165,3 +165,29 @@ def test_grouped_sgmv_prefill_qkv():
         r.y_in = None
         ref, _ = oracle.lora_forward(r, nthreads=16)
         assert_close(decode(outs[p], "bf16"), ref, "bf16", f"prefill projection {p}")
+
+
+def test_grouped_sgmv_chunk_expand_rank32():
+    """Enough (chunk, column tile) items for the 64-row chunk expand, ranks up
+    to 32 (two 16-rank steps) including ranks that are not multiples of 4
+    (scalar B loads), d_out 4096 / 1024 / 1024, against the oracle."""
+    say("case grouped sgmv chunk expand rank 32")
+    rng = np.random.default_rng(77)
+    ids = np.repeat(rng.permutation(12), 256).astype(np.int32)
+    ids[rng.random(ids.size) < 0.03] = -1
+    ranks = {0: [32, 24, 17, 32, 8, 16, 32, 30, 32, 9, 20, 32], 1: [16, 32, 8, 5, 32, 16, 12, 32, 32, 32, 4, 28],
+             2: [32] * 12}
+    probs = projections(ids, "bf16", [1024] * 3, [4096, 1024, 1024], lambda p: ranks[p], seed=80)
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    pools = [B.DevicePool.from_problem(q) for q in probs]
+    plans = [B.Plan(q.T).build(q.ids, pool).upload() for q, pool in zip(probs, pools)]
+    items = sum(pl.header()["num_chunks"] * ((q.d_out + 255) // 256) for pl, q in zip(plans, probs))
+    assert items >= 1024, items
+    outs, y0, *_, used = run_grouped(probs, zero_base=True, plans_override=plans)
+    assert used == 2
+    for p, q in enumerate(probs):
+        r = copy.copy(q)
+        r.y_in = None
+        ref, _ = oracle.lora_forward(r, nthreads=16)
+        assert_close(decode(outs[p], "bf16"), ref, "bf16", f"projection {p}")
