@@ -869,7 +869,7 @@ __device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, in
                                                  const int32_t *__restrict__ pool_rank,
                                                  const float *__restrict__ pool_alpha, int n_adapters, int max_rank,
                                                  void *__restrict__ y, int64_t ldy, int d_out, bool vec_b, int ldl,
-                                                 const M &mem = M{})
+                                                 int ncol_wg, const M &mem = M{})
 {
     extern __shared__ floatx4 vl4[];
     __shared__ Group grp;
@@ -889,8 +889,8 @@ __device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, in
         const int n = grp.n, total = grp.total;
         if (n == 0) return;
         expand_rows<DT, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
-                                            blockIdx.y * kExpandCols, vec_b, grp.rows, -1, n,
-                                            reinterpret_cast<float *>(vl4), ldl, mem);
+                                            ncol_wg, vec_b, grp.rows, -1, n, reinterpret_cast<float *>(vl4), ldl,
+                                            mem);
         if (kRows * (pass + 1) >= total) break;
     }
 }
@@ -905,15 +905,17 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restric
                                                           bool vec_b, int ldl, const M mem)
 {
     bgmv_expand_body<DT, SLOT, VECY, UPT>(v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters,
-                                          max_rank, y, ldy, d_out, vec_b, ldl, mem);
+                                          max_rank, y, ldy, d_out, vec_b, ldl, int(blockIdx.y) * kExpandCols, mem);
 }
 
 // ----------------------------------------------------------------------------
 // Grouped BGMV: several projections of a layer, each with its own x, y, sizes
 // and adapter tables but one adapter id per token for all of them, in one
-// shrink launch and one expand launch.  blockIdx.z is the projection; its
-// arguments come from a table in the kernel arguments.  Workgroups past a
-// projection's own d_in slices or column tiles exit at once.
+// shrink launch and one expand launch.  Shrink: blockIdx.z is the projection
+// and workgroups past a projection's own d_in slices exit at once.  Expand:
+// blockIdx.y runs over the column tiles of all projections in order, so
+// projections of different widths leave no idle workgroups.  Each
+// projection's arguments come from a table in the kernel arguments.
 // ----------------------------------------------------------------------------
 struct GShrink {
     const void *x;
@@ -934,6 +936,8 @@ struct GExpand {
     void *y;
     int64_t ldv, sl_stride, ldy;
     int32_t nsl, max_rank, d_out, ldl, ncol, vec_b;
+    int32_t col0; // first column tile of this projection along blockIdx.y
+    int32_t pad;
 };
 struct GExpandTable {
     GExpand p[LORA_MAX_PROJ];
@@ -951,12 +955,18 @@ __global__ __launch_bounds__(W * 64) void bgmv_shrink_grouped_kernel(int T, cons
 
 template <int DT, bool SLOT, bool VECY, int UPT>
 __global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const int32_t *__restrict__ ids,
-                                                                  int n_adapters, const GExpandTable tab)
+                                                                  int n_adapters, const GExpandTable tab, int n_proj)
 {
-    const GExpand &P = tab.p[blockIdx.z];
-    if (int(blockIdx.y) >= P.ncol) return;
+    const int cy = int(blockIdx.y);
+    int p = 0;
+    for (int q = 1; q < n_proj; ++q)
+        if (cy >= tab.p[q].col0) p = q;
+    const GExpand &P = tab.p[p];
+    const int col = cy - P.col0;
+    if (col >= P.ncol) return;
     bgmv_expand_body<DT, SLOT, VECY, UPT>(P.v, P.ldv, P.sl_stride, P.nsl, T, ids, P.pool_B, P.pool_rank, P.pool_alpha,
-                                          n_adapters, P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl);
+                                          n_adapters, P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl,
+                                          col * kExpandCols);
 }
 
 // ----------------------------------------------------------------------------
@@ -1384,12 +1394,12 @@ void bgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
 
 template <int DT, bool SLOT, bool VECY>
 void bgmv_expand_grouped_go(hipStream_t s, dim3 grid, size_t shm, int upt, int T, const int32_t *ids, int n_adapters,
-                            const GExpandTable &tab)
+                            const GExpandTable &tab, int n)
 {
     switch (upt) {
-    case 1: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 1>, grid, dim3(256), shm, s, T, ids, n_adapters, tab); break;
-    case 2: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 2>, grid, dim3(256), shm, s, T, ids, n_adapters, tab); break;
-    default: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 4>, grid, dim3(256), shm, s, T, ids, n_adapters, tab);
+    case 1: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 1>, grid, dim3(256), shm, s, T, ids, n_adapters, tab, n); break;
+    case 2: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 2>, grid, dim3(256), shm, s, T, ids, n_adapters, tab, n); break;
+    default: launch_kernel(bgmv_expand_grouped_kernel<DT, SLOT, VECY, 4>, grid, dim3(256), shm, s, T, ids, n_adapters, tab, n);
     }
 }
 
@@ -1537,7 +1547,7 @@ int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_
     GExpandTable etab{};
     // template choices shared by all projections: the most general one
     bool vec = true, vecy = true, two = true;
-    int rt = 1, kc_max = 1, ncol_max = 1, ldl_max = 4;
+    int rt = 1, kc_max = 1, ncol_sum = 0, ldl_max = 4;
     for (int p = 0; p < n; ++p) {
         const GroupedProj &g = pr[p];
         // the same split as a single lora_bgmv call of this projection
@@ -1549,13 +1559,13 @@ int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_
         stab.p[p] = GShrink{g.sa.x, g.pool_A, g.pool_rank, g.sa.v, g.sa.ldx, ldw, sl_stride, g.sa.d_in, g.max_rank,
                             sp.slice_len, sp.kc};
         etab.p[p] = GExpand{g.sa.v, g.pool_B, g.pool_rank, g.pool_alpha, g.ea.y, ldw, sl_stride, g.ea.ldy, sp.kc,
-                            g.max_rank, g.ea.d_out, ldl, ncol, g.ea.vec_b ? 1 : 0};
+                            g.max_rank, g.ea.d_out, ldl, ncol, g.ea.vec_b ? 1 : 0, ncol_sum, 0};
         vec = vec && g.sa.vec;
         vecy = vecy && g.ea.vec_y && g.ea.d_out % 16 == 0;
         two = two && sp.nstep == 2;
         rt = rt > rank_tiles(g.max_rank) ? rt : rank_tiles(g.max_rank);
         kc_max = kc_max > sp.kc ? kc_max : sp.kc;
-        ncol_max = ncol_max > ncol ? ncol_max : ncol;
+        ncol_sum += ncol;
         ldl_max = ldl_max > ldl ? ldl_max : ldl;
     }
     const unsigned groups = unsigned(slot ? n_adapters : T);
@@ -1563,10 +1573,10 @@ int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_
                                         stab);
     int st = check_launch("bgmv grouped shrink");
     if (st) return st;
-    const dim3 egrid(groups, ncol_max, n);
+    const dim3 egrid(groups, static_cast<unsigned>(ncol_sum), 1);
     const size_t shm = (size_t(kRows) * ldl_max + 4) * sizeof(float);
     const int upt = units_per_thread(1, ldl_max);
-#define LORA_BGMV_GEXPAND(DT_, SLOT_, VECY_) bgmv_expand_grouped_go<DT_, SLOT_, VECY_>(s, egrid, shm, upt, T, ids, n_adapters, etab)
+#define LORA_BGMV_GEXPAND(DT_, SLOT_, VECY_) bgmv_expand_grouped_go<DT_, SLOT_, VECY_>(s, egrid, shm, upt, T, ids, n_adapters, etab, n)
     if (dtype == LORA_BF16) {
         if (slot) { if (vecy) LORA_BGMV_GEXPAND(LORA_BF16, true, true); else LORA_BGMV_GEXPAND(LORA_BF16, true, false); }
         else { if (vecy) LORA_BGMV_GEXPAND(LORA_BF16, false, true); else LORA_BGMV_GEXPAND(LORA_BF16, false, false); }
