@@ -549,6 +549,7 @@ int lora_sgmv_grouped(void *stream, int dtype, const lora_sgmv_proj *projs, int3
         if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "projection %d: plan has %d blocks", p, h->num_blocks);
         need += grouped_region_bytes(h->num_sorted, q.d_in < 1 ? 1 : q.d_in, h->max_rank);
     }
+    if (need == 0) return LORA_OK; // no projection has an adapted token
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     char *wp = static_cast<char *>(ws);

@@ -364,3 +364,15 @@ def test_grouped_sgmv_host_checks():
     projs[1].x = FX
     projs[1].plan_host = None
     assert g(None, 1, projs, 2, FX, need) != 0           # no plan
+
+
+def test_grouped_sgmv_all_empty_is_noop():
+    """Projections whose plans hold no adapted token: nothing to do, no
+    workspace needed, no GPU call."""
+    L = B.load()
+    empty = HostPlan(0)
+    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
+    projs = (B.LoraSgmvProj * 2)()
+    for p in range(2):
+        projs[p] = B.LoraSgmvProj(None, FX + 0x100000 * (p + 1), empty.ptr, None, 256, 256, 256, 256)
+    assert L.lora_sgmv_grouped(None, 1, projs, 2, None, 0) == 0

@@ -160,3 +160,15 @@ def test_paged_empty_and_no_adapter():
     assert np.array_equal(yp, prob.y_base())
     yp, yd = _paged_vs_dense(prob, 256, "bgmv", zero_base=False, oracle_check=False)
     assert np.array_equal(yp, prob.y_base())
+
+
+@pytest.mark.parametrize("path", ["sgmv", "bgmv"])
+def test_paged_max_rank(path):
+    """Rank 256 (the largest the ABI takes) next to small ranks, 256-byte pages:
+    each A row (1 KB) and each B row (512 B) spans several pages, and the
+    expand takes the general one-16-rank-step-at-a-time body."""
+    rng = np.random.default_rng(31)
+    ids = rng.integers(-1, 3, 120).astype(np.int32)
+    prob = make_problem(name="paged_rank256", dtype="bf16", ids=ids, ranks=[256, 100, 3], alphas=[64.0, 32.0, 8.0],
+                        d_in=512, d_out=520, seed=31, a_std=0.05, b_std=0.05)
+    _paged_vs_dense(prob, 256, path)
