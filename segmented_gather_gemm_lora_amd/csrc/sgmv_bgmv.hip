@@ -545,12 +545,92 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
 }
 
-template <int DT, bool VECY, bool VIND, int UPT, class M = DenseMem>
+// expand_rows_impl for bf16 B with r % 4 == 0 and r <= 16 * NCH: the B
+// fragments of every 16-rank step are loaded at once with the y tile, kept as
+// packed bf16 (two ranks per register, half the registers of widened ones) and
+// widened just before their MFMAs, so a block waits for one round trip
+// instead of one per 16 ranks.  Same multiply order as expand_rows_impl.
+template <bool VECY, bool VIND, int UPT, int NCH, class M>
+__device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+                                                   int nsl, const void *__restrict__ Bv, int r, float scale,
+                                                   void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
+                                                   const int *yrows, int vrow0, int nrows, float *vl, int ldl,
+                                                   const M &mem)
+{
+    constexpr int DT = LORA_BF16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int ncol0 = ncol_wg + 64 * wave;
+    const int yr = m < nrows ? yrows[m] : -1;
+    const int ysafe = yrows[0];
+    VStage<UPT> vst;
+    stage_v_load<true, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    // column of MFMA row m in tile t, and whether it is inside d_out
+    bool cok[4];
+    u32x2 braw[NCH][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int ncol = ncol0 + Cols<DT>::of(m >> 2, 4 * t + (m & 3));
+        cok[t] = ncol < d_out;
+        const int64_t rowoff = int64_t(cok[t] ? ncol : d_out - 1) * r;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j0 = 16 * c + 4 * g;
+            braw[c][t] = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + (j0 < r ? j0 : 0)));
+        }
+    }
+    YTile<DT> yt;
+    y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
+    stage_v_store<true, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
+    __syncthreads();
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = floatx4{};
+    const float *vrow = vl + (m < nrows ? m : 0) * ldl;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int j0 = 16 * c + 4 * g;
+        floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
+        if (m >= nrows || j0 >= ldl) vf = floatx4{};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool ok = cok[t] && j0 < r;
+            const u32x2 q2 = braw[c][t];
+            const float b[4] = {ok ? bf16_to_f32(q2[0] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[0] >> 16) : 0.f,
+                                ok ? bf16_to_f32(q2[1] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[1] >> 16) : 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q], vf[q], acc[t], 0, 0, 0);
+        }
+    }
+    if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
+}
+
+// MAXNCH = 0: one 16-rank step at a time (expand_rows_impl).  MAXNCH = 2 or 4
+// (every rank of the launch <= 16 * MAXNCH): bf16 blocks with r % 4 == 0 take
+// expand_rows_packed with the smallest step count that covers their rank,
+// chosen by one wave-uniform branch before any load.
+template <int DT, bool VECY, bool VIND, int UPT, class M = DenseMem, int MAXNCH = 0>
 __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                             const void *__restrict__ Bv, int r, float scale, void *__restrict__ yv,
                                             int64_t ldy, int d_out, int ncol_wg, bool vec_b, const int *yrows,
                                             int vrow0, int nrows, float *vl, int ldl, const M &mem = M{})
 {
+    if constexpr (DT == LORA_BF16 && MAXNCH > 0) {
+        if (vec_b && (r & 3) == 0) {
+            if (MAXNCH >= 4 && r > 32)
+                expand_rows_packed<VECY, VIND, UPT, (MAXNCH >= 4 ? 4 : 1)>(v, ldv, sl_stride, nsl, Bv, r, scale, yv,
+                                                                           ldy, d_out, ncol_wg, yrows, vrow0, nrows,
+                                                                           vl, ldl, mem);
+            else if (r > 16)
+                expand_rows_packed<VECY, VIND, UPT, 2>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+                                                       yrows, vrow0, nrows, vl, ldl, mem);
+            else
+                expand_rows_packed<VECY, VIND, UPT, 1>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
+                                                       yrows, vrow0, nrows, vl, ldl, mem);
+            return;
+        }
+    }
     if (vec_b && (r & 3) == 0)
         expand_rows_impl<DT, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
                                                         yrows, vrow0, nrows, vl, ldl, mem);
@@ -660,7 +740,7 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restr
                                             mem);
 }
 
-template <int DT, bool VECY, int UPT, class M>
+template <int DT, bool VECY, int UPT, class M, int MAXNCH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                           int nsl, const lora_blk_desc *__restrict__ blks,
                                                           void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
@@ -668,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
 {
     extern __shared__ floatx4 vl4[];
     const lora_blk_desc *d = blks + blockIdx.y;
-    expand_rows<DT, VECY, false, UPT>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
+    expand_rows<DT, VECY, false, UPT, M, MAXNCH>(v, ldv, sl_stride, nsl, reinterpret_cast<const void *>(d->B), d->rank,
                                          d->scale, y, ldy, d_out, blockIdx.x * kExpandCols, vec_b, d->rows, d->p0,
                                          d->n, reinterpret_cast<float *>(vl4), ldl, mem);
 }
@@ -1224,8 +1304,8 @@ bool slot_major(int T, int n_adapters) { return n_adapters <= 2 * T; }
 // float4 units of staged v per thread for RB blocks of 16 rows at pitch ldl
 int units_per_thread(int rb, int ldl) { const int u = (rb * kRows * (ldl / 4) + 255) / 256; return u <= 1 ? 1 : (u <= 2 ? 2 : 4); }
 
-template <int DT, bool VECY, class M>
-void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+template <int DT, bool VECY, class M, int MAXNCH>
+void sgmv_expand_go_n(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
                     const lora_blk_desc *blks, int nblk, int ldl, const M &mem)
 {
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
@@ -1233,16 +1313,33 @@ void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t 
     const dim3 grid(ncol, nblk);
     switch (units_per_thread(1, ldl)) {
     case 1:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 1, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 1, M, MAXNCH>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     case 2:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 2, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 2, M, MAXNCH>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl, mem);
         break;
     default:
-        launch_kernel(sgmv_expand_kernel<DT, VECY, 4, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
+        launch_kernel(sgmv_expand_kernel<DT, VECY, 4, M, MAXNCH>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, blks, a.y,
                       a.ldy, a.d_out, a.vec_b, ldl, mem);
+    }
+}
+
+// The largest rank of the plan (through the LDS pitch) picks how many 16-rank
+// steps of B a bf16 block may hold at once (ranks <= 16 and above 64: one).
+// Paged adapters keep one step at a time: their 64-bit addresses would make
+// the packed body spill at six waves per SIMD (measured slower).
+template <int DT, bool VECY, class M>
+void sgmv_expand_go(hipStream_t s, const ExpandArgs &a, const float *v, int64_t ldv, int64_t sl_stride, int nsl,
+                    const lora_blk_desc *blks, int nblk, int ldl, const M &mem)
+{
+    if constexpr (!std::is_same_v<M, DenseMem>) {
+        sgmv_expand_go_n<DT, VECY, M, 0>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
+    } else {
+        if (ldl > 16 && ldl <= 32) sgmv_expand_go_n<DT, VECY, M, 2>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
+        else if (ldl > 32 && ldl <= 64) sgmv_expand_go_n<DT, VECY, M, 4>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
+        else sgmv_expand_go_n<DT, VECY, M, 0>(s, a, v, ldv, sl_stride, nsl, blks, nblk, ldl, mem);
     }
 }
 
