@@ -726,8 +726,28 @@ __device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int
     const int xr0 = bd->rows[0];
     const int k_begin = c * slice_len;
     const int k_end = min(d_in, k_begin + slice_len);
-    shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, xr0, reinterpret_cast<const void *>(bd->A), d_in, bd->rank,
-                                        k_begin, k_end, out + c * sl_stride, ldo, bd->p0, nullptr, bd->n, red, mem);
+    const int r = bd->rank;
+    const void *A = reinterpret_cast<const void *>(bd->A);
+    float *o = out + c * sl_stride;
+    // A block computes only the rank tiles its own rank needs (the launch's RT
+    // covers the largest rank of the plan): one wave-uniform branch before any
+    // load.  Each tile's sum is formed in the same order whatever RT is.
+    if constexpr (RT >= 2) {
+        if (r <= 16) {
+            shrink_block<DT, VEC, W, NSTEP, 1>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr,
+                                               bd->n, red, mem);
+            return;
+        }
+    }
+    if constexpr (RT >= 4) {
+        if (r <= 32) {
+            shrink_block<DT, VEC, W, NSTEP, 2>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr,
+                                               bd->n, red, mem);
+            return;
+        }
+    }
+    shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr, bd->n,
+                                        red, mem);
 }
 
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
