@@ -63,6 +63,7 @@ struct AdapterRec {
     size_t off = 0, len = 0; // extent while resident
     int64_t last_use = -1;   // batch index
     int64_t mark = -1;       // prepare call that last listed it (duplicate filter)
+    int64_t evict_mark = -1; // prepare call whose placement chose it as a victim
 };
 
 // One gather-copy launch: entries (source, destination, bytes), each cut
@@ -166,24 +167,23 @@ size_t extent_bytes(const lora_cache *c, int32_t r)
            round_up(size_t(c->d_out) * size_t(r) * size_t(c->es), kAlign);
 }
 
-// First fit; returns false when no free extent is large enough.
-bool take(lora_cache *c, size_t len, size_t *off)
+// First fit in free list `fl`; returns false when no free extent is large enough.
+bool take(std::vector<Extent> &fl, size_t len, size_t *off)
 {
-    for (size_t i = 0; i < c->free_list.size(); ++i) {
-        Extent &e = c->free_list[i];
+    for (size_t i = 0; i < fl.size(); ++i) {
+        Extent &e = fl[i];
         if (e.len < len) continue;
         *off = e.off;
         e.off += len;
         e.len -= len;
-        if (e.len == 0) c->free_list.erase(c->free_list.begin() + long(i));
+        if (e.len == 0) fl.erase(fl.begin() + long(i));
         return true;
     }
     return false;
 }
 
-void give_back(lora_cache *c, size_t off, size_t len)
+void give_back(std::vector<Extent> &fl, size_t off, size_t len)
 {
-    auto &fl = c->free_list;
     auto it = std::lower_bound(fl.begin(), fl.end(), off, [](const Extent &e, size_t o) { return e.off < o; });
     it = fl.insert(it, Extent{off, len});
     // merge with the next, then with the previous extent
@@ -367,6 +367,39 @@ int lora_cache_prepare(lora_cache *c, const int32_t *ids_host, int32_t T, void *
         return fail(LORA_ERR_WORKSPACE, "batch needs %zu B of adapters; the cache holds %zu B (%zu B pinned)", need,
                     c->data_bytes, pinned_other);
 
+    // Placement, on a scratch copy of the free list: every miss gets an
+    // extent, evicting least recently used adapters that are neither pinned
+    // nor in this batch.  Nothing of the cache changes until every miss has
+    // its place, so a batch that cannot be placed leaves the cache as it was.
+    static thread_local std::vector<Extent> fl;
+    static thread_local std::vector<int32_t> victims;
+    static thread_local std::vector<std::pair<int32_t, size_t>> placed;
+    fl = c->free_list;
+    victims.clear();
+    placed.clear();
+    for (int32_t a : used) {
+        const AdapterRec &r = c->ad[size_t(a)];
+        if (r.resident) continue;
+        const size_t len = extent_bytes(c, r.rank);
+        size_t off = 0;
+        while (!take(fl, len, &off)) {
+            int32_t victim = -1;
+            for (int32_t b = 0; b < c->n; ++b) {
+                const AdapterRec &q = c->ad[size_t(b)];
+                if (!q.resident || q.pinned || q.mark == m || q.evict_mark == m) continue;
+                if (victim < 0 || q.last_use < c->ad[size_t(victim)].last_use) victim = b;
+            }
+            if (victim < 0)
+                return fail(LORA_ERR_WORKSPACE, "no evictable adapter leaves %zu contiguous bytes for adapter %d "
+                            "(fragmented cache)", len, a);
+            AdapterRec &q = c->ad[size_t(victim)];
+            q.evict_mark = m;
+            give_back(fl, q.off, q.len);
+            victims.push_back(victim);
+        }
+        placed.emplace_back(a, off);
+    }
+
     hipStream_t cs = static_cast<hipStream_t>(compute_stream), xs = static_cast<hipStream_t>(copy_stream);
     hipEvent_t start_ev = nullptr;
     if (!c->dry) {
@@ -374,47 +407,32 @@ int lora_cache_prepare(lora_cache *c, const int32_t *ids_host, int32_t T, void *
         hipError_t e = hipEventRecord(start_ev, cs);
         if (e != hipSuccess) return hip_fail(e, "lora_cache_prepare: event record");
     }
-    // placement: every miss gets an extent, evicting least recently used
-    // adapters that are neither pinned nor in this batch
+    // commit the placement
+    c->free_list.swap(fl);
+    int64_t wait_batch = -1; // newest batch whose reads an overwrite must follow
+    for (int32_t v : victims) {
+        AdapterRec &q = c->ad[size_t(v)];
+        q.resident = false;
+        wait_batch = std::max(wait_batch, q.last_use);
+        c->st.resident_bytes -= int64_t(q.len);
+        --c->st.resident;
+        ++c->st.evictions;
+        set_table(c, v);
+    }
     static thread_local std::vector<int32_t> loads;
     loads.clear();
-    int64_t wait_batch = -1; // newest batch whose reads an overwrite must follow
-    for (int32_t a : used) {
-        AdapterRec &r = c->ad[size_t(a)];
-        if (r.resident) {
-            ++c->st.hits;
-            continue;
-        }
-        const size_t len = extent_bytes(c, r.rank);
-        size_t off = 0;
-        while (!take(c, len, &off)) {
-            int32_t victim = -1;
-            for (int32_t b = 0; b < c->n; ++b) {
-                const AdapterRec &q = c->ad[size_t(b)];
-                if (!q.resident || q.pinned || q.mark == m) continue;
-                if (victim < 0 || q.last_use < c->ad[size_t(victim)].last_use) victim = b;
-            }
-            if (victim < 0)
-                return fail(LORA_ERR_WORKSPACE, "no evictable adapter leaves %zu contiguous bytes for adapter %d "
-                            "(fragmented cache)", len, a);
-            AdapterRec &q = c->ad[size_t(victim)];
-            q.resident = false;
-            give_back(c, q.off, q.len);
-            wait_batch = std::max(wait_batch, q.last_use);
-            c->st.resident_bytes -= int64_t(q.len);
-            --c->st.resident;
-            ++c->st.evictions;
-            set_table(c, victim);
-        }
+    for (const auto &pa : placed) {
+        AdapterRec &r = c->ad[size_t(pa.first)];
         r.resident = true;
-        r.off = off;
-        r.len = len;
-        c->st.resident_bytes += int64_t(len);
+        r.off = pa.second;
+        r.len = extent_bytes(c, r.rank);
+        c->st.resident_bytes += int64_t(r.len);
         ++c->st.resident;
         ++c->st.misses;
-        set_table(c, a);
-        loads.push_back(a);
+        set_table(c, pa.first);
+        loads.push_back(pa.first);
     }
+    c->st.hits += int64_t(used.size() - placed.size());
     for (int32_t a : used) c->ad[size_t(a)].last_use = k;
     ++c->st.batches;
     c->batch = k + 1;
@@ -495,7 +513,18 @@ int lora_cache_prepare(lora_cache *c, const int32_t *ids_host, int32_t T, void *
     }
     if (e == hipSuccess) e = hipEventRecord(c->copy_ev, xs);
     if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->copy_ev, 0);
-    if (e != hipSuccess) return hip_fail(e, "lora_cache_prepare: copies");
+    if (e != hipSuccess) {
+        // the batch's copies were not all enqueued: its misses are not resident
+        for (int32_t a : loads) {
+            AdapterRec &r = c->ad[size_t(a)];
+            r.resident = false;
+            give_back(c->free_list, r.off, r.len);
+            c->st.resident_bytes -= int64_t(r.len);
+            --c->st.resident;
+            set_table(c, a);
+        }
+        return hip_fail(e, "lora_cache_prepare: copies");
+    }
     return LORA_OK;
 }
 

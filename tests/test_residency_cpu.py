@@ -120,6 +120,31 @@ def test_fragmentation_error():
     assert e.value.status == -6 and "fragmented" in B.load().lora_last_error().decode()
 
 
+def test_failed_prepare_leaves_cache_unchanged():
+    """A batch that cannot be placed changes nothing: adapters placed before
+    the failure are not left resident without their copy, victims are not
+    evicted, and the next batch that needs them counts a miss and copies."""
+    c, _ = cache_for(6, ranks={9: 32})
+    for a in (0, 2, 4):
+        c.pin(a)
+    c.prepare([0, 1, 2, 3, 4, 5])
+    before_tables = [t.copy() for t in c.host_tables()]
+    before = c.stats()
+    with pytest.raises(B.LoraError) as e:
+        c.prepare([6, 9])  # 6 fits after evicting 1; 9 (rank 32) finds no two adjacent free units
+    assert e.value.status == -6 and "fragmented" in B.load().lora_last_error().decode()
+    assert resident(c) == {0, 1, 2, 3, 4, 5}
+    after = c.stats()
+    assert after == before
+    for t0, t1 in zip(before_tables, c.host_tables()):
+        assert np.array_equal(t0, t1)
+    c.prepare([6])
+    st = c.stats()
+    assert st["misses"] == before["misses"] + 1 and st["hits"] == before["hits"]
+    assert st["bytes_copied"] == before["bytes_copied"] + 2 * 16 * (D_IN + D_OUT)
+    assert 6 in resident(c) and st["evictions"] == before["evictions"] + 1
+
+
 def test_rejections():
     lib = B.load()
     h = ctypes.c_void_p()
