@@ -520,8 +520,11 @@ int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t l
  * from the same batch (its perm also lists the tokens without an adapter).
  * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_FUSED, T, d_in, d_out, max_rank)
  * (the shrink's slice partials plus T * 2 * round16(max_rank) bf16).
+ * x (T rows at pitch ldx) and W0 must each span less than 4 GiB: the GEMM
+ * addresses their rows with 32-bit byte offsets.
  * Errors: as lora_sgmv_shrink; LORA_ERR_DTYPE for fp32; LORA_ERR_ALIGN for
- * the alignment rules above; LORA_ERR_WORKSPACE. */
+ * the alignment rules above; LORA_ERR_ARG for x or W0 of 4 GiB or more;
+ * LORA_ERR_WORKSPACE. */
 int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
                       const void *W0, int32_t d_out,
                       const void *plan_host, const void *plan_dev,
@@ -566,6 +569,32 @@ int lora_profile_launches(void **start_events, void **stop_events, int32_t count
 /* Number of events of the current lora_profile_launches request that kernels
  * have taken so far on this thread (how many kernels a call enqueued). */
 int32_t lora_profile_launches_used(void);
+
+/* ------------------------------------------------------------ measurement aids
+ * Reference kernels a benchmark times beside the adapter kernels, so that each
+ * adapter kernel can be read against what the chip achieves for the same
+ * bytes without the method's dependent loads.  None of them is part of the
+ * adapter path.
+ *
+ * lora_probe_empty: an empty kernel of `workgroups` workgroups of 256 threads
+ * (the per-launch floor).  Errors: LORA_ERR_ARG, LORA_ERR_HIP. */
+int lora_probe_empty(void *stream, int32_t workgroups);
+
+/* One kernel that reads read_bytes of src and reads, modifies and writes back
+ * rmw_bytes of rmw (the data written equals the data read), with 16-byte
+ * accesses, over at most max_workgroups workgroups split in proportion to the
+ * bytes each part moves.  Both counts are multiples of 16, the buffers are
+ * 16-byte aligned device memory; sink is a device buffer of max_workgroups
+ * uint32 that the kernel may write.  Errors: LORA_ERR_ARG, LORA_ERR_ALIGN,
+ * LORA_ERR_HIP. */
+int lora_probe_stream(void *stream, const void *src, int64_t read_bytes, void *rmw, int64_t rmw_bytes, void *sink,
+                      int32_t max_workgroups);
+
+/* One lane of one workgroup follows `steps` dependent loads i = next[i] from
+ * i = 0 (the cost of a global-memory round trip), then writes i to sink[0].
+ * Every next[i] reached must index inside the caller's array.
+ * Errors: LORA_ERR_ARG, LORA_ERR_HIP. */
+int lora_probe_chase(void *stream, const uint32_t *next, int32_t steps, uint32_t *sink);
 
 /* Library version string. */
 const char *lora_version(void);

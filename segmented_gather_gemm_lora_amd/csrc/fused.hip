@@ -19,8 +19,8 @@
 //     operand is the split scale_s * v (zero on rows outside the segment); the
 //     two halves share the B_s fragment, so one 32-deep step covers 16 ranks.
 //
-// GEMM tiling: a workgroup computes 192 output columns x 256 plan rows with 4
-// waves (2 x 2, 96 columns x 128 rows each, accumulators in AGPRs).  k
+// GEMM tiling: a workgroup computes 192 output columns x 256 plan rows with 8
+// waves (2 per SIMD; 2 x 4 waves of 96 columns x 64 rows each).  k
 // advances 32 per stage through a ring of kStages LDS stages filled by
 // direct global-to-LDS loads (global_load_lds_dwordx4), issued kStages - 1
 // stages ahead so that several HBM round trips are in flight per CU while
@@ -127,7 +127,6 @@ struct FusedArgs {
     uint16_t *y;
     int64_t ldy;
     int tiles_m, tiles_n;
-    int off32; // byte offsets into x and W0 fit in 32 bits
 };
 
 // v of sorted row p, scaled and split, for the fused GEMM: for every 16 ranks
@@ -343,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // are read.
     auto issue = [&](int kt) {
         const uint32_t base = lds0 + uint32_t((kt % kStages) * kStageBytes);
-        if (a.off32 && (kt + 1) * kBK <= a.d_in) {
+        if ((kt + 1) * kBK <= a.d_in) {
             const char *wb = reinterpret_cast<const char *>(a.W0) + int64_t(kt) * kRowBytes;
             const char *xb = reinterpret_cast<const char *>(a.x) + int64_t(kt) * kRowBytes;
 #pragma unroll
@@ -501,6 +500,12 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
 {
     const int T = p.h->num_tokens;
     if (T == 0) return LORA_OK;
+    // The direct loads address x and W0 rows with 32-bit byte offsets from the
+    // matrix start: both must span less than 4 GiB (every row start plus one
+    // row).  Checked before anything is launched.
+    const bool off32 = (int64_t(T) * sa.ldx + sa.d_in) * 2 < (int64_t(1) << 32) &&
+                       (int64_t(ea.d_out) * sa.d_in + sa.d_in) * 2 < (int64_t(1) << 32);
+    if (!off32) return fail(LORA_ERR_ARG, "fused layer: x or W0 spans 4 GiB or more");
     float *v = static_cast<float *>(ws);
     int64_t ldw = 0, sl_stride = 0;
     int nsl = 0;
@@ -536,9 +541,6 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     a.ldh = ldh;
     a.y = static_cast<uint16_t *>(ea.y);
     a.ldy = ea.ldy;
-    // 32-bit byte offsets hold every x row and W0 row start plus one row
-    a.off32 = (int64_t(T) * sa.ldx + sa.d_in) * 2 < (int64_t(1) << 32) &&
-              (int64_t(ea.d_out) * sa.d_in + sa.d_in) * 2 < (int64_t(1) << 32);
     a.tiles_m = (T + kBM - 1) / kBM;
     a.tiles_n = (ea.d_out + kBN - 1) / kBN;
     const int64_t nwg = int64_t(a.tiles_m) * a.tiles_n;
