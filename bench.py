@@ -2,8 +2,7 @@
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
     python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|prefill_qkv|decode_cache]
-                    [--steps K] [--warmup W]
-                    [--paged PAGE_BYTES]
+                    [--steps K] [--warmup W] [--paged PAGE_BYTES] [--eager] [--probe]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
 every token (BGMV for the decode workload, SGMV from a prebuilt plan for the
@@ -12,11 +11,20 @@ instances (own adapters, activations and outputs) whose total footprint is at
 least twice the 256 MB last-level cache, so timed calls read HBM as real
 layers do.  Inputs are resident in HBM before timing starts.
 
+Set-up (untimed): one step on every rotated instance (first touch of all
+their memory), then W warmup steps; before each timed region a 512 MB read
+evicts the last-level cache.  The timed region is exactly K steps, recorded
+once as a HIP graph (the library calls issue kernels only, so they capture)
+and replayed: what a serving loop does with a launch-bound step.  The same K
+steps issued one call at a time are timed beside it (eager_ms_per_step).
+
 Prints one JSON line: tokens/s per layer, ms per step, achieved algorithmic
-HBM GB/s and its fraction of the 8 TB/s peak, a roofline object for the
-dominant kernel (its average duration from HIP events that the library
-attaches to the kernel's own start and end, on the launch stream) and the
-fp64 CPU oracle timed on the host cores (cpu_baseline).
+HBM GB/s and its fraction of the 8 TB/s peak, the per-kernel durations and
+their sum, the probes (empty launch, same-footprint stream, one dependent
+round trip), a roofline object for the dominant kernel (its average duration
+from HIP events that the library attaches to the kernel's own start and end,
+on the launch stream) and the fp64 CPU oracle timed on the host cores
+(cpu_baseline).  --probe prints the probe figures alone.
 """
 
 from __future__ import annotations
@@ -74,9 +82,10 @@ def algorithmic_flops(prob, part="total"):
 
 
 class Instance:
-    """One layer's worth of device-resident inputs."""
+    """One layer's worth of device-resident inputs, and its step as a
+    prepared library call on the bench stream."""
 
-    def __init__(self, prob, kind, page_bytes=0, seed=0):
+    def __init__(self, prob, kind, stream, page_bytes=0, seed=0):
         import torch
 
         from segmented_gather_gemm_lora_amd import binding as B
@@ -103,71 +112,59 @@ class Instance:
             self.W0 = B.to_device(prob.W0, self.dt)
             nbytes = B.lora_workspace_bytes(B.LORA_OP_FUSED, prob.T, prob.d_in, prob.d_out, prob.max_rank)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-
-    def fused(self):
-        from segmented_gather_gemm_lora_amd import binding as B
-
-        B.fused_linear(self.x, self.W0, self.plan, self.y, self.ws, self.dt)
-
-    def step(self):
-        """One adapted layer: a single library call (two kernels for SGMV/BGMV)."""
-        from segmented_gather_gemm_lora_amd import binding as B
-
-        if self.kind == "fused":
-            self.fused()
-        elif self.kind == "bgmv":
-            if self.page_bytes:
-                B.bgmv_paged(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
-            else:
-                B.bgmv(self.x, self.ids, self.pool, self.y, self.ws, self.dt)
-        elif self.page_bytes:
-            B.sgmv_paged(self.x, self.plan, self.pool, self.y, self.ws, self.dt)
+        # the step: one library call with its arguments converted once
+        if kind == "fused":
+            self.step = B.fused_prepared(self.x, self.W0, self.plan, self.y, self.ws, self.dt, stream)
+        elif kind == "bgmv":
+            mk = B.bgmv_paged_prepared if page_bytes else B.bgmv_prepared
+            self.step = mk(self.x, self.ids, self.pool, self.y, self.ws, self.dt, stream)
+        elif page_bytes:
+            self.step = B.sgmv_paged_prepared(self.x, self.plan, self.pool, self.y, self.ws, self.dt, stream)
         else:
-            B.sgmv(self.x, self.plan, self.y, self.ws, self.dt)
+            self.step = B.sgmv_prepared(self.x, self.plan, self.y, self.ws, self.dt, stream)
 
 
 class GroupedInstance:
     """One layer's q, k, v inputs (shared x, own adapters and outputs) for the
     grouped call (BGMV for decode, SGMV from per-projection plans for
-    prefill), and the same work as separate single calls."""
+    prefill), and the same work as separate single calls, as prepared calls
+    on the bench stream."""
 
-    def __init__(self, probs, sgmv=False):
+    def __init__(self, probs, stream, sgmv=False):
         import torch
 
         from segmented_gather_gemm_lora_amd import binding as B
 
         self.sgmv = sgmv
         self.probs = probs
+        dt = probs[0].dtype
         self.pools = [B.DevicePool.from_problem(p) for p in probs]
-        self.x = B.to_device(probs[0].x, probs[0].dtype)
-        self.ys = [B.to_device(p.y_base(), p.dtype) for p in probs]
+        self.x = B.to_device(probs[0].x, dt)
+        self.ys = [B.to_device(p.y_base(), dt) for p in probs]
         self.ids = torch.from_numpy(np.ascontiguousarray(probs[0].ids, dtype=np.int32)).cuda()
         self.xs = [self.x] * len(probs)
-        self.projs = B.proj_array(self.xs, self.pools, self.ys)
-        self.ws = B.bgmv_grouped_workspace(probs[0].T, self.projs)
-        self.ws1 = [B.workspace(B.LORA_OP_BGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
         if sgmv:
             self.plans = [B.Plan(p.T).build(p.ids, pool).upload() for p, pool in zip(probs, self.pools)]
-            self.sprojs = B.sgmv_proj_array(self.xs, self.plans, self.ys)
-            self.ws = B.sgmv_grouped_workspace(self.sprojs)
+            self.projs = B.sgmv_proj_array(self.xs, self.plans, self.ys)
+            self.ws = B.sgmv_grouped_workspace(self.projs)
             self.ws1 = [B.workspace(B.LORA_OP_SGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
-
-    def step(self):
-        from segmented_gather_gemm_lora_amd import binding as B
-
-        if self.sgmv:
-            B.sgmv_grouped(self.xs, self.plans, self.ys, self.ws, self.probs[0].dtype, projs=self.sprojs)
+            self.step = B.sgmv_grouped_prepared(self.projs, self.ws, dt, stream, keep=(self.xs, self.plans, self.ys))
+            sep = [B.sgmv_prepared(self.x, self.plans[p], self.ys[p], self.ws1[p], dt, stream)
+                   for p in range(len(probs))]
         else:
-            B.bgmv_grouped(self.xs, self.ids, self.pools, self.ys, self.ws, self.probs[0].dtype, projs=self.projs)
+            self.projs = B.proj_array(self.xs, self.pools, self.ys)
+            self.ws = B.bgmv_grouped_workspace(probs[0].T, self.projs)
+            self.ws1 = [B.workspace(B.LORA_OP_BGMV, p.T, p.d_in, p.d_out, p.max_rank) for p in probs]
+            self.step = B.bgmv_grouped_prepared(probs[0].T, self.ids, probs[0].n_adapters, self.projs, self.ws, dt,
+                                                stream, keep=(self.xs, self.pools, self.ys))
+            sep = [B.bgmv_prepared(self.x, self.ids, self.pools[p], self.ys[p], self.ws1[p], dt, stream)
+                   for p in range(len(probs))]
 
-    def step_separate(self):
-        from segmented_gather_gemm_lora_amd import binding as B
+        def step_separate():
+            for f in sep:
+                f()
 
-        for p, prob in enumerate(self.probs):
-            if self.sgmv:
-                B.sgmv(self.x, self.plans[p], self.ys[p], self.ws1[p], prob.dtype)
-            else:
-                B.bgmv(self.x, self.ids, self.pools[p], self.ys[p], self.ws1[p], prob.dtype)
+        self.step_separate = step_separate
 
 
 def grouped_bytes(probs):
@@ -180,30 +177,187 @@ def grouped_bytes(probs):
     return {"shrink": shrink, "expand": expand, "total": shrink + expand}
 
 
-def time_steps(step, K, stream):
+FLUSH_BYTES = 512 << 20
+
+
+class Timing:
+    """Set-up, cache flush and the timed region of a benchmark on one stream.
+
+    steps[i % L] is the step of rotated instance i.  Set-up runs every
+    instance once and then W warmup steps; each timed region is preceded by a
+    read of FLUSH_BYTES (twice the last-level cache) so that it starts with
+    nothing of the workload cached."""
+
+    def __init__(self, stream):
+        import torch
+
+        from segmented_gather_gemm_lora_amd import binding as B
+
+        self.torch = torch
+        self.B = B
+        self.stream = stream
+        self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+
+    def flush(self):
+        B = self.B
+        B._check(B.load().lora_probe_stream(self.stream.cuda_stream, self.flush_buf.data_ptr(), FLUSH_BYTES, None, 0,
+                                            self.sink.data_ptr(), 2048), "lora_probe_stream")
+
+    def setup(self, steps, W):
+        for f in steps:
+            f()
+        for i in range(W):
+            steps[i % len(steps)]()
+        self.torch.cuda.synchronize()
+
+    def eager(self, steps, K, first=0):
+        """ms per step of K steps issued one call at a time, and the host wall time."""
+        torch = self.torch
+        L = len(steps)
+        self.flush()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(self.stream)
+        for i in range(K):
+            steps[(first + i) % L]()
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / K, time.perf_counter() - t0
+
+    def graph(self, steps, K, first=0):
+        """ms per step of the same K steps recorded once as a graph and replayed
+        (one untimed replay first), and the host wall time of the timed replay."""
+        torch = self.torch
+        L = len(steps)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(K):
+                steps[(first + i) % L]()
+        with torch.cuda.stream(self.stream):
+            g.replay()
+        torch.cuda.synchronize()
+        self.flush()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(self.stream)
+        with torch.cuda.stream(self.stream):
+            g.replay()
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del g
+        return ev0.elapsed_time(ev1) / K, wall
+
+    def per_kernel(self, steps, names, K2):
+        """Average duration of each kernel of a step (HIP events on the kernels
+        themselves), over K2 eager steps; {name: us}."""
+        torch, B = self.torch, self.B
+        L = len(steps)
+        nk = len(names)
+        self.flush()
+        torch.cuda.synchronize()
+        timer = B.KernelTimer(K2 * nk)
+        for i in range(K2):
+            timer.arm(i * nk, nk)
+            steps[i % L]()
+        timer.disarm()
+        torch.cuda.synchronize()
+        out = {n: float(np.mean([timer.elapsed_us(i * nk + j) for i in range(K2)])) for j, n in enumerate(names)}
+        timer.close()
+        return out
+
+
+def launches_per_step(step):
+    """Kernels one library call enqueues (a probe step with events armed)."""
     import torch
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    probe = B.KernelTimer(8)
+    probe.arm(0, 8)
+    step()
+    used = B.KernelTimer.used()
+    probe.disarm()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / K, time.perf_counter() - t0
+    probe.close()
+    return used
 
 
-def grouped_main(args, sgmv=False):
+def run_probes(stream, read_bytes, rmw_bytes, L, reps=200):
+    """The achievable-at-this-size references: an empty launch back to back,
+    one kernel moving the step's bytes (read_bytes read, rmw_bytes read and
+    written back) rotating over L regions like the steps, and one dependent
+    global-memory round trip.  Returns {name: us}."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    lib = B.load()
+    sh = stream.cuda_stream
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    rd = (int(read_bytes) + 15) // 16 * 16
+    rm = (int(rmw_bytes) + 15) // 16 * 16
+    region = (rd + rm + 255) // 256 * 256
+    buf = torch.zeros(region * L, dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, n):
+        for i in range(min(n, 20)):
+            fn(i)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            fn(i)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+    out = {}
+    out["empty_launch_us"] = timed(lambda i: B._check(lib.lora_probe_empty(sh, 1), "probe"), reps)
+    out["empty_launch_1024wg_us"] = timed(lambda i: B._check(lib.lora_probe_empty(sh, 1024), "probe"), reps)
+    base = buf.data_ptr()
+
+    def stream_probe(i):
+        r0 = base + (i % L) * region
+        B._check(lib.lora_probe_stream(sh, r0, rd, r0 + rd, rm, sink.data_ptr(), 2048), "probe")
+
+    n_stream = max(2 * L, min(reps, 20 * L))
+    out["stream_same_bytes_us"] = timed(stream_probe, n_stream)
+    out["stream_same_bytes_GBps"] = (rd + 2 * rm) / (out["stream_same_bytes_us"] * 1e-6) / 1e9
+    # dependent loads 4 KB apart; run j follows its own chain (offset 64 j
+    # bytes inside each 4 KB), so after the flush every load of a run misses
+    # every cache
+    stride, steps, runs = 1024, 2000, 5
+    nxt = torch.zeros(stride * (steps + 1), dtype=torch.int32, device="cuda")
+    k = torch.arange(steps, device="cuda", dtype=torch.int64)
+    for j in range(runs):
+        nxt[k * stride + 16 * j] = ((k + 1) * stride).to(torch.int32)
+    assert int(nxt.max()) + 16 * runs < nxt.numel()
+    Timing(stream).flush()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for j in range(runs):
+        B._check(lib.lora_probe_chase(sh, nxt.data_ptr() + 64 * j, steps, sink.data_ptr()), "probe")
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    out["dependent_load_us"] = ev[0].elapsed_time(ev[1]) * 1e3 / (runs * steps)
+    del buf, nxt
+    return {k: round(v, 3) for k, v in out.items()}
+
+
+def grouped_main(args, stream, sgmv=False):
     """The q, k, v projections in one grouped shrink + expand (two launches),
     with the same work as three single calls timed beside it: decode (BGMV)
     or, with sgmv, prefill (SGMV from per-projection plans)."""
     import torch
 
-    import oracle
     from lora_workloads import PREFILL_QKV_NAME, QKV_NAME, make_decode_qkv, make_prefill_qkv
-    from segmented_gather_gemm_lora_amd import binding as B
 
     make = make_prefill_qkv if sgmv else make_decode_qkv
     name = PREFILL_QKV_NAME if sgmv else QKV_NAME
@@ -213,38 +367,24 @@ def grouped_main(args, sgmv=False):
     L = args.rotation or rotation_count(ab0["total"])
     print(f"[bench] {name}: T={probs0[0].T} d_in={probs0[0].d_in} d_out={[p.d_out for p in probs0]} "
           f"rotation={L} bytes/layer={ab0['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
-    insts = [GroupedInstance(probs0, sgmv)] + [GroupedInstance(make(seed=2000 + i), sgmv) for i in range(1, L)]
+    insts = [GroupedInstance(probs0, stream, sgmv)] + [GroupedInstance(make(seed=2000 + i), stream, sgmv)
+                                                       for i in range(1, L)]
+    torch.cuda.synchronize()
     ab_all = [grouped_bytes(g.probs) for g in insts]
     bytes_step = float(np.mean([a["total"] for a in ab_all]))
     T = probs0[0].T
     K = args.steps if args.steps is not None else 20 * L
     W = args.warmup if args.warmup is not None else 10 * L
-    stream = torch.cuda.current_stream()
-    for i in range(W):
-        insts[i % L].step()
-        insts[i % L].step_separate()
-    torch.cuda.synchronize()
-    ms_step, t_wall = time_steps(lambda i: insts[i % L].step(), K, stream)
-    ms_sep, _ = time_steps(lambda i: insts[i % L].step_separate(), K, stream)
-
-    probe = B.KernelTimer(8)
-    probe.arm(0, 8)
-    insts[0].step()
-    used = B.KernelTimer.used()
-    probe.disarm()
-    torch.cuda.synchronize()
-    probe.close()
+    steps = [g.step for g in insts]
+    sep = [g.step_separate for g in insts]
+    tm = Timing(stream)
+    tm.setup(steps, W)
+    tm.setup(sep, 0)
+    ms_step, t_wall, mode, eager_ms, graph_note = timed_steps(tm, steps, K, W, args.eager)
+    ms_sep, _, _, _, _ = timed_steps(tm, sep, K, W, args.eager)
     names = ["shrink", "expand"]
-    assert used == 2, used
-    K2 = max(L, min(K, 20 * L))
-    timer = B.KernelTimer(K2 * 2)
-    for i in range(K2):
-        timer.arm(i * 2, 2)
-        insts[i % L].step()
-    timer.disarm()
-    torch.cuda.synchronize()
-    per_kernel_us = {n: float(np.mean([timer.elapsed_us(i * 2 + j) for i in range(K2)])) for j, n in enumerate(names)}
-    timer.close()
+    assert launches_per_step(steps[0]) == 2
+    per_kernel_us = tm.per_kernel(steps, names, max(L, min(K, 20 * L)))
     dominant = max(names, key=lambda n: per_kernel_us[n])
     dom_bytes = float(np.mean([a[dominant] for a in ab_all]))
     dom_us = per_kernel_us[dominant]
@@ -257,8 +397,10 @@ def grouped_main(args, sgmv=False):
 
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle
+
         oracle.build(force=False)
-        cores = max(1, min(16, os.cpu_count() or 1))
+        cores = max(1, min(HOST_CORES, os.cpu_count() or 1))
         reps, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < args.cpu_budget:
             for p in probs0:
@@ -266,7 +408,8 @@ def grouped_main(args, sgmv=False):
             reps += 1
         el = time.perf_counter() - t0
         cpu = {"value": reps * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"{reps} full q/k/v layers of {T} tokens ({el:.1f} s, fp64, OpenMP over tokens)"}
+               "sample": f"{reps} full q/k/v layers of {T} tokens ({el:.1f} s, fp64, OpenMP over tokens)",
+               "host_nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
     gbps = bytes_step / (ms_step * 1e-3) / 1e9
     out = {
@@ -286,20 +429,25 @@ def grouped_main(args, sgmv=False):
                    "ranks": [16], "pool_adapters": probs0[0].n_adapters,
                    "distinct_adapters": int(len(probs0[0].distinct_adapters())), "rotated_instances": L,
                    "path": f"{kind}_grouped"},
+        "timed_mode": mode,
+        "eager_ms_per_step": round(eager_ms, 6),
         "achieved_GBps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": round(bytes_step),
         "per_kernel_us": {n: round(v, 3) for n, v in per_kernel_us.items()},
+        "kernel_sum_us": round(sum(per_kernel_us.values()), 3),
         "separate_calls_ms_per_step": round(ms_sep, 6),
         "separate_calls": f"the same q, k, v work as three lora_{kind} calls (six launches)",
         "wall_s_timed": round(t_wall, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph_note:
+        out["graph_note"] = graph_note
     print(json.dumps(out))
 
 
-def cache_main(args):
+def cache_main(args, stream):
     """Decode batches whose adapters come through the residency cache: 256
     adapters of rank 16 in pinned host memory, Zipf(1.1) popularity, a cache
     of 64 adapters; a step is lora_cache_prepare (copies of missing adapters on
@@ -330,16 +478,16 @@ def cache_main(args):
     ids_dev = [torch.from_numpy(b).cuda() for b in batches]
     ws = B.workspace(B.LORA_OP_BGMV, T, prob.d_in, prob.d_out, 16)
     copy_stream = torch.cuda.Stream()
-    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
     cache.prepare(batches[0], copy_stream, stream)
     cpool = cache.pool()  # device tables keep their addresses; host mirrors are not needed for BGMV
 
     def step_cache(i):
         cache.prepare(batches[i % nb], copy_stream, stream)
-        B.bgmv(x, ids_dev[i % nb], cpool, y, ws, "bf16", max_rank=16)
+        B.bgmv(x, ids_dev[i % nb], cpool, y, ws, "bf16", max_rank=16, stream=stream)
 
     def step_resident(i):
-        B.bgmv(x, ids_dev[i % nb], resident, y, ws, "bf16", max_rank=16)
+        B.bgmv(x, ids_dev[i % nb], resident, y, ws, "bf16", max_rank=16, stream=stream)
 
     K = args.steps if args.steps is not None else 4 * nb
     W = args.warmup if args.warmup is not None else nb
@@ -347,10 +495,11 @@ def cache_main(args):
         step_cache(i)
         step_resident(i)
     torch.cuda.synchronize()
+    tm = Timing(stream)
     s0 = cache.stats()
-    ms_cache, t_wall = time_steps(step_cache, K, stream)
+    ms_cache, t_wall = tm.eager([lambda i=i: step_cache(i) for i in range(nb)], K)
     s1 = cache.stats()
-    ms_res, _ = time_steps(step_resident, K, stream)
+    ms_res, _ = tm.eager([lambda i=i: step_resident(i) for i in range(nb)], K)
     misses = (s1["misses"] - s0["misses"]) / K
     h2d = (s1["bytes_copied"] - s0["bytes_copied"]) / K
     hits = (s1["hits"] - s0["hits"]) / K
@@ -412,22 +561,23 @@ def dataclasses_replace_ids(prob, ids):
     return dataclasses.replace(prob, ids=np.asarray(ids, dtype=np.int32))
 
 
-def base_gemm_reference_us(inst, reps=50):
+def base_gemm_reference_us(inst, stream, reps=50):
     """Average time of torch.matmul for the base product alone (same shape,
     bf16): the vendor-library figure the fused kernel is compared with."""
     import torch
 
     wt = inst.W0.t()
     out = torch.empty((inst.prob.T, inst.prob.d_out), dtype=inst.W0.dtype, device="cuda")
-    for _ in range(5):
-        torch.matmul(inst.x, wt, out=out)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        torch.matmul(inst.x, wt, out=out)
-    e1.record()
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            torch.matmul(inst.x, wt, out=out)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(inst.x, wt, out=out)
+        e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
 
@@ -437,52 +587,67 @@ def rotation_count(bytes_per_instance):
     return 1 << (n - 1).bit_length()
 
 
-def cpu_baseline(prob, budget_s):
-    """The fp64 oracle as it stands, on the host cores, over whole layers of the
-    same workload (repeated, or a prefix of the tokens when one layer would
-    exceed the budget)."""
+HOST_CORES = 16  # the host CPU share of one GPU on the benchmark machine
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _prefix(prob, n):
     import copy
 
+    sub = copy.copy(prob)
+    sub.T = n
+    sub.ids = prob.ids[:n]
+    sub.x = prob.x[:n]
+    sub.y_in = None if prob.y_in is None else prob.y_in[:n]
+    return sub
+
+
+def cpu_baseline(prob, budget_s):
+    """The fp64 oracle as it stands, on the host cores (the machine's CPU share
+    of one GPU, HOST_CORES threads, or fewer if fewer exist) and on one thread:
+    median of 3 timed runs each, over whole layers of the same workload, or
+    over a prefix of its tokens when a layer would not fit the budget."""
     import oracle
 
-    cores = max(1, min(16, os.cpu_count() or 1))
+    fused = bool(prob.meta.get("fused"))
+    cores = max(1, min(HOST_CORES, os.cpu_count() or 1))
     oracle.build(force=False)
-    sample = prob
-    # one-token timing probe to size the sample
-    probe = copy.copy(prob)
     n_probe = min(prob.T, 8)
-    probe.T = n_probe
-    probe.ids = prob.ids[:n_probe]
-    probe.x = prob.x[:n_probe]
-    probe.y_in = None if prob.y_in is None else prob.y_in[:n_probe]
     t0 = time.perf_counter()
-    oracle.lora_forward(probe, nthreads=1, fused=bool(prob.meta.get("fused")))
-    per_tok_1core = (time.perf_counter() - t0) / n_probe
-    est_layer = per_tok_1core * prob.T / cores
-    if est_layer > budget_s:
-        n = max(cores, int(budget_s / per_tok_1core * cores))
-        n = min(n, prob.T)
-        sample = copy.copy(prob)
-        sample.T = n
-        sample.ids = prob.ids[:n]
-        sample.x = prob.x[:n]
-        sample.y_in = None if prob.y_in is None else prob.y_in[:n]
-        desc = f"first {n} of {prob.T} tokens of one layer"
-    else:
-        desc = None
-    reps, tokens = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.lora_forward(sample, nthreads=cores, fused=bool(prob.meta.get("fused")))
-        reps += 1
-        tokens += sample.T
-        el = time.perf_counter() - t0
-        if el >= budget_s or desc is not None:
-            break
-    if desc is None:
-        desc = f"{reps} full layers of {prob.T} tokens"
-    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{desc} ({el:.1f} s, fp64, OpenMP over tokens)"}
+    oracle.lora_forward(_prefix(prob, n_probe), nthreads=1, fused=fused)
+    per_tok_1 = (time.perf_counter() - t0) / n_probe
+
+    def med_rate(sample, nthreads, reps=3):
+        rates = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            oracle.lora_forward(sample, nthreads=nthreads, fused=fused)
+            rates.append(sample.T / (time.perf_counter() - t))
+        return float(np.median(rates)), rates
+
+    # multi-thread leg: about 2/3 of the budget over 3 runs; whole layers when they fit
+    per_run = budget_s * 2 / 9
+    n_mt = prob.T if per_tok_1 * prob.T / cores <= per_run else max(cores, min(prob.T, int(per_run / per_tok_1 * cores)))
+    mt, _ = med_rate(_prefix(prob, n_mt), cores)
+    # one-thread leg: the rest of the budget
+    per_run1 = budget_s / 9
+    n_1 = max(1, min(prob.T, int(per_run1 / per_tok_1)))
+    one, _ = med_rate(_prefix(prob, n_1), 1)
+    what = "full layers" if n_mt == prob.T else f"the first {n_mt} of {prob.T} tokens of one layer"
+    return {"value": mt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}, median of 3 runs, fp64, OpenMP over tokens",
+            "value_1thread": one, "sample_1thread": f"the first {n_1} tokens, median of 3 runs",
+            "host_nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -534,6 +699,20 @@ def copy_calibration(reps=8):
     print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "reps": reps}))
 
 
+def timed_steps(tm, steps, K, W, eager_only):
+    """The contract's timed region: K steps after set-up.  Returns
+    (ms_per_step, wall_s, mode, eager_ms, graph_note)."""
+    L = len(steps)
+    eager_ms, eager_wall = tm.eager(steps, K, first=W % L)
+    if eager_only:
+        return eager_ms, eager_wall, "eager", eager_ms, None
+    try:
+        graph_ms, graph_wall = tm.graph(steps, K, first=W % L)
+    except Exception as e:  # capture unsupported: report the eager figure
+        return eager_ms, eager_wall, "eager", eager_ms, f"graph capture failed: {e}"
+    return graph_ms, graph_wall, "graph", eager_ms, None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,8 +720,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", choices=sorted(CONFIG_OF) + ["decode_qkv", "prefill_qkv", "decode_cache"],
                     default="decode")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time the K steps issued one call at a time (no graph)")
+    ap.add_argument("--probe", action="store_true", help="only run the probes for the workload's bytes and exit")
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_BYTES",
                     help="adapters in a page pool of this page size (decode, prefill, hetero); 0 = dense pool")
@@ -567,11 +749,12 @@ def main():
         copy_calibration()
         return
     B.load()
+    stream = torch.cuda.Stream()  # default priority
     if args.config in ("decode_qkv", "prefill_qkv"):
-        grouped_main(args, sgmv=args.config == "prefill_qkv")
+        grouped_main(args, stream, sgmv=args.config == "prefill_qkv")
         return
     if args.config == "decode_cache":
-        cache_main(args)
+        cache_main(args, stream)
         return
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
@@ -585,48 +768,26 @@ def main():
     L = args.rotation or rotation_count(ab["total"])
     print(f"[bench] {CONFIG_NAMES[k]}: T={prob0.T} d_in={prob0.d_in} d_out={prob0.d_out} rotation={L} "
           f"bytes/layer={ab['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
-    insts = [Instance(prob0, kind, page, seed=0)]
+    if args.probe:
+        rmw = 0 if kind == "fused" else int(np.count_nonzero(prob0.ids >= 0)) * prob0.d_out * prob0.esize
+        print(json.dumps({"workload": CONFIG_NAMES[k], "probes": run_probes(stream, ab["total"] - 2 * rmw, rmw, L)}))
+        return
+    insts = [Instance(prob0, kind, stream, page, seed=0)]
     for i in range(1, L):
-        insts.append(Instance(make_config(k, seed=1000 * k + i), kind, page, seed=i))
+        insts.append(Instance(make_config(k, seed=1000 * k + i), kind, stream, page, seed=i))
+    torch.cuda.synchronize()
     # every instance has its own distinct-adapter count; average the algorithmic bytes
     ab_all = [algorithmic_bytes(inst.prob) for inst in insts]
     bytes_step = float(np.mean([a["total"] for a in ab_all]))
     flops_step = float(np.mean([algorithmic_flops(inst.prob) for inst in insts]))
     T = prob0.T
+    steps = [inst.step for inst in insts]
 
     K = args.steps if args.steps is not None else 20 * L
     W = args.warmup if args.warmup is not None else 10 * L
-    stream = torch.cuda.current_stream()
-    for i in range(W):
-        insts[i % L].step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        insts[i % L].step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / K
-    tokens_per_s = T / (ms_step * 1e-3)
-    gbps = bytes_step / (ms_step * 1e-3) / 1e9
-
-    # ---- per-kernel durations: HIP events attached to each kernel's own start
-    # and end (hipExtLaunchKernelGGL), on the stream the kernels run on
-    # kernels per step: a probe step counts the launches of one library call
-    probe = B.KernelTimer(8)
-    probe.arm(0, 8)
-    insts[0].step()
-    used = B.KernelTimer.used()
-    probe.disarm()
-    torch.cuda.synchronize()
-    probe.close()
+    tm = Timing(stream)
+    tm.setup(steps, W)
+    used = launches_per_step(steps[0])
     if kind == "fused":
         names = ["shrink", "prep", "fused"]
     elif used == 1:
@@ -634,23 +795,22 @@ def main():
     else:
         names = ["shrink", "expand"]
     assert len(names) == used, (names, used)
-    nk = len(names)
+
+    # ---- timed region: exactly K steps
+    ms_step, t_wall, mode, eager_ms, graph_note = timed_steps(tm, steps, K, W, args.eager)
+    tokens_per_s = T / (ms_step * 1e-3)
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+
+    # ---- per-kernel durations: HIP events attached to each kernel's own start
+    # and end (hipExtLaunchKernelGGL), on the stream the kernels run on
     K2 = max(L, min(K, 20 * L))
-    timer = B.KernelTimer(K2 * nk)
-    for i in range(K2):
-        timer.arm(i * nk, nk)
-        insts[i % L].step()
-    timer.disarm()
-    torch.cuda.synchronize()
-    per_kernel_us = {n: float(np.mean([timer.elapsed_us(i * nk + j) for i in range(K2)])) for j, n in enumerate(names)}
-    timer.close()
+    per_kernel_us = tm.per_kernel(steps, names, K2)
     dominant = max(names, key=lambda n: per_kernel_us[n])
-    dom_bytes = float(np.mean([a.get(dominant, a["total"]) for a in ab_all]))
     dom_us = per_kernel_us[dominant]
-    if kind not in ("fused",) and names == [kind]:
+    if kind != "fused" and names == [kind]:
         for a in ab_all:
             a[kind] = a["total"]
-        dom_bytes = float(np.mean([a[kind] for a in ab_all]))
+    dom_bytes = float(np.mean([a.get(dominant, a["total"]) for a in ab_all]))
     if kind == "fused":
         dominant = "fused"
         dom_us = per_kernel_us["fused"]
@@ -670,13 +830,20 @@ def main():
     roof["algorithmic_bytes_per_launch"] = round(dom_bytes)
     roof["avg_launch_us"] = round(dom_us, 3)
 
+    extra = {}
     if kind == "fused":
         roof["algorithmic_flops_per_launch"] = round(fused_flops)
-        base_us = base_gemm_reference_us(insts[0])
+        base_us = base_gemm_reference_us(insts[0], stream)
         extra = {"base_gemm_reference_us": round(base_us, 3), "base_gemm_reference": "torch.matmul (hipBLASLt), "
                  "x [T, d_in] @ W0^T, bf16, same shape, no adapters; a library reference, not part of the path"}
-    else:
-        extra = {}
+    probes = None
+    if not args.no_probes:
+        # y of the adapted tokens is read and written back; everything else is read
+        rmw = int(np.mean([np.count_nonzero(inst.prob.ids >= 0) * inst.prob.d_out * inst.prob.esize
+                           for inst in insts])) if kind != "fused" else 0
+        del insts, steps
+        torch.cuda.empty_cache()
+        probes = run_probes(stream, bytes_step - 2 * rmw, rmw, L)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -699,15 +866,21 @@ def main():
                    "ranks": sorted(set(int(r) for r in prob0.ranks)), "pool_adapters": prob0.n_adapters,
                    "distinct_adapters": int(len(prob0.distinct_adapters())), "rotated_instances": L,
                    "path": kind + ("_paged" if page else ""), **({"page_bytes": page} if page else {})},
+        "timed_mode": mode,
+        "eager_ms_per_step": round(eager_ms, 6),
         "achieved_GBps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": round(bytes_step),
         "algorithmic_flops_per_step": round(flops_step),
         "per_kernel_us": {n: round(v, 3) for n, v in per_kernel_us.items()},
+        "kernel_sum_us": round(sum(per_kernel_us.values()), 3),
+        "probes": probes,
         "wall_s_timed": round(t_wall, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph_note:
+        out["graph_note"] = graph_note
     out.update(extra)
     print(json.dumps(out))
 

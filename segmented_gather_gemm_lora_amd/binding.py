@@ -46,7 +46,8 @@ EXPORTS = [
     "lora_cache_register", "lora_cache_pin", "lora_cache_prepare", "lora_cache_view_get", "lora_cache_stats_get",
     "lora_pages_needed", "lora_page_alloc_create", "lora_page_alloc_destroy", "lora_page_alloc_take",
     "lora_page_alloc_give", "lora_page_alloc_free_count", "lora_pages_write", "lora_sgmv_paged", "lora_bgmv_paged",
-    "lora_sgmv_grouped", "lora_sgmv_grouped_workspace_bytes",
+    "lora_sgmv_grouped", "lora_sgmv_grouped_workspace_bytes", "lora_probe_empty", "lora_probe_stream",
+    "lora_probe_chase",
 ]
 LORA_CACHE_DRY = 1
 MAX_PROJ = 8
@@ -102,6 +103,9 @@ _SIGS = {
     "lora_pages_needed": (_i64, [_i64, _i64]),
     "lora_sgmv_grouped": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _sz]),
     "lora_sgmv_grouped_workspace_bytes": (_sz, [_vp, _i32]),
+    "lora_probe_empty": (ctypes.c_int, [_vp, _i32]),
+    "lora_probe_stream": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i32]),
+    "lora_probe_chase": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
     "lora_page_alloc_create": (ctypes.c_int, [_i32, _vp]),
     "lora_page_alloc_destroy": (None, [_vp]),
     "lora_page_alloc_take": (ctypes.c_int, [_vp, _i32, _vp]),
@@ -409,6 +413,30 @@ class KernelTimer:
         for i in range(self.n):
             KernelTimer._hip.hipEventDestroy(self.start[i])
             KernelTimer._hip.hipEventDestroy(self.stop[i])
+
+
+class Prepared:
+    """One library call with its arguments converted to C types once, for
+    loops that repeat the same call (benchmarks, serving loops): calling the
+    object makes the C call and raises on a non-zero status.  `keep` holds
+    the tensors whose addresses the arguments carry."""
+
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, name: str, args, keep=()):
+        res, types = _SIGS[name]
+        if len(types) != len(args):
+            raise TypeError(f"{name} takes {len(types)} arguments, got {len(args)}")
+        self._fn = getattr(load(), name)
+        self._args = tuple(None if a is None else (a if isinstance(a, ctypes._SimpleCData) else t(a))
+                           for t, a in zip(types, args))
+        self._name = name
+        self._keep = tuple(keep)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            _check(st, self._name)
 
 
 # ------------------------------------------------------------------ torch-facing helpers
@@ -723,6 +751,58 @@ def bgmv(x, ids_dev, pool: DevicePool, y, ws, dtype: str, max_rank: Optional[int
                      _ptr(pool.alpha_dev), pool.n_adapters, max_rank or pool.max_rank, _ptr(y), y.stride(0),
                      y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_bgmv")
+
+
+def sgmv_prepared(x, plan: Plan, y, ws, dtype: str, stream) -> Prepared:
+    """lora_sgmv with its arguments converted once (see Prepared)."""
+    return Prepared("lora_sgmv", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
+                                  plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1],
+                                  _ptr(ws), ws.numel() * ws.element_size()), keep=(x, plan, y, ws))
+
+
+def bgmv_prepared(x, ids_dev, pool, y, ws, dtype: str, stream, max_rank: Optional[int] = None) -> Prepared:
+    """lora_bgmv with its arguments converted once (see Prepared)."""
+    return Prepared("lora_bgmv", (_stream_handle(stream), DTYPES[dtype], x.shape[0], _ptr(x), x.stride(0),
+                                  x.shape[1], _ptr(ids_dev), _ptr(pool.addr_A_dev), _ptr(pool.addr_B_dev),
+                                  _ptr(pool.rank_dev), _ptr(pool.alpha_dev), pool.n_adapters,
+                                  max_rank or pool.max_rank, _ptr(y), y.stride(0), y.shape[1], _ptr(ws),
+                                  ws.numel() * ws.element_size()), keep=(x, ids_dev, pool, y, ws))
+
+
+def sgmv_paged_prepared(x, plan: Plan, pool: "PagedPool", y, ws, dtype: str, stream) -> Prepared:
+    return Prepared("lora_sgmv_paged", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
+                                        plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(pool.pages),
+                                        pool.page_bytes, _ptr(y), y.stride(0), y.shape[1], _ptr(ws),
+                                        ws.numel() * ws.element_size()), keep=(x, plan, pool, y, ws))
+
+
+def bgmv_paged_prepared(x, ids_dev, pool: "PagedPool", y, ws, dtype: str, stream,
+                        max_rank: Optional[int] = None) -> Prepared:
+    return Prepared("lora_bgmv_paged", (_stream_handle(stream), DTYPES[dtype], x.shape[0], _ptr(x), x.stride(0),
+                                        x.shape[1], _ptr(ids_dev), _ptr(pool.addr_A_dev), _ptr(pool.addr_B_dev),
+                                        _ptr(pool.rank_dev), _ptr(pool.alpha_dev), pool.n_adapters,
+                                        max_rank or pool.max_rank, _ptr(pool.pages), pool.page_bytes, _ptr(y),
+                                        y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+                    keep=(x, ids_dev, pool, y, ws))
+
+
+def fused_prepared(x, W0, plan: Plan, y, ws, dtype: str, stream) -> Prepared:
+    return Prepared("lora_fused_linear", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
+                                          _ptr(W0), W0.shape[0], plan.host.data_ptr(), plan.dev.data_ptr(),
+                                          _ptr(y), y.stride(0), _ptr(ws), ws.numel() * ws.element_size()),
+                    keep=(x, W0, plan, y, ws))
+
+
+def sgmv_grouped_prepared(projs, ws, dtype: str, stream, keep=()) -> Prepared:
+    return Prepared("lora_sgmv_grouped", (_stream_handle(stream), DTYPES[dtype], ctypes.cast(projs, _vp).value,
+                                          len(projs), _ptr(ws), ws.numel() * ws.element_size()),
+                    keep=(projs, ws, *keep))
+
+
+def bgmv_grouped_prepared(T: int, ids_dev, n_adapters: int, projs, ws, dtype: str, stream, keep=()) -> Prepared:
+    return Prepared("lora_bgmv_grouped", (_stream_handle(stream), DTYPES[dtype], T, _ptr(ids_dev), n_adapters,
+                                          ctypes.cast(projs, _vp).value, len(projs), _ptr(ws),
+                                          ws.numel() * ws.element_size()), keep=(ids_dev, projs, ws, *keep))
 
 
 def sgmv_paged(x, plan: Plan, pool: PagedPool, y, ws, dtype: str, stream=None):
