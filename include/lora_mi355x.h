@@ -253,16 +253,46 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
                      int32_t n_adapters, int32_t max_rank,
                      void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
-/* Decode correction in one call: bgmv_shrink then bgmv_expand, with the
+/* Decode correction in one call: the shrink then the expand, with the
  * intermediate kept in the workspace as fp32 partial sums over slices of d_in
  * (fixed summation order).  Needs ws_bytes >=
  * lora_workspace_bytes(LORA_OP_BGMV, T, d_in, d_out, max_rank).
+ *
+ * One kernel launch when x and y rows are 16-byte aligned, d_out % 16 == 0
+ * and max_rank <= 64 (else two): its first workgroups compute the partial
+ * sums of (adapter, d_in slice) and publish each by writing the launch's key
+ * (from its dispatch id and queue) into a flag in the workspace; the others
+ * load their B tile and y rows, wait until their adapter's flags hold the key,
+ * then expand (the per-launch cost the pages put on naive per-adapter
+ * launches, "Multi-LoRA Serving in Production ...", section "Mathematical
+ * Formulation and the Batching Challenge", paid once).  Both forms compute
+ * the same sums in the same order, so their outputs are equal.
+ *
+ * Workspace: the flags need no preparation and no reset (a value left by an
+ * earlier launch never equals a new launch's key).  Calls that share a
+ * workspace must be ordered on one stream.  The int32 at the start of the
+ * workspace is a status word, sticky: nonzero once a wait of the one-launch
+ * form gave up (see lora_debug_wait_limit; that call's output is incomplete);
+ * lora_workspace_clear resets it.  Allocate the workspace zero-filled (or
+ * clear it) so that the status word starts at zero.
  * Errors: as lora_bgmv_shrink, plus LORA_ERR_WORKSPACE. */
 int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
               const int32_t *ids_dev, const uint64_t *pool_A_dev, const uint64_t *pool_B_dev,
               const int32_t *pool_rank_dev, const float *pool_alpha_dev,
               int32_t n_adapters, int32_t max_rank,
               void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+
+/* Enqueue a kernel that zero-fills ws_bytes of a workspace (16-byte aligned
+ * device memory), which resets lora_bgmv's status word.  A kernel, not a
+ * memset, so that it can be recorded in a graph.
+ * Errors: LORA_ERR_ARG, LORA_ERR_ALIGN, LORA_ERR_HIP. */
+int lora_workspace_clear(void *stream, void *ws, size_t ws_bytes);
+
+/* Diagnostic: polls the one-launch BGMV's wait makes before it gives up, for
+ * the calls this thread makes from now on: 0 = the default (about 4 million
+ * polls, seconds), > 0 = that many, < 0 = give up at once (used to test the
+ * give-up path; the call's output is then incomplete).  Always LORA_OK. */
+int lora_debug_wait_limit(int32_t polls);
 
 /* ------------------------------------------------------------ grouped BGMV
  * Several projections of a layer in one shrink launch and one expand launch,

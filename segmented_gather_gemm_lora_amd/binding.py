@@ -47,7 +47,7 @@ EXPORTS = [
     "lora_pages_needed", "lora_page_alloc_create", "lora_page_alloc_destroy", "lora_page_alloc_take",
     "lora_page_alloc_give", "lora_page_alloc_free_count", "lora_pages_write", "lora_sgmv_paged", "lora_bgmv_paged",
     "lora_sgmv_grouped", "lora_sgmv_grouped_workspace_bytes", "lora_probe_empty", "lora_probe_stream",
-    "lora_probe_chase",
+    "lora_probe_chase", "lora_workspace_clear", "lora_debug_wait_limit",
 ]
 LORA_CACHE_DRY = 1
 MAX_PROJ = 8
@@ -104,6 +104,8 @@ _SIGS = {
     "lora_sgmv_grouped": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _sz]),
     "lora_sgmv_grouped_workspace_bytes": (_sz, [_vp, _i32]),
     "lora_probe_empty": (ctypes.c_int, [_vp, _i32]),
+    "lora_workspace_clear": (ctypes.c_int, [_vp, _vp, _sz]),
+    "lora_debug_wait_limit": (ctypes.c_int, [_i32]),
     "lora_probe_stream": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i32]),
     "lora_probe_chase": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
     "lora_page_alloc_create": (ctypes.c_int, [_i32, _vp]),
@@ -731,10 +733,26 @@ def sgmv_expand(v, plan: Plan, y, dtype: str, stream=None):
 
 
 def workspace(op: int, T: int, d_in: int, d_out: int, max_rank: int, device="cuda"):
-    """A device workspace of the size the library asks for (uint8 tensor)."""
+    """A zero-filled device workspace of the size the library asks for (uint8
+    tensor; lora_bgmv needs its control words zero before the first call)."""
     torch = _torch()
     n = lora_workspace_bytes(op, T, d_in, d_out, max_rank)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def workspace_clear(ws, stream=None):
+    """lora_workspace_clear on a workspace tensor."""
+    _check(load().lora_workspace_clear(_stream_handle(stream), _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_workspace_clear")
+
+
+def workspace_status(ws) -> int:
+    """The status word at the start of a BGMV workspace (synchronises)."""
+    return int(ws[:4].view(_torch().int32).item())
+
+
+def debug_wait_limit(polls: int):
+    _check(load().lora_debug_wait_limit(int(polls)), "lora_debug_wait_limit")
 
 
 def sgmv(x, plan: Plan, y, ws, dtype: str, stream=None):

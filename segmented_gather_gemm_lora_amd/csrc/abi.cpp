@@ -119,6 +119,21 @@ static int make_expand_args(int dtype, const float *v, int64_t ldv, int32_t max_
     return LORA_OK;
 }
 
+int bgmv_run(hipStream_t s, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in, const int32_t *ids_dev,
+             const uint64_t *pool_A_dev, const uint64_t *pool_B_dev, const int32_t *pool_rank_dev,
+             const float *pool_alpha_dev, int32_t n_adapters, int32_t max_rank, void *y, int64_t ldy, int32_t d_out,
+             float *part, int32_t *ctl, bool one_launch)
+{
+    const int64_t ldw = (max_rank + 3) / 4 * 4;
+    ShrinkArgs sa{};
+    int st = make_shrink_args(dtype, x, ldx, d_in, part, ldw, max_rank, &sa);
+    if (st) return st;
+    ExpandArgs ea{};
+    if ((st = make_expand_args(dtype, part, ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_bgmv(s, sa, ea, T, ids_dev, pool_A_dev, pool_B_dev, pool_rank_dev, pool_alpha_dev, n_adapters,
+                       max_rank, part, ctl, one_launch);
+}
+
 } // namespace lora
 
 using namespace lora;
@@ -189,8 +204,9 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_BGMV_EXPAND: return 0;
     case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     case LORA_OP_SGMV:
-    case LORA_OP_BGMV:
         return combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
+    case LORA_OP_BGMV:
+        return bgmv_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     default: return size_t(-1);
     }
 }
@@ -426,16 +442,29 @@ int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, in
     if (T == 0) return LORA_OK;
     if (!ids_dev || !pool_A_dev || !pool_B_dev || !pool_rank_dev || !pool_alpha_dev)
         return fail(LORA_ERR_ARG, "device tables are NULL");
-    const size_t need = combined_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
+    const size_t need = bgmv_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
-    const int64_t ldw = (max_rank + 3) / 4 * 4;
-    ShrinkArgs sa{};
-    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, max_rank, &sa))) return st;
-    ExpandArgs ea{};
-    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
-    return launch_bgmv(static_cast<hipStream_t>(stream), sa, ea, T, ids_dev, pool_A_dev, pool_B_dev, pool_rank_dev,
-                       pool_alpha_dev, n_adapters, max_rank, ws);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + bgmv_ctl_bytes(T));
+    return bgmv_run(static_cast<hipStream_t>(stream), dtype, T, x, ldx, d_in, ids_dev, pool_A_dev, pool_B_dev,
+                    pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, y, ldy, d_out, part,
+                    static_cast<int32_t *>(ws), true);
+}
+
+int lora_workspace_clear(void *stream, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    if (ws_bytes == 0) return LORA_OK;
+    if (!ws) return fail(LORA_ERR_ARG, "ws is NULL");
+    if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    return launch_workspace_clear(static_cast<hipStream_t>(stream), ws, ws_bytes);
+}
+
+int lora_debug_wait_limit(int32_t polls)
+{
+    clear_error();
+    wait_limit() = polls;
+    return LORA_OK;
 }
 
 // pages / page_bytes of the paged calls; *shift = log2(page_bytes).
@@ -495,16 +524,17 @@ int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t l
     if (T == 0) return LORA_OK;
     if (!ids_dev || !pool_A_dev || !pool_B_dev || !pool_rank_dev || !pool_alpha_dev)
         return fail(LORA_ERR_ARG, "device tables are NULL");
-    const size_t need = combined_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
+    const size_t need = bgmv_workspace_bytes(T, d_in < 1 ? 1 : d_in, max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t ldw = (max_rank + 3) / 4 * 4;
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + bgmv_ctl_bytes(T));
     ShrinkArgs sa{};
-    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, max_rank, &sa))) return st;
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, part, ldw, max_rank, &sa))) return st;
     ExpandArgs ea{};
-    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
+    if ((st = make_expand_args(dtype, part, ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
     return launch_bgmv_paged(static_cast<hipStream_t>(stream), sa, ea, T, ids_dev, pool_A_dev, pool_B_dev,
-                             pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, ws, pages, shift);
+                             pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, part, pages, shift);
 }
 
 size_t lora_sgmv_grouped_workspace_bytes(const lora_sgmv_proj *projs, int32_t n_proj)

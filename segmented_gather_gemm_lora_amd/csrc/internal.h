@@ -52,9 +52,28 @@ int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int3
                        const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                        int32_t n_adapters, int32_t max_rank);
 int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws);
+// The combined BGMV: one launch (shrink and expand workgroups in one grid,
+// handing over through the status word and flags at `ctl`) when one_launch
+// and the shapes allow it, else the shrink and expand kernels.  ws: the slice
+// partials.
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
-                int32_t n_adapters, int32_t max_rank, void *ws);
+                int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl, bool one_launch);
+// A BGMV workspace: control words (status, a flag per group and slice;
+// 256-byte multiple), then the slice partials.
+size_t bgmv_ctl_bytes(int32_t T);
+size_t bgmv_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank);
+// Argument checks of x, y and the partials, then launch_bgmv.  part: the slice
+// partials; ctl: control words of the one-launch form (nullptr: two kernels).
+int bgmv_run(hipStream_t s, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in, const int32_t *ids_dev,
+             const uint64_t *pool_A_dev, const uint64_t *pool_B_dev, const int32_t *pool_rank_dev,
+             const float *pool_alpha_dev, int32_t n_adapters, int32_t max_rank, void *y, int64_t ldy, int32_t d_out,
+             float *part, int32_t *ctl, bool one_launch);
+// Zero `bytes` of device memory with a kernel (no memset node in a graph).
+int launch_workspace_clear(hipStream_t s, void *ws, size_t bytes);
+// Polls of the one-launch BGMV's wait before it gives up (per thread; 0 = the
+// default, < 0 = give up at once).
+int &wait_limit();
 // The combined SGMV / BGMV calls over paged adapter storage: the adapter
 // table entries (plan descriptors, pool_A / pool_B) are int32 page tables of
 // frames in `pages`, pages of 2^page_shift bytes.

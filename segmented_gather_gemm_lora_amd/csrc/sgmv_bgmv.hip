@@ -46,6 +46,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = LORA_PLAN_ROW_BLOCK; // rows per block (MFMA M)
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 constexpr int kExpandCols = 256;          // output columns per expand workgroup (4 waves x 64)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -192,7 +195,15 @@ __device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, cons
 // Results of the W waves are added in wave order through LDS (`red`, W*RT*1 KB).
 // Output row of block row mm: orows[mm] if orows (LDS) is given, else orow0 + mm.
 // ----------------------------------------------------------------------------
-template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem>
+// Stores of a result another workgroup reads in the same launch: device-scope
+// (write-through) stores, so that the reader's device-scope loads see them.
+template <bool SCOPED> __device__ __forceinline__ void put_result(float *p, float v)
+{
+    if constexpr (SCOPED) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem, bool SCOPED = false>
 __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xr, int xr0,
                                              const void *__restrict__ Av, int d_in, int r, int k_begin, int k_end,
                                              float *__restrict__ out, int64_t ldo, int orow0, const int *orows, int n,
@@ -249,7 +260,7 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int mm = 4 * g + q, j = 16 * (rt0 + i) + m;
-                    if (mm < n && j < r) out[int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j] = acc[i][q];
+                    if (mm < n && j < r) put_result<SCOPED>(out + int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, acc[i][q]);
                 }
         } else {
 #pragma unroll
@@ -263,7 +274,7 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
                 for (int w = 0; w < W; ++w) sum += red[((w * RT + i) * 64 + l2) * 4 + q];
                 const int mm = 4 * (l2 >> 4) + q, j = 16 * (rt0 + i) + (l2 & 15);
-                if (mm < n && j < r) out[int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j] = sum;
+                if (mm < n && j < r) put_result<SCOPED>(out + int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, sum);
             }
             __syncthreads();
         }
@@ -445,7 +456,13 @@ template <int UPT> struct VStage {
     int off[UPT];
 };
 
-template <bool BV, bool VIND, int UPT>
+// A float written by another workgroup of the same launch (device-scope load).
+__device__ __forceinline__ float get_result(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool BV, bool VIND, int UPT, bool SCOPED = false>
 __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                              const int *yrows, int vrow0, int nrows, int r, int ldl, VStage<UPT> &st)
 {
@@ -466,7 +483,10 @@ __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_
 #pragma unroll
         for (int sl = 0; sl < kMaxSlices; ++sl) {
             const float *ps = p + (sl < nsl ? sl : 0) * sl_stride;
-            if constexpr (BV) {
+            if constexpr (SCOPED) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.w[k][sl][e] = get_result(ps + (BV || j + e < r ? e : 0));
+            } else if constexpr (BV) {
                 st.w[k][sl] = *reinterpret_cast<const floatx4 *>(ps);
             } else {
 #pragma unroll
@@ -503,12 +523,21 @@ __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare
     (void)q4;
 }
 
-template <int DT, bool VECY, bool BV, bool VIND, int UPT, class M>
+// A hook an expand body runs after it has issued its B and y loads and before
+// it loads v: the one-launch BGMV waits there for the shrink results of its
+// group.  Returns false when the workgroup must not use v (the wait gave up);
+// the body then stores nothing.  NoPre keeps the plain order (v first).
+struct NoPre {
+    static constexpr bool kWaits = false;
+    __device__ __forceinline__ bool operator()() const { return true; }
+};
+
+template <int DT, bool VECY, bool BV, bool VIND, int UPT, class M, class Pre = NoPre>
 __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                  const void *__restrict__ Bv, int r, float scale,
                                                  void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
                                                  const int *yrows, int vrow0, int nrows, float *vl, int ldl,
-                                                 const M &mem)
+                                                 const M &mem, const Pre &pre = Pre{})
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -518,13 +547,18 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     const int yr = m < nrows ? yrows[m] : -1;
     const int ysafe = yrows[0];
     // 2. v slices, 3. B fragments of the first 16 ranks, 4. the y tile; then the
-    // v slices are added into LDS while B and y are still in flight
+    // v slices are added into LDS while B and y are still in flight (with a
+    // waiting hook: B and y first, then the hook, then v)
     VStage<UPT> vst;
-    stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    if constexpr (!Pre::kWaits) stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[4][4];
     load_bfrag<DT, BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, bf);
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
+    if constexpr (Pre::kWaits) {
+        if (!pre()) return;
+        stage_v_load<BV, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    }
     stage_v_store<BV, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
     __syncthreads();
 
@@ -550,12 +584,12 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
 // packed bf16 (two ranks per register, half the registers of widened ones) and
 // widened just before their MFMAs, so a block waits for one round trip
 // instead of one per 16 ranks.  Same multiply order as expand_rows_impl.
-template <bool VECY, bool VIND, int UPT, int NCH, class M>
+template <bool VECY, bool VIND, int UPT, int NCH, class M, class Pre = NoPre>
 __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                    int nsl, const void *__restrict__ Bv, int r, float scale,
                                                    void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
                                                    const int *yrows, int vrow0, int nrows, float *vl, int ldl,
-                                                   const M &mem)
+                                                   const M &mem, const Pre &pre = Pre{})
 {
     constexpr int DT = LORA_BF16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -564,7 +598,7 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
     const int yr = m < nrows ? yrows[m] : -1;
     const int ysafe = yrows[0];
     VStage<UPT> vst;
-    stage_v_load<true, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    if constexpr (!Pre::kWaits) stage_v_load<true, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     // column of MFMA row m in tile t, and whether it is inside d_out
     bool cok[4];
     u32x2 braw[NCH][4];
@@ -581,6 +615,10 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
     }
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
+    if constexpr (Pre::kWaits) {
+        if (!pre()) return;
+        stage_v_load<true, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    }
     stage_v_store<true, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
     __syncthreads();
 
@@ -610,33 +648,34 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
 // (every rank of the launch <= 16 * MAXNCH): bf16 blocks with r % 4 == 0 take
 // expand_rows_packed with the smallest step count that covers their rank,
 // chosen by one wave-uniform branch before any load.
-template <int DT, bool VECY, bool VIND, int UPT, class M = DenseMem, int MAXNCH = 0>
+template <int DT, bool VECY, bool VIND, int UPT, class M = DenseMem, int MAXNCH = 0, class Pre = NoPre>
 __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                             const void *__restrict__ Bv, int r, float scale, void *__restrict__ yv,
                                             int64_t ldy, int d_out, int ncol_wg, bool vec_b, const int *yrows,
-                                            int vrow0, int nrows, float *vl, int ldl, const M &mem = M{})
+                                            int vrow0, int nrows, float *vl, int ldl, const M &mem = M{},
+                                            const Pre &pre = Pre{})
 {
     if constexpr (DT == LORA_BF16 && MAXNCH > 0) {
         if (vec_b && (r & 3) == 0) {
             if (MAXNCH >= 4 && r > 32)
-                expand_rows_packed<VECY, VIND, UPT, (MAXNCH >= 4 ? 4 : 1)>(v, ldv, sl_stride, nsl, Bv, r, scale, yv,
-                                                                           ldy, d_out, ncol_wg, yrows, vrow0, nrows,
-                                                                           vl, ldl, mem);
+                expand_rows_packed<VECY, VIND, UPT, (MAXNCH >= 4 ? 4 : 1), M, Pre>(
+                    v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg, yrows, vrow0, nrows, vl, ldl, mem,
+                    pre);
             else if (r > 16)
-                expand_rows_packed<VECY, VIND, UPT, 2>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                       yrows, vrow0, nrows, vl, ldl, mem);
+                expand_rows_packed<VECY, VIND, UPT, 2, M, Pre>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out,
+                                                               ncol_wg, yrows, vrow0, nrows, vl, ldl, mem, pre);
             else
-                expand_rows_packed<VECY, VIND, UPT, 1>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                       yrows, vrow0, nrows, vl, ldl, mem);
+                expand_rows_packed<VECY, VIND, UPT, 1, M, Pre>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out,
+                                                               ncol_wg, yrows, vrow0, nrows, vl, ldl, mem, pre);
             return;
         }
     }
     if (vec_b && (r & 3) == 0)
-        expand_rows_impl<DT, VECY, true, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                        yrows, vrow0, nrows, vl, ldl, mem);
+        expand_rows_impl<DT, VECY, true, VIND, UPT, M, Pre>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out,
+                                                            ncol_wg, yrows, vrow0, nrows, vl, ldl, mem, pre);
     else
-        expand_rows_impl<DT, VECY, false, VIND, UPT>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out, ncol_wg,
-                                                         yrows, vrow0, nrows, vl, ldl, mem);
+        expand_rows_impl<DT, VECY, false, VIND, UPT, M, Pre>(v, ldv, sl_stride, nsl, Bv, r, scale, yv, ldy, d_out,
+                                                             ncol_wg, yrows, vrow0, nrows, vl, ldl, mem, pre);
 }
 
 // Expand of one plan chunk (up to 64 rows of one segment) over this
@@ -919,35 +958,37 @@ __device__ bool bgmv_group(const int32_t *__restrict__ ids, int T, int t, int a,
 // (blockIdx.x = adapter; its tokens are all tokens with that id), else one per
 // token (blockIdx.x = t; it serves its adapter's tokens when it is the first
 // of them).  The adapter tables are read in parallel with the ids scan.
-template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M = DenseMem>
-__device__ __forceinline__ void bgmv_shrink_body(const void *__restrict__ x, int64_t ldx, int d_in, int T,
+// Group gx (an adapter when SLOT, else a leader token), d_in slice c.  Returns
+// true when the group has tokens and this workgroup wrote their partial sums.
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M = DenseMem, bool SCOPED = false>
+__device__ __forceinline__ bool bgmv_shrink_body(const void *__restrict__ x, int64_t ldx, int d_in, int T,
                                                  const int32_t *__restrict__ ids, const uint64_t *__restrict__ pool_A,
                                                  const int32_t *__restrict__ pool_rank, int n_adapters, int max_rank,
                                                  int slice_len, float *__restrict__ out, int64_t ldo,
-                                                 int64_t sl_stride, const M &mem = M{})
+                                                 int64_t sl_stride, int gx, int c, const M &mem = M{})
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     __shared__ Group grp;
     __shared__ int cnt[16];
-    const int c = blockIdx.y;
     const int id0 = int(threadIdx.x) < T ? ids[threadIdx.x] : -2; // first chunk of the ids scan
-    const int t = SLOT ? 0 : int(blockIdx.x);
-    const int a = SLOT ? int(blockIdx.x) : ids[t];
-    if (a < 0 || a >= n_adapters) return;
+    const int t = SLOT ? 0 : gx;
+    const int a = SLOT ? gx : ids[t];
+    if (a < 0 || a >= n_adapters) return false;
     const int r = pool_rank[a];
     const void *A = reinterpret_cast<const void *>(pool_A[a]);
-    if (r < 1 || r > max_rank) return;
+    if (r < 1 || r > max_rank) return false;
     const int k_begin = c * slice_len;
     const int k_end = min(d_in, k_begin + slice_len);
     for (int pass = 0;; ++pass) {
-        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return;
+        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return false;
         const int n = grp.n, total = grp.total;
-        if (n == 0) return;
+        if (n == 0) return false;
         const int xr = grp.rows[threadIdx.x & 15];
-        shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end, out + c * sl_stride,
-                                            ldo, 0, grp.rows, n, red, mem);
+        shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end,
+                                                       out + c * sl_stride, ldo, 0, grp.rows, n, red, mem);
         if (kRows * (pass + 1) >= total) break;
     }
+    return true;
 }
 
 template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M>
@@ -959,40 +1000,53 @@ __global__ __launch_bounds__(W * 64) void bgmv_shrink_kernel(const void *__restr
                                                              int64_t ldo, int64_t sl_stride, const M mem)
 {
     bgmv_shrink_body<DT, VEC, W, NSTEP, RT, SLOT>(x, ldx, d_in, T, ids, pool_A, pool_rank, n_adapters, max_rank,
-                                                  slice_len, out, ldo, sl_stride, mem);
+                                                  slice_len, out, ldo, sl_stride, int(blockIdx.x), int(blockIdx.y),
+                                                  mem);
 }
 
-template <int DT, bool SLOT, bool VECY, int UPT, class M = DenseMem>
-__device__ __forceinline__ void bgmv_expand_body(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+// Group gx's tokens over the column tile from ncol_wg.  The first pass runs
+// `pre` between its B / y loads and its v loads (NoPre: none).  Returns true
+// when the group has tokens and this workgroup went through all of its passes
+// (with a waiting hook: and the wait did not give up).
+template <int DT, bool SLOT, bool VECY, int UPT, class M = DenseMem, class Pre = NoPre>
+__device__ __forceinline__ bool bgmv_expand_body(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                  int T, const int32_t *__restrict__ ids,
                                                  const uint64_t *__restrict__ pool_B,
                                                  const int32_t *__restrict__ pool_rank,
                                                  const float *__restrict__ pool_alpha, int n_adapters, int max_rank,
                                                  void *__restrict__ y, int64_t ldy, int d_out, bool vec_b, int ldl,
-                                                 int ncol_wg, const M &mem = M{})
+                                                 int ncol_wg, int gx, const M &mem = M{}, const Pre &pre = Pre{})
 {
     extern __shared__ floatx4 vl4[];
     __shared__ Group grp;
     __shared__ int cnt[16];
     const int id0 = int(threadIdx.x) < T ? ids[threadIdx.x] : -2;
-    const int t = SLOT ? 0 : int(blockIdx.x);
-    const int a = SLOT ? int(blockIdx.x) : ids[t];
-    if (a < 0 || a >= n_adapters) return;
+    const int t = SLOT ? 0 : gx;
+    const int a = SLOT ? gx : ids[t];
+    if (a < 0 || a >= n_adapters) return false;
     const int r = pool_rank[a];
     const void *B = reinterpret_cast<const void *>(pool_B[a]);
     const float alpha = pool_alpha[a];
-    if (r < 1 || r > max_rank) return;
+    if (r < 1 || r > max_rank) return false;
     const float scale = alpha / float(r);
     for (int pass = 0;; ++pass) {
         // bgmv_group starts with a barrier, so the previous pass is done with grp and vl
-        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return;
+        if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return false;
         const int n = grp.n, total = grp.total;
-        if (n == 0) return;
-        expand_rows<DT, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out,
-                                            ncol_wg, vec_b, grp.rows, -1, n, reinterpret_cast<float *>(vl4), ldl,
-                                            mem);
+        if (n == 0) return false;
+        if (pass == 0) {
+            expand_rows<DT, VECY, true, UPT, M, 0, Pre>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncol_wg,
+                                                        vec_b, grp.rows, -1, n, reinterpret_cast<float *>(vl4), ldl,
+                                                        mem, pre);
+            if constexpr (Pre::kWaits)
+                if (!pre.ok()) return false;
+        } else {
+            expand_rows<DT, VECY, true, UPT>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncol_wg, vec_b,
+                                             grp.rows, -1, n, reinterpret_cast<float *>(vl4), ldl, mem);
+        }
         if (kRows * (pass + 1) >= total) break;
     }
+    return true;
 }
 
 template <int DT, bool SLOT, bool VECY, int UPT, class M>
@@ -1005,7 +1059,128 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restric
                                                           bool vec_b, int ldl, const M mem)
 {
     bgmv_expand_body<DT, SLOT, VECY, UPT>(v, ldv, sl_stride, nsl, T, ids, pool_B, pool_rank, pool_alpha, n_adapters,
-                                          max_rank, y, ldy, d_out, vec_b, ldl, int(blockIdx.y) * kExpandCols, mem);
+                                          max_rank, y, ldy, d_out, vec_b, ldl, int(blockIdx.y) * kExpandCols,
+                                          int(blockIdx.x), mem);
+}
+
+// ----------------------------------------------------------------------------
+// One-launch BGMV.  The two halves of the decode correction run in one grid:
+// workgroups [0, groups * kc) are the shrink of (group, d_in slice); the rest
+// are the expand of (group, column tile), which issue their B and y loads,
+// wait until every slice of their group is published, then load the partial
+// sums.  A consumer never waits on a workgroup of higher index and producers
+// wait on nothing, so the grid completes under any dispatch that starts
+// workgroups in index order within an XCD; the wait is bounded all the same.
+//
+// Hand-over without cache maintenance.  Every launch has a 64-bit key made
+// from its HSA dispatch id (unique per launch on a hardware queue, replays of
+// a graph included) and its queue's address.  A producer writes its partial
+// sums with device-scope stores, waits until they are complete
+// (s_waitcnt vmcnt(0) in every wave), and then thread 0 writes the key into the
+// slice's flag (device-scope store).  A consumer polls its group's kc flags
+// with device-scope loads until all hold the key, then reads the partial sums
+// with device-scope loads.  Device-scope accesses bypass the XCD-local caches
+// that are not coherent across XCDs, so no L2 write-back or invalidate is
+// needed (measured: one agent-scope acquire fence per consumer wave made the
+// launch two to three times slower).  A flag holds the key of the last launch
+// that wrote it, so nothing is reset between calls: a stale or arbitrary value
+// equals a new launch's key only by a 64-bit coincidence.  A consumer that
+// gives up sets *status (sticky) and stores nothing.
+// ----------------------------------------------------------------------------
+extern "C" __device__ uint64_t lora_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+__device__ __forceinline__ uint64_t launch_key()
+{
+    const uint64_t q = uint64_t(uintptr_t(__builtin_amdgcn_queue_ptr()));
+    return (lora_dispatch_id() + 1) * 0x9E3779B97F4A7C15ull ^ q;
+}
+
+struct Waiter {
+    static constexpr bool kWaits = true;
+    const uint64_t *flags; // the group's kc slice flags
+    uint64_t key;          // this launch's key
+    int need;              // slices of the group (kc <= 64)
+    int32_t *status;       // set to 1 when the wait gives up
+    int limit;             // polls before giving up; < 0: give up at once
+    int *flag;             // LDS word: 1 = go on, 0 = gave up
+    __device__ __forceinline__ bool operator()() const
+    {
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            bool ok = limit >= 0;
+            for (int spins = 0; ok; ++spins) {
+                const uint64_t f = lane < need
+                                       ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                       : key;
+                if (__all(f == key)) break;
+                if (spins >= limit) ok = false;
+                else __builtin_amdgcn_s_sleep(1);
+            }
+            if (lane == 0) {
+                if (!ok) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *flag = ok ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        return *flag != 0;
+    }
+    __device__ __forceinline__ bool ok() const { return *flag != 0; }
+};
+
+struct OnepassArgs {
+    const void *x;
+    const int32_t *ids;
+    const uint64_t *pool_A;
+    const uint64_t *pool_B;
+    const int32_t *pool_rank;
+    const float *pool_alpha;
+    float *part;       // slice partial sums [kc][T][ldw]
+    void *y;
+    int32_t *status;   // control words: status, then flags[groups][kc]
+    uint64_t *flags;
+    int64_t ldx, ldw, sl_stride, ldy;
+    int32_t d_in, T, n_adapters, max_rank, slice_len, kc;
+    int32_t d_out, ncol, ldl, vec_b, groups, wait_limit;
+};
+
+template <int DT, int NSTEP, int RT, bool SLOT, int UPT, class M>
+__global__ __launch_bounds__(256) void bgmv_onepass_kernel(const OnepassArgs a, const M mem)
+{
+    const int b = int(blockIdx.x);
+    const int n_prod = a.groups * a.kc;
+    const uint64_t key = launch_key();
+    if (b < n_prod) {
+        const int g = b / a.kc, c = b - (b / a.kc) * a.kc;
+        const bool did = bgmv_shrink_body<DT, true, 4, NSTEP, RT, SLOT, M, true>(
+            a.x, a.ldx, a.d_in, a.T, a.ids, a.pool_A, a.pool_rank, a.n_adapters, a.max_rank, a.slice_len, a.part,
+            a.ldw, a.sl_stride, g, c, mem);
+        if (did) {
+            // every wave's partial sums are complete before the flag moves
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(a.flags + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    __shared__ int go;
+    const int q = b - n_prod;
+    const int g = q / a.ncol, col = q - (q / a.ncol) * a.ncol;
+    const Waiter w{a.flags + int64_t(g) * a.kc, key, a.kc, a.status, a.wait_limit, &go};
+    bgmv_expand_body<DT, SLOT, true, UPT, M, Waiter>(a.part, a.ldw, a.sl_stride, a.kc, a.T, a.ids, a.pool_B,
+                                                      a.pool_rank, a.pool_alpha, a.n_adapters, a.max_rank, a.y,
+                                                      a.ldy, a.d_out, a.vec_b != 0, a.ldl, col * kExpandCols, g, mem,
+                                                      w);
+}
+
+// Zero-fill of a workspace (its control words), as a kernel so that it can be
+// recorded in a graph.
+__global__ __launch_bounds__(256) void workspace_clear_kernel(u32x4 *__restrict__ p, int64_t n16, uint8_t *tail,
+                                                              int ntail)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n16) p[i] = u32x4{0, 0, 0, 0};
+    if (i < ntail) tail[i] = 0;
 }
 
 // ----------------------------------------------------------------------------
@@ -1050,7 +1225,8 @@ __global__ __launch_bounds__(W * 64) void bgmv_shrink_grouped_kernel(int T, cons
     const GShrink &P = tab.p[blockIdx.z];
     if (int(blockIdx.y) >= P.kc) return;
     bgmv_shrink_body<DT, VEC, W, NSTEP, RT, SLOT>(P.x, P.ldx, P.d_in, T, ids, P.pool_A, P.pool_rank, n_adapters,
-                                                  P.max_rank, P.slice_len, P.out, P.ldo, P.sl_stride);
+                                                  P.max_rank, P.slice_len, P.out, P.ldo, P.sl_stride,
+                                                  int(blockIdx.x), int(blockIdx.y));
 }
 
 template <int DT, bool SLOT, bool VECY, int UPT>
@@ -1066,7 +1242,7 @@ __global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const i
     if (col >= P.ncol) return;
     bgmv_expand_body<DT, SLOT, VECY, UPT>(P.v, P.ldv, P.sl_stride, P.nsl, T, ids, P.pool_B, P.pool_rank, P.pool_alpha,
                                           n_adapters, P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl,
-                                          col * kExpandCols);
+                                          col * kExpandCols, int(blockIdx.x));
 }
 
 // ----------------------------------------------------------------------------
@@ -1632,12 +1808,111 @@ int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int3
     return check_launch("bgmv_expand");
 }
 
+namespace {
+template <int DT, int NSTEP, int RT, bool SLOT>
+void onepass_go(hipStream_t s, dim3 grid, size_t shm, const OnepassArgs &a)
+{
+    launch_kernel(bgmv_onepass_kernel<DT, NSTEP, RT, SLOT, 1, DenseMem>, grid, dim3(256), shm, s, a, DenseMem{});
+}
+
+template <bool SLOT>
+void onepass_dispatch(hipStream_t s, int dtype, int rt, bool two, dim3 grid, size_t shm, const OnepassArgs &a)
+{
+    if (dtype == LORA_F32) {
+        onepass_go<LORA_F32, 1, 4, SLOT>(s, grid, shm, a);
+    } else if (rt == 1) {
+        if (two) onepass_go<LORA_BF16, 2, 1, SLOT>(s, grid, shm, a);
+        else onepass_go<LORA_BF16, 1, 1, SLOT>(s, grid, shm, a);
+    } else if (rt == 2) {
+        if (two) onepass_go<LORA_BF16, 2, 2, SLOT>(s, grid, shm, a);
+        else onepass_go<LORA_BF16, 1, 2, SLOT>(s, grid, shm, a);
+    } else {
+        onepass_go<LORA_BF16, 1, 4, SLOT>(s, grid, shm, a);
+    }
+}
+} // namespace
+
+size_t bgmv_ctl_bytes(int32_t T)
+{
+    // status block (256 B), then a 64-bit flag per (group, d_in slice): a
+    // group is an adapter (pools of at most 2T adapters) or a leader token,
+    // and there are at most kMaxSlices slices
+    return (256 + 8 * size_t(kMaxSlices) * 2 * size_t(T < 1 ? 1 : T) + 255) / 256 * 256;
+}
+
+size_t bgmv_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
+{
+    return bgmv_ctl_bytes(T) + combined_workspace_bytes(T, d_in, max_rank);
+}
+
+int &wait_limit()
+{
+    static thread_local int limit = 0;
+    return limit;
+}
+
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
-                int32_t n_adapters, int32_t max_rank, void *ws)
+                int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl, bool one_launch)
 {
-    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
-                         DenseMem{});
+    if (n_adapters == 0) return LORA_OK;
+    const bool slot = slot_major(T, n_adapters);
+    const int groups = slot ? n_adapters : T;
+    const int ncol = (ea.d_out + kExpandCols - 1) / kExpandCols;
+    const Split sp = choose_split(sa.d_in, groups, sa.dtype);
+    const int64_t grid = int64_t(groups) * (sp.kc + ncol);
+    // one launch for aligned rows and ranks up to 64 (one float4 of staged v
+    // per thread); otherwise the shrink and expand kernels
+    const bool fits = one_launch && ctl && sa.vec && ea.vec_y && ea.d_out % 16 == 0 && lds_pitch(max_rank) <= 64 &&
+                      grid < (int64_t(1) << 31);
+    if (!fits)
+        return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
+                             DenseMem{});
+    OnepassArgs a{};
+    a.x = sa.x;
+    a.ids = ids;
+    a.pool_A = pool_A;
+    a.pool_B = pool_B;
+    a.pool_rank = pool_rank;
+    a.pool_alpha = pool_alpha;
+    a.part = static_cast<float *>(ws);
+    a.y = ea.y;
+    a.status = ctl;
+    a.flags = reinterpret_cast<uint64_t *>(ctl + 64);
+    a.ldx = sa.ldx;
+    a.ldw = (max_rank + 3) / 4 * 4;
+    a.sl_stride = int64_t(T) * a.ldw;
+    a.ldy = ea.ldy;
+    a.d_in = sa.d_in;
+    a.T = T;
+    a.n_adapters = n_adapters;
+    a.max_rank = max_rank;
+    a.slice_len = sp.slice_len;
+    a.kc = sp.kc;
+    a.d_out = ea.d_out;
+    a.ncol = ncol;
+    a.ldl = lds_pitch(max_rank);
+    a.vec_b = ea.vec_b ? 1 : 0;
+    a.groups = groups;
+    const int lim = wait_limit();
+    a.wait_limit = lim == 0 ? (1 << 22) : (lim < 0 ? -1 : lim);
+    const size_t shm = (size_t(kRows) * a.ldl + 4) * sizeof(float);
+    const int rt = rank_tiles(max_rank);
+    const bool two = sp.nstep == 2 && rt < 4;
+    if (slot) onepass_dispatch<true>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a);
+    else onepass_dispatch<false>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a);
+    return check_launch("bgmv one-launch");
+}
+
+int launch_workspace_clear(hipStream_t s, void *ws, size_t bytes)
+{
+    const int64_t n16 = int64_t(bytes / 16);
+    const int ntail = int(bytes % 16);
+    const int64_t threads = n16 > ntail ? n16 : ntail;
+    if (threads == 0) return LORA_OK;
+    launch_kernel(workspace_clear_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s,
+                  static_cast<u32x4 *>(ws), n16, static_cast<uint8_t *>(ws) + n16 * 16, ntail);
+    return check_launch("workspace clear");
 }
 
 int launch_bgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,

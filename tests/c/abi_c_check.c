@@ -57,7 +57,9 @@ int main(void)
     CHECK(lora_build_plan(T, ids, N, pool_A, pool_B, rank, alpha, plan, 16) == LORA_ERR_WORKSPACE);
     CHECK(lora_profile_launches(NULL, NULL, -1) == LORA_ERR_ARG);
 
-    /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection regions;
+    /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection
+     * regions of slice partial sums (the size of an SGMV workspace of the same
+     * shape; a single lora_bgmv workspace also holds control words);
      * malformed calls are rejected on the host */
     lora_proj pr[2];
     memset(pr, 0, sizeof(pr));
@@ -74,8 +76,9 @@ int main(void)
         pr[p].d_out = 1024;
         pr[p].max_rank = p == 0 ? 16 : 64;
     }
-    const size_t r0 = lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 16);
-    const size_t r1 = lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 64);
+    const size_t r0 = lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 16);
+    const size_t r1 = lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 64);
+    CHECK(lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 16) > r0);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == (r0 + 255) / 256 * 256 + (r1 + 255) / 256 * 256);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 0) == 0);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, LORA_MAX_PROJ + 1) == 0);

@@ -273,7 +273,10 @@ def test_combined_argument_errors():
     assert sg(None, 1, None, 0, 0, empty.ptr, None, None, 0, 0, None, 0) == 0
     bg = B.lora_bgmv
     needb = B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, 4096, 4096, 16)
-    assert needb >= 64 * 16 * 4
+    # control words (256 B status block, a 64-bit flag per group and d_in
+    # slice: 2T groups, 4 slices at most) in front of the fp32 partial sums of
+    # 4 d_in slices
+    assert needb == (256 + 8 * 4 * 2 * 64 + 255) // 256 * 256 + 4 * 64 * 16 * 4 + 256
     assert bg(None, 1, 0, None, 0, 0, None, None, None, None, None, 0, 16, None, 0, 0, None, 0) == 0
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 4096, 4096, FX, needb - 1) == -6
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, None, FX, FX, 32, 16, FX, 4096, 4096, FX, needb) == -1
@@ -289,7 +292,10 @@ def test_grouped_bgmv_host_checks():
     projs = (B.LoraProj * 3)()
     for p, (d_in, d_out, r) in enumerate([(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)]):
         projs[p] = B.LoraProj(FX, FX + 0x100000 * (p + 1), FX, FX, FX, FX, d_in, d_out, d_in, d_out, r, 0)
-    want = sum((B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, d_in, d_out, r) + 255) // 256 * 256
+    def partials(T, d_in, r):  # fp32 partial sums over at most 4 slices of 256+ elements of d_in, plus slack
+        return min((d_in + 255) // 256, 4) * T * ((r + 3) // 4 * 4) * 4 + 256
+
+    want = sum((partials(64, d_in, r) + 255) // 256 * 256
                for d_in, d_out, r in [(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)])
     ptr = C.cast(projs, C.c_void_p)
     assert B.lora_bgmv_grouped_workspace_bytes(64, ptr, 3) == want
