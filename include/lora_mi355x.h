@@ -600,6 +600,26 @@ int lora_profile_launches(void **start_events, void **stop_events, int32_t count
  * have taken so far on this thread (how many kernels a call enqueued). */
 int32_t lora_profile_launches_used(void);
 
+/* ------------------------------------------------------------ no allocation
+ * lora_bgmv for callers that cannot allocate device memory or pass a
+ * workspace (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The arguments are lora_bgmv's without the workspace: the
+ * fp32 slice partial sums live in a static array the library holds on every
+ * device it runs on (LORA_NOALLOC_SCRATCH_BYTES each, until the process ends),
+ * and the call runs lora_bgmv's shrink and expand kernels (two launches) on
+ * the current device.  The shrink writes every partial sum the expand reads,
+ * so the array needs no clearing between calls.  Calls on one device share
+ * the array: calls that may overlap on one device (streams without an
+ * ordering between them) race.  The call allocates and frees nothing.
+ * Errors: as lora_bgmv; LORA_ERR_WORKSPACE when the batch's partial sums
+ * (lora_workspace_bytes(LORA_OP_SGMV, T, d_in, d_out, max_rank)) exceed the
+ * array; LORA_ERR_HIP when the array's device address cannot be found. */
+#define LORA_NOALLOC_SCRATCH_BYTES (4u << 20)
+int lora_bgmv_noalloc(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
+                      const int32_t *ids_dev, const uint64_t *pool_A_dev, const uint64_t *pool_B_dev,
+                      const int32_t *pool_rank_dev, const float *pool_alpha_dev, int32_t n_adapters,
+                      int32_t max_rank, void *y, int64_t ldy, int32_t d_out);
+
 /* ------------------------------------------------------------ measurement aids
  * Reference kernels a benchmark times beside the adapter kernels, so that each
  * adapter kernel can be read against what the chip achieves for the same

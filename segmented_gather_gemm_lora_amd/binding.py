@@ -47,7 +47,7 @@ EXPORTS = [
     "lora_pages_needed", "lora_page_alloc_create", "lora_page_alloc_destroy", "lora_page_alloc_take",
     "lora_page_alloc_give", "lora_page_alloc_free_count", "lora_pages_write", "lora_sgmv_paged", "lora_bgmv_paged",
     "lora_sgmv_grouped", "lora_sgmv_grouped_workspace_bytes", "lora_probe_empty", "lora_probe_stream",
-    "lora_probe_chase", "lora_workspace_clear", "lora_debug_wait_limit",
+    "lora_probe_chase", "lora_workspace_clear", "lora_debug_wait_limit", "lora_bgmv_noalloc",
 ]
 LORA_CACHE_DRY = 1
 MAX_PROJ = 8
@@ -106,6 +106,8 @@ _SIGS = {
     "lora_probe_empty": (ctypes.c_int, [_vp, _i32]),
     "lora_workspace_clear": (ctypes.c_int, [_vp, _vp, _sz]),
     "lora_debug_wait_limit": (ctypes.c_int, [_i32]),
+    "lora_bgmv_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                                         _i32, _vp, _i64, _i32]),
     "lora_probe_stream": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i32]),
     "lora_probe_chase": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
     "lora_page_alloc_create": (ctypes.c_int, [_i32, _vp]),

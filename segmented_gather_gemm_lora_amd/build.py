@@ -22,7 +22,7 @@ OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "liblora_mi355x.so"
 
-SOURCES = ["sgmv_bgmv.hip", "fused.hip", "abi.cpp", "residency.cpp", "pages.hip", "probes.hip"]
+SOURCES = ["sgmv_bgmv.hip", "fused.hip", "abi.cpp", "residency.cpp", "pages.hip", "probes.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
