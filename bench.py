@@ -829,8 +829,10 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
     traffic, kname = recorded_traffic(CONFIG_NAMES[k] + (f"_paged{page}" if page else ""), dominant)
     roof["traffic"] = traffic
-    roof["kernel"] = kname or {"shrink": f"{kind}_shrink", "expand": f"{kind}_expand", "fused": "fused_linear",
-                               kind: f"{kind}_onepass"}[dominant]
+    default_names = {"shrink": f"{kind}_shrink", "expand": f"{kind}_expand", "fused": "fused_linear"}
+    if names == [kind]:
+        default_names[kind] = f"{kind}_onepass"
+    roof["kernel"] = kname or default_names[dominant]
     roof["algorithmic_bytes_per_launch"] = round(dom_bytes)
     roof["avg_launch_us"] = round(dom_us, 3)
 

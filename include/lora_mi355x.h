@@ -76,20 +76,29 @@ typedef enum lora_dtype {
 #define LORA_MAX_RANK 256     /* largest adapter rank accepted */
 #define LORA_PLAN_ROW_BLOCK 16 /* rows per block in a plan's block list */
 
-/* ------------------------------------------------------------------ plans
- * A plan is the grouping of one batch's tokens into segments: tokens sorted by
- * adapter id (ascending), the original order kept inside a segment, tokens with
- * id -1 left out.  The pages fix the grouping but not its order; the ascending
- * stable order makes the plan unique.  ("Multi-LoRA Serving in Production ...",
+/* ------------------------------------------------------------------ segments
+ * The grouping of one batch's tokens into segments: tokens sorted by adapter
+ * id (ascending), the original order kept inside a segment, tokens with id -1
+ * left out.  The pages fix the grouping but not its order; the ascending
+ * stable order makes it unique.  ("Multi-LoRA Serving in Production ...",
  * section "Punica and Segmented Gather Matrix-Vector Multiplication (SGMV)":
  * the batch is split into contiguous segments whose tokens reference one
- * adapter id; the adapters are reached through a pointer array.)
+ * adapter id, given by segment start indices; the adapters are reached through
+ * a pointer array, with a rank per adapter.)
  *
- * A plan lives in one contiguous buffer with the same layout on the host and
- * the device, so a single copy moves it:
+ * lora_build_segments emits, for S segments over the T' adapted tokens:
+ *   perm[T']          original token index at each sorted position (then the
+ *                     T - T' tokens without an adapter, in their order)
+ *   seg_indptr[S + 1] segment s covers sorted positions [seg_indptr[s], seg_indptr[s+1])
+ *   seg_adapter[S], seg_A[S], seg_B[S], seg_rank[S], seg_scale[S] (alpha / r, fp32)
+ * All of it lives in one buffer, with the same layout on the host and the
+ * device, so one copy moves it (lora_segments_upload).  The buffer also holds
+ * the descriptors the kernels start from (below), so that a workgroup reads
+ * one record before it fetches activations and adapter weights.
  *
+ * Buffer layout (a "plan"):
  *   [lora_plan_header][lora_seg_desc x S][lora_blk_desc x n_blocks][int32 perm x T]
- *   [lora_chunk_desc x n_chunks][int32 segidx x T']
+ *   [lora_chunk_desc x n_chunks][int32 segidx x T'][segment arrays]
  *
  * perm[p] is the original token index at sorted position p (p < T'); the
  * tokens without an adapter follow in their original order (perm[T' .. T)),
@@ -139,7 +148,10 @@ typedef struct lora_plan_header {
     uint64_t bytes_used;  /* bytes from the start of the buffer that hold the plan */
     uint64_t chunk_offset; /* byte offset of the lora_chunk_desc array (64-byte aligned) */
     uint64_t segidx_offset; /* byte offset of segidx (16-byte aligned) */
-    uint64_t reserved[2];
+    uint64_t soa_offset;  /* byte offset of the segment arrays (16-byte aligned): seg_A[S],
+                             seg_B[S] (uint64), seg_indptr[S + 1], seg_adapter[S], seg_rank[S]
+                             (int32), seg_scale[S] (float) */
+    uint64_t reserved;
 } lora_plan_header; /* 96 bytes */
 
 /* A chunk is up to this many consecutive blocks of one segment (64 rows): the
@@ -164,27 +176,60 @@ typedef struct lora_chunk_desc {
 
 #define LORA_PLAN_MAGIC 0x4C6F5241u
 
-/* Bytes a plan buffer needs for a batch of up to `capacity` tokens (>= 0). */
-size_t lora_plan_bytes(int32_t capacity);
+/* A batch's segments, on the host or on the device: counts, and pointers into
+ * the buffer the struct is bound to (host addresses in a host struct, device
+ * addresses in a device struct).  The first eleven fields are the segment
+ * table; the rest tie the struct to its buffer. */
+typedef struct lora_segments {
+    int32_t num_segments;  /* S */
+    int32_t num_tokens;    /* T' = seg_indptr[S], tokens that have an adapter */
+    int32_t max_rank;      /* largest r_s (0 when S = 0) */
+    int32_t capacity;      /* largest batch the bound buffer holds */
+    int32_t *perm;         /* [batch_tokens] */
+    int32_t *seg_indptr;   /* [S + 1] */
+    int32_t *seg_adapter;  /* [S] */
+    int32_t *seg_rank;     /* [S] */
+    uint64_t *seg_A;       /* [S] device addresses of A_s */
+    uint64_t *seg_B;       /* [S] device addresses of B_s */
+    float *seg_scale;      /* [S] alpha_s / r_s */
+    int32_t batch_tokens;  /* T of the batch, tokens without an adapter included */
+    int32_t reserved0;
+    void *buf;             /* the bound buffer (holds the plan) */
+    const void *host;      /* device struct: the host buffer it was uploaded from (the calls read the
+                              launch geometry there); NULL in a host struct */
+} lora_segments;
 
-/* Build the plan of one batch on the host (no GPU call).  O(T + n_adapters).
- *   ids        [T] host, adapter per token, -1 = none
+/* Bytes a segments buffer needs for batches of up to `capacity` tokens (>= 0). */
+size_t lora_segments_bytes(int32_t capacity);
+
+/* Bind a caller buffer (host or device memory, 16-byte aligned, at least
+ * lora_segments_bytes(capacity) bytes) to *out; counts and pointers are set by
+ * lora_build_segments (host) or lora_segments_upload (device).  The buffer
+ * stays the caller's.  Errors: LORA_ERR_ARG, LORA_ERR_ALIGN. */
+int lora_segments_bind(void *buf, int32_t capacity, lora_segments *out);
+
+/* Build the segments of one batch into a host-bound struct (no GPU call),
+ * O(T + n_adapters).
+ *   ids        [T] host, adapter per token, -1 = none; T <= out_host->capacity
  *   pool_A/B   [n_adapters] host, device addresses of A_i / B_i (16-byte aligned)
  *   pool_rank  [n_adapters] host, r_i in [1, 256]
- *   pool_alpha [n_adapters] host, alpha_i; the plan stores alpha_i / r_i in fp32
- *   plan       host buffer of plan_bytes >= lora_plan_bytes(T), 8-byte aligned
+ *   pool_alpha [n_adapters] host, alpha_i; seg_scale = alpha_i / r_i in fp32
+ * Only the adapters the batch uses are looked at.
  * Errors: LORA_ERR_ARG, LORA_ERR_ADAPTER_ID, LORA_ERR_RANK, LORA_ERR_ALIGN,
- * LORA_ERR_WORKSPACE (buffer too small). */
-int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters,
-                    const uint64_t *pool_A, const uint64_t *pool_B,
-                    const int32_t *pool_rank, const float *pool_alpha,
-                    void *plan, size_t plan_bytes);
+ * LORA_ERR_WORKSPACE (batch larger than the capacity). */
+int lora_build_segments(int32_t T, const int32_t *ids, int32_t n_adapters,
+                        const uint64_t *pool_A, const uint64_t *pool_B,
+                        const int32_t *pool_rank, const float *pool_alpha,
+                        lora_segments *out_host);
 
-/* Enqueue one host-to-device copy of header.bytes_used bytes of a built plan
- * (plan_host should be pinned memory; it must stay unchanged until the copy
- * has run).  plan_dev must hold at least that many bytes.
- * Errors: LORA_ERR_ARG, LORA_ERR_PLAN, LORA_ERR_HIP. */
-int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_bytes, void *stream);
+/* Enqueue one host-to-device copy of a built host struct's buffer into the
+ * buffer `dev` is bound to, and set dev's counts and device pointers; dev
+ * remembers host's buffer.  host's buffer should be pinned memory and must stay
+ * unchanged while the copy is pending and while dev is passed to the calls
+ * below (they read the launch geometry from it).
+ * Errors: LORA_ERR_ARG, LORA_ERR_PLAN, LORA_ERR_WORKSPACE (dev too small),
+ * LORA_ERR_HIP. */
+int lora_segments_upload(const lora_segments *host, lora_segments *dev, void *stream);
 
 /* ------------------------------------------------------------------ SGMV
  * Segmented shrink, the pages' "Shrink Stage" ("Multi-LoRA Serving in
@@ -193,17 +238,16 @@ int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_byte
  *     v[p, j] = sum_k x[perm[p], k] * A_s[j, k]    for j < r_s,
  * for every sorted position p of segment s.  v rows are in sorted order; the
  * columns j >= r_s of a row are left untouched.  Overwrites v.
- *   plan_host / plan_dev  the same plan, on the host (read during the call for
- *                         the launch geometry, and by the expand for the chunk
- *                         descriptors it passes in the kernel arguments) and on
- *                         the device (read by the kernels)
- *   v                     device fp32 [header.num_sorted, ldv], ldv >= max_rank,
+ *   seg                   the batch's segments, uploaded (a device struct; the
+ *                         call reads the launch geometry, and the expand the
+ *                         chunk descriptors it passes in the kernel arguments,
+ *                         from its host copy)
+ *   v                     device fp32 [seg->num_tokens, ldv], ldv >= max_rank,
  *                         ldv a multiple of 4
  * Errors: LORA_ERR_ARG, LORA_ERR_DTYPE, LORA_ERR_RANK, LORA_ERR_ALIGN,
  * LORA_ERR_PLAN, LORA_ERR_HIP. */
 int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
-                     const void *plan_host, const void *plan_dev,
-                     float *v, int64_t ldv, void *ws, size_t ws_bytes);
+                     const lora_segments *seg, float *v, int64_t ldv, void *ws, size_t ws_bytes);
 
 /* Segmented expand, the pages' "Expand Stage" (same section): scale and
  * accumulate into the base output,
@@ -211,20 +255,18 @@ int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_
  * Rows of tokens without an adapter are not touched.
  * Errors: as lora_sgmv_shrink. */
 int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
-                     const void *plan_host, const void *plan_dev,
-                     void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+                     const lora_segments *seg, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
-/* One call for the whole correction of a batch from a plan, shrink then
+/* One call for the whole correction of a batch from its segments, shrink then
  * expand (same section): y[perm[p], :] += scale_s (x[perm[p], :] A_s) B_s.
  * The low-rank intermediate stays in the workspace as fp32 partial sums over
  * slices of d_in (summed in a fixed order by the expand, so results are
  * reproducible run to run).  Two kernel launches on `stream`.
  * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_SGMV, T, d_in, d_out, max_rank)
- * with T >= header.num_sorted and max_rank >= header.max_rank.
+ * with T >= seg->num_tokens and max_rank >= seg->max_rank.
  * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */
 int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
-              const void *plan_host, const void *plan_dev,
-              void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
+              const lora_segments *seg, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------ BGMV
  * Decode-shaped gather (one row per request, "Multi-LoRA Serving in
@@ -338,7 +380,7 @@ int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev
  * The prefill form of the grouped invocation (same sections as grouped BGMV):
  * several projections of a layer, each with its own plan, x, y and sizes, in
  * one shrink launch and one expand launch.  Each projection's plan is built
- * (lora_build_plan) from the batch's ids with that projection's adapter
+ * (lora_build_segments) from the batch's ids with that projection's adapter
  * tables, so every projection applies
  *     y_p[t, :] += (alpha_{i,p} / r_{i,p}) (x_p[t, :] A_{i,p}) B_{i,p},  i = ids[t].
  * Projections whose inputs are the same tensor (q, k, v; gate, up) may pass the
@@ -351,8 +393,7 @@ int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev
 typedef struct lora_sgmv_proj {
     const void *x;          /* device [T, ldx] of the call's dtype */
     void *y;                /* device [T, ldy]; the y of two projections share no element */
-    const void *plan_host;  /* this projection's plan (host copy) */
-    const void *plan_dev;   /* and its device copy (lora_plan_upload) */
+    const lora_segments *seg; /* this projection's segments, uploaded (device struct) */
     int64_t ldx, ldy;
     int32_t d_in, d_out;
 } lora_sgmv_proj;
@@ -410,7 +451,7 @@ typedef struct lora_cache_view {
     const int32_t *rank_dev;
     const float *alpha_dev;
     const uint64_t *pool_A_host; /* host mirrors, current after the last prepare: the */
-    const uint64_t *pool_B_host; /* inputs of lora_build_plan for the batch */
+    const uint64_t *pool_B_host; /* inputs of lora_build_segments for the batch */
     const int32_t *rank_host;
     const float *alpha_host;
     int32_t n_adapters;
@@ -516,12 +557,13 @@ int32_t lora_page_alloc_free_count(const lora_page_alloc *alloc);
 int lora_pages_write(void *stream, void *pages, int64_t page_bytes, const int32_t *table_dev,
                      const void *src, int64_t bytes);
 
-/* lora_sgmv over paged adapters: the plan was built (lora_build_plan) with
- * pool_A[i] / pool_B[i] = device addresses of adapter i's A and B page tables.
+/* lora_sgmv over paged adapters: the segments were built (lora_build_segments)
+ * with pool_A[i] / pool_B[i] = device addresses of adapter i's A and B page
+ * tables.
  * Errors: as lora_sgmv, plus LORA_ERR_ARG / LORA_ERR_ALIGN for pages or
  * page_bytes. */
 int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
-                    const void *plan_host, const void *plan_dev, const void *pages, int64_t page_bytes,
+                    const lora_segments *seg, const void *pages, int64_t page_bytes,
                     void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
 /* lora_bgmv over paged adapters: pool_A_dev[i] / pool_B_dev[i] are the
@@ -556,8 +598,7 @@ int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t l
  * the alignment rules above; LORA_ERR_ARG for x or W0 of 4 GiB or more;
  * LORA_ERR_WORKSPACE. */
 int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
-                      const void *W0, int32_t d_out,
-                      const void *plan_host, const void *plan_dev,
+                      const void *W0, int32_t d_out, const lora_segments *seg,
                       void *y, int64_t ldy, void *ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------ helpers */

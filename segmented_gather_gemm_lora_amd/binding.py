@@ -38,7 +38,7 @@ STATUS = {
 
 # Every symbol the public header declares.
 EXPORTS = [
-    "lora_plan_bytes", "lora_build_plan", "lora_plan_upload", "lora_sgmv_shrink",
+    "lora_segments_bytes", "lora_segments_bind", "lora_build_segments", "lora_segments_upload", "lora_sgmv_shrink",
     "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
     "lora_version", "lora_profile_launches", "lora_profile_launches_used", "lora_bgmv_grouped",
@@ -69,20 +69,20 @@ _LIB = None
 _LOCK = threading.Lock()
 
 _SIGS = {
-    "lora_plan_bytes": (_sz, [_i32]),
-    "lora_build_plan": (ctypes.c_int, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz]),
-    "lora_plan_upload": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
-    "lora_sgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _sz]),
-    "lora_sgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz]),
-    "lora_sgmv": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i32, _vp, _sz]),
+    "lora_segments_bytes": (_sz, [_i32]),
+    "lora_segments_bind": (ctypes.c_int, [_vp, _i32, _vp]),
+    "lora_build_segments": (ctypes.c_int, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "lora_segments_upload": (ctypes.c_int, [_vp, _vp, _vp]),
+    "lora_sgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _i64, _vp, _sz]),
+    "lora_sgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _vp, _vp, _i64, _i32, _vp, _sz]),
+    "lora_sgmv": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _i64, _i32, _vp, _sz]),
     "lora_bgmv": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                  _vp, _i64, _i32, _vp, _sz]),
     "lora_bgmv_shrink": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _i32, _i32,
                                         _vp, _i64, _vp, _sz]),
     "lora_bgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
                                         _vp, _i64, _i32, _vp, _sz]),
-    "lora_fused_linear": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _i64,
-                                         _vp, _sz]),
+    "lora_fused_linear": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _sz]),
     "lora_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32, _i32]),
     "lora_adapter_numel": (_i64, [_i32, _i32, _i32]),
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -116,8 +116,8 @@ _SIGS = {
     "lora_page_alloc_give": (ctypes.c_int, [_vp, _vp, _i32]),
     "lora_page_alloc_free_count": (_i32, [_vp]),
     "lora_pages_write": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64]),
-    "lora_sgmv_paged": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i32,
-                                       _vp, _sz]),
+    "lora_sgmv_paged": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _vp, _i64, _vp, _i64, _i32, _vp,
+                                       _sz]),
     "lora_bgmv_paged": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
                                        _i32, _vp, _i64, _vp, _i64, _i32, _vp, _sz]),
 }
@@ -152,14 +152,25 @@ class LoraProj(ctypes.Structure):
 assert ctypes.sizeof(LoraProj) == 80
 
 
+class LoraSegments(ctypes.Structure):
+    """struct lora_segments: a batch's segments, bound to a host or device buffer."""
+
+    _fields_ = [("num_segments", _i32), ("num_tokens", _i32), ("max_rank", _i32), ("capacity", _i32),
+                ("perm", _vp), ("seg_indptr", _vp), ("seg_adapter", _vp), ("seg_rank", _vp), ("seg_A", _vp),
+                ("seg_B", _vp), ("seg_scale", _vp), ("batch_tokens", _i32), ("reserved0", _i32), ("buf", _vp),
+                ("host", _vp)]
+
+
+assert ctypes.sizeof(LoraSegments) == 96
+
+
 class LoraSgmvProj(ctypes.Structure):
     """struct lora_sgmv_proj: one projection of a grouped SGMV call."""
 
-    _fields_ = [("x", _vp), ("y", _vp), ("plan_host", _vp), ("plan_dev", _vp), ("ldx", _i64), ("ldy", _i64),
-                ("d_in", _i32), ("d_out", _i32)]
+    _fields_ = [("x", _vp), ("y", _vp), ("seg", _vp), ("ldx", _i64), ("ldy", _i64), ("d_in", _i32), ("d_out", _i32)]
 
 
-assert ctypes.sizeof(LoraSgmvProj) == 56
+assert ctypes.sizeof(LoraSgmvProj) == 48
 
 
 def lib_path() -> str:
@@ -194,8 +205,8 @@ def last_error() -> str:
 
 
 # ------------------------------------------------------------------ raw C calls (same names)
-def lora_plan_bytes(capacity: int) -> int:
-    return int(load().lora_plan_bytes(capacity))
+def lora_segments_bytes(capacity: int) -> int:
+    return int(load().lora_segments_bytes(capacity))
 
 
 def lora_workspace_bytes(op: int, T: int, d_in: int, d_out: int, max_rank: int) -> int:
@@ -214,26 +225,30 @@ def lora_status_string(status: int) -> str:
     return load().lora_status_string(status).decode()
 
 
-def lora_build_plan(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr, pool_alpha_ptr,
-                    plan_ptr, plan_bytes) -> int:
-    return int(load().lora_build_plan(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr,
-                                      pool_alpha_ptr, plan_ptr, plan_bytes))
+def lora_segments_bind(buf_ptr, capacity, seg_ptr) -> int:
+    return int(load().lora_segments_bind(buf_ptr, capacity, seg_ptr))
 
 
-def lora_plan_upload(plan_host_ptr, plan_dev_ptr, plan_dev_bytes, stream) -> int:
-    return int(load().lora_plan_upload(plan_host_ptr, plan_dev_ptr, plan_dev_bytes, stream))
+def lora_build_segments(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr, pool_alpha_ptr,
+                        seg_ptr) -> int:
+    return int(load().lora_build_segments(T, ids_ptr, n_adapters, pool_A_ptr, pool_B_ptr, pool_rank_ptr,
+                                          pool_alpha_ptr, seg_ptr))
 
 
-def lora_sgmv_shrink(stream, dtype, x, ldx, d_in, plan_host, plan_dev, v, ldv, ws, ws_bytes) -> int:
-    return int(load().lora_sgmv_shrink(stream, dtype, x, ldx, d_in, plan_host, plan_dev, v, ldv, ws, ws_bytes))
+def lora_segments_upload(host_ptr, dev_ptr, stream) -> int:
+    return int(load().lora_segments_upload(host_ptr, dev_ptr, stream))
 
 
-def lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes) -> int:
-    return int(load().lora_sgmv_expand(stream, dtype, v, ldv, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes))
+def lora_sgmv_shrink(stream, dtype, x, ldx, d_in, seg, v, ldv, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv_shrink(stream, dtype, x, ldx, d_in, seg, v, ldv, ws, ws_bytes))
 
 
-def lora_sgmv(stream, dtype, x, ldx, d_in, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes) -> int:
-    return int(load().lora_sgmv(stream, dtype, x, ldx, d_in, plan_host, plan_dev, y, ldy, d_out, ws, ws_bytes))
+def lora_sgmv_expand(stream, dtype, v, ldv, seg, y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv_expand(stream, dtype, v, ldv, seg, y, ldy, d_out, ws, ws_bytes))
+
+
+def lora_sgmv(stream, dtype, x, ldx, d_in, seg, y, ldy, d_out, ws, ws_bytes) -> int:
+    return int(load().lora_sgmv(stream, dtype, x, ldx, d_in, seg, y, ldy, d_out, ws, ws_bytes))
 
 
 def lora_bgmv(stream, dtype, T, x, ldx, d_in, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank,
@@ -340,7 +355,7 @@ class AdapterCache:
         return v
 
     def pool(self) -> "DevicePool":
-        """The current tables as a DevicePool: host mirrors for lora_build_plan,
+        """The current tables as a DevicePool: host mirrors for lora_build_segments,
         device tables for the BGMV calls.  Valid until the next prepare."""
         v = self.view()
         A, Bt, r, a = self.host_tables()
@@ -358,9 +373,8 @@ class AdapterCache:
         return A, Bt, r, a
 
 
-def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy, ws, ws_bytes) -> int:
-    return int(load().lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, plan_host, plan_dev, y, ldy,
-                                        ws, ws_bytes))
+def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes) -> int:
+    return int(load().lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes))
 
 
 def lora_profile_launches(start_events, stop_events, count) -> int:
@@ -667,7 +681,7 @@ def plan_header(h: np.ndarray) -> dict:
             "num_segments": int(i32[3]), "num_blocks": int(i32[4]), "max_rank": int(i32[5]),
             "max_len": int(i32[6]), "num_chunks": int(i32[7]), "seg_offset": int(u64[0]),
             "blk_offset": int(u64[1]), "perm_offset": int(u64[2]), "bytes_used": int(u64[3]),
-            "chunk_offset": int(u64[4]), "segidx_offset": int(u64[5])}
+            "chunk_offset": int(u64[4]), "segidx_offset": int(u64[5]), "soa_offset": int(u64[6])}
 
 
 def plan_arrays(buf: np.ndarray, h: dict) -> dict:
@@ -689,28 +703,39 @@ def plan_arrays(buf: np.ndarray, h: dict) -> dict:
 
 
 class Plan:
-    """A batch's segment plan: pinned host copy + device copy (one upload)."""
+    """A batch's segments (struct lora_segments): a pinned host buffer and a
+    device buffer, each bound to a struct; build() fills the host one,
+    upload() copies it to the device one (one copy).  `seg` is the address of
+    the device struct, which the calls take."""
 
     def __init__(self, capacity: int, device="cuda"):
         torch = _torch()
         self.capacity = int(capacity)
-        self.nbytes = lora_plan_bytes(self.capacity)
+        self.nbytes = lora_segments_bytes(self.capacity)
         self.host = torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True)
         self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.h = LoraSegments()
+        self.d = LoraSegments()
+        _check(lora_segments_bind(self.host.data_ptr(), self.capacity, ctypes.addressof(self.h)), "lora_segments_bind")
+        _check(lora_segments_bind(self.dev.data_ptr(), self.capacity, ctypes.addressof(self.d)), "lora_segments_bind")
+
+    @property
+    def seg(self) -> int:
+        return ctypes.addressof(self.d)
 
     def build(self, ids: np.ndarray, pool: DevicePool):
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         if ids.shape[0] > self.capacity:
-            raise ValueError("batch larger than the plan capacity")
-        st = lora_build_plan(ids.shape[0], ids.ctypes.data, pool.n_adapters, pool.addr_A.ctypes.data,
-                             pool.addr_B.ctypes.data, pool.rank.ctypes.data, pool.alpha.ctypes.data,
-                             self.host.data_ptr(), self.nbytes)
-        _check(st, "lora_build_plan")
+            raise ValueError("batch larger than the segments' capacity")
+        st = lora_build_segments(ids.shape[0], ids.ctypes.data, pool.n_adapters, pool.addr_A.ctypes.data,
+                                 pool.addr_B.ctypes.data, pool.rank.ctypes.data, pool.alpha.ctypes.data,
+                                 ctypes.addressof(self.h))
+        _check(st, "lora_build_segments")
         return self
 
     def upload(self, stream=None):
-        _check(lora_plan_upload(self.host.data_ptr(), self.dev.data_ptr(), self.nbytes, _stream_handle(stream)),
-               "lora_plan_upload")
+        _check(lora_segments_upload(ctypes.addressof(self.h), ctypes.addressof(self.d), _stream_handle(stream)),
+               "lora_segments_upload")
         return self
 
     def header(self) -> dict:
@@ -720,17 +745,40 @@ class Plan:
         """Host copies of the plan's arrays (for tests)."""
         return plan_arrays(self.host.numpy(), self.header())
 
+    def segment_table(self) -> dict:
+        """The host struct's segment table as numpy arrays (copies)."""
+        return segment_table(self.h)
+
+
+_NP_OF = {ctypes.c_int32: np.int32, ctypes.c_uint64: np.uint64, ctypes.c_float: np.float32}
+
+
+def segment_table(h: LoraSegments) -> dict:
+    """perm, seg_indptr, seg_adapter, seg_rank, seg_A, seg_B, seg_scale of a
+    host-bound struct, as numpy copies."""
+    S, Tp = h.num_segments, h.num_tokens
+
+    def arr(ptr, ctype, n):
+        if n == 0 or not ptr:
+            return np.zeros(0, dtype=_NP_OF[ctype])
+        return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctype)), (n,)).copy()
+
+    return {"perm": arr(h.perm, ctypes.c_int32, Tp), "seg_indptr": arr(h.seg_indptr, ctypes.c_int32, S + 1),
+            "seg_adapter": arr(h.seg_adapter, ctypes.c_int32, S), "seg_rank": arr(h.seg_rank, ctypes.c_int32, S),
+            "seg_A": arr(h.seg_A, ctypes.c_uint64, S), "seg_B": arr(h.seg_B, ctypes.c_uint64, S),
+            "seg_scale": arr(h.seg_scale, ctypes.c_float, S)}
+
 
 def sgmv_shrink(x, plan: Plan, v, dtype: str, stream=None):
     d_in = x.shape[1]
     _check(lora_sgmv_shrink(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), d_in,
-                            plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(v), v.stride(0), None, 0),
+                            plan.seg, _ptr(v), v.stride(0), None, 0),
            "lora_sgmv_shrink")
 
 
 def sgmv_expand(v, plan: Plan, y, dtype: str, stream=None):
-    _check(lora_sgmv_expand(_stream_handle(stream), DTYPES[dtype], _ptr(v), v.stride(0), plan.host.data_ptr(),
-                            plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1], None, 0),
+    _check(lora_sgmv_expand(_stream_handle(stream), DTYPES[dtype], _ptr(v), v.stride(0), plan.seg, _ptr(y),
+                            y.stride(0), y.shape[1], None, 0),
            "lora_sgmv_expand")
 
 
@@ -759,8 +807,8 @@ def debug_wait_limit(polls: int):
 
 def sgmv(x, plan: Plan, y, ws, dtype: str, stream=None):
     """y[perm] += scale (x[perm] A) B for the whole plan (shrink + expand)."""
-    _check(lora_sgmv(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1], plan.host.data_ptr(),
-                     plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
+    _check(lora_sgmv(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1], plan.seg, _ptr(y),
+                     y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_sgmv")
 
 
@@ -776,7 +824,7 @@ def bgmv(x, ids_dev, pool: DevicePool, y, ws, dtype: str, max_rank: Optional[int
 def sgmv_prepared(x, plan: Plan, y, ws, dtype: str, stream) -> Prepared:
     """lora_sgmv with its arguments converted once (see Prepared)."""
     return Prepared("lora_sgmv", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
-                                  plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(y), y.stride(0), y.shape[1],
+                                  plan.seg, _ptr(y), y.stride(0), y.shape[1],
                                   _ptr(ws), ws.numel() * ws.element_size()), keep=(x, plan, y, ws))
 
 
@@ -791,7 +839,7 @@ def bgmv_prepared(x, ids_dev, pool, y, ws, dtype: str, stream, max_rank: Optiona
 
 def sgmv_paged_prepared(x, plan: Plan, pool: "PagedPool", y, ws, dtype: str, stream) -> Prepared:
     return Prepared("lora_sgmv_paged", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
-                                        plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(pool.pages),
+                                        plan.seg, _ptr(pool.pages),
                                         pool.page_bytes, _ptr(y), y.stride(0), y.shape[1], _ptr(ws),
                                         ws.numel() * ws.element_size()), keep=(x, plan, pool, y, ws))
 
@@ -808,7 +856,7 @@ def bgmv_paged_prepared(x, ids_dev, pool: "PagedPool", y, ws, dtype: str, stream
 
 def fused_prepared(x, W0, plan: Plan, y, ws, dtype: str, stream) -> Prepared:
     return Prepared("lora_fused_linear", (_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
-                                          _ptr(W0), W0.shape[0], plan.host.data_ptr(), plan.dev.data_ptr(),
+                                          _ptr(W0), W0.shape[0], plan.seg,
                                           _ptr(y), y.stride(0), _ptr(ws), ws.numel() * ws.element_size()),
                     keep=(x, W0, plan, y, ws))
 
@@ -828,7 +876,7 @@ def bgmv_grouped_prepared(T: int, ids_dev, n_adapters: int, projs, ws, dtype: st
 def sgmv_paged(x, plan: Plan, pool: PagedPool, y, ws, dtype: str, stream=None):
     """lora_sgmv over paged adapters (plan built from the PagedPool)."""
     _check(load().lora_sgmv_paged(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1],
-                                  plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(pool.pages), pool.page_bytes,
+                                  plan.seg, _ptr(pool.pages), pool.page_bytes,
                                   _ptr(y), y.stride(0), y.shape[1], _ptr(ws), ws.numel() * ws.element_size()),
            "lora_sgmv_paged")
 
@@ -847,7 +895,7 @@ def sgmv_proj_array(xs, plans, ys):
     """Host array of struct lora_sgmv_proj for projections (xs[p], plans[p], ys[p])."""
     arr = (LoraSgmvProj * len(xs))()
     for p, (x, plan, y) in enumerate(zip(xs, plans, ys)):
-        arr[p] = LoraSgmvProj(_ptr(x), _ptr(y), plan.host.data_ptr(), plan.dev.data_ptr(), x.stride(0), y.stride(0),
+        arr[p] = LoraSgmvProj(_ptr(x), _ptr(y), plan.seg, x.stride(0), y.stride(0),
                               x.shape[1], y.shape[1])
     return arr
 
@@ -922,7 +970,7 @@ def bgmv_expand(v, ids_dev, pool: DevicePool, y, dtype: str, max_rank: Optional[
 
 def fused_linear(x, W0, plan: Plan, y, ws, dtype: str = "bf16", stream=None):
     _check(lora_fused_linear(_stream_handle(stream), DTYPES[dtype], _ptr(x), x.stride(0), x.shape[1], _ptr(W0),
-                             W0.shape[0], plan.host.data_ptr(), plan.dev.data_ptr(), _ptr(y), y.stride(0),
+                             W0.shape[0], plan.seg, _ptr(y), y.stride(0),
                              _ptr(ws), ws.numel() * ws.element_size()),
            "lora_fused_linear")
 

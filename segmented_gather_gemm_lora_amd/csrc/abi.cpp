@@ -37,6 +37,27 @@ LaunchEvents &launch_events()
 
 static size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
+// The segment table as arrays, at the plan's soa_offset: seg_A[S], seg_B[S]
+// (uint64), seg_indptr[S + 1], seg_adapter[S], seg_rank[S] (int32),
+// seg_scale[S] (float).
+struct SoA {
+    uint64_t *A, *B;
+    int32_t *indptr, *adapter, *rank;
+    float *scale;
+};
+static size_t soa_bytes(int32_t S) { return 16 * size_t(S) + 4 * (size_t(S) + 1) + 12 * size_t(S); }
+static SoA soa_at(char *p, int32_t S)
+{
+    SoA t;
+    t.A = reinterpret_cast<uint64_t *>(p);
+    t.B = t.A + S;
+    t.indptr = reinterpret_cast<int32_t *>(t.B + S);
+    t.adapter = t.indptr + S + 1;
+    t.rank = t.adapter + S;
+    t.scale = reinterpret_cast<float *>(t.rank + S);
+    return t;
+}
+
 static int esize_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 
 static bool elem_aligned(const void *p, int es)
@@ -44,18 +65,30 @@ static bool elem_aligned(const void *p, int es)
     return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(es)) == 0;
 }
 
-// Validates a host plan buffer and returns its header.
+// Validates a host buffer holding a built plan and returns its header.
 static int check_plan(const void *plan_host, const lora_plan_header **out)
 {
-    if (!plan_host) return fail(LORA_ERR_ARG, "plan_host is NULL");
+    if (!plan_host) return fail(LORA_ERR_ARG, "the segments' host buffer is NULL");
     if (reinterpret_cast<uintptr_t>(plan_host) & 7u)
-        return fail(LORA_ERR_ALIGN, "plan_host is not 8-byte aligned");
+        return fail(LORA_ERR_ALIGN, "the segments' host buffer is not 8-byte aligned");
     const auto *h = static_cast<const lora_plan_header *>(plan_host);
     if (h->magic != LORA_PLAN_MAGIC) return fail(LORA_ERR_PLAN, "plan buffer holds no built plan");
     if (h->num_segments < 0 || h->num_sorted < 0 || h->num_blocks < 0 ||
         h->num_sorted > h->num_tokens || h->max_rank < 0 || h->max_rank > LORA_MAX_RANK)
         return fail(LORA_ERR_PLAN, "plan header is inconsistent");
     *out = h;
+    return LORA_OK;
+}
+
+// Validates a device segments struct: the header comes from its host copy
+// (launch geometry), *dev is the device copy the kernels read.
+static int check_segments(const lora_segments *seg, const lora_plan_header **h, const char **dev)
+{
+    if (!seg) return fail(LORA_ERR_ARG, "segments is NULL");
+    if (!seg->host) return fail(LORA_ERR_ARG, "segments have no host copy (not uploaded with lora_segments_upload)");
+    const int st = check_plan(seg->host, h);
+    if (st) return st;
+    *dev = static_cast<const char *>(seg->buf);
     return LORA_OK;
 }
 
@@ -183,15 +216,15 @@ int64_t lora_adapter_numel(int32_t r, int32_t d_in, int32_t d_out)
     return int64_t(r) * (int64_t(d_in) + int64_t(d_out));
 }
 
-size_t lora_plan_bytes(int32_t capacity)
+size_t lora_segments_bytes(int32_t capacity)
 {
     if (capacity < 0) capacity = 0;
     const size_t c = size_t(capacity);
     // header, segment descriptors (S <= T), block descriptors (blocks <= T'),
-    // perm (T), chunk descriptors (chunks <= T'), segment index (T' <= T),
-    // alignment slack
+    // perm (T), chunk descriptors (chunks <= T'), segment index (T' <= T), the
+    // segment arrays (S <= T), alignment slack
     return sizeof(lora_plan_header) + sizeof(lora_seg_desc) * c + 128 + sizeof(lora_blk_desc) * c + 4 * c + 64 +
-           sizeof(lora_chunk_desc) * c + 4 * c + 16;
+           sizeof(lora_chunk_desc) * c + 4 * c + 16 + soa_bytes(capacity) + 16;
 }
 
 size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int32_t max_rank)
@@ -211,17 +244,19 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     }
 }
 
-int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uint64_t *pool_A,
-                    const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha, void *plan,
-                    size_t plan_bytes)
+// The plan of one batch in `plan` (plan_bytes >= segments_bytes(T)): see the
+// layout in the public header.  Pure host work, O(T + n_adapters).
+static int build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uint64_t *pool_A,
+                      const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha, void *plan,
+                      size_t plan_bytes)
 {
-    clear_error();
     if (T < 0) return fail(LORA_ERR_ARG, "T %d < 0", T);
     if (n_adapters < 0) return fail(LORA_ERR_ARG, "n_adapters %d < 0", n_adapters);
     if (!plan) return fail(LORA_ERR_ARG, "plan is NULL");
-    if (reinterpret_cast<uintptr_t>(plan) & 7u) return fail(LORA_ERR_ALIGN, "plan is not 8-byte aligned");
-    if (plan_bytes < lora_plan_bytes(T))
-        return fail(LORA_ERR_WORKSPACE, "plan buffer %zu B < %zu B needed", plan_bytes, lora_plan_bytes(T));
+    if (reinterpret_cast<uintptr_t>(plan) & 15u) return fail(LORA_ERR_ALIGN, "buffer is not 16-byte aligned");
+    if (plan_bytes < lora_segments_bytes(T))
+        return fail(LORA_ERR_WORKSPACE, "buffer of %zu B < %zu B needed for %d tokens", plan_bytes,
+                    lora_segments_bytes(T), T);
     if (T > 0 && !ids) return fail(LORA_ERR_ARG, "ids is NULL");
 
     // Count tokens per adapter; reject ids outside [-1, n_adapters).
@@ -272,7 +307,8 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
     h->perm_offset = align16(h->blk_offset + sizeof(lora_blk_desc) * size_t(nblk));
     h->chunk_offset = (h->perm_offset + 4 * size_t(T) + 63) & ~size_t(63);
     h->segidx_offset = align16(h->chunk_offset + sizeof(lora_chunk_desc) * size_t(nchunk));
-    h->bytes_used = h->segidx_offset + 4 * size_t(sorted);
+    h->soa_offset = align16(h->segidx_offset + 4 * size_t(sorted));
+    h->bytes_used = h->soa_offset + soa_bytes(S);
 
     auto *seg = reinterpret_cast<lora_seg_desc *>(base + h->seg_offset);
     auto *blk = reinterpret_cast<lora_blk_desc *>(base + h->blk_offset);
@@ -347,74 +383,138 @@ int lora_build_plan(int32_t T, const int32_t *ids, int32_t n_adapters, const uin
         }
         c0 += (d.len + LORA_PLAN_CHUNK_ROWS - 1) / LORA_PLAN_CHUNK_ROWS;
     }
+    // the segment table as arrays (seg_A, seg_B, seg_indptr, seg_adapter,
+    // seg_rank, seg_scale)
+    SoA t = soa_at(base + h->soa_offset, S);
+    for (int32_t si = 0; si < S; ++si) {
+        t.A[si] = seg[si].A;
+        t.B[si] = seg[si].B;
+        t.indptr[si] = seg[si].start;
+        t.adapter[si] = seg[si].adapter;
+        t.rank[si] = seg[si].rank;
+        t.scale[si] = seg[si].scale;
+    }
+    t.indptr[S] = sorted;
     h->magic = LORA_PLAN_MAGIC;
     return LORA_OK;
 }
 
-int lora_plan_upload(const void *plan_host, void *plan_dev, size_t plan_dev_bytes, void *stream)
+// Pointer and count fields of a segments struct bound to `buf` holding the plan.
+static void fill_segments(lora_segments *s, char *buf, const lora_plan_header *h)
+{
+    const SoA t = soa_at(buf + h->soa_offset, h->num_segments);
+    s->num_segments = h->num_segments;
+    s->num_tokens = h->num_sorted;
+    s->max_rank = h->max_rank;
+    s->batch_tokens = h->num_tokens;
+    s->perm = reinterpret_cast<int32_t *>(buf + h->perm_offset);
+    s->seg_indptr = t.indptr;
+    s->seg_adapter = t.adapter;
+    s->seg_rank = t.rank;
+    s->seg_A = t.A;
+    s->seg_B = t.B;
+    s->seg_scale = t.scale;
+}
+
+int lora_segments_bind(void *buf, int32_t capacity, lora_segments *out)
 {
     clear_error();
-    const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
-    if (st) return st;
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
-    if (!aligned16(plan_dev)) return fail(LORA_ERR_ALIGN, "plan_dev is not 16-byte aligned");
-    if (plan_dev_bytes < h->bytes_used)
-        return fail(LORA_ERR_WORKSPACE, "plan_dev %zu B < %llu B used", plan_dev_bytes,
-                    (unsigned long long)h->bytes_used);
-    hipError_t e = hipMemcpyAsync(plan_dev, plan_host, h->bytes_used, hipMemcpyHostToDevice,
-                                  static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(LORA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    if (!out) return fail(LORA_ERR_ARG, "out is NULL");
+    if (!buf) return fail(LORA_ERR_ARG, "buf is NULL");
+    if (capacity < 0) return fail(LORA_ERR_ARG, "capacity %d < 0", capacity);
+    if (!aligned16(buf)) return fail(LORA_ERR_ALIGN, "buf is not 16-byte aligned");
+    std::memset(out, 0, sizeof *out);
+    out->capacity = capacity;
+    out->buf = buf;
     return LORA_OK;
 }
 
-int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
-                     const void *plan_dev, float *v, int64_t ldv, void *ws, size_t ws_bytes)
+int lora_build_segments(int32_t T, const int32_t *ids, int32_t n_adapters, const uint64_t *pool_A,
+                        const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                        lora_segments *out_host)
 {
-    (void)ws;
-    (void)ws_bytes;
     clear_error();
-    const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
+    if (!out_host || !out_host->buf) return fail(LORA_ERR_ARG, "segments are not bound to a buffer");
+    if (T > out_host->capacity)
+        return fail(LORA_ERR_WORKSPACE, "batch of %d tokens > capacity %d", T, out_host->capacity);
+    out_host->host = nullptr;
+    const int st = build_plan(T, ids, n_adapters, pool_A, pool_B, pool_rank, pool_alpha, out_host->buf,
+                              lora_segments_bytes(out_host->capacity));
     if (st) return st;
-    if ((st = check_dtype(dtype))) return st;
-    if (h->num_sorted == 0) return LORA_OK;
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
-    ShrinkArgs sa{};
-    if ((st = make_shrink_args(dtype, x, ldx, d_in, v, ldv, h->max_rank, &sa))) return st;
-    return launch_sgmv_shrink(static_cast<hipStream_t>(stream), sa, PlanView{h, static_cast<const char *>(plan_dev)});
+    char *buf = static_cast<char *>(out_host->buf);
+    fill_segments(out_host, buf, reinterpret_cast<const lora_plan_header *>(buf));
+    return LORA_OK;
 }
 
-int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv, const void *plan_host,
-                     const void *plan_dev, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
+int lora_segments_upload(const lora_segments *host, lora_segments *dev, void *stream)
+{
+    clear_error();
+    if (!host || !dev) return fail(LORA_ERR_ARG, "host or dev is NULL");
+    const lora_plan_header *h = nullptr;
+    int st = check_plan(host->buf, &h);
+    if (st) return st;
+    if (!dev->buf) return fail(LORA_ERR_ARG, "dev is not bound to a buffer");
+    if (dev->buf == host->buf) return fail(LORA_ERR_ARG, "dev and host are bound to the same buffer");
+    if (lora_segments_bytes(dev->capacity) < h->bytes_used)
+        return fail(LORA_ERR_WORKSPACE, "dev holds %d tokens; the batch has %d", dev->capacity, h->num_tokens);
+    hipError_t e = hipMemcpyAsync(dev->buf, host->buf, h->bytes_used, hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LORA_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    fill_segments(dev, static_cast<char *>(dev->buf), h);
+    dev->host = host->buf;
+    return LORA_OK;
+}
+
+int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const lora_segments *seg,
+                     float *v, int64_t ldv, void *ws, size_t ws_bytes)
 {
     (void)ws;
     (void)ws_bytes;
     clear_error();
     const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
+    const char *plan_dev = nullptr;
+    int st = check_segments(seg, &h, &plan_dev);
     if (st) return st;
     if ((st = check_dtype(dtype))) return st;
     if (h->num_sorted == 0) return LORA_OK;
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
+    ShrinkArgs sa{};
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, v, ldv, h->max_rank, &sa))) return st;
+    return launch_sgmv_shrink(static_cast<hipStream_t>(stream), sa, PlanView{h, plan_dev});
+}
+
+int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv, const lora_segments *seg, void *y,
+                     int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
+{
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    const lora_plan_header *h = nullptr;
+    const char *plan_dev = nullptr;
+    int st = check_segments(seg, &h, &plan_dev);
+    if (st) return st;
+    if ((st = check_dtype(dtype))) return st;
+    if (h->num_sorted == 0) return LORA_OK;
+    if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     // B rows are r_s elements long: vector loads of 4 elements need r % 4 == 0 for
     // every segment; decided per segment on the device, so pass true here.
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
     ExpandArgs ea{};
     if ((st = make_expand_args(dtype, v, ldv, h->max_rank, y, ldy, d_out, true, &ea))) return st;
-    return launch_sgmv_expand(static_cast<hipStream_t>(stream), ea, PlanView{h, static_cast<const char *>(plan_dev)});
+    return launch_sgmv_expand(static_cast<hipStream_t>(stream), ea, PlanView{h, plan_dev});
 }
 
-int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
-              const void *plan_dev, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
+int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const lora_segments *seg, void *y,
+              int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes)
 {
     clear_error();
     const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
+    const char *plan_dev = nullptr;
+    int st = check_segments(seg, &h, &plan_dev);
     if (st) return st;
     if ((st = check_dtype(dtype))) return st;
     if (h->num_sorted == 0) return LORA_OK;
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
     const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
@@ -425,7 +525,7 @@ int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
     ExpandArgs ea{};
     if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
         return st;
-    return launch_sgmv(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, static_cast<const char *>(plan_dev)}, ws);
+    return launch_sgmv(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, plan_dev}, ws);
 }
 
 int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in, const int32_t *ids_dev,
@@ -480,19 +580,20 @@ static int check_pages(const void *pages, int64_t page_bytes, int *shift)
     return LORA_OK;
 }
 
-int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *plan_host,
-                    const void *plan_dev, const void *pages, int64_t page_bytes, void *y, int64_t ldy,
-                    int32_t d_out, void *ws, size_t ws_bytes)
+int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const lora_segments *seg,
+                    const void *pages, int64_t page_bytes, void *y, int64_t ldy, int32_t d_out, void *ws,
+                    size_t ws_bytes)
 {
     clear_error();
     const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
+    const char *plan_dev = nullptr;
+    int st = check_segments(seg, &h, &plan_dev);
     if (st) return st;
     if ((st = check_dtype(dtype))) return st;
     int shift = 0;
     if ((st = check_pages(pages, page_bytes, &shift))) return st;
     if (h->num_sorted == 0) return LORA_OK;
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
     const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
@@ -504,7 +605,7 @@ int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t
     if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
         return st;
     return launch_sgmv_paged(static_cast<hipStream_t>(stream), sa, ea,
-                             PlanView{h, static_cast<const char *>(plan_dev)}, ws, pages, shift);
+                             PlanView{h, plan_dev}, ws, pages, shift);
 }
 
 int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,
@@ -543,7 +644,8 @@ size_t lora_sgmv_grouped_workspace_bytes(const lora_sgmv_proj *projs, int32_t n_
     size_t total = 0;
     for (int p = 0; p < n_proj; ++p) {
         const lora_plan_header *h = nullptr;
-        if (check_plan(projs[p].plan_host, &h)) return 0;
+        const char *dev = nullptr;
+        if (check_segments(projs[p].seg, &h, &dev)) return 0;
         clear_error();
         total += grouped_region_bytes(h->num_sorted, projs[p].d_in < 1 ? 1 : projs[p].d_in,
                                       h->max_rank < 1 ? 1 : h->max_rank);
@@ -565,17 +667,18 @@ int lora_sgmv_grouped(void *stream, int dtype, const lora_sgmv_proj *projs, int3
     for (int p = 0; p < n_proj; ++p) {
         const lora_sgmv_proj &q = projs[p];
         const lora_plan_header *h = nullptr;
-        if ((st = check_plan(q.plan_host, &h))) return st;
+        const char *plan_dev = nullptr;
+        if ((st = check_segments(q.seg, &h, &plan_dev))) return st;
         for (int o = 0; o < p; ++o)
             if (projs[o].y == q.y) return fail(LORA_ERR_ARG, "projections %d and %d write the same y", o, p);
-        g[p].plan = PlanView{h, static_cast<const char *>(q.plan_dev)};
+        g[p].plan = PlanView{h, plan_dev};
         g[p].ws = nullptr;
         if (h->num_sorted == 0) {
             g[p].sa = ShrinkArgs{};
             g[p].ea = ExpandArgs{};
             continue;
         }
-        if (!q.plan_dev) return fail(LORA_ERR_ARG, "projection %d: plan_dev is NULL", p);
+        if (!plan_dev) return fail(LORA_ERR_ARG, "projection %d: the segments' device buffer is NULL", p);
         if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "projection %d: plan has %d blocks", p, h->num_blocks);
         need += grouped_region_bytes(h->num_sorted, q.d_in < 1 ? 1 : q.d_in, h->max_rank);
     }
@@ -699,12 +802,12 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
 }
 
 int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *W0,
-                      int32_t d_out, const void *plan_host, const void *plan_dev, void *y, int64_t ldy, void *ws,
-                      size_t ws_bytes)
+                      int32_t d_out, const lora_segments *seg, void *y, int64_t ldy, void *ws, size_t ws_bytes)
 {
     clear_error();
     const lora_plan_header *h = nullptr;
-    int st = check_plan(plan_host, &h);
+    const char *plan_dev = nullptr;
+    int st = check_segments(seg, &h, &plan_dev);
     if (st) return st;
     if ((st = check_dtype(dtype))) return st;
     if (dtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "the fused entry takes bf16 only");
@@ -715,7 +818,7 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     if (ldx < d_in || ldy < d_out) return fail(LORA_ERR_ARG, "row pitch smaller than the row");
     if (!aligned16(x) || !aligned16(W0) || !aligned16(y) || (ldx * 2) % 16 || (ldy * 2) % 16 || (d_in * 2) % 16)
         return fail(LORA_ERR_ALIGN, "fused entry needs 16-byte aligned x, W0, y rows and d_in %% 8 == 0");
-    if (!plan_dev) return fail(LORA_ERR_ARG, "plan_dev is NULL");
+    if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     const size_t need = fused_workspace_bytes(T, d_in, h->max_rank < 1 ? 1 : h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -733,7 +836,7 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     ea.vec_b = true;
     ea.vec_y = true;
     return launch_fused_linear(static_cast<hipStream_t>(stream), sa, W0, ea,
-                               PlanView{h, static_cast<const char *>(plan_dev)}, ws);
+                               PlanView{h, plan_dev}, ws);
 }
 
 } // extern "C"

@@ -26,7 +26,7 @@ int main(void)
     CHECK(lora_workspace_bytes(LORA_OP_SGMV_SHRINK, 8, 64, 64, 8) == 0);
     CHECK(lora_workspace_bytes(99, 8, 64, 64, 8) == (size_t)-1);
 
-    /* plan of 6 tokens over 3 adapters: ids 2, 0, -1, 2, 0, 2 */
+    /* segments of 6 tokens over 3 adapters: ids 2, 0, -1, 2, 0, 2 */
     const int32_t T = 6, N = 3;
     const int32_t ids[6] = {2, 0, -1, 2, 0, 2};
     uint64_t pool_A[3], pool_B[3];
@@ -36,25 +36,35 @@ int main(void)
         pool_A[i] = 0x7f0000000000ull + 0x10000ull * (uint64_t)i;
         pool_B[i] = 0x7f0000008000ull + 0x10000ull * (uint64_t)i;
     }
-    const size_t bytes = lora_plan_bytes(T);
-    uint64_t *plan = (uint64_t *)calloc((bytes + 7) / 8, 8);
-    CHECK(plan != NULL);
-    CHECK(lora_build_plan(T, ids, N, pool_A, pool_B, rank, alpha, plan, bytes) == LORA_OK);
-    const lora_plan_header *h = (const lora_plan_header *)plan;
-    CHECK(h->magic == LORA_PLAN_MAGIC);
-    CHECK(h->num_tokens == 6 && h->num_sorted == 5 && h->num_segments == 2 && h->max_rank == 16);
-    const lora_seg_desc *seg = (const lora_seg_desc *)((const char *)plan + h->seg_offset);
-    const int32_t *perm = (const int32_t *)((const char *)plan + h->perm_offset);
+    const size_t bytes = lora_segments_bytes(T);
+    uint64_t *buf = (uint64_t *)calloc((bytes + 15) / 8 + 2, 8);
+    CHECK(buf != NULL);
+    void *aligned = (void *)(((uintptr_t)buf + 15) & ~(uintptr_t)15);
+    lora_segments sg;
+    CHECK(lora_segments_bind(aligned, T, &sg) == LORA_OK);
+    CHECK(lora_build_segments(T, ids, N, pool_A, pool_B, rank, alpha, &sg) == LORA_OK);
     /* ascending adapter id, original order inside a segment, then the unadapted token */
-    CHECK(seg[0].adapter == 0 && seg[0].start == 0 && seg[0].len == 2 && seg[0].scale == 8.f / 4.f);
-    CHECK(seg[1].adapter == 2 && seg[1].start == 2 && seg[1].len == 3 && seg[1].scale == 32.f / 16.f);
+    CHECK(sg.num_segments == 2 && sg.num_tokens == 5 && sg.batch_tokens == 6 && sg.max_rank == 16);
+    CHECK(sg.seg_indptr[0] == 0 && sg.seg_indptr[1] == 2 && sg.seg_indptr[2] == 5);
+    CHECK(sg.seg_adapter[0] == 0 && sg.seg_adapter[1] == 2);
+    CHECK(sg.seg_rank[0] == 4 && sg.seg_rank[1] == 16);
+    CHECK(sg.seg_A[0] == pool_A[0] && sg.seg_A[1] == pool_A[2] && sg.seg_B[1] == pool_B[2]);
+    CHECK(sg.seg_scale[0] == 8.f / 4.f && sg.seg_scale[1] == 32.f / 16.f);
     const int32_t want[6] = {1, 4, 0, 3, 5, 2};
-    for (int i = 0; i < 6; ++i) CHECK(perm[i] == want[i]);
+    for (int i = 0; i < 6; ++i) CHECK(sg.perm[i] == want[i]);
+    /* the same segments through the buffer's own layout */
+    const lora_plan_header *h = (const lora_plan_header *)aligned;
+    CHECK(h->magic == LORA_PLAN_MAGIC && h->num_sorted == 5 && h->num_segments == 2);
+    const lora_seg_desc *seg = (const lora_seg_desc *)((const char *)aligned + h->seg_offset);
+    CHECK(seg[1].adapter == 2 && seg[1].start == 2 && seg[1].len == 3);
 
     /* host-side rejections */
     const int32_t bad[2] = {0, 3};
-    CHECK(lora_build_plan(2, bad, N, pool_A, pool_B, rank, alpha, plan, bytes) == LORA_ERR_ADAPTER_ID);
-    CHECK(lora_build_plan(T, ids, N, pool_A, pool_B, rank, alpha, plan, 16) == LORA_ERR_WORKSPACE);
+    CHECK(lora_build_segments(2, bad, N, pool_A, pool_B, rank, alpha, &sg) == LORA_ERR_ADAPTER_ID);
+    lora_segments small;
+    CHECK(lora_segments_bind(aligned, 2, &small) == LORA_OK);
+    CHECK(lora_build_segments(T, ids, N, pool_A, pool_B, rank, alpha, &small) == LORA_ERR_WORKSPACE);
+    CHECK(lora_segments_bind((char *)aligned + 4, T, &small) == LORA_ERR_ALIGN);
     CHECK(lora_profile_launches(NULL, NULL, -1) == LORA_ERR_ARG);
 
     /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection
@@ -106,7 +116,7 @@ int main(void)
     CHECK(lora_page_alloc_give(pa, fr + 1, 2) == LORA_OK && lora_page_alloc_free_count(pa) == 4);
     CHECK(lora_page_alloc_give(pa, fr + 1, 1) == LORA_ERR_ARG);
     lora_page_alloc_destroy(pa);
-    free(plan);
+    free(buf);
     printf("ok\n");
     return 0;
 }

@@ -1,5 +1,5 @@
 """The C-ABI library on the CPU: it loads, exports what the header declares,
-builds plans identical to the oracle's brute-force segments, and rejects bad
+builds segments identical to the oracle's brute-force segments, and rejects bad
 arguments from the host before any GPU call."""
 
 import ctypes
@@ -51,32 +51,58 @@ def test_adapter_numel_negative():
 
 
 class HostPlan:
-    """A plan in plain host memory (numpy), read back through the header layout."""
+    """Segments built into plain host memory (numpy, bound with
+    lora_segments_bind), read back through the header layout and the struct."""
 
     def __init__(self, capacity):
-        self.nbytes = B.lora_plan_bytes(capacity)
-        self.buf = np.zeros((self.nbytes + 7) // 8, dtype=np.uint64)
+        self.capacity = capacity
+        self.nbytes = B.lora_segments_bytes(capacity)
+        self.raw = np.zeros((self.nbytes + 32) // 8, dtype=np.uint64)
+        self.off = (-self.raw.ctypes.data) % 16  # 16-byte aligned start
+        self.h = B.LoraSegments()
+        assert B.lora_segments_bind(self.ptr, capacity, ctypes.addressof(self.h)) == 0
+        self._devs = []
 
     @property
     def ptr(self):
-        return self.buf.ctypes.data
+        return self.raw.ctypes.data + self.off
+
+    @property
+    def seg(self):
+        return ctypes.addressof(self.h)
+
+    def dev(self, buf=FAKE_BASE + 0x1000000, host=None):
+        """Address of a device-style struct for argument checks (no GPU call):
+        the host copy is this buffer (or `host`), the device buffer `buf`."""
+        d = B.LoraSegments()
+        ctypes.memmove(ctypes.addressof(d), ctypes.addressof(self.h), ctypes.sizeof(d))
+        d.buf = buf
+        d.host = self.ptr if host is None else host
+        self._devs.append(d)
+        return ctypes.addressof(d)
+
+    def _u8(self):
+        return self.raw.view(np.uint8)[self.off: self.off + self.nbytes]
 
     def header(self):
-        h = B.plan_header(self.buf.view(np.uint8))
+        h = B.plan_header(self._u8())
         return dict(magic=h["magic"], T=h["num_tokens"], Tp=h["num_sorted"], S=h["num_segments"],
                     nblk=h["num_blocks"], max_rank=h["max_rank"], max_len=h["max_len"], seg=h["seg_offset"],
                     blk=h["blk_offset"], perm=h["perm_offset"], used=h["bytes_used"], nchunk=h["num_chunks"],
                     chunk=h["chunk_offset"])
 
     def arrays(self):
-        h = B.plan_header(self.buf.view(np.uint8))
-        a = B.plan_arrays(self.buf.view(np.uint8), h)
+        h = B.plan_header(self._u8())
+        a = B.plan_arrays(self._u8(), h)
         return a["desc"], a["blocks"], a["perm"], a["chunks"]
 
     def tail(self):
-        h = B.plan_header(self.buf.view(np.uint8))
-        a = B.plan_arrays(self.buf.view(np.uint8), h)
+        h = B.plan_header(self._u8())
+        a = B.plan_arrays(self._u8(), h)
         return a["unadapted"], a["segidx"], h
+
+    def table(self):
+        return B.segment_table(self.h)
 
 
 def make_tables(N, rng, ranks=None):
@@ -89,11 +115,11 @@ def make_tables(N, rng, ranks=None):
     return A, Bt, ranks, alpha
 
 
-def build(ids, N, A, Bt, ranks, alpha, plan=None, nbytes=None):
+def build(ids, N, A, Bt, ranks, alpha, plan=None):
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     plan = plan or HostPlan(len(ids))
-    st = B.lora_build_plan(len(ids), ids.ctypes.data if len(ids) else None, N, A.ctypes.data, Bt.ctypes.data,
-                           ranks.ctypes.data, alpha.ctypes.data, plan.ptr, nbytes or plan.nbytes)
+    st = B.lora_build_segments(len(ids), ids.ctypes.data if len(ids) else None, N, A.ctypes.data, Bt.ctypes.data,
+                               ranks.ctypes.data, alpha.ctypes.data, plan.seg)
     return st, plan
 
 
@@ -118,6 +144,14 @@ def test_plan_matches_oracle_segments(T, N, none_p, seed):
     assert np.array_equal(desc["len"], np.diff(indptr_o))
     assert np.array_equal(desc["rank"], ranks[adapter_o])
     assert np.array_equal(desc["A"], A[adapter_o]) and np.array_equal(desc["B"], Bt[adapter_o])
+    # the segment table of the struct (the boundary's outputs)
+    t = plan.table()
+    assert plan.h.num_segments == len(adapter_o) and plan.h.num_tokens == len(perm_o) and plan.h.batch_tokens == T
+    assert plan.h.max_rank == (int(ranks[adapter_o].max()) if len(adapter_o) else 0)
+    assert np.array_equal(t["perm"], perm_o) and np.array_equal(t["seg_indptr"], indptr_o)
+    assert np.array_equal(t["seg_adapter"], adapter_o) and np.array_equal(t["seg_rank"], ranks[adapter_o])
+    assert np.array_equal(t["seg_A"], A[adapter_o]) and np.array_equal(t["seg_B"], Bt[adapter_o])
+    assert np.array_equal(t["seg_scale"], (alpha[adapter_o] / ranks[adapter_o].astype(np.float32)).astype(np.float32))
     # scale = alpha / rank in fp32 (correctly rounded division)
     assert np.array_equal(desc["scale"], (alpha[adapter_o] / ranks[adapter_o].astype(np.float32)).astype(np.float32))
     nb = (np.diff(indptr_o) + 15) // 16
@@ -156,7 +190,9 @@ def test_plan_matches_oracle_segments(T, N, none_p, seed):
     assert np.array_equal(rest, np.nonzero(ids < 0)[0])
     assert np.array_equal(segidx, np.repeat(np.arange(len(adapter_o)), np.diff(indptr_o)))
     assert hh["segidx_offset"] % 16 == 0 and hh["segidx_offset"] >= hh["chunk_offset"] + 320 * h["nchunk"]
-    assert hh["bytes_used"] == hh["segidx_offset"] + 4 * h["Tp"]
+    S = len(adapter_o)
+    assert hh["soa_offset"] % 16 == 0 and hh["soa_offset"] >= hh["segidx_offset"] + 4 * h["Tp"]
+    assert hh["bytes_used"] == hh["soa_offset"] + 16 * S + 4 * (S + 1) + 12 * S
 
 
 def test_plan_errors():
@@ -172,16 +208,35 @@ def test_plan_errors():
     A2 = A.copy()
     A2[1] += 8
     assert build([1], 4, A2, Bt, ranks, alpha)[0] == -4  # misaligned adapter address
-    plan = HostPlan(4)
-    assert build(ok_ids, 4, A, Bt, ranks, alpha, plan=plan, nbytes=64)[0] == -6  # buffer too small
+    small = HostPlan(2)
+    assert build(ok_ids, 4, A, Bt, ranks, alpha, plan=small)[0] == -6  # batch larger than the capacity
     assert "ids[1]" in (build([0, 9], 4, A, Bt, ranks, alpha)[0] and B.last_error())
+    plan = HostPlan(4)
     lib = B.load()
-    assert lib.lora_build_plan(3, None, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data, alpha.ctypes.data,
-                               plan.ptr, plan.nbytes) == -1  # NULL ids
-    assert lib.lora_build_plan(-1, None, 4, None, None, None, None, plan.ptr, plan.nbytes) == -1
-    assert lib.lora_build_plan(2, ok_ids.ctypes.data, 4, None, None, None, None, plan.ptr, plan.nbytes) == -1
-    assert lib.lora_build_plan(2, ok_ids.ctypes.data, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data,
-                               alpha.ctypes.data, plan.ptr + 4, plan.nbytes) == -4  # misaligned plan buffer
+    assert lib.lora_build_segments(3, None, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data, alpha.ctypes.data,
+                                   plan.seg) == -1  # NULL ids
+    assert lib.lora_build_segments(-1, None, 4, None, None, None, None, plan.seg) == -1
+    assert lib.lora_build_segments(2, ok_ids.ctypes.data, 4, None, None, None, None, plan.seg) == -1
+    assert lib.lora_build_segments(2, ok_ids.ctypes.data, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data,
+                                   alpha.ctypes.data, None) == -1  # no struct
+    unbound = B.LoraSegments()
+    assert lib.lora_build_segments(2, ok_ids.ctypes.data, 4, A.ctypes.data, Bt.ctypes.data, ranks.ctypes.data,
+                                   alpha.ctypes.data, ctypes.addressof(unbound)) == -1  # not bound
+    s2 = B.LoraSegments()
+    assert lib.lora_segments_bind(plan.ptr + 4, 4, ctypes.addressof(s2)) == -4  # misaligned buffer
+    assert lib.lora_segments_bind(None, 4, ctypes.addressof(s2)) == -1
+    assert lib.lora_segments_bind(plan.ptr, -1, ctypes.addressof(s2)) == -1
+    # upload checks before any copy: unbound device struct, the same buffer twice, too small a device buffer
+    st, full = build(ok_ids, 4, A, Bt, ranks, alpha)
+    assert st == 0
+    assert lib.lora_segments_upload(full.seg, ctypes.addressof(unbound), None) == -1
+    same = B.LoraSegments()
+    assert lib.lora_segments_bind(full.ptr, 4, ctypes.addressof(same)) == 0
+    assert lib.lora_segments_upload(full.seg, ctypes.addressof(same), None) == -1
+    tiny = B.LoraSegments()
+    assert lib.lora_segments_bind(FX, 1, ctypes.addressof(tiny)) == 0
+    assert lib.lora_segments_upload(full.seg, ctypes.addressof(tiny), None) == -6
+    assert lib.lora_segments_upload(None, ctypes.addressof(tiny), None) == -1
 
 
 def _valid_plan(T=8, N=2, rank=8):
@@ -199,34 +254,34 @@ FX = 0x7F1000000000  # fake 16-byte-aligned device pointers: validation fails be
 def test_sgmv_argument_errors():
     plan = _valid_plan()
     empty = HostPlan(0)
-    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
+    assert B.lora_build_segments(0, None, 0, None, None, None, None, empty.seg) == 0
     sh = B.lora_sgmv_shrink
     # bad dtype
-    assert sh(None, 7, FX, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -5
+    assert sh(None, 7, FX, 256, 256, plan.dev(), FX, 8, None, 0) == -5
     # NULL plan / plan without magic
-    assert sh(None, 1, FX, 256, 256, None, FX, FX, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 256, None, FX, 8, None, 0) == -1
     junk = np.zeros(64, dtype=np.uint64)
-    assert sh(None, 1, FX, 256, 256, junk.ctypes.data, FX, FX, 8, None, 0) == -8
+    assert sh(None, 1, FX, 256, 256, plan.dev(host=junk.ctypes.data), FX, 8, None, 0) == -8
     # an empty batch is a successful no-op, even with NULL buffers
-    assert sh(None, 1, None, 0, 0, empty.ptr, None, None, 0, None, 0) == 0
-    assert B.lora_sgmv_expand(None, 1, None, 0, empty.ptr, None, None, 0, 0, None, 0) == 0
-    # NULL x, v, plan_dev
-    assert sh(None, 1, None, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -1
-    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, None, 8, None, 0) == -1
-    assert sh(None, 1, FX, 256, 256, plan.ptr, None, FX, 8, None, 0) == -1
+    assert sh(None, 1, None, 0, 0, empty.dev(None), None, 0, None, 0) == 0
+    assert B.lora_sgmv_expand(None, 1, None, 0, empty.dev(None), None, 0, 0, None, 0) == 0
+    # NULL x, v, device buffer of the segments
+    assert sh(None, 1, None, 256, 256, plan.dev(), FX, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 256, plan.dev(), None, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 256, plan.dev(None), FX, 8, None, 0) == -1
     # ldv smaller than the plan's max rank; ldv not a multiple of 4; v misaligned
-    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX, 4, None, 0) == -2
-    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX, 10, None, 0) == -4
-    assert sh(None, 1, FX, 256, 256, plan.ptr, FX, FX + 4, 8, None, 0) == -4
+    assert sh(None, 1, FX, 256, 256, plan.dev(), FX, 4, None, 0) == -2
+    assert sh(None, 1, FX, 256, 256, plan.dev(), FX, 10, None, 0) == -4
+    assert sh(None, 1, FX, 256, 256, plan.dev(), FX + 4, 8, None, 0) == -4
     # x not aligned to its element size; ldx < d_in; d_in < 1
-    assert sh(None, 1, FX + 1, 256, 256, plan.ptr, FX, FX, 8, None, 0) == -4
-    assert sh(None, 1, FX, 100, 256, plan.ptr, FX, FX, 8, None, 0) == -1
-    assert sh(None, 1, FX, 256, 0, plan.ptr, FX, FX, 8, None, 0) == -1
+    assert sh(None, 1, FX + 1, 256, 256, plan.dev(), FX, 8, None, 0) == -4
+    assert sh(None, 1, FX, 100, 256, plan.dev(), FX, 8, None, 0) == -1
+    assert sh(None, 1, FX, 256, 0, plan.dev(), FX, 8, None, 0) == -1
     ex = B.lora_sgmv_expand
-    assert ex(None, 1, FX, 8, plan.ptr, FX, None, 256, 256, None, 0) == -1
-    assert ex(None, 1, FX, 8, plan.ptr, FX, FX, 100, 256, None, 0) == -1
-    assert ex(None, 0, FX, 8, plan.ptr, FX, FX + 2, 256, 256, None, 0) == -4  # f32 y misaligned
-    assert ex(None, 1, FX, 2, plan.ptr, FX, FX, 256, 256, None, 0) == -2
+    assert ex(None, 1, FX, 8, plan.dev(), None, 256, 256, None, 0) == -1
+    assert ex(None, 1, FX, 8, plan.dev(), FX, 100, 256, None, 0) == -1
+    assert ex(None, 0, FX, 8, plan.dev(), FX + 2, 256, 256, None, 0) == -4  # f32 y misaligned
+    assert ex(None, 1, FX, 2, plan.dev(), FX, 256, 256, None, 0) == -2
 
 
 def test_bgmv_argument_errors():
@@ -248,11 +303,11 @@ def test_bgmv_argument_errors():
 def test_fused_argument_errors():
     plan = _valid_plan()
     f = B.lora_fused_linear
-    assert f(None, 0, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -5  # f32 not offered
-    assert f(None, 1, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 16) == -6  # workspace too small
-    assert f(None, 1, FX, 256, 256, FX, 256, plan.ptr, FX, FX, 256, None, 1 << 20) == -6
-    assert f(None, 1, FX + 2, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -4
-    assert f(None, 1, None, 256, 256, FX, 256, plan.ptr, FX, FX, 256, FX, 1 << 20) == -1
+    assert f(None, 0, FX, 256, 256, FX, 256, plan.dev(), FX, 256, FX, 1 << 20) == -5  # f32 not offered
+    assert f(None, 1, FX, 256, 256, FX, 256, plan.dev(), FX, 256, FX, 16) == -6  # workspace too small
+    assert f(None, 1, FX, 256, 256, FX, 256, plan.dev(), FX, 256, None, 1 << 20) == -6
+    assert f(None, 1, FX + 2, 256, 256, FX, 256, plan.dev(), FX, 256, FX, 1 << 20) == -4
+    assert f(None, 1, None, 256, 256, FX, 256, plan.dev(), FX, 256, FX, 1 << 20) == -1
     need = B.lora_workspace_bytes(B.LORA_OP_FUSED, 8, 256, 256, 8)
     assert need >= 8 * 16 * 4
 
@@ -262,15 +317,15 @@ def test_combined_argument_errors():
     sg = B.lora_sgmv
     need = B.lora_workspace_bytes(B.LORA_OP_SGMV, 8, 256, 256, 8)
     assert need >= 8 * 8 * 4
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need - 1) == -6
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, None, need) == -6
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX + 8, need) == -4
-    assert sg(None, 1, None, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need) == -1
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, None, 256, 256, FX, need) == -1
-    assert sg(None, 9, FX, 256, 256, plan.ptr, FX, FX, 256, 256, FX, need) == -5
+    assert sg(None, 1, FX, 256, 256, plan.dev(), FX, 256, 256, FX, need - 1) == -6
+    assert sg(None, 1, FX, 256, 256, plan.dev(), FX, 256, 256, None, need) == -6
+    assert sg(None, 1, FX, 256, 256, plan.dev(), FX, 256, 256, FX + 8, need) == -4
+    assert sg(None, 1, None, 256, 256, plan.dev(), FX, 256, 256, FX, need) == -1
+    assert sg(None, 1, FX, 256, 256, plan.dev(), None, 256, 256, FX, need) == -1
+    assert sg(None, 9, FX, 256, 256, plan.dev(), FX, 256, 256, FX, need) == -5
     empty = HostPlan(0)
-    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
-    assert sg(None, 1, None, 0, 0, empty.ptr, None, None, 0, 0, None, 0) == 0
+    assert B.lora_build_segments(0, None, 0, None, None, None, None, empty.seg) == 0
+    assert sg(None, 1, None, 0, 0, empty.dev(None), None, 0, 0, None, 0) == 0
     bg = B.lora_bgmv
     needb = B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, 4096, 4096, 16)
     # control words (256 B status block, a 64-bit flag per group and d_in
@@ -350,7 +405,7 @@ def test_grouped_sgmv_host_checks():
     plan = _valid_plan()  # T = 8, max rank 8
     projs = (B.LoraSgmvProj * 2)()
     for p in range(2):
-        projs[p] = B.LoraSgmvProj(FX, FX + 0x100000 * (p + 1), plan.ptr, FX, 256, 256, 256, 256)
+        projs[p] = B.LoraSgmvProj(FX, FX + 0x100000 * (p + 1), plan.dev(), 256, 256, 256, 256)
     one = B.lora_workspace_bytes(B.LORA_OP_SGMV, 8, 256, 256, 8)
     need = L.lora_sgmv_grouped_workspace_bytes(projs, 2)
     assert need == 2 * ((one + 255) // 256 * 256)
@@ -368,7 +423,7 @@ def test_grouped_sgmv_host_checks():
     projs[1].x = None
     assert g(None, 1, projs, 2, FX, need) == -1          # NULL x
     projs[1].x = FX
-    projs[1].plan_host = None
+    projs[1].seg = None
     assert g(None, 1, projs, 2, FX, need) != 0           # no plan
 
 
@@ -377,8 +432,8 @@ def test_grouped_sgmv_all_empty_is_noop():
     workspace needed, no GPU call."""
     L = B.load()
     empty = HostPlan(0)
-    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
+    assert B.lora_build_segments(0, None, 0, None, None, None, None, empty.seg) == 0
     projs = (B.LoraSgmvProj * 2)()
     for p in range(2):
-        projs[p] = B.LoraSgmvProj(None, FX + 0x100000 * (p + 1), empty.ptr, None, 256, 256, 256, 256)
+        projs[p] = B.LoraSgmvProj(None, FX + 0x100000 * (p + 1), empty.dev(None), 256, 256, 256, 256)
     assert L.lora_sgmv_grouped(None, 1, projs, 2, None, 0) == 0

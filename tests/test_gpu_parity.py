@@ -301,3 +301,62 @@ def test_bgmv_large_pool(T, n_pool, dtype, path):
                         d_in=256, d_out=320, seed=T + n_pool, a_std=0.05, b_std=0.05)
     check_case(prob, path, False)
     check_case(prob, path, True)
+
+
+def test_segments_boundary_end_to_end():
+    """The batch's segments through the boundary calls alone: lora_segments_bind
+    on a pinned host buffer and a device buffer, lora_build_segments,
+    lora_segments_upload, then lora_sgmv.  The device copy of the segment table
+    equals the host one (and the oracle's brute-force segments), and y matches
+    the oracle."""
+    import ctypes
+
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob = make_config(4)  # mixed ranks, Zipf ids, decode tokens and long segments
+    say("case segments boundary end to end")
+    pool = B.DevicePool.from_problem(prob)
+    T = prob.T
+    nbytes = B.lora_segments_bytes(T)
+    hbuf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hs, ds = B.LoraSegments(), B.LoraSegments()
+    assert B.lora_segments_bind(hbuf.data_ptr(), T, ctypes.addressof(hs)) == 0
+    assert B.lora_segments_bind(dbuf.data_ptr(), T, ctypes.addressof(ds)) == 0
+    ids = np.ascontiguousarray(prob.ids, dtype=np.int32)
+    assert B.lora_build_segments(T, ids.ctypes.data, pool.n_adapters, pool.addr_A.ctypes.data,
+                                 pool.addr_B.ctypes.data, pool.rank.ctypes.data, pool.alpha.ctypes.data,
+                                 ctypes.addressof(hs)) == 0, B.last_error()
+    stream = torch.cuda.current_stream()
+    assert B.lora_segments_upload(ctypes.addressof(hs), ctypes.addressof(ds), stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert (ds.num_segments, ds.num_tokens, ds.max_rank) == (hs.num_segments, hs.num_tokens, hs.max_rank)
+    assert ds.host == hbuf.data_ptr() and ds.buf == dbuf.data_ptr()
+    # the device struct's arrays, read back through their device addresses
+    dev = dbuf.cpu().numpy()
+    base = dbuf.data_ptr()
+    S, Tp = ds.num_segments, ds.num_tokens
+
+    def read(addr, dtype, n):
+        off = addr - base
+        return dev[off: off + n * np.dtype(dtype).itemsize].view(dtype)
+
+    host = B.segment_table(hs)
+    perm_o, indptr_o, adapter_o = oracle.segments(prob.ids, prob.n_adapters)
+    assert np.array_equal(read(ds.perm, np.int32, Tp), perm_o) and np.array_equal(host["perm"], perm_o)
+    assert np.array_equal(read(ds.seg_indptr, np.int32, S + 1), indptr_o)
+    assert np.array_equal(read(ds.seg_adapter, np.int32, S), adapter_o)
+    assert np.array_equal(read(ds.seg_rank, np.int32, S), prob.ranks[adapter_o])
+    assert np.array_equal(read(ds.seg_A, np.uint64, S), pool.addr_A[adapter_o])
+    assert np.array_equal(read(ds.seg_B, np.uint64, S), pool.addr_B[adapter_o])
+    assert np.array_equal(read(ds.seg_scale, np.float32, S), host["seg_scale"])
+    c = GpuCase(prob, y_init="zero")
+    ws = B.workspace(B.LORA_OP_SGMV, T, prob.d_in, prob.d_out, prob.max_rank)
+    assert B.lora_sgmv(stream.cuda_stream, B.LORA_BF16, c.x.data_ptr(), c.x.stride(0), prob.d_in,
+                       ctypes.addressof(ds), c.y.data_ptr(), c.y.stride(0), prob.d_out, ws.data_ptr(),
+                       ws.numel()) == 0, B.last_error()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.lora_forward(_with_zero_base(prob), nthreads=16)
+    assert_close(c.y_out(), y_ref, "bf16", "segments boundary")

@@ -118,14 +118,14 @@ def test_paged_call_argument_errors():
     need = B.lora_workspace_bytes(B.LORA_OP_SGMV, 8, 256, 256, 8)
     sg = L.lora_sgmv_paged
     for page, st in [(0, -1), (32, -1), (100, -1), (1 << 25, -1)]:
-        assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, page, FX, 256, 256, FX, need) == st
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, None, 16384, FX, 256, 256, FX, need) == -1
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX + 8, 16384, FX, 256, 256, FX, need) == -4
-    assert sg(None, 1, FX, 256, 256, plan.ptr, FX, FX, 16384, FX, 256, 256, FX, need - 1) == -6
-    assert sg(None, 9, FX, 256, 256, plan.ptr, FX, FX, 16384, FX, 256, 256, FX, need) == -5
+        assert sg(None, 1, FX, 256, 256, plan.dev(), FX, page, FX, 256, 256, FX, need) == st
+    assert sg(None, 1, FX, 256, 256, plan.dev(), None, 16384, FX, 256, 256, FX, need) == -1
+    assert sg(None, 1, FX, 256, 256, plan.dev(), FX + 8, 16384, FX, 256, 256, FX, need) == -4
+    assert sg(None, 1, FX, 256, 256, plan.dev(), FX, 16384, FX, 256, 256, FX, need - 1) == -6
+    assert sg(None, 9, FX, 256, 256, plan.dev(), FX, 16384, FX, 256, 256, FX, need) == -5
     empty = HostPlan(0)
-    assert B.lora_build_plan(0, None, 0, None, None, None, None, empty.ptr, empty.nbytes) == 0
-    assert sg(None, 1, None, 0, 0, empty.ptr, None, FX, 16384, None, 0, 0, None, 0) == 0
+    assert B.lora_build_segments(0, None, 0, None, None, None, None, empty.seg) == 0
+    assert sg(None, 1, None, 0, 0, empty.dev(None), FX, 16384, None, 0, 0, None, 0) == 0
     bg = L.lora_bgmv_paged
     needb = B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, 4096, 4096, 16)
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 48, FX, 4096, 4096, FX, needb) == -1
