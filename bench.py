@@ -732,6 +732,8 @@ def main():
     ap.add_argument("--rotation", type=int, default=None, help="override the number of rotated instances")
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE_BYTES",
                     help="adapters in a page pool of this page size (decode, prefill, hetero); 0 = dense pool")
+    ap.add_argument("--path", choices=["bgmv", "sgmv"], default=None,
+                    help="run the decode workload through this call (default: bgmv)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain copies of a known size (counter calibration) and exit")
     args = ap.parse_args()
@@ -762,6 +764,8 @@ def main():
         return
     k = CONFIG_OF[args.config]
     kind = {1: "sgmv", 2: "bgmv", 3: "sgmv", 4: "sgmv", 5: "fused"}[k]
+    if args.path and k == 2:
+        kind = args.path
     page = args.paged
     if page and kind == "fused":
         print("--paged applies to the SGMV/BGMV workloads, not the fused layer", file=sys.stderr)

@@ -261,7 +261,14 @@ int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
  * expand (same section): y[perm[p], :] += scale_s (x[perm[p], :] A_s) B_s.
  * The low-rank intermediate stays in the workspace as fp32 partial sums over
  * slices of d_in (summed in a fixed order by the expand, so results are
- * reproducible run to run).  Two kernel launches on `stream`.
+ * reproducible run to run).  Small plans (about one round of resident
+ * workgroups) with x and y rows 16-byte aligned, d_out % 16 == 0 and every
+ * rank <= 32 run in one kernel launch: the shrink workgroups, then the expand
+ * workgroups of every (64-row chunk, 256 columns), which wait for their
+ * chunk's partial sums through launch-keyed flags in the workspace (as
+ * lora_bgmv).  Larger plans run as two launches.  Both forms give the same
+ * result.  The int32 at the start of the workspace is the same sticky status
+ * word as lora_bgmv's.
  * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_SGMV, T, d_in, d_out, max_rank)
  * with T >= seg->num_tokens and max_rank >= seg->max_rank.
  * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */

@@ -237,7 +237,8 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_BGMV_EXPAND: return 0;
     case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     case LORA_OP_SGMV:
-        return combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
+        return sgmv_ctl_bytes(T < 0 ? 0 : T) +
+               combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     case LORA_OP_BGMV:
         return bgmv_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     default: return size_t(-1);
@@ -516,16 +517,19 @@ int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
     if (h->num_sorted == 0) return LORA_OK;
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
-    const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    // control words (status, a flag per block and slice), then the partials
+    const size_t ctl_bytes = sgmv_ctl_bytes(h->num_blocks);
+    const size_t need = ctl_bytes + combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + ctl_bytes);
     ShrinkArgs sa{};
-    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, h->max_rank, &sa))) return st;
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, part, ldw, h->max_rank, &sa))) return st;
     ExpandArgs ea{};
-    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
-        return st;
-    return launch_sgmv(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, plan_dev}, ws);
+    if ((st = make_expand_args(dtype, part, ldw, h->max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_sgmv(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, plan_dev}, part,
+                       static_cast<int32_t *>(ws));
 }
 
 int lora_bgmv(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in, const int32_t *ids_dev,
@@ -595,17 +599,18 @@ int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t
     if (h->num_sorted == 0) return LORA_OK;
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
-    const size_t need = combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    // the workspace of lora_sgmv: control words, then the partials
+    const size_t ctl_bytes = sgmv_ctl_bytes(h->num_blocks);
+    const size_t need = ctl_bytes + combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t ldw = (h->max_rank + 3) / 4 * 4;
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + ctl_bytes);
     ShrinkArgs sa{};
-    if ((st = make_shrink_args(dtype, x, ldx, d_in, static_cast<float *>(ws), ldw, h->max_rank, &sa))) return st;
+    if ((st = make_shrink_args(dtype, x, ldx, d_in, part, ldw, h->max_rank, &sa))) return st;
     ExpandArgs ea{};
-    if ((st = make_expand_args(dtype, static_cast<float *>(ws), ldw, h->max_rank, y, ldy, d_out, true, &ea)))
-        return st;
-    return launch_sgmv_paged(static_cast<hipStream_t>(stream), sa, ea,
-                             PlanView{h, plan_dev}, ws, pages, shift);
+    if ((st = make_expand_args(dtype, part, ldw, h->max_rank, y, ldy, d_out, true, &ea))) return st;
+    return launch_sgmv_paged(static_cast<hipStream_t>(stream), sa, ea, PlanView{h, plan_dev}, part, pages, shift);
 }
 
 int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,

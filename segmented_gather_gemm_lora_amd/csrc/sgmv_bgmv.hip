@@ -685,12 +685,13 @@ __device__ __forceinline__ void expand_rows(const float *__restrict__ v, int64_t
 // stored one at a time, with only one block's accumulators live.  The B
 // fragments of all NCH * 16 ranks stay in registers for the whole chunk.
 // CONTIG: the rows are the consecutive tokens ybase, ybase + 1, ... (yrows unused)
-template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB, bool CONTIG = false, class M = DenseMem>
+template <int DT, bool VECY, bool BV, int NCH, int UPT, int RB, bool CONTIG = false, class M = DenseMem,
+          class Pre = NoPre>
 __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                                   const void *__restrict__ Bv, int r, float scale,
                                                   void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
                                                   const int *yrows, int vrow0, int nrows, float *vl, int ldl,
-                                                  int ybase = 0, const M &mem = M{})
+                                                  int ybase = 0, const M &mem = M{}, const Pre &pre = Pre{})
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -705,7 +706,7 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
     }
     const int ysafe = CONTIG ? ybase : yrows[0];
     VStage<UPT> vst;
-    stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    if constexpr (!Pre::kWaits) stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     float bf[NCH][4][4];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) load_bfrag<DT, BV>(mem, Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
@@ -713,6 +714,10 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
     YTile<DT> yt[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
+    if constexpr (Pre::kWaits) {
+        if (!pre()) return;
+        stage_v_load<BV, false, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    }
     stage_v_store<BV, UPT>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
     __syncthreads();
 
@@ -744,6 +749,41 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
 // SGMV kernels.  Shrink: one workgroup per (plan block, d_in slice).  Expand:
 // one workgroup per (256 columns, plan block) or (256 columns, plan chunk).
 // ----------------------------------------------------------------------------
+// Shrink of one 16-row block (rows `rows`, n of them, sorted positions p0 ..,
+// adapter A of rank r) over d_in slice c.  A block computes only the rank
+// tiles its own rank needs (the launch's RT covers the largest rank): one
+// wave-uniform branch before any load.  Each tile's sum is formed in the same
+// order whatever RT is.
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M, bool SCOPED = false>
+__device__ __forceinline__ void shrink_block_slice(const void *__restrict__ x, int64_t ldx, int d_in,
+                                                   const int *__restrict__ rows, int n, int p0, const void *A, int r,
+                                                   int c, int slice_len, float *__restrict__ out, int64_t ldo,
+                                                   int64_t sl_stride, const M &mem)
+{
+    __shared__ float red[W > 1 ? W * RT * 256 : 1];
+    const int xr = rows[threadIdx.x & 15];
+    const int xr0 = rows[0];
+    const int k_begin = c * slice_len;
+    const int k_end = min(d_in, k_begin + slice_len);
+    float *o = out + c * sl_stride;
+    if constexpr (RT >= 2) {
+        if (r <= 16) {
+            shrink_block<DT, VEC, W, NSTEP, 1, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
+                                                          nullptr, n, red, mem);
+            return;
+        }
+    }
+    if constexpr (RT >= 4) {
+        if (r <= 32) {
+            shrink_block<DT, VEC, W, NSTEP, 2, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
+                                                          nullptr, n, red, mem);
+            return;
+        }
+    }
+    shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0, nullptr,
+                                                   n, red, mem);
+}
+
 // Item b of a shrink launch (b = the workgroup's index along x).
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
 __device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int64_t ldx, int d_in,
@@ -751,7 +791,6 @@ __device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int
                                                  int slice_len, float *__restrict__ out, int64_t ldo,
                                                  int64_t sl_stride, unsigned b, const M &mem)
 {
-    __shared__ float red[W > 1 ? W * RT * 256 : 1];
     // Workgroup b runs on XCD b % 8.  Give each XCD a contiguous run of
     // (block, slice) items, blocks fastest, so that the blocks of a segment
     // share one L2 and its A slice is fetched into few L2s.
@@ -760,33 +799,9 @@ __device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int
     const int item = int(b & 7) * per + int(b >> 3);
     if (item >= total) return;
     const lora_blk_desc *bd = blks + item % nblk;
-    const int c = item / nblk;
-    const int xr = bd->rows[threadIdx.x & 15];
-    const int xr0 = bd->rows[0];
-    const int k_begin = c * slice_len;
-    const int k_end = min(d_in, k_begin + slice_len);
-    const int r = bd->rank;
-    const void *A = reinterpret_cast<const void *>(bd->A);
-    float *o = out + c * sl_stride;
-    // A block computes only the rank tiles its own rank needs (the launch's RT
-    // covers the largest rank of the plan): one wave-uniform branch before any
-    // load.  Each tile's sum is formed in the same order whatever RT is.
-    if constexpr (RT >= 2) {
-        if (r <= 16) {
-            shrink_block<DT, VEC, W, NSTEP, 1>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr,
-                                               bd->n, red, mem);
-            return;
-        }
-    }
-    if constexpr (RT >= 4) {
-        if (r <= 32) {
-            shrink_block<DT, VEC, W, NSTEP, 2>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr,
-                                               bd->n, red, mem);
-            return;
-        }
-    }
-    shrink_block<DT, VEC, W, NSTEP, RT>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, bd->p0, nullptr, bd->n,
-                                        red, mem);
+    shrink_block_slice<DT, VEC, W, NSTEP, RT, M>(x, ldx, d_in, bd->rows, bd->n, bd->p0,
+                                                 reinterpret_cast<const void *>(bd->A), bd->rank, item / nblk,
+                                                 slice_len, out, ldo, sl_stride, mem);
 }
 
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
@@ -1171,6 +1186,76 @@ __global__ __launch_bounds__(256) void bgmv_onepass_kernel(const OnepassArgs a, 
                                                       a.pool_rank, a.pool_alpha, a.n_adapters, a.max_rank, a.y,
                                                       a.ldy, a.d_out, a.vec_b != 0, a.ldl, col * kExpandCols, g, mem,
                                                       w);
+}
+
+// ----------------------------------------------------------------------------
+// One-launch SGMV for small plans (where the second launch and the gap between
+// two kernels are a large part of the time).  The grid holds every shrink item
+// ((block, d_in slice), numbered as the shrink kernel numbers them), then one
+// expand item per (64-row chunk, 256 output columns); an expand item waits for
+// the flags of its chunk's (block, slice) items, which have lower indices, so
+// the grid completes under any dispatch in index order within an XCD.
+// Hand-over as in the one-launch BGMV (launch key in a per-(block, slice)
+// flag, device-scope stores and loads of the partial sums, no reset).
+// Measured on the prefill workload (2,200 workgroups) it is slower than the
+// two kernels (34.2 against 32.7 us; ordering the grid chunk by chunk, 42.7),
+// so large plans keep the two kernels.
+// ----------------------------------------------------------------------------
+struct SgmvOnepassArgs {
+    const void *x;
+    const lora_chunk_desc *chunks;
+    const lora_blk_desc *blks;
+    float *part;       // slice partial sums [kc][T'][ldw]
+    void *y;
+    int32_t *status;
+    uint64_t *flags;   // [n_blocks][kc]
+    int64_t ldx, ldw, sl_stride, ldy;
+    int32_t d_in, slice_len, kc, d_out, ncol, ldl, vec_b, wait_limit;
+    int32_t nblk, nchunk;
+};
+
+template <int DT, int NSTEP, int RT, int NCH, int UPT>
+__global__ __launch_bounds__(256) void sgmv_onepass_kernel(const SgmvOnepassArgs a)
+{
+    extern __shared__ floatx4 vl4[];
+    __shared__ int go;
+    const int b = int(blockIdx.x);
+    const uint64_t key = launch_key();
+    // shrink items first, numbered as the shrink kernel's (XCD-grouped)
+    const int n_prod = (a.nblk * a.kc + 7) / 8 * 8;
+    if (b < n_prod) {
+        const int total = a.nblk * a.kc, per = (total + 7) >> 3;
+        if ((b >> 3) >= per) return;
+        const int item = (b & 7) * per + (b >> 3);
+        if (item >= total) return;
+        const int blk = item % a.nblk, sl = item / a.nblk;
+        const lora_blk_desc *bd = a.blks + blk;
+        shrink_block_slice<DT, true, 4, NSTEP, RT, DenseMem, true>(
+            a.x, a.ldx, a.d_in, bd->rows, bd->n, bd->p0, reinterpret_cast<const void *>(bd->A), bd->rank, sl,
+            a.slice_len, a.part, a.ldw, a.sl_stride, DenseMem{});
+        // every wave's partial sums are complete before the flag moves
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.flags + int64_t(blk) * a.kc + sl, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int q = b - n_prod;
+    const int ci = q / a.ncol, col = q - ci * a.ncol;
+    const lora_chunk_desc *cd = a.chunks + ci;
+    const int r = cd->rank;
+    const int n = min(cd->n, kChunkRB * kRows);
+    const Waiter w{a.flags + int64_t(cd->first_blk) * a.kc, key, cd->nblk * a.kc, a.status, a.wait_limit, &go};
+    const void *B = reinterpret_cast<const void *>(cd->B);
+    float *vl = reinterpret_cast<float *>(vl4);
+    if (a.vec_b && (r & 3) == 0)
+        expand_chunk_impl<DT, true, true, NCH, UPT, kChunkRB, false, DenseMem, Waiter>(
+            a.part, a.ldw, a.sl_stride, a.kc, B, r, cd->scale, a.y, a.ldy, a.d_out, col * kExpandCols, cd->rows,
+            cd->p0, n, vl, a.ldl, 0, DenseMem{}, w);
+    else
+        expand_chunk_impl<DT, true, false, NCH, UPT, kChunkRB, false, DenseMem, Waiter>(
+            a.part, a.ldw, a.sl_stride, a.kc, B, r, cd->scale, a.y, a.ldy, a.d_out, col * kExpandCols, cd->rows,
+            cd->p0, n, vl, a.ldl, 0, DenseMem{}, w);
 }
 
 // Zero-fill of a workspace (its control words), as a kernel so that it can be
@@ -1736,10 +1821,67 @@ int shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *
     return check_launch("sgmv shrink");
 }
 
+// Largest grid of the one-launch SGMV: about one round of resident workgroups.
+constexpr int64_t kOnepassMaxGrid = 1536;
+
+template <int DT, int NSTEP, int RT, int NCH, int UPT>
+void sgmv_onepass_go(hipStream_t s, dim3 grid, size_t shm, const SgmvOnepassArgs &a)
+{
+    launch_kernel(sgmv_onepass_kernel<DT, NSTEP, RT, NCH, UPT>, grid, dim3(256), shm, s, a);
+}
+
 template <class M>
-int sgmv_combined(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws, const M &mem)
+int sgmv_combined(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws, const M &mem,
+                  int32_t *ctl = nullptr)
 {
     if (p.h->num_blocks == 0) return LORA_OK;
+    const int ldl = lds_pitch(p.h->max_rank);
+    const int ncol = (ea.d_out + kExpandCols - 1) / kExpandCols;
+    // One launch for small plans with aligned rows and ranks up to 32 (the
+    // chunk expand's register budget), when there is a control area.
+    if (std::is_same_v<M, DenseMem> && ctl && sa.vec && ea.vec_y && ea.d_out % 16 == 0 && ldl <= 32) {
+        const Split sp = choose_split(sa.d_in, p.h->num_blocks, sa.dtype);
+        const int64_t grid = (int64_t(p.h->num_blocks) * sp.kc + 7) / 8 * 8 + int64_t(p.h->num_chunks) * ncol;
+        if (grid <= kOnepassMaxGrid) {
+            SgmvOnepassArgs a{};
+            a.x = sa.x;
+            a.chunks = plan_chunks(p);
+            a.blks = plan_blocks(p);
+            a.nblk = p.h->num_blocks;
+            a.nchunk = p.h->num_chunks;
+            a.part = static_cast<float *>(ws);
+            a.y = ea.y;
+            a.status = ctl;
+            a.flags = reinterpret_cast<uint64_t *>(ctl + 64);
+            a.ldx = sa.ldx;
+            a.ldw = (p.h->max_rank + 3) / 4 * 4;
+            a.sl_stride = int64_t(p.h->num_sorted) * a.ldw;
+            a.ldy = ea.ldy;
+            a.d_in = sa.d_in;
+            a.slice_len = sp.slice_len;
+            a.kc = sp.kc;
+            a.d_out = ea.d_out;
+            a.ncol = ncol;
+            a.ldl = ldl;
+            a.vec_b = ea.vec_b ? 1 : 0;
+            const int lim = wait_limit();
+            a.wait_limit = lim == 0 ? (1 << 22) : (lim < 0 ? -1 : lim);
+            const size_t shm = (size_t(kChunkRB * kRows) * ldl + 4) * sizeof(float);
+            const dim3 g(static_cast<unsigned>(grid));
+            const bool two = sp.nstep == 2;
+            if (sa.dtype == LORA_F32) {
+                if (ldl <= 16) sgmv_onepass_go<LORA_F32, 1, 4, 1, 1>(s, g, shm, a);
+                else sgmv_onepass_go<LORA_F32, 1, 4, 2, 2>(s, g, shm, a);
+            } else if (ldl <= 16) {
+                if (two) sgmv_onepass_go<LORA_BF16, 2, 1, 1, 1>(s, g, shm, a);
+                else sgmv_onepass_go<LORA_BF16, 1, 1, 1, 1>(s, g, shm, a);
+            } else {
+                if (two) sgmv_onepass_go<LORA_BF16, 2, 2, 2, 2>(s, g, shm, a);
+                else sgmv_onepass_go<LORA_BF16, 1, 2, 2, 2>(s, g, shm, a);
+            }
+            return check_launch("sgmv one-launch");
+        }
+    }
     float *vp = static_cast<float *>(ws);
     int64_t ldw = 0, sl_stride = 0;
     int nsl = 0;
@@ -1778,9 +1920,15 @@ int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView
     return shrink_split(s, sa, p, ws, ldw, sl_stride, nsl, DenseMem{});
 }
 
-int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws)
+int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws, int32_t *ctl)
 {
-    return sgmv_combined(s, sa, ea, p, ws, DenseMem{});
+    return sgmv_combined(s, sa, ea, p, ws, DenseMem{}, ctl);
+}
+
+size_t sgmv_ctl_bytes(int32_t n_blocks)
+{
+    // status block (256 B), then a 64-bit flag per (block, d_in slice)
+    return (256 + 8 * size_t(kMaxSlices) * size_t(n_blocks < 1 ? 1 : n_blocks) + 255) / 256 * 256;
 }
 
 int launch_sgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws,

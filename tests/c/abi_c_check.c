@@ -68,9 +68,9 @@ int main(void)
     CHECK(lora_profile_launches(NULL, NULL, -1) == LORA_ERR_ARG);
 
     /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection
-     * regions of slice partial sums (the size of an SGMV workspace of the same
-     * shape; a single lora_bgmv workspace also holds control words);
-     * malformed calls are rejected on the host */
+     * regions of fp32 slice partial sums (4 slices of d_in, T rows of
+     * round4(rank), plus 256 B of slack; a single lora_bgmv workspace also holds
+     * control words); malformed calls are rejected on the host */
     lora_proj pr[2];
     memset(pr, 0, sizeof(pr));
     for (int p = 0; p < 2; ++p) {
@@ -86,9 +86,10 @@ int main(void)
         pr[p].d_out = 1024;
         pr[p].max_rank = p == 0 ? 16 : 64;
     }
-    const size_t r0 = lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 16);
-    const size_t r1 = lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 64);
+    const size_t r0 = 4u * 64u * 16u * 4u + 256u;
+    const size_t r1 = 4u * 64u * 64u * 4u + 256u;
     CHECK(lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 16) > r0);
+    CHECK(lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 16) > r0);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == (r0 + 255) / 256 * 256 + (r1 + 255) / 256 * 256);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 0) == 0);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, LORA_MAX_PROJ + 1) == 0);

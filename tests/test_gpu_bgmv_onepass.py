@@ -190,3 +190,37 @@ def test_onepass_graph_replays():
         assert np.array_equal(B.to_host_bits(c.y, "bf16"), eager), f"replay {rep}"
         assert B.workspace_status(ws) == 0
     del g
+
+
+@pytest.mark.parametrize("ranks", [[16], [8, 16, 32, 4]], ids=["rank16", "mixed_le32"])
+def test_sgmv_onepass_equals_two_kernels(ranks):
+    """A small plan runs lora_sgmv in one launch; lora_sgmv_paged over the same
+    adapters always runs the two kernels with the same d_in split and sums:
+    the outputs are equal bitwise, and both match the oracle."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    rng = np.random.default_rng(31)
+    n = 12
+    ids = rng.integers(-1, n, 96).astype(np.int32)
+    rk = [ranks[i % len(ranks)] for i in range(n)]
+    prob = make_problem(name="sgmv_small", dtype="bf16", ids=ids, ranks=rk, alphas=[32.0] * n, d_in=2048,
+                        d_out=1536, seed=31, a_std=0.05, b_std=0.05)
+    say(f"case sgmv one-launch vs two kernels ranks={ranks}")
+    c1 = GpuCase(prob)
+    timer = B.KernelTimer(8)
+    timer.arm(0, 8)
+    c1.run("sgmv")
+    assert B.KernelTimer.used() == 1, "small plan: one launch"
+    timer.disarm()
+    timer.close()
+    c2 = GpuCase(prob)
+    paged = B.PagedPool.from_problem(prob, page_bytes=65536, shuffle_seed=5)
+    plan = B.Plan(prob.T).build(prob.ids, paged).upload()
+    ws = B.workspace(B.LORA_OP_SGMV, prob.T, prob.d_in, prob.d_out, max(rk))
+    B.sgmv_paged(c2.x, plan, paged, c2.y, ws, "bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(B.to_host_bits(c1.y, "bf16"), B.to_host_bits(c2.y, "bf16"))
+    y_ref, _ = oracle.lora_forward(prob, nthreads=16)
+    assert_close(c1.y_out(), y_ref, "bf16", "sgmv one-launch")

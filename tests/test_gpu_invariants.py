@@ -171,8 +171,9 @@ def test_side_stream(path):
 
 def test_launch_counts():
     """The combined calls enqueue exactly the kernels they document: SGMV one
-    shrink and one expand; BGMV one kernel for aligned rows and ranks up to
-    64, else a shrink and an expand; the fused layer shrink, split and GEMM."""
+    kernel for aligned rows and ranks up to 32, BGMV one kernel for aligned
+    rows and ranks up to 64, else a shrink and an expand each; the fused layer
+    shrink, split and GEMM."""
     import torch
 
     from segmented_gather_gemm_lora_amd import binding as B
@@ -181,7 +182,7 @@ def test_launch_counts():
     c = GpuCase(prob)
     say("case launch counts")
     timer = B.KernelTimer(8)
-    for path, want in (("sgmv", 2), ("bgmv", 1)):
+    for path, want in (("sgmv", 1), ("bgmv", 1)):
         timer.arm(0, 8)
         c.run(path)
         assert B.KernelTimer.used() == want, path
@@ -189,10 +190,11 @@ def test_launch_counts():
     # d_out not a multiple of 16: the two-kernel form
     odd = make_problem(name="bgmv_two", dtype="bf16", ids=[0, 1, 1, -1], ranks=[8, 16], alphas=[16.0, 32.0],
                        d_in=64, d_out=40, seed=4)
-    timer.arm(0, 8)
-    GpuCase(odd).run("bgmv")
-    assert B.KernelTimer.used() == 2, "bgmv two-kernel form"
-    timer.disarm()
+    for path in ("sgmv", "bgmv"):
+        timer.arm(0, 8)
+        GpuCase(odd).run(path)
+        assert B.KernelTimer.used() == 2, f"{path} two-kernel form"
+        timer.disarm()
     fused = make_problem(name="fused_count", dtype="bf16", ids=[0, 1, -1, 0], ranks=[8, 16], alphas=[16.0, 32.0],
                          d_in=64, d_out=64, seed=3, w0_std=0.05)
     pool = B.DevicePool.from_problem(fused)
