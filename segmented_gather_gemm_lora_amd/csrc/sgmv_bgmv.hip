@@ -464,13 +464,14 @@ __device__ __forceinline__ float get_result(const float *p)
 
 template <bool BV, bool VIND, int UPT, bool SCOPED = false>
 __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
-                                             const int *yrows, int vrow0, int nrows, int r, int ldl, VStage<UPT> &st)
+                                             const int *yrows, int vrow0, int nrows, int r, int ldl, VStage<UPT> &st,
+                                             int unit0 = 0)
 {
     const int q4 = ldl >> 2;
     const int units = nrows * q4;
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
-        const int u = threadIdx.x + k * int(blockDim.x);
+        const int u = unit0 + threadIdx.x + k * int(blockDim.x);
         st.uok[k] = u < units;
         const int uu = st.uok[k] ? u : 0;
         const int row = uu / q4, j = 4 * (uu - row * q4);
@@ -910,6 +911,137 @@ __global__ __launch_bounds__(256) void sgmv_expand_chunk_arg_kernel(const float 
         else
             expand_chunk_impl<DT, VECY, false, NCH, UPT, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
                                                                    d_out, ncw, rows, p0, n, vl, ldl, 0, mem);
+    }
+}
+
+// Expand of one plan chunk of rank 33 .. 64 (bf16 B, r % 4 == 0) over this
+// workgroup's 256 columns: the B fragments of all four 16-rank steps are
+// loaded once, packed as bf16 (two ranks per register), with the chunk's four
+// y tiles; v is staged at the chunk's own rank pitch in two phases of two
+// units per thread (so that the four d_in slices of 64 rows x 64 ranks never
+// sit in registers at once); then the blocks are computed and stored one at a
+// time.  Same multiply order as expand_rows_packed, so the same bits as the
+// 16-row block form.
+template <bool VECY, class M>
+__device__ __forceinline__ void expand_chunk_wide(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
+                                                  const void *__restrict__ Bv, int r, float scale,
+                                                  void *__restrict__ yv, int64_t ldy, int d_out, int ncol_wg,
+                                                  const int *yrows, int vrow0, int nrows, float *vl, const M &mem)
+{
+    constexpr int DT = LORA_BF16, RB = kChunkRB, NCH = 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int ncol0 = ncol_wg + 64 * wave;
+    const int ldl = (r + 3) & ~3;
+    int yr[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int row = 16 * i + m;
+        yr[i] = row < nrows ? yrows[row] : -1;
+    }
+    const int ysafe = yrows[0];
+    bool cok[4];
+    u32x2 braw[NCH][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int ncol = ncol0 + Cols<DT>::of(m >> 2, 4 * t + (m & 3));
+        cok[t] = ncol < d_out;
+        const int64_t rowoff = int64_t(cok[t] ? ncol : d_out - 1) * r;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j0 = 16 * c + 4 * g;
+            braw[c][t] = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + (j0 < r ? j0 : 0)));
+        }
+    }
+    YTile<DT> yt[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
+    // 64 rows x 16 float4 units at most: two phases of two units per thread
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+        VStage<2> vst;
+        stage_v_load<true, false, 2>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, 512 * ph);
+        stage_v_store<true, 2>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
+    }
+    __syncthreads();
+
+    const int nblk = (nrows + kRows - 1) / kRows;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        if (i >= nblk) break;
+        floatx4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = floatx4{};
+        const int row = 16 * i + m;
+        const float *vrow = vl + (row < nrows ? row : 0) * ldl;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j0 = 16 * c + 4 * g;
+            floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
+            if (row >= nrows || j0 >= ldl) vf = floatx4{};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool ok = cok[t] && j0 < r;
+                const u32x2 q2 = braw[c][t];
+                const float b[4] = {ok ? bf16_to_f32(q2[0] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[0] >> 16) : 0.f,
+                                    ok ? bf16_to_f32(q2[1] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[1] >> 16) : 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q], vf[q], acc[t], 0, 0, 0);
+            }
+        }
+        if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc, scale);
+    }
+}
+
+// The expand of a plan with ranks up to 64 in one launch, one workgroup per
+// (256 output columns, plan chunk), each choosing its form from its own chunk
+// (the pages' per-segment path choice, "Multi-LoRA serving: the single
+// translator ...", section "SGMV: the kernel that holds it all up"):
+//  * a chunk of at most 16 rows (a short segment, or the tail of a long one):
+//    the 16-row block form, v staged at the chunk's own rank pitch;
+//  * longer chunks: the 64-row chunk form, which reads each B tile once for
+//    four blocks -- B held as widened fp32 for ranks up to 32, packed bf16 for
+//    ranks 33 .. 64 (expand_chunk_wide).
+// Chunk forms of other shapes (fp32, ranks not a multiple of 4) run the block
+// form once per 16-row block of the chunk.  Every form computes each output
+// with the same sums in the same order as the block form.
+template <int DT, bool VECY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sgmv_expand_mixed_kernel(
+    const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl, const lora_chunk_desc *__restrict__ chunks,
+    void *__restrict__ y, int64_t ldy, int d_out, int vec_b)
+{
+    extern __shared__ floatx4 vl4[];
+    const lora_chunk_desc *d = chunks + blockIdx.y;
+    const int r = d->rank;
+    const int n = d->n < kChunkRB * kRows ? d->n : kChunkRB * kRows;
+    const void *B = reinterpret_cast<const void *>(d->B);
+    const float scale = d->scale;
+    const int ncw = blockIdx.x * kExpandCols;
+    float *vl = reinterpret_cast<float *>(vl4);
+    const int ldl = (r + 3) & ~3; // the chunk's own rank pitch
+    const bool bv = vec_b && (r & 3) == 0;
+    if (n > kRows && bv) {
+        if (r <= 16)
+            expand_chunk_impl<DT, VECY, true, 1, 1, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw,
+                                                              d->rows, d->p0, n, vl, ldl);
+        else if (r <= 32)
+            expand_chunk_impl<DT, VECY, true, 2, 2, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw,
+                                                              d->rows, d->p0, n, vl, ldl);
+        else if constexpr (DT == LORA_BF16)
+            expand_chunk_wide<VECY>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, d->rows, d->p0, n, vl,
+                                    DenseMem{});
+        else
+            for (int q0 = 0; q0 < n; q0 += kRows) {
+                if (q0) __syncthreads();
+                expand_rows<DT, VECY, false, 1>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, true,
+                                                d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl);
+            }
+        return;
+    }
+    for (int q0 = 0; q0 < n; q0 += kRows) {
+        if (q0) __syncthreads(); // the previous block is done with vl
+        expand_rows<DT, VECY, false, 1, DenseMem, 4>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, bv,
+                                                    d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl);
     }
 }
 
@@ -1706,6 +1838,24 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const int ldl = lds_pitch(p.h->max_rank);
     const bool vecy = a.vec_y && a.d_out % 16 == 0;
+    // Dense plans with ranks up to 64, except the ones the argument-table
+    // chunk kernel serves (ranks <= 32, enough chunk items): one launch whose
+    // workgroups choose the block or chunk form per plan chunk.
+    const bool arg_chunks = p.h->num_chunks * ncol >= 1024 && ldl <= 32 && p.h->num_chunks <= kArgChunks;
+    if (std::is_same_v<M, DenseMem> && ldl <= 64 && !arg_chunks) {
+        const dim3 grid(ncol, p.h->num_chunks);
+        const size_t shm = (size_t(kChunkRB * kRows) * 64 + 4) * sizeof(float);
+        const lora_chunk_desc *d = plan_chunks(p);
+        const int vb = a.vec_b ? 1 : 0;
+        if (a.dtype == LORA_BF16) {
+            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, true>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+            else launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, false>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+        } else {
+            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, true>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+            else launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, false>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+        }
+        return;
+    }
     // chunks of up to 64 rows reuse B four times; use them when they still give
     // enough workgroups and the B fragments of every rank fit in registers
     // next to four y tiles (ranks <= 32; larger ranks lose more to occupancy

@@ -360,3 +360,40 @@ def test_segments_boundary_end_to_end():
     torch.cuda.synchronize()
     y_ref, _ = oracle.lora_forward(_with_zero_base(prob), nthreads=16)
     assert_close(c.y_out(), y_ref, "bf16", "segments boundary")
+
+
+def test_per_chunk_form_choice_in_one_launch():
+    """One expand launch over a plan mixing long segments (64-row chunk form;
+    ranks <= 32 with B held, 33 .. 64 with B packed) and short ones (16-row
+    block form), ranks not a multiple of 4 included (block form for every
+    chunk): lora_sgmv enqueues the shrink and one expand, and y matches the
+    oracle."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    rng = np.random.default_rng(77)
+    ranks = [64, 48, 40, 8, 33, 16, 32, 1, 64, 12]
+    long_ids = np.repeat(np.arange(5), [300, 130, 70, 200, 90])      # long segments, ranks 64, 48, 40, 8, 33
+    short_ids = rng.integers(5, 10, 60)                                # short ones over the other adapters
+    ids = np.concatenate([long_ids, short_ids]).astype(np.int32)
+    ids = ids[rng.permutation(len(ids))]
+    ids[rng.random(len(ids)) < 0.03] = -1
+    prob = make_problem(name="mixed_forms", dtype="bf16", ids=ids, ranks=ranks, alphas=[32.0] * len(ranks),
+                        d_in=1024, d_out=2560, seed=77, a_std=0.05, b_std=0.05)
+    say("case per-chunk form choice in one launch")
+    c = GpuCase(prob, y_init="zero")
+    timer = B.KernelTimer(8)
+    timer.arm(0, 8)
+    c.run("sgmv")
+    assert B.KernelTimer.used() == 2, "shrink + one expand"
+    timer.disarm()
+    timer.close()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.lora_forward(_with_zero_base(prob), nthreads=16)
+    assert_close(c.y_out(), y_ref, "bf16", "mixed forms")
+    # the same batch, y preset
+    c2 = GpuCase(prob)
+    c2.run("sgmv")
+    y_ref2, _ = oracle.lora_forward(prob, nthreads=16)
+    assert_close(c2.y_out(), y_ref2, "bf16", "mixed forms, y preset")
