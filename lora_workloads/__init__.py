@@ -21,4 +21,8 @@ from .synth import (  # noqa: F401
     QKV_NAME,
     CONFIG_NAMES,
     zipf_probs,
+    e4m3_codes,
+    with_e4m3_base,
+    make_fused_fp8,
+    FUSED_FP8_NAME,
 )

@@ -83,6 +83,10 @@ class LoraProblem:
     y_in: Optional[np.ndarray]  # [T, d_out] base output to accumulate into (None = zeros)
     W0: Optional[np.ndarray]  # [d_out, d_in] base weight for the fused entry
     meta: dict = field(default_factory=dict)
+    # FP8 base: [d_out, d_in] uint8 E4M3 codes standing for w0_scale * code
+    # (W0 is then None)
+    W0_e4m3: Optional[np.ndarray] = None
+    w0_scale: float = 1.0
 
     @property
     def n_adapters(self) -> int:
@@ -207,6 +211,47 @@ def make_problem(
         alphas=alphas, pool=pool, a_off=a_off, b_off=b_off, x=x, y_in=y_in, W0=W0,
         meta=dict(meta or {}),
     )
+
+
+def e4m3_codes(a) -> np.ndarray:
+    """float32 values -> uint8 E4M3 codes by torch's float8_e4m3fn cast (round to
+    nearest even); values are first clipped to the format's largest finite
+    magnitude, 448, so that none becomes NaN."""
+    import torch
+
+    a = np.clip(np.ascontiguousarray(a, dtype=np.float32), -448.0, 448.0)
+    return torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def with_e4m3_base(prob: LoraProblem, seed: int, q_std: float = 32.0, w0_std: float = 0.02,
+                   name: Optional[str] = None) -> LoraProblem:
+    """The same problem with its base weight replaced by an FP8 one: codes of
+    Gaussian draws with standard deviation q_std (so that the codes use the
+    format's range) and one fp32 scale w0_std / q_std, so that the weight the
+    codes stand for has standard deviation w0_std.  Draws from its own seed."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((prob.d_out, prob.d_in), dtype=np.float32) * np.float32(q_std)
+    import copy
+
+    out = copy.copy(prob)
+    out.W0 = None
+    out.W0_e4m3 = e4m3_codes(q)
+    out.w0_scale = float(np.float32(w0_std / q_std))
+    out.meta = dict(prob.meta, fused=True, w0_format="e4m3")
+    if name is not None:
+        out.name = name
+    return out
+
+
+FUSED_FP8_NAME = "fused_layer_fp8w_bf16"
+
+
+def make_fused_fp8(seed: int = 5) -> LoraProblem:
+    """The fused-layer workload (1024 tokens, Zipf requests over 200 resident
+    rank-16 slots, W0 [12288, 4096], y overwritten) with an FP8 E4M3 base of
+    one fp32 scale, weight std 0.02 as in the bf16 form; adapters, x and the
+    plan are those of the bf16 workload with the same seed."""
+    return with_e4m3_base(make_config(5, seed), seed=1000 + seed, name=FUSED_FP8_NAME)
 
 
 def dirichlet_lengths(rng, total: int, k: int) -> np.ndarray:

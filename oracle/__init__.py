@@ -14,6 +14,11 @@ Functions and what they follow:
 * ``segments`` -- brute-force grouping of tokens by adapter id into contiguous
   segments ("Multi-LoRA Serving in Production ...", section "Punica and
   Segmented Gather Matrix-Vector Multiplication (SGMV)"), ascending id, stable.
+* ``e4m3_decode`` -- the value of each 8-bit E4M3 code, exactly, from the
+  format's definition (OCP 8-bit floating point specification, E4M3 encoding);
+  ``lora_forward`` uses it for an FP8 base W0 = w0_scale * codes ("Multi-LoRA
+  serving: the single translator ...", section "Combined pattern with
+  quantisation and disaggregated serving": BF16 adapters over an FP8 base).
 * ``adapter_numel`` / ``adapter_bytes`` -- r (d_in + d_out) parameters
   ("Multi-LoRA Serving: Many Adapters on One GPU" (gpusmith.com), section "LoRA
   recap and why adapters are small"; bytes per matrix from "Multi-LoRA serving:
@@ -47,7 +52,8 @@ def lib_path(mutant: int = 0) -> str:
 def build(mutant: int = 0, force: bool = True) -> str:
     """Compile oracle.c with gcc (-O2, fp64, no fast-math, OpenMP over tokens)."""
     out = lib_path(mutant)
-    if not force and os.path.exists(out):
+    src = os.path.join(_HERE, "oracle.c")
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
         return out
     os.makedirs(_BUILD, exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
@@ -76,7 +82,9 @@ def _load(mutant: int = 0):
         lib.oracle_lora_forward.restype = ctypes.c_int
         lib.oracle_lora_forward.argtypes = [
             _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
-            _vp, _i64, _vp, _vp, _i64, _vp, _i32]
+            _vp, _i64, _vp, _i32, ctypes.c_double, _vp, _i64, _vp, _i32]
+        lib.oracle_e4m3_decode.restype = None
+        lib.oracle_e4m3_decode.argtypes = [_vp, _i64, _vp]
         assert lib.oracle_mutant_id() == mutant
         _LIBS[mutant] = lib
         return lib
@@ -108,12 +116,21 @@ def segments(ids, n_adapters: int, mutant: int = 0):
     return perm[:n].copy(), indptr[: S + 1].copy(), adapter[:S].copy()
 
 
+def e4m3_decode(codes, mutant: int = 0) -> np.ndarray:
+    """float64 values of uint8 E4M3 codes (NaN for the two NaN codes)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load(mutant).oracle_e4m3_decode(_ptr(c), int(c.size), _ptr(out))
+    return out
+
+
 def lora_forward(prob, *, nthreads: int = 1, want_v: bool = False, fused: bool = None,
                  ids=None, alphas=None, pool=None, mutant: int = 0):
     """fp64 layer output for a ``lora_workloads.LoraProblem``.
 
-    fused=True uses x W0 as the base (prob.W0 must exist); otherwise the base
-    is prob.y_in (zeros if None).  ``ids``, ``alphas`` and ``pool`` override the
+    fused=True uses x W0 as the base: W0 = prob.w0_scale * prob.W0_e4m3 when
+    the problem holds E4M3 codes, else prob.W0 (one of them must exist);
+    otherwise the base is prob.y_in (zeros if None).  ``ids``, ``alphas`` and ``pool`` override the
     problem's arrays (for invariance tests).  Returns (y, v) with v None unless
     want_v; v rows of tokens without an adapter are zero.
     """
@@ -127,9 +144,14 @@ def lora_forward(prob, *, nthreads: int = 1, want_v: bool = False, fused: bool =
     ranks = np.ascontiguousarray(prob.ranks, dtype=np.int32)
     x = np.ascontiguousarray(prob.x)
     y_in = None if (fused or prob.y_in is None) else np.ascontiguousarray(prob.y_in)
-    W0 = np.ascontiguousarray(prob.W0) if fused else None
+    w0_codes = getattr(prob, "W0_e4m3", None) if fused else None
+    if w0_codes is not None:
+        W0 = np.ascontiguousarray(w0_codes, dtype=np.uint8)
+    else:
+        W0 = np.ascontiguousarray(prob.W0) if (fused and prob.W0 is not None) else None
     if fused and W0 is None:
         raise ValueError("fused oracle run needs W0")
+    w0_scale = float(getattr(prob, "w0_scale", 1.0))
     T = prob.T
     y = np.zeros((T, prob.d_out), dtype=np.float64)
     ldv = max(prob.max_rank, 1)
@@ -138,7 +160,8 @@ def lora_forward(prob, *, nthreads: int = 1, want_v: bool = False, fused: bool =
         T, prob.d_in, prob.d_out, is_bf16, _ptr(x), prob.d_in, _ptr(ids), prob.n_adapters,
         _ptr(pool), _ptr(np.ascontiguousarray(prob.a_off, dtype=np.int64)),
         _ptr(np.ascontiguousarray(prob.b_off, dtype=np.int64)), _ptr(ranks), _ptr(alphas),
-        _ptr(y_in), prob.d_out, _ptr(W0), _ptr(v), ldv, _ptr(y), int(nthreads))
+        _ptr(y_in), prob.d_out, _ptr(W0), 1 if w0_codes is not None else 0, w0_scale, _ptr(v), ldv, _ptr(y),
+        int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem (bad id or rank)")
     return y, v

@@ -26,10 +26,18 @@
  * fp32) to double; all sums are accumulated in double; the scale alpha/r is
  * formed in double.  Output is double.
  *
+ * Quantised base: "Multi-LoRA serving: the single translator with a thousand
+ * glossaries" (blog.lo0.es), section "Combined pattern with quantisation and
+ * disaggregated serving", serves the adapters in BF16 over an FP8 base.  Here
+ * that base is W0 = w0_scale * q, q the matrix of 8-bit E4M3 codes (one fp32
+ * scale for the whole matrix, the plainest reading: the pages fix no scale
+ * granularity), decoded exactly to double.
+ *
  * Planted mistakes: building with -DORACLE_MUTANT=k (k >= 1) compiles one
  * deliberate error so that the pin tests can show they would catch it.  The
  * default build (ORACLE_MUTANT undefined or 0) has none.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,6 +59,45 @@ static double load_elem(const void *base, int is_bf16, int64_t i)
 }
 
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }
+
+/*
+ * One 8-bit E4M3 code as a double, exactly, from the format's definition in the
+ * OCP 8-bit floating point specification (OFP8, revision 1.0), section on the
+ * E4M3 encoding: bit 7 is the sign, bits 6..3 the exponent field e (bias 7),
+ * bits 2..0 the mantissa field m.  e = 0 encodes the subnormals m/8 * 2^-6
+ * (and the two zeros); the pattern with e = 15 and m = 7 is NaN (the format
+ * has no infinities); every other code is the normal number (1 + m/8) 2^(e-7),
+ * the largest being e = 15, m = 6: 448.
+ */
+static double e4m3_value(uint8_t c)
+{
+    const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+#if ORACLE_MUTANT == 14
+    (void)0; /* planted: the NaN pattern decoded as a normal number */
+#else
+    if (e == 15 && m == 7) return NAN;
+#endif
+    double mag;
+#if ORACLE_MUTANT == 12
+    mag = ldexp(1.0 + m / 8.0, e - 7); /* planted: subnormals given the implicit one */
+#else
+    if (e == 0)
+        mag = ldexp(m / 8.0, -6);
+    else
+#if ORACLE_MUTANT == 11
+        mag = ldexp(1.0 + m / 8.0, e - 8); /* planted: exponent bias 8 */
+#else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+#endif
+#endif
+    return sign ? -mag : mag;
+}
+
+/* Decodes n E4M3 codes to doubles (see e4m3_value). */
+void oracle_e4m3_decode(const uint8_t *codes, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+}
 
 /*
  * Adapter size: "Multi-LoRA Serving: Many Adapters on One GPU" (gpusmith.com),
@@ -118,7 +165,9 @@ int32_t oracle_segments(int32_t T, const int32_t *ids, int32_t n_adapters,
  *                        B_i at pool + b_off[i] ([d_out, r_i]) (element offsets)
  *   rank    [N], alpha [N]
  *   y_in    [T, ldy]     base output accumulated into; NULL = zero base
- *   W0      [d_out, d_in] when non-NULL the base is x W0 (y_in is then ignored)
+ *   W0      [d_out, d_in] when non-NULL the base is x W0 (y_in is then ignored);
+ *           stored like x, or, when w0_e4m3 is set, as E4M3 codes (one byte
+ *           each) standing for w0_scale * code
  *   v_out   [T, ldv]     optional: the shrink result x A_a(t) (rows of tokens
  *                        without an adapter are left untouched)
  *   y_out   [T, d_out]   result
@@ -130,7 +179,7 @@ int oracle_lora_forward(int32_t T, int32_t d_in, int32_t d_out, int32_t is_bf16,
                         const void *pool, const int64_t *a_off, const int64_t *b_off,
                         const int32_t *rank, const float *alpha,
                         const void *y_in, int64_t ldy, const void *W0,
-                        double *v_out, int64_t ldv, double *y_out, int32_t nthreads)
+                        int32_t w0_e4m3, double w0_scale, double *v_out, int64_t ldv, double *y_out, int32_t nthreads)
 {
     int bad = 0;
     for (int32_t t = 0; t < T; ++t) {
@@ -147,7 +196,16 @@ int oracle_lora_forward(int32_t T, int32_t d_in, int32_t d_out, int32_t is_bf16,
         /* base term: x W0 (fused) or the stored base output */
         for (int32_t n = 0; n < d_out; ++n) {
             double b = 0.0;
-            if (W0) {
+            if (W0 && w0_e4m3) {
+                for (int32_t k = 0; k < d_in; ++k) {
+#if ORACLE_MUTANT == 13
+                    const double w = e4m3_value(((const uint8_t *)W0)[(int64_t)n * d_in + k]); /* planted: scale dropped */
+#else
+                    const double w = w0_scale * e4m3_value(((const uint8_t *)W0)[(int64_t)n * d_in + k]);
+#endif
+                    b += load_elem(x, is_bf16, (int64_t)t * ldx + k) * w;
+                }
+            } else if (W0) {
                 for (int32_t k = 0; k < d_in; ++k)
                     b += load_elem(x, is_bf16, (int64_t)t * ldx + k) *
                          load_elem(W0, is_bf16, (int64_t)n * d_in + k);

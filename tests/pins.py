@@ -11,6 +11,10 @@ Independent references used here: the pages' printed numbers
 (tests/golden/adapter_sizes.json), numpy matrix products (a library routine,
 not the oracle's loops), exact integer arithmetic in pure Python, Python's
 stable ``sorted``, and special cases (zero adapter, scale doubling, padding).
+For the E4M3 decode: the values the OCP 8-bit floating point specification
+names (tests/golden/e4m3_values.json), torch's float8_e4m3fn conversion (a
+library routine), an exact pure-Python decode with fractions, and the
+format's structure (order, spacing, symmetry).
 """
 
 from __future__ import annotations
@@ -192,6 +196,96 @@ def pin_nan_locality(mutant=0):
     assert bad.tolist() == [t == 3 for t in range(prob.T)]
 
 
+# ---------------------------------------------------------------- E4M3 decode
+def _e4m3_exact(code: int):
+    """Exact value of an E4M3 code as a Fraction (None for NaN), from the
+    format's definition: sign, 4-bit exponent field (bias 7), 3-bit mantissa;
+    exponent field 0 is subnormal; S.1111.111 is NaN."""
+    from fractions import Fraction
+
+    sign = -1 if code & 0x80 else 1
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    if e == 0:
+        mag = Fraction(m, 8) * Fraction(1, 2**6)
+    else:
+        mag = Fraction(8 + m, 8) * (Fraction(2) ** (e - 7))
+    return sign * mag
+
+
+def pin_e4m3_decode(mutant=0):
+    """All 256 codes: the values the specification names, torch's
+    float8_e4m3fn decode, an exact decode with fractions, and the format's
+    structure."""
+    import math
+
+    import torch
+
+    got = oracle.e4m3_decode(np.arange(256, dtype=np.uint8), mutant=mutant)
+    with open(os.path.join(GOLDEN, "e4m3_values.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        v = got[c["code"]]
+        if c["value"] is None:
+            assert math.isnan(v), c
+        else:
+            want = math.ldexp(c["value"][0], c["value"][1])
+            assert v == want and math.copysign(1.0, v) == math.copysign(1.0, want), (c, v)
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(got[fin], lib[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(lib[fin]))
+    for code in range(256):
+        ex = _e4m3_exact(code)
+        assert (ex is None) == math.isnan(got[code]), code
+        if ex is not None:
+            assert got[code] == float(ex), (code, got[code], ex)
+    pos = got[:127]  # +0 .. 448
+    assert np.all(np.diff(pos) > 0)  # codes 0x00 .. 0x7E increase strictly
+    assert np.array_equal(got[128:255], -pos)  # sign bit mirrors
+    for e in range(1, 16):  # normals: 8 values per binade, equally spaced
+        vals = got[8 * e : 8 * e + (7 if e == 15 else 8)]
+        assert np.all(np.diff(vals) == vals[0] / 8)
+    assert np.all(np.diff(got[0:9]) == got[1])  # subnormals continue the spacing of the first binade
+    assert int(np.isnan(got).sum()) == 2
+
+
+def pin_e4m3_base(mutant=0):
+    """The layer over an FP8 base: with a power-of-two scale every weight
+    w0_scale * q is exact in bf16, and the output equals the oracle's bf16-base
+    output for those weights (converted by torch's float8 decode, not the
+    oracle's); a scale of three times that gives three times the base product
+    (no adapters)."""
+    import copy
+
+    import torch
+
+    from lora_workloads import bf16_bits_to_f32, f32_to_bf16_bits, with_e4m3_base
+
+    rng = np.random.default_rng(41)
+    ids = rng.integers(-1, 3, 13).astype(np.int32)
+    prob = make_problem(name="fp8base", dtype="bf16", ids=ids, ranks=[4, 8, 2], alphas=[8.0, 4.0, 6.0],
+                        d_in=48, d_out=20, seed=42, a_std=0.2, b_std=0.2, y_mode="zero", w0_std=0.1)
+    q = with_e4m3_base(prob, seed=43, q_std=40.0)
+    q.w0_scale = 2.0 ** -8
+    y8, _ = oracle.lora_forward(q, fused=True, mutant=mutant)
+    wq = torch.from_numpy(q.W0_e4m3).view(torch.float8_e4m3fn).to(torch.float32).numpy() * np.float32(2.0 ** -8)
+    b = copy.copy(prob)
+    b.W0 = f32_to_bf16_bits(wq).reshape(wq.shape)
+    assert np.array_equal(bf16_bits_to_f32(b.W0).reshape(wq.shape), wq)  # exact in bf16
+    yb, _ = oracle.lora_forward(b, fused=True, mutant=mutant)
+    assert np.max(np.abs(y8 - yb)) <= 1e-12 * max(1.0, np.max(np.abs(yb)))
+    none = np.full(q.T, -1, dtype=np.int32)
+    y1, _ = oracle.lora_forward(q, ids=none, fused=True, mutant=mutant)
+    q3 = copy.copy(q)
+    q3.w0_scale = 3 * 2.0 ** -8
+    y3, _ = oracle.lora_forward(q3, ids=none, fused=True, mutant=mutant)
+    assert np.max(np.abs(y3 - 3 * y1)) <= 1e-12 * np.max(np.abs(y3))
+    assert np.max(np.abs(y1)) > 0
+
+
 # ---------------------------------------------------------------- segments
 def pin_segments(mutant=0):
     """Segments equal Python's stable sort of token indices by id (ids < 0
@@ -220,6 +314,8 @@ ALL_PINS = [
     pin_padding_invariance,
     pin_nan_locality,
     pin_segments,
+    pin_e4m3_decode,
+    pin_e4m3_base,
 ]
 
 # Planted mistakes compiled into oracle.c with -DORACLE_MUTANT=k.
@@ -234,6 +330,10 @@ MUTANTS = {
     8: "order within a segment reversed",
     9: "size formula parenthesis dropped",
     10: "correction sign flipped",
+    11: "E4M3 exponent bias 8",
+    12: "E4M3 subnormals given the implicit one",
+    13: "FP8 base scale dropped",
+    14: "E4M3 NaN pattern decoded as a number",
 }
 
 
