@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-LoRA adapter path on one MI355X.
 
-    python bench.py [--config decode|prefill|hetero|fused|tiny|decode_qkv|prefill_qkv|decode_cache]
+    python bench.py [--config decode|prefill|hetero|fused|fused_fp8|tiny|decode_qkv|prefill_qkv|decode_cache]
                     [--steps K] [--warmup W] [--paged PAGE_BYTES] [--graph] [--probe]
 
 A step is one adapted layer-projection over one batch: shrink + expand for
@@ -46,7 +46,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
 MALL_BYTES = 256 << 20
 
 METRIC = "SGMV/BGMV tokens/s per layer + achieved HBM GB/s (% of MI355X peak)"
-CONFIG_OF = {"tiny": 1, "decode": 2, "prefill": 3, "hetero": 4, "fused": 5}
+CONFIG_OF = {"tiny": 1, "decode": 2, "prefill": 3, "hetero": 4, "fused": 5, "fused_fp8": 5}
 
 
 def algorithmic_bytes(prob):
@@ -59,7 +59,7 @@ def algorithmic_bytes(prob):
     b_bytes = sum(int(prob.ranks[a]) * prob.d_out * es for a in distinct)
     x_bytes = prob.T * prob.d_in * es
     if prob.meta.get("fused"):
-        w_bytes = prob.d_out * prob.d_in * es
+        w_bytes = prob.d_out * prob.d_in * (1 if prob.W0_e4m3 is not None else es)
         y_bytes = prob.T * prob.d_out * es
         total = x_bytes + a_bytes + b_bytes + w_bytes + y_bytes
         return {"shrink": x_bytes + a_bytes, "fused": x_bytes + b_bytes + w_bytes + y_bytes, "total": total}
@@ -109,11 +109,16 @@ class Instance:
         if op is not None:
             self.ws = B.workspace(op, prob.T, prob.d_in, prob.d_out, prob.max_rank)
         if kind == "fused":
-            self.W0 = B.to_device(prob.W0, self.dt)
+            if prob.W0_e4m3 is not None:  # FP8 base: E4M3 codes, one byte each
+                self.W0 = torch.from_numpy(np.ascontiguousarray(prob.W0_e4m3)).cuda()
+            else:
+                self.W0 = B.to_device(prob.W0, self.dt)
             nbytes = B.lora_workspace_bytes(B.LORA_OP_FUSED, prob.T, prob.d_in, prob.d_out, prob.max_rank)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         # the step: one library call with its arguments converted once
-        if kind == "fused":
+        if kind == "fused" and prob.W0_e4m3 is not None:
+            self.step = B.fused_e4m3_prepared(self.x, self.W0, prob.w0_scale, self.plan, self.y, self.ws, stream)
+        elif kind == "fused":
             self.step = B.fused_prepared(self.x, self.W0, self.plan, self.y, self.ws, self.dt, stream)
         elif kind == "bgmv":
             mk = B.bgmv_paged_prepared if page_bytes else B.bgmv_prepared
@@ -564,11 +569,15 @@ def dataclasses_replace_ids(prob, ids):
 
 def base_gemm_reference_us(inst, stream, reps=50):
     """Average time of torch.matmul for the base product alone (same shape,
-    bf16): the vendor-library figure the fused kernel is compared with."""
+    bf16; an FP8 base is widened to bf16 first): the vendor-library figure the
+    fused kernel is compared with."""
     import torch
 
-    wt = inst.W0.t()
-    out = torch.empty((inst.prob.T, inst.prob.d_out), dtype=inst.W0.dtype, device="cuda")
+    w = inst.W0
+    if w.dtype == torch.uint8:
+        w = w.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    wt = w.t()
+    out = torch.empty((inst.prob.T, inst.prob.d_out), dtype=torch.bfloat16, device="cuda")
     with torch.cuda.stream(stream):
         for _ in range(5):
             torch.matmul(inst.x, wt, out=out)
@@ -745,7 +754,7 @@ def main():
 
     import torch
 
-    from lora_workloads import CONFIG_NAMES, make_config
+    from lora_workloads import CONFIG_NAMES, FUSED_FP8_NAME, make_config, make_fused_fp8
     from segmented_gather_gemm_lora_amd import binding as B
 
     if not torch.cuda.is_available():
@@ -771,18 +780,26 @@ def main():
         print("--paged applies to the SGMV/BGMV workloads, not the fused layer", file=sys.stderr)
         sys.exit(2)
 
-    prob0 = make_config(k)
+    fp8 = args.config == "fused_fp8"
+    wname = FUSED_FP8_NAME if fp8 else CONFIG_NAMES[k]
+
+    def make(seed=None):
+        if fp8:  # the fused workload over an FP8 (E4M3) base
+            return make_fused_fp8(k if seed is None else seed)
+        return make_config(k, seed=seed)
+
+    prob0 = make()
     ab = algorithmic_bytes(prob0)
     L = args.rotation or rotation_count(ab["total"])
-    print(f"[bench] {CONFIG_NAMES[k]}: T={prob0.T} d_in={prob0.d_in} d_out={prob0.d_out} rotation={L} "
+    print(f"[bench] {wname}: T={prob0.T} d_in={prob0.d_in} d_out={prob0.d_out} rotation={L} "
           f"bytes/layer={ab['total']/1e6:.2f} MB", file=sys.stderr, flush=True)
     if args.probe:
         rmw = 0 if kind == "fused" else int(np.count_nonzero(prob0.ids >= 0)) * prob0.d_out * prob0.esize
-        print(json.dumps({"workload": CONFIG_NAMES[k], "probes": run_probes(stream, ab["total"] - 2 * rmw, rmw, L)}))
+        print(json.dumps({"workload": wname, "probes": run_probes(stream, ab["total"] - 2 * rmw, rmw, L)}))
         return
     insts = [Instance(prob0, kind, stream, page, seed=0)]
     for i in range(1, L):
-        insts.append(Instance(make_config(k, seed=1000 * k + i), kind, stream, page, seed=i))
+        insts.append(Instance(make(1000 * k + i), kind, stream, page, seed=i))
     torch.cuda.synchronize()
     # every instance has its own distinct-adapter count; average the algorithmic bytes
     ab_all = [algorithmic_bytes(inst.prob) for inst in insts]
@@ -831,7 +848,7 @@ def main():
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
-    traffic, kname = recorded_traffic(CONFIG_NAMES[k] + (f"_paged{page}" if page else ""), dominant)
+    traffic, kname = recorded_traffic(wname + (f"_paged{page}" if page else ""), dominant)
     roof["traffic"] = traffic
     default_names = {"shrink": f"{kind}_shrink", "expand": f"{kind}_expand", "fused": "fused_linear"}
     if names == [kind]:
@@ -872,10 +889,11 @@ def main():
         "vs_baseline": None,
         "dtype": prob0.dtype,
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[k], "T": T, "d_in": prob0.d_in, "d_out": prob0.d_out,
+        "config": {"workload": wname, "T": T, "d_in": prob0.d_in, "d_out": prob0.d_out,
                    "ranks": sorted(set(int(r) for r in prob0.ranks)), "pool_adapters": prob0.n_adapters,
                    "distinct_adapters": int(len(prob0.distinct_adapters())), "rotated_instances": L,
-                   "path": kind + ("_paged" if page else ""), **({"page_bytes": page} if page else {})},
+                   "path": kind + ("_paged" if page else ""), **({"page_bytes": page} if page else {}),
+                   **({"w0_format": "e4m3", "w0_scale": "one fp32 per matrix"} if fp8 else {})},
         "timed_mode": mode,
         ("graph_ms_per_step" if mode == "eager" else "eager_ms_per_step"):
             None if other_ms is None else round(other_ms, 6),

@@ -608,6 +608,29 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
                       const void *W0, int32_t d_out, const lora_segments *seg,
                       void *y, int64_t ldy, void *ws, size_t ws_bytes);
 
+/* The fused layer over an FP8 base: W0 holds one OCP E4M3 code per element
+ * (sign, 4-bit exponent of bias 7, 3-bit mantissa; subnormals; the two codes
+ * 0x7F and 0xFF are NaN; largest finite 448) and stands for w0_scale * code,
+ * one fp32 scale for the whole matrix; x, y and the adapters are bf16
+ * ("Multi-LoRA serving: the single translator with a thousand glossaries"
+ * (blog.lo0.es), section "Combined pattern with quantisation and
+ * disaggregated serving": BF16 adapters over an FP8 base; the pages fix no
+ * scale granularity, one per matrix is the plainest reading).
+ * y = x (w0_scale q)^T + scale_s (x A_s) B_s, overwriting y.  The codes are
+ * widened to bf16 exactly (an E4M3 value has 4 significant bits) and
+ * multiplied on bf16 MFMA with fp32 accumulation; the accumulator holds
+ * x q^T + (scale_s / w0_scale) v B_s and is multiplied by w0_scale once
+ * before the single rounding to bf16.  Same launches, plan, workspace
+ * (lora_workspace_bytes(LORA_OP_FUSED, ...)) and rules as lora_fused_linear,
+ * except: W0 is [d_out, d_in] bytes with row pitch d_in, 16-byte aligned,
+ * d_in a multiple of 16, and W0 must span less than 4 GiB.
+ * Errors: as lora_fused_linear; LORA_ERR_ARG also for a w0_scale that is zero,
+ * infinite or NaN; LORA_ERR_ALIGN for d_in % 16 != 0. */
+int lora_fused_linear_e4m3(void *stream, const void *x, int64_t ldx, int32_t d_in,
+                           const void *W0, float w0_scale, int32_t d_out,
+                           const lora_segments *seg, void *y, int64_t ldy,
+                           void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------ helpers */
 enum {
     LORA_OP_SGMV_SHRINK = 0,

@@ -39,7 +39,7 @@ STATUS = {
 # Every symbol the public header declares.
 EXPORTS = [
     "lora_segments_bytes", "lora_segments_bind", "lora_build_segments", "lora_segments_upload", "lora_sgmv_shrink",
-    "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear",
+    "lora_sgmv_expand", "lora_sgmv", "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_fused_linear", "lora_fused_linear_e4m3",
     "lora_workspace_bytes", "lora_adapter_numel", "lora_status_string", "lora_last_error",
     "lora_version", "lora_profile_launches", "lora_profile_launches_used", "lora_bgmv_grouped",
     "lora_bgmv_grouped_workspace_bytes", "lora_cache_table_bytes", "lora_cache_create", "lora_cache_destroy",
@@ -83,6 +83,8 @@ _SIGS = {
     "lora_bgmv_expand": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32,
                                         _vp, _i64, _i32, _vp, _sz]),
     "lora_fused_linear": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _sz]),
+    "lora_fused_linear_e4m3": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, ctypes.c_float, _i32, _vp, _vp, _i64, _vp,
+                                              _sz]),
     "lora_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32, _i32]),
     "lora_adapter_numel": (_i64, [_i32, _i32, _i32]),
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -375,6 +377,10 @@ class AdapterCache:
 
 def lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes) -> int:
     return int(load().lora_fused_linear(stream, dtype, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes))
+
+
+def lora_fused_linear_e4m3(stream, x, ldx, d_in, W0, w0_scale, d_out, seg, y, ldy, ws, ws_bytes) -> int:
+    return int(load().lora_fused_linear_e4m3(stream, x, ldx, d_in, W0, w0_scale, d_out, seg, y, ldy, ws, ws_bytes))
 
 
 def lora_profile_launches(start_events, stop_events, count) -> int:
@@ -861,6 +867,14 @@ def fused_prepared(x, W0, plan: Plan, y, ws, dtype: str, stream) -> Prepared:
                     keep=(x, W0, plan, y, ws))
 
 
+def fused_e4m3_prepared(x, W0, w0_scale: float, plan: Plan, y, ws, stream) -> Prepared:
+    """W0: uint8 E4M3 codes [d_out, d_in] standing for w0_scale * code."""
+    return Prepared("lora_fused_linear_e4m3", (_stream_handle(stream), _ptr(x), x.stride(0), x.shape[1], _ptr(W0),
+                                               float(w0_scale), W0.shape[0], plan.seg, _ptr(y), y.stride(0), _ptr(ws),
+                                               ws.numel() * ws.element_size()),
+                    keep=(x, W0, plan, y, ws))
+
+
 def sgmv_grouped_prepared(projs, ws, dtype: str, stream, keep=()) -> Prepared:
     return Prepared("lora_sgmv_grouped", (_stream_handle(stream), DTYPES[dtype], ctypes.cast(projs, _vp).value,
                                           len(projs), _ptr(ws), ws.numel() * ws.element_size()),
@@ -973,6 +987,15 @@ def fused_linear(x, W0, plan: Plan, y, ws, dtype: str = "bf16", stream=None):
                              W0.shape[0], plan.seg, _ptr(y), y.stride(0),
                              _ptr(ws), ws.numel() * ws.element_size()),
            "lora_fused_linear")
+
+
+def fused_linear_e4m3(x, W0, w0_scale: float, plan: Plan, y, ws, stream=None):
+    """The fused layer over an FP8 base: W0 holds uint8 E4M3 codes [d_out, d_in]
+    standing for w0_scale * code; x, y and the adapters are bf16."""
+    _check(lora_fused_linear_e4m3(_stream_handle(stream), _ptr(x), x.stride(0), x.shape[1], _ptr(W0),
+                                  float(w0_scale), W0.shape[0], plan.seg, _ptr(y), y.stride(0),
+                                  _ptr(ws), ws.numel() * ws.element_size()),
+           "lora_fused_linear_e4m3")
 
 
 def v_pitch(max_rank: int) -> int:

@@ -9,6 +9,8 @@
 
 #include "internal.h"
 
+#include <cmath>
+
 static_assert(sizeof(lora_blk_desc) == 128, "block descriptor is one 128-byte record");
 static_assert(sizeof(lora_seg_desc) == 40, "segment descriptor layout");
 static_assert(sizeof(lora_chunk_desc) == 320, "chunk descriptor layout");
@@ -806,16 +808,17 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
                               pool_alpha_dev, n_adapters, max_rank);
 }
 
-int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *W0,
-                      int32_t d_out, const lora_segments *seg, void *y, int64_t ldy, void *ws, size_t ws_bytes)
+// Checks and launch shared by the bf16 and E4M3 forms of the fused entry.
+static int fused_common(void *stream, const void *x, int64_t ldx, int32_t d_in, const void *W0, int32_t d_out,
+                        const lora_segments *seg, void *y, int64_t ldy, void *ws, size_t ws_bytes, bool e4m3,
+                        float w0_scale)
 {
-    clear_error();
     const lora_plan_header *h = nullptr;
     const char *plan_dev = nullptr;
     int st = check_segments(seg, &h, &plan_dev);
     if (st) return st;
-    if ((st = check_dtype(dtype))) return st;
-    if (dtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "the fused entry takes bf16 only");
+    if (e4m3 && !(std::isfinite(w0_scale) && w0_scale != 0.0f))
+        return fail(LORA_ERR_ARG, "w0_scale must be finite and non-zero");
     const int32_t T = h->num_tokens;
     if (T == 0) return LORA_OK;
     if (!x || !W0 || !y) return fail(LORA_ERR_ARG, "x, W0 or y is NULL");
@@ -823,25 +826,44 @@ int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32
     if (ldx < d_in || ldy < d_out) return fail(LORA_ERR_ARG, "row pitch smaller than the row");
     if (!aligned16(x) || !aligned16(W0) || !aligned16(y) || (ldx * 2) % 16 || (ldy * 2) % 16 || (d_in * 2) % 16)
         return fail(LORA_ERR_ALIGN, "fused entry needs 16-byte aligned x, W0, y rows and d_in %% 8 == 0");
+    if (e4m3 && d_in % 16)
+        return fail(LORA_ERR_ALIGN, "an E4M3 W0 needs d_in %% 16 == 0 (16-byte rows), got %d", d_in);
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     const size_t need = fused_workspace_bytes(T, d_in, h->max_rank < 1 ? 1 : h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     ShrinkArgs sa{};
-    sa.dtype = dtype;
+    sa.dtype = LORA_BF16;
     sa.x = x;
     sa.ldx = ldx;
     sa.d_in = d_in;
     sa.vec = true;
     ExpandArgs ea{};
-    ea.dtype = dtype;
+    ea.dtype = LORA_BF16;
     ea.y = y;
     ea.ldy = ldy;
     ea.d_out = d_out;
     ea.vec_b = true;
     ea.vec_y = true;
-    return launch_fused_linear(static_cast<hipStream_t>(stream), sa, W0, ea,
-                               PlanView{h, plan_dev}, ws);
+    return launch_fused_linear(static_cast<hipStream_t>(stream), sa, W0, ea, PlanView{h, plan_dev}, ws, e4m3,
+                               w0_scale);
+}
+
+int lora_fused_linear(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in, const void *W0,
+                      int32_t d_out, const lora_segments *seg, void *y, int64_t ldy, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    int st = check_dtype(dtype);
+    if (st) return st;
+    if (dtype != LORA_BF16) return fail(LORA_ERR_DTYPE, "the fused entry takes bf16 only");
+    return fused_common(stream, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes, false, 1.0f);
+}
+
+int lora_fused_linear_e4m3(void *stream, const void *x, int64_t ldx, int32_t d_in, const void *W0, float w0_scale,
+                           int32_t d_out, const lora_segments *seg, void *y, int64_t ldy, void *ws, size_t ws_bytes)
+{
+    clear_error();
+    return fused_common(stream, x, ldx, d_in, W0, d_out, seg, y, ldy, ws, ws_bytes, true, w0_scale);
 }
 
 } // extern "C"

@@ -31,6 +31,17 @@
 // 24 consecutive output columns of one token: y is written with 16-byte
 // stores.  Workgroups are numbered so that the tiles that share W0 column
 // slabs run on the same XCD (its own L2).
+//
+// FP8 base (W0 = w0_scale * q, q as OCP E4M3 codes, one byte each; "Multi-LoRA
+// serving: the single translator ..." (blog.lo0.es), section "Combined pattern
+// with quantisation and disaggregated serving": BF16 adapters over an FP8
+// base): the W0 part of a stage holds rows of 32 bytes (2 units of 16 codes),
+// so a stage is 22 KB and the ring has 7 stages.  Each lane reads its 8 codes
+// of a fragment (8 bytes) from LDS and widens them to bf16 in registers with
+// the hardware E4M3 -> fp32 conversion and a bf16 pack (both exact: an E4M3
+// value has 4 significant bits).  The accumulators hold x q + (scale_s /
+// w0_scale) v B_s, which is multiplied by w0_scale once before the store; the
+// prep pass divides scale_s * v by w0_scale.
 #include "internal.h"
 
 namespace lora {
@@ -46,27 +57,36 @@ template <typename T> __device__ __forceinline__ gptr<T> as_global(const void *p
 constexpr int kBN = 192;                 // output columns per workgroup
 constexpr int kBM = 256;                 // plan rows per workgroup
 constexpr int kBK = 32;                  // k per stage
-constexpr int kStages = 5;               // LDS ring depth
 constexpr int kThreads = 512;            // 8 waves, 2 per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int kWN = 96, kWM = 64;        // wave tile: 2 x 4 waves cover 192 x 256
 constexpr int kTN = kWN / 16;            // MFMA tiles along columns (6)
 constexpr int kTM = kWM / 16;            // MFMA tiles along rows (4)
-constexpr int kRowBytes = kBK * 2;       // 64
-constexpr int kWBytes = kBN * kRowBytes; // W0 part of a stage
+constexpr int kRowBytes = kBK * 2;       // 64: an x row of a stage
 constexpr int kXBytes = kBM * kRowBytes; // x part of a stage
-constexpr int kStageBytes = kWBytes + kXBytes;
-// 1 KB direct loads per stage: W0 part 12, split 2/1 over the waves (waves
-// below kWExtra take one more); x part 16, two per wave
-constexpr int kWInst = kWBytes / 1024, kXInst = kXBytes / 1024;
-constexpr int kWBase = kWInst / kWaves, kWExtra = kWInst % kWaves;
-constexpr int kWDma = kWBase + (kWExtra ? 1 : 0); // most W0 loads of a wave
+constexpr int kXInst = kXBytes / 1024;   // 1 KB direct loads for it: 16, two per wave
 constexpr int kXDma = kXInst / kWaves;
-constexpr int kDma = kWDma + kXDma;
 constexpr int kMaxSlicesFused = 4; // bound on the shrink's d_in slices
-static_assert(kXDma * kWaves == kXInst && kWBase >= 1, "tile / wave split");
-static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
-static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
+static_assert(kXDma * kWaves == kXInst, "tile / wave split");
+
+// Stage geometry for a bf16 (W8 = false) or E4M3 (W8 = true) base.  The W0
+// part takes kWInst 1 KB direct loads per stage (12 or 6), split over the
+// waves: waves below kWExtra take one more than kWBase.
+template <bool W8> struct Geo {
+    static constexpr int kWElem = W8 ? 1 : 2;                // bytes per W0 element
+    static constexpr int kWRowBytes = kBK * kWElem;          // 32 or 64
+    static constexpr int kWUnits = kWRowBytes / 16;          // 16-byte units per W0 row
+    static constexpr int kWBytes = kBN * kWRowBytes;         // W0 part of a stage
+    static constexpr int kStageBytes = kWBytes + kXBytes;
+    static constexpr int kStages = W8 ? 7 : 5;               // LDS ring depth
+    static constexpr int kWInst = kWBytes / 1024;
+    static constexpr int kWBase = kWInst / kWaves, kWExtra = kWInst % kWaves;
+    static constexpr int kWDma = kWBase + (kWExtra ? 1 : 0); // most W0 loads of a wave
+    static constexpr int kDma = kWDma + kXDma;
+    static_assert(kWInst * 1024 == kWBytes && kWDma >= 1, "W0 stage split");
+    static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+    static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
+};
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
@@ -90,6 +110,27 @@ __device__ __forceinline__ int wave_col(int m, int j) { return (m >> 2) * 24 + 4
 // consecutive rows of a quarter-wave fragment read fall in 8 distinct 16-byte
 // bank groups (the fastest of the patterns measured on gfx950).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// E4M3 W0 rows (32 bytes, 2 units): unit u of row r sits in slot u ^ swz8(r).
+// A fragment read (8 bytes per lane, rows r0 .. r0 + 15 of one lane group)
+// then covers each 4-byte bank once per 32 lanes: rows r and r + 8 are 256
+// bytes apart and take opposite slots.
+__device__ __forceinline__ int swz8(int r) { return (r >> 3) & 1; }
+template <bool W8> __device__ __forceinline__ int wswz(int r) { return W8 ? swz8(r) : swz(r); }
+
+// Eight E4M3 codes (bytes of lo, then hi; byte i is element i) as bf16,
+// exactly: v_cvt_pk_f32_fp8 decodes two codes (OCP E4M3 on gfx950, NaN codes
+// to NaN) and every E4M3 value fits bf16's 8-bit significand and range.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    typedef float floatx2 __attribute__((ext_vector_type(2)));
+    const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(int(lo), false);
+    const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(int(lo), true);
+    const floatx2 c = __builtin_amdgcn_cvt_pk_f32_fp8(int(hi), false);
+    const floatx2 d = __builtin_amdgcn_cvt_pk_f32_fp8(int(hi), true);
+    const u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                     pack_bf16x2(d[0], d[1])};
+    return __builtin_bit_cast(bf16x8, u);
+}
 
 // s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt in 6:4, lgkmcnt in 11:8).  Written through the builtin, so that the compiler's
@@ -116,7 +157,8 @@ struct FusedArgs {
     const uint16_t *x;
     int64_t ldx;
     int d_in;
-    const uint16_t *W0;
+    const void *W0; // bf16 or E4M3 codes, [d_out, d_in]
+    float wscale;   // E4M3 base: the scale the codes stand for (1 for bf16)
     int d_out;
     const int32_t *perm;      // [T] plan row -> token
     const int32_t *segidx;    // [T'] sorted position -> segment
@@ -132,10 +174,13 @@ struct FusedArgs {
 // v of sorted row p, scaled and split, for the fused GEMM: for every 16 ranks
 // (chunk c) 32 bf16 at vh[p * ldh + 32 c]: hi of ranks 16c .. 16c+15, then lo
 // of the same ranks; ranks past r are zero.  One thread per 8 ranks of a row.
+// DIV (E4M3 base): the value is scale_s * v / wdiv, so that the accumulators
+// can be multiplied by the base's scale wdiv once at the end.
+template <bool DIV>
 __global__ __launch_bounds__(256) void fused_prep_kernel(const float *__restrict__ v, int64_t ldw, int64_t sl_stride,
                                                          int nsl, const int32_t *__restrict__ segidx,
                                                          const lora_seg_desc *__restrict__ seg, int Tp, int units,
-                                                         uint16_t *__restrict__ vh, int64_t ldh)
+                                                         float wdiv, uint16_t *__restrict__ vh, int64_t ldh)
 {
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int p = int(idx / units), u = int(idx % units);
@@ -161,7 +206,9 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(const float *__restrict
 #pragma unroll
         for (int c = 0; c < kMaxSlicesFused; ++c)
             if (c < nsl) sum += f[c][e >> 2][e & 3];
-        val[e] = j + e < r ? sum * scale : 0.f;
+        float t = sum * scale;
+        if (DIV) t = t / wdiv;
+        val[e] = j + e < r ? t : 0.f;
     }
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -290,9 +337,13 @@ __device__ __forceinline__ void lora_correction(const FusedArgs &a, int s0, int 
     }
 }
 
-template <bool VECB>
+template <bool VECB, bool W8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fused_linear_kernel(FusedArgs a)
 {
+    typedef Geo<W8> G;
+    constexpr int kStages = G::kStages, kStageBytes = G::kStageBytes, kWBytes = G::kWBytes;
+    constexpr int kWBase = G::kWBase, kWExtra = G::kWExtra, kWDma = G::kWDma, kDma = G::kDma;
+    constexpr int kWElem = G::kWElem, kWUnits = G::kWUnits, kWRowBytes = G::kWRowBytes;
     __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,23 +360,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int m0 = tm * kBM, n0 = tn * kBN;
 
     // Direct loads: lane `lane` of load instruction i fills 16-byte unit
-    // 64 i + lane of the W0 or x part of a stage, i.e. LDS row u / 4, slot
-    // u % 4, which holds k unit (u % 4) ^ swz(row).  This wave issues W0
-    // instructions wi0 .. wi0 + nw - 1 and x instructions kXDma * wave + j.
-    // Per lane: the byte offset of the unit in stage 0 (row start + 16 *
-    // unit) and the unit's first k.
+    // 64 i + lane of the W0 or x part of a stage, i.e. LDS row u / units, slot
+    // u % units, which holds k unit slot ^ swz(row) (units = 4 for x and a
+    // bf16 W0, 2 for an E4M3 W0).  This wave issues W0 instructions
+    // wi0 .. wi0 + nw - 1 and x instructions kXDma * wave + j.  Per lane: the
+    // byte offset of the unit in stage 0 (row start + 16 * unit) and the
+    // unit's first k.
     const int nw = kWBase + (wave < kWExtra ? 1 : 0);
     const int wi0 = wave * kWBase + (wave < kWExtra ? wave : kWExtra);
     uint32_t woff32[kWDma], xoff32[kXDma];
     int wk[kWDma], xk[kXDma];
 #pragma unroll
     for (int j = 0; j < kWDma; ++j) {
-        const int u = ((j < nw ? wi0 + j : wi0)) * 64 + lane, rho = u >> 2;
-        wk[j] = 8 * ((u & 3) ^ swz(rho));
+        const int u = ((j < nw ? wi0 + j : wi0)) * 64 + lane, rho = u / kWUnits;
+        wk[j] = (16 / kWElem) * ((u % kWUnits) ^ wswz<W8>(rho));
         const int rp = rho % kWN;
         int c = n0 + (rho / kWN) * kWN + wave_col(rp & 15, rp >> 4);
         c = c < a.d_out ? c : a.d_out - 1;
-        woff32[j] = uint32_t((int64_t(c) * a.d_in + wk[j]) * 2);
+        woff32[j] = uint32_t((int64_t(c) * a.d_in + wk[j]) * kWElem);
     }
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
@@ -336,14 +388,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         xoff32[j] = uint32_t((int64_t(as_global<int32_t>(a.perm)[p]) * a.ldx + xk[j]) * 2);
     }
     const int nk = (a.d_in + kBK - 1) / kBK;
-    // stage kt into ring slot kt % kStages.  A full stage adds kt * 64 bytes
-    // to the uniform bases; in a partial last stage, k units past d_in read
-    // the row's first unit (d_in % 8 == 0) and are zeroed when the fragments
-    // are read.
+    // stage kt into ring slot kt % kStages.  A full stage adds kt * kBK
+    // elements to the uniform bases; in a partial last stage, k units past
+    // d_in read the row's first unit (d_in is a multiple of the unit) and are
+    // zeroed when the fragments are read.
     auto issue = [&](int kt) {
         const uint32_t base = lds0 + uint32_t((kt % kStages) * kStageBytes);
         if ((kt + 1) * kBK <= a.d_in) {
-            const char *wb = reinterpret_cast<const char *>(a.W0) + int64_t(kt) * kRowBytes;
+            const char *wb = reinterpret_cast<const char *>(a.W0) + int64_t(kt) * kWRowBytes;
             const char *xb = reinterpret_cast<const char *>(a.x) + int64_t(kt) * kRowBytes;
 #pragma unroll
             for (int j = 0; j < kWDma; ++j)
@@ -355,8 +407,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int j = 0; j < kWDma; ++j) {
                 const int k = kt * kBK + wk[j];
-                const char *row = reinterpret_cast<const char *>(a.W0) + woff32[j] - 2 * wk[j];
-                if (j < nw) dma16(row + 2 * (k < a.d_in ? k : 0), base + uint32_t((wi0 + j) * 1024));
+                const char *row = reinterpret_cast<const char *>(a.W0) + woff32[j] - kWElem * wk[j];
+                if (j < nw) dma16(row + kWElem * (k < a.d_in ? k : 0), base + uint32_t((wi0 + j) * 1024));
             }
 #pragma unroll
             for (int j = 0; j < kXDma; ++j) {
@@ -400,7 +452,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int t = 0; t < kTN; ++t) {
         const int rho = kWN * wn + 16 * t + m;
-        woff[t] = uint32_t(rho * kRowBytes + ((g ^ swz(rho)) << 4));
+        if (W8) // 8 codes: half g & 1 of k unit g >> 1
+            woff[t] = uint32_t(rho * kWRowBytes + (((g >> 1) ^ swz8(rho)) << 4) + ((g & 1) << 3));
+        else
+            woff[t] = uint32_t(rho * kWRowBytes + ((g ^ swz(rho)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -412,13 +467,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // LDS and its MFMAs run; the ring then holds stages kt + 1 .. kt + 4.
     auto read_frags = [&](int kt, bf16x8 (&wf)[kTN], bf16x8 (&xf)[kTM]) {
         const char *st = lds + (kt % kStages) * kStageBytes;
+        if (W8) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int t = 0; t < kTN; ++t) wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + woff[t]));
+            for (int t = 0; t < kTN; ++t) {
+                const u32x2 q = *reinterpret_cast<const u32x2 *>(st + woff[t]);
+                wf[t] = e4m3x8_to_bf16(q[0], q[1]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kTN; ++t)
+                wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + woff[t]));
+        }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) xf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + xoff[i]));
         if (kt * kBK + 8 * g >= a.d_in) {
 #pragma unroll
             for (int i = 0; i < kTM; ++i) xf[i] = bf16x8{};
+            // an E4M3 unit past d_in holds codes of the row's first unit,
+            // which may be NaN: zero the weights too
+            if (W8) {
+#pragma unroll
+                for (int t = 0; t < kTN; ++t) wf[t] = bf16x8{};
+            }
         }
     };
     bf16x8 wc[kTN], xc[kTM], wn_[kTN], xn[kTM];
@@ -452,6 +523,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // no direct load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
+    if (W8) {
+#pragma unroll
+        for (int t = 0; t < kTN; ++t)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) acc[t][i] *= a.wscale;
+    }
     // y[token, cw0 + 24 g + 4 t + q] = acc[t][i][q]
     const int c0 = cw0 + 24 * g;
 #pragma unroll
@@ -496,15 +573,16 @@ size_t fused_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
 }
 
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
-                        const PlanView &p, void *ws)
+                        const PlanView &p, void *ws, bool w0_e4m3, float w0_scale)
 {
     const int T = p.h->num_tokens;
     if (T == 0) return LORA_OK;
     // The direct loads address x and W0 rows with 32-bit byte offsets from the
     // matrix start: both must span less than 4 GiB (every row start plus one
     // row).  Checked before anything is launched.
+    const int64_t wel = w0_e4m3 ? 1 : 2;
     const bool off32 = (int64_t(T) * sa.ldx + sa.d_in) * 2 < (int64_t(1) << 32) &&
-                       (int64_t(ea.d_out) * sa.d_in + sa.d_in) * 2 < (int64_t(1) << 32);
+                       (int64_t(ea.d_out) * sa.d_in + sa.d_in) * wel < (int64_t(1) << 32);
     if (!off32) return fail(LORA_ERR_ARG, "fused layer: x or W0 spans 4 GiB or more");
     float *v = static_cast<float *>(ws);
     int64_t ldw = 0, sl_stride = 0;
@@ -521,8 +599,13 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     if (Tp > 0) {
         const int units = int(ldh / 16);
         const int64_t threads = int64_t(Tp) * units;
-        launch_kernel(fused_prep_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, v, ldw, sl_stride,
-                      nsl, segidx, segs, Tp, units, vh, ldh);
+        const dim3 grid(unsigned((threads + 255) / 256));
+        if (w0_e4m3)
+            launch_kernel(fused_prep_kernel<true>, grid, dim3(256), 0, s, v, ldw, sl_stride, nsl, segidx, segs, Tp,
+                          units, w0_scale, vh, ldh);
+        else
+            launch_kernel(fused_prep_kernel<false>, grid, dim3(256), 0, s, v, ldw, sl_stride, nsl, segidx, segs, Tp,
+                          units, 1.0f, vh, ldh);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(LORA_ERR_HIP, "fused layer prep launch: %s", hipGetErrorString(e));
     }
@@ -530,7 +613,8 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     a.x = static_cast<const uint16_t *>(sa.x);
     a.ldx = sa.ldx;
     a.d_in = sa.d_in;
-    a.W0 = static_cast<const uint16_t *>(W0);
+    a.W0 = W0;
+    a.wscale = w0_e4m3 ? w0_scale : 1.0f;
     a.d_out = ea.d_out;
     a.perm = reinterpret_cast<const int32_t *>(p.dev + p.h->perm_offset);
     a.segidx = segidx;
@@ -549,8 +633,14 @@ int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, con
     const lora_seg_desc *hseg = reinterpret_cast<const lora_seg_desc *>(reinterpret_cast<const char *>(p.h) +
                                                                         p.h->seg_offset);
     for (int i = 0; i < p.h->num_segments; ++i) vecb = vecb && (hseg[i].rank & 7) == 0;
-    if (vecb) launch_kernel(fused_linear_kernel<true>, dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
-    else launch_kernel(fused_linear_kernel<false>, dim3(unsigned(nwg)), dim3(kThreads), 0, s, a);
+    const dim3 grid(static_cast<unsigned>(nwg));
+    if (w0_e4m3) {
+        if (vecb) launch_kernel(fused_linear_kernel<true, true>, grid, dim3(kThreads), 0, s, a);
+        else launch_kernel(fused_linear_kernel<false, true>, grid, dim3(kThreads), 0, s, a);
+    } else {
+        if (vecb) launch_kernel(fused_linear_kernel<true, false>, grid, dim3(kThreads), 0, s, a);
+        else launch_kernel(fused_linear_kernel<false, false>, grid, dim3(kThreads), 0, s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(LORA_ERR_HIP, "fused layer launch: %s", hipGetErrorString(e));
     return LORA_OK;

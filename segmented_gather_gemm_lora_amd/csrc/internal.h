@@ -123,8 +123,10 @@ size_t combined_workspace_bytes(int32_t rows, int32_t d_in, int32_t max_rank);
 // written).  ldw = round4(max_rank), sl_stride = T' * ldw.
 int launch_sgmv_shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *ws, int64_t *ldw,
                              int64_t *sl_stride, int *nsl);
+// w0_e4m3: W0 holds OCP E4M3 codes standing for w0_scale * code (finite,
+// non-zero scale); otherwise bf16.
 int launch_fused_linear(hipStream_t s, const ShrinkArgs &sa, const void *W0, const ExpandArgs &ea,
-                        const PlanView &p, void *ws);
+                        const PlanView &p, void *ws, bool w0_e4m3 = false, float w0_scale = 1.0f);
 size_t fused_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -21,7 +21,7 @@ FAKE_BASE = 0x7F0000000000  # plan building never dereferences device addresses
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_header_function():
@@ -310,6 +310,23 @@ def test_fused_argument_errors():
     assert f(None, 1, None, 256, 256, FX, 256, plan.dev(), FX, 256, FX, 1 << 20) == -1
     need = B.lora_workspace_bytes(B.LORA_OP_FUSED, 8, 256, 256, 8)
     assert need >= 8 * 16 * 4
+
+
+def test_fused_e4m3_argument_errors():
+    """The FP8-base entry: the scale must be finite and non-zero, d_in a
+    multiple of 16; otherwise the bf16 entry's rules."""
+    plan = _valid_plan()
+    f = B.lora_fused_linear_e4m3
+    ok = 1 << 20
+    for bad in (0.0, float("inf"), float("-inf"), float("nan")):
+        assert f(None, FX, 256, 256, FX, bad, 256, plan.dev(), FX, 256, FX, ok) == -1, bad
+    assert f(None, FX, 264, 264, FX, 0.5, 256, plan.dev(), FX, 256, FX, ok) == -4  # d_in % 16 = 8
+    assert f(None, FX, 256, 256, FX + 8, 0.5, 256, plan.dev(), FX, 256, FX, ok) == -4  # W0 not 16-byte aligned
+    assert f(None, FX, 256, 256, FX, 0.5, 256, plan.dev(), FX, 256, FX, 16) == -6  # workspace too small
+    assert f(None, FX, 256, 256, None, 0.5, 256, plan.dev(), FX, 256, FX, ok) == -1
+    empty = HostPlan(0)
+    assert B.lora_build_segments(0, None, 0, None, None, None, None, empty.seg) == 0
+    assert f(None, None, 0, 256, None, 0.5, 256, empty.dev(None), None, 256, None, 0) == 0  # T = 0
 
 
 def test_combined_argument_errors():
