@@ -481,7 +481,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
 #pragma unroll
         for (int i = 0; i < kTM; ++i) xf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + xoff[i]));
-        if (kt * kBK + 8 * g >= a.d_in) {
+        // only a partial last stage (a wave-uniform test) holds k past d_in
+        if ((kt + 1) * kBK > a.d_in && kt * kBK + 8 * g >= a.d_in) {
 #pragma unroll
             for (int i = 0; i < kTM; ++i) xf[i] = bf16x8{};
             // an E4M3 unit past d_in holds codes of the row's first unit,
@@ -492,34 +493,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
     };
-    bf16x8 wc[kTN], xc[kTM], wn_[kTN], xn[kTM];
+    // One k stage: wait for stage kt + 1, refill the ring, read stage
+    // kt + 1's fragments into (wnx, xnx) while the MFMAs of stage kt run on
+    // (wcur, xcur).  The loop below alternates the two register sets, so no
+    // fragment is copied between them.
+    auto stage = [&](int kt, bf16x8(&wcur)[kTN], bf16x8(&xcur)[kTM], bf16x8(&wnx)[kTN], bf16x8(&xnx)[kTM]) {
+        // stage kt + 1 complete (later stages may be outstanding); after the
+        // barrier every wave is past its reads of stage kt, so the slot of
+        // stage kt - 1 is free for stage kt + kStages - 1
+        if (nw == kWDma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((kDma - 1) * (kStages - 3)));
+        __builtin_amdgcn_s_barrier();
+        const int nxt = kt + kStages - 1;
+        issue(nxt < nk ? nxt : nk - 1);
+        read_frags(kt + 1 < nk ? kt + 1 : kt, wnx, xnx);
+#pragma unroll
+        for (int t = 0; t < kTN; ++t)
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[t], xcur[i], acc[t][i], 0, 0, 0);
+    };
+    bf16x8 wa[kTN], xa[kTM], wb[kTN], xb[kTM];
     // Drain every load issued so far (the first stages and the correction's
     // operands): the compiler then knows that no load of its own is pending
     // in the loop, and inserts no wait there that would also wait for the
     // direct loads in flight.  The barrier publishes every wave's stage 0.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    read_frags(0, wc, xc);
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt + 1 complete (stages kt + 2, kt + 3 may be outstanding);
-        // after the barrier every wave is past its reads of stage kt, so the
-        // slot of stage kt - 1 is free for stage kt + 4
-        if (nw == kWDma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((kDma - 1) * (kStages - 3)));
-        __builtin_amdgcn_s_barrier();
-        const int nxt = kt + kStages - 1;
-        issue(nxt < nk ? nxt : nk - 1);
-        read_frags(kt + 1 < nk ? kt + 1 : kt, wn_, xn);
-#pragma unroll
-        for (int t = 0; t < kTN; ++t)
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
-                acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[t], xc[i], acc[t][i], 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < kTN; ++t) wc[t] = wn_[t];
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) xc[i] = xn[i];
+    read_frags(0, wa, xa);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        stage(kt, wa, xa, wb, xb);
+        stage(kt + 1, wb, xb, wa, xa);
     }
+    if (kt < nk) stage(kt, wa, xa, wb, xb);
     // no direct load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
