@@ -36,12 +36,14 @@
 // serving: the single translator ..." (blog.lo0.es), section "Combined pattern
 // with quantisation and disaggregated serving": BF16 adapters over an FP8
 // base): the W0 part of a stage holds rows of 32 bytes (2 units of 16 codes),
-// so a stage is 22 KB and the ring has 7 stages.  Each lane reads its 8 codes
-// of a fragment (8 bytes) from LDS and widens them to bf16 in registers with
-// the hardware E4M3 -> fp32 conversion and a bf16 pack (both exact: an E4M3
-// value has 4 significant bits).  The accumulators hold x q + (scale_s /
-// w0_scale) v B_s, which is multiplied by w0_scale once before the store; the
-// prep pass divides scale_s * v by w0_scale.
+// so a stage is 22 KB and the ring has 6 stages.  Once per stage the
+// workgroup widens the stage's codes to bf16 (the hardware E4M3 -> fp32
+// conversion and a bf16 pack, both exact: an E4M3 value has 4 significant
+// bits) into one of two bf16 W0 tiles laid out as the bf16 base's, two stages
+// ahead of the MFMAs, so the fragment reads are the bf16 kernel's.  The
+// accumulators hold x q + (scale_s / w0_scale) v B_s, which is multiplied by
+// w0_scale once before the store; the prep pass divides scale_s * v by
+// w0_scale.
 #include "internal.h"
 
 namespace lora {
@@ -78,14 +80,23 @@ template <bool W8> struct Geo {
     static constexpr int kWUnits = kWRowBytes / 16;          // 16-byte units per W0 row
     static constexpr int kWBytes = kBN * kWRowBytes;         // W0 part of a stage
     static constexpr int kStageBytes = kWBytes + kXBytes;
-    static constexpr int kStages = W8 ? 7 : 5;               // LDS ring depth
+    static constexpr int kStages = W8 ? 6 : 5;               // LDS ring depth
+    // E4M3: two bf16 W0 tiles after the ring; the codes of stage c are
+    // widened into tile c % 2 while stage c - 1 is consumed
+    static constexpr int kWbfBytes = kBN * kBK * 2;
+    static constexpr int kLdsBytes = kStages * kStageBytes + (W8 ? 2 * kWbfBytes : 0);
+    // stages past the one being consumed that must have landed at the top of
+    // an iteration: the next (its fragments are read), and for E4M3 the one
+    // after it (its codes are widened)
+    static constexpr int kAhead = W8 ? 2 : 1;
     static constexpr int kWInst = kWBytes / 1024;
     static constexpr int kWBase = kWInst / kWaves, kWExtra = kWInst % kWaves;
     static constexpr int kWDma = kWBase + (kWExtra ? 1 : 0); // most W0 loads of a wave
     static constexpr int kDma = kWDma + kXDma;
     static_assert(kWInst * 1024 == kWBytes && kWDma >= 1, "W0 stage split");
-    static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     static_assert(kDma * (kStages - 2) <= 63, "vmcnt range");
+    static_assert(kStages - 2 - kAhead >= 1, "ring depth");
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
@@ -110,12 +121,9 @@ __device__ __forceinline__ int wave_col(int m, int j) { return (m >> 2) * 24 + 4
 // consecutive rows of a quarter-wave fragment read fall in 8 distinct 16-byte
 // bank groups (the fastest of the patterns measured on gfx950).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
-// E4M3 W0 rows (32 bytes, 2 units): unit u of row r sits in slot u ^ swz8(r).
-// A fragment read (8 bytes per lane, rows r0 .. r0 + 15 of one lane group)
-// then covers each 4-byte bank once per 32 lanes: rows r and r + 8 are 256
-// bytes apart and take opposite slots.
-__device__ __forceinline__ int swz8(int r) { return (r >> 3) & 1; }
-template <bool W8> __device__ __forceinline__ int wswz(int r) { return W8 ? swz8(r) : swz(r); }
+// E4M3 W0 rows (32 bytes, 2 units) are stored unswizzled: they are read
+// only by the widening pass, one 16-byte unit per lane in address order.
+template <bool W8> __device__ __forceinline__ int wswz(int r) { return W8 ? 0 : swz(r); }
 
 // Eight E4M3 codes (bytes of lo, then hi; byte i is element i) as bf16,
 // exactly: v_cvt_pk_f32_fp8 decodes two codes (OCP E4M3 on gfx950, NaN codes
@@ -136,6 +144,8 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi)
 // 15:14, expcnt in 6:4, lgkmcnt in 11:8).  Written through the builtin, so that the compiler's
 // own wait insertion knows about them.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate for lgkmcnt(0) alone
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // 16 bytes per lane from global memory to LDS at m0 + 16 * lane.  The
 // compiler does not see this write to LDS; the kernel waits for it with an
@@ -344,7 +354,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int kStages = G::kStages, kStageBytes = G::kStageBytes, kWBytes = G::kWBytes;
     constexpr int kWBase = G::kWBase, kWExtra = G::kWExtra, kWDma = G::kWDma, kDma = G::kDma;
     constexpr int kWElem = G::kWElem, kWUnits = G::kWUnits, kWRowBytes = G::kWRowBytes;
-    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
+    constexpr int kWbfBytes = G::kWbfBytes, kAhead = G::kAhead;
+    __shared__ __attribute__((aligned(1024))) char lds[G::kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, g = lane >> 4;
@@ -450,12 +461,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // fragment byte offsets inside a stage
     uint32_t woff[kTN], xoff[kTM];
 #pragma unroll
-    for (int t = 0; t < kTN; ++t) {
+    for (int t = 0; t < kTN; ++t) { // bf16 W0 rows of 64 bytes (an E4M3 base's widened tile too)
         const int rho = kWN * wn + 16 * t + m;
-        if (W8) // 8 codes: half g & 1 of k unit g >> 1
-            woff[t] = uint32_t(rho * kWRowBytes + (((g >> 1) ^ swz8(rho)) << 4) + ((g & 1) << 3));
-        else
-            woff[t] = uint32_t(rho * kWRowBytes + ((g ^ swz(rho)) << 4));
+        woff[t] = uint32_t(rho * 64 + ((g ^ swz(rho)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -467,18 +475,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // LDS and its MFMAs run; the ring then holds stages kt + 1 .. kt + 4.
     auto read_frags = [&](int kt, bf16x8 (&wf)[kTN], bf16x8 (&xf)[kTM]) {
         const char *st = lds + (kt % kStages) * kStageBytes;
-        if (W8) {
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const char *sw = W8 ? lds + kStages * kStageBytes + (kt & 1) * kWbfBytes : st;
 #pragma unroll
-            for (int t = 0; t < kTN; ++t) {
-                const u32x2 q = *reinterpret_cast<const u32x2 *>(st + woff[t]);
-                wf[t] = e4m3x8_to_bf16(q[0], q[1]);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < kTN; ++t)
-                wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + woff[t]));
-        }
+        for (int t = 0; t < kTN; ++t)
+            wf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw + woff[t]));
 #pragma unroll
         for (int i = 0; i < kTM; ++i) xf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(st + xoff[i]));
         // only a partial last stage (a wave-uniform test) holds k past d_in
@@ -493,25 +493,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
     };
-    // One k stage: wait for stage kt + 1, refill the ring, read stage
-    // kt + 1's fragments into (wnx, xnx) while the MFMAs of stage kt run on
-    // (wcur, xcur).  The loop below alternates the two register sets, so no
-    // fragment is copied between them.
+    // E4M3: widen the codes of stage c into bf16 W0 tile c % 2.  Threads
+    // below kBN * kWUnits (whole waves) take one 16-code unit each: unit u is
+    // row u / 2, k 16 (u % 2) .. + 15, i.e. bf16 units 2 (u % 2) and
+    // 2 (u % 2) + 1 of the row.
+    // widen_load reads the unit, widen_store converts and writes it, so that
+    // a stage can put its fragment reads and MFMAs between the two.
+    const bool widener = W8 && tid < kBN * kWUnits; // wave-uniform
+    auto widen_load = [&](int c) {
+        u32x4 q = u32x4{};
+        if (widener && c < nk) q = *reinterpret_cast<const u32x4 *>(lds + (c % kStages) * kStageBytes + 16 * tid);
+        return q;
+    };
+    auto widen_store = [&](int c, const u32x4 &q) {
+        if (!widener || c >= nk) return;
+        const int rho = tid >> 1, j0 = 2 * (tid & 1);
+        char *dst = lds + kStages * kStageBytes + (c & 1) * kWbfBytes + rho * 64;
+        *reinterpret_cast<bf16x8 *>(dst + ((j0 ^ swz(rho)) << 4)) = e4m3x8_to_bf16(q[0], q[1]);
+        *reinterpret_cast<bf16x8 *>(dst + (((j0 + 1) ^ swz(rho)) << 4)) = e4m3x8_to_bf16(q[2], q[3]);
+    };
+    // One k stage: wait for stage kt + kAhead, refill the ring, (E4M3) widen
+    // stage kt + 2, read stage kt + 1's fragments into (wnx, xnx) while the
+    // MFMAs of stage kt run on (wcur, xcur).  The loop below alternates the
+    // two register sets, so no fragment is copied between them.
     auto stage = [&](int kt, bf16x8(&wcur)[kTN], bf16x8(&xcur)[kTM], bf16x8(&wnx)[kTN], bf16x8(&xnx)[kTM]) {
-        // stage kt + 1 complete (later stages may be outstanding); after the
-        // barrier every wave is past its reads of stage kt, so the slot of
+        // stages up to kt + kAhead complete (later ones may be outstanding);
+        // after the barrier every wave is past its reads of stage kt (and of
+        // bf16 tile kt % 2, which stage kt + 2 reuses), so the ring slot of
         // stage kt - 1 is free for stage kt + kStages - 1
-        if (nw == kWDma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 3)));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((kDma - 1) * (kStages - 3)));
+        if (nw == kWDma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma * (kStages - 2 - kAhead)));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm((kDma - 1) * (kStages - 2 - kAhead)));
+        // E4M3: this wave's reads of tile kt % 2 (stage kt's fragments,
+        // issued in the previous stage) are complete before any wave passes
+        // the barrier and widens stage kt + 2 into that tile
+        if (W8) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
         const int nxt = kt + kStages - 1;
         issue(nxt < nk ? nxt : nk - 1);
+        const u32x4 q = widen_load(kt + 2);
         read_frags(kt + 1 < nk ? kt + 1 : kt, wnx, xnx);
 #pragma unroll
         for (int t = 0; t < kTN; ++t)
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
                 acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[t], xcur[i], acc[t][i], 0, 0, 0);
+        widen_store(kt + 2, q);
     };
     bf16x8 wa[kTN], xa[kTM], wb[kTN], xb[kTM];
     // Drain every load issued so far (the first stages and the correction's
@@ -520,6 +546,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // direct loads in flight.  The barrier publishes every wave's stage 0.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
+    if (W8) { // the first two widened tiles
+        widen_store(0, widen_load(0));
+        widen_store(1, widen_load(1));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+    }
     read_frags(0, wa, xa);
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
