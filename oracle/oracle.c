@@ -184,7 +184,7 @@ int oracle_lora_forward(int32_t T, int32_t d_in, int32_t d_out, int32_t is_bf16,
     int bad = 0;
     for (int32_t t = 0; t < T; ++t) {
         if (ids[t] >= n_adapters) bad = 1;
-        if (ids[t] >= 0 && rank[ids[t]] < 1) bad = 1;
+        else if (ids[t] >= 0 && rank[ids[t]] < 1) bad = 1;
     }
     if (bad) return -1;
     if (nthreads < 1) nthreads = 1;
