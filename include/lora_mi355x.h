@@ -252,7 +252,12 @@ int lora_sgmv_shrink(void *stream, int dtype, const void *x, int64_t ldx, int32_
 /* Segmented expand, the pages' "Expand Stage" (same section): scale and
  * accumulate into the base output,
  *     y[perm[p], n] += scale_s * sum_{j < r_s} v[p, j] * B_s[n, j]   for n < d_out.
- * Rows of tokens without an adapter are not touched.
+ * Rows of tokens without an adapter are not touched.  Precision (every
+ * expand of the library, SGMV and BGMV): bf16 calls multiply on bf16 MFMA with
+ * fp32 accumulation, each fp32 v value fed as its two bf16 halves hi = bf16(v)
+ * and lo = bf16(v - hi) (16 significant bits, a residual below 2^-17 of v);
+ * the sum is scaled in fp32 and rounded to bf16 once.  fp32 calls multiply
+ * exactly in fp32.
  * Errors: as lora_sgmv_shrink. */
 int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
                      const lora_segments *seg, void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);

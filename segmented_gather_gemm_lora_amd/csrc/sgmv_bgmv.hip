@@ -23,11 +23,13 @@
 //    slice results are fp32 partial sums, added in slice order by the expand.
 //    Each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of
 //    blocks, so the A slice of a segment is fetched into few L2s.
-//  * expand: D[column, token] += B[column, j] * v[token, j] on the fp32 MFMA
-//    (v stays fp32; bf16 B is widened exactly).  Output columns are assigned to
-//    MFMA rows so that each lane owns 16 consecutive columns of one token: y is
-//    prefetched at the start and written once, with 16-byte accesses, rounded
-//    to bf16 with v_cvt_pk_bf16_f32.
+//  * expand: D[column, token] += B[column, j] * v[token, j].  bf16: on
+//    v_mfma_f32_16x16x32_bf16, one instruction per 16 ranks, the fp32 v fed as
+//    its hi and lo bf16 halves (16 significant bits; see mfma_bf16_step);
+//    fp32: on v_mfma_f32_16x16x4_f32 with v and B exact.  Output columns are
+//    assigned to MFMA rows so that each lane owns 16 consecutive columns of one
+//    token: y is prefetched at the start and written once, with 16-byte
+//    accesses, rounded to bf16 with v_cvt_pk_bf16_f32.
 //
 // Latency: every load a workgroup needs depends on at most one earlier load
 // (the block descriptor, or the decode ids), so a kernel costs about two
@@ -446,6 +448,63 @@ __device__ __forceinline__ void load_bfrag(const M &mem, const void *Bv, int r, 
     }
 }
 
+// bf16 expand step on bf16 MFMA.  Lane group g holds 4 ranks j0 .. j0 + 3 (j0
+// = 16 c + 4 g) of B (bf16, the A operand: MFMA row = output column) and of v
+// (fp32, the B operand: MFMA column = token).  One v_mfma_f32_16x16x32_bf16
+// covers the step's 16 ranks: lane group g fills k slots 8 g .. 8 g + 3 with
+// its ranks against the hi bf16 halves of v and slots 8 g + 4 .. 8 g + 7 with
+// the same ranks against the lo halves (hi = bf16(v), lo = bf16(v - hi): the
+// fp32 v to 16 significant bits, a residual below 2^-17 of it), B repeated.
+// Every bf16 expand form multiplies through this helper in the same step
+// order, so all forms give the same bits.
+struct VHalves { // the hi and lo halves of 4 v values, packed bf16 (element 2e in the low half of dword e)
+    uint32_t h0, h1, l0, l1;
+};
+__device__ __forceinline__ VHalves v_halves(const floatx4 &vf)
+{
+    VHalves r;
+    r.h0 = pack_bf16x2(vf[0], vf[1]);
+    r.h1 = pack_bf16x2(vf[2], vf[3]);
+    r.l0 = pack_bf16x2(vf[0] - bf16_to_f32(r.h0 & 0xffffu), vf[1] - bf16_to_f32(r.h0 >> 16));
+    r.l1 = pack_bf16x2(vf[2] - bf16_to_f32(r.h1 & 0xffffu), vf[3] - bf16_to_f32(r.h1 >> 16));
+    return r;
+}
+// b: B of the lane's 4 ranks, packed bf16 (zero where out of range).
+__device__ __forceinline__ floatx4 mfma_bf16_step(const u32x2 &b, const VHalves &vh, const floatx4 &acc)
+{
+    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], b[0], b[1]});
+    const bf16x8 x = __builtin_bit_cast(bf16x8, u32x4{vh.h0, vh.h1, vh.l0, vh.l1});
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x, acc, 0, 0, 0);
+}
+
+// B of ranks j0 .. j0 + 3 of this lane's column in each of the 4 tiles, packed
+// bf16; zero past r or d_out.  BV: r % 4 == 0, one 8-byte load.
+template <bool BV, class M>
+__device__ __forceinline__ void load_braw(const M &mem, const void *Bv, int r, int j0, int ncol0, int m, int d_out,
+                                          u32x2 (&br)[4])
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int ncol = ncol0 + Cols<LORA_BF16>::of(m >> 2, 4 * t + (m & 3));
+        const bool cok = ncol < d_out;
+        const int64_t rowoff = int64_t(cok ? ncol : d_out - 1) * r;
+        if constexpr (BV) {
+            const u32x2 q = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + (j0 < r ? j0 : 0)));
+            br[t] = cok && j0 < r ? q : u32x2{0u, 0u};
+        } else {
+            uint32_t w[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = j0 + 2 * e;
+                const uint32_t lo = *mem.template at<uint16_t>(Bv, rowoff + (j < r ? j : r - 1));
+                const uint32_t hi = *mem.template at<uint16_t>(Bv, rowoff + (j + 1 < r ? j + 1 : r - 1));
+                w[e] = (cok && j < r ? lo : 0u) | ((cok && j + 1 < r ? hi : 0u) << 16);
+            }
+            br[t] = u32x2{w[0], w[1]};
+        }
+    }
+}
+
 // v rows of a block: VIND = indexed through yrows (BGMV: the token index),
 // else contiguous from vrow0 (SGMV: sorted positions).  UPT = float4 units of v
 // per thread (the launcher sizes it so that UPT*256 >= rows*ldl/4).  Split in a
@@ -552,8 +611,10 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     // waiting hook: B and y first, then the hook, then v)
     VStage<UPT> vst;
     if constexpr (!Pre::kWaits) stage_v_load<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
-    float bf[4][4];
-    load_bfrag<DT, BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, bf);
+    float bf[4][4]; // fp32 B
+    u32x2 br[4];    // bf16 B
+    if constexpr (DT == LORA_BF16) load_braw<BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, br);
+    else load_bfrag<DT, BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, bf);
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
     if constexpr (Pre::kWaits) {
@@ -569,13 +630,23 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     const int nch = (r + 15) >> 4;
     for (int c = 0; c < nch; ++c) {
         const int j0 = 16 * c + 4 * g;
-        if (c > 0) load_bfrag<DT, BV>(mem, Bv, r, j0, ncol0, m, d_out, bf);
+        if (c > 0) {
+            if constexpr (DT == LORA_BF16) load_braw<BV>(mem, Bv, r, j0, ncol0, m, d_out, br);
+            else load_bfrag<DT, BV>(mem, Bv, r, j0, ncol0, m, d_out, bf);
+        }
         floatx4 vf = *reinterpret_cast<const floatx4 *>(vl + (m < nrows ? m : 0) * ldl + (j0 < ldl ? j0 : 0));
         if (m >= nrows || j0 >= ldl) vf = floatx4{};
+        if constexpr (DT == LORA_BF16) {
+            const VHalves vh = v_halves(vf);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_step(br[t], vh, acc[t]);
+        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[t][q], vf[q], acc[t], 0, 0, 0);
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[t][q], vf[q], acc[t], 0, 0, 0);
+        }
     }
     if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
 }
@@ -612,6 +683,7 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
         for (int c = 0; c < NCH; ++c) {
             const int j0 = 16 * c + 4 * g;
             braw[c][t] = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + (j0 < r ? j0 : 0)));
+            if (!(cok[t] && j0 < r)) braw[c][t] = u32x2{0u, 0u};
         }
     }
     YTile<DT> yt;
@@ -632,15 +704,9 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
         const int j0 = 16 * c + 4 * g;
         floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
         if (m >= nrows || j0 >= ldl) vf = floatx4{};
+        const VHalves vh = v_halves(vf);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool ok = cok[t] && j0 < r;
-            const u32x2 q2 = braw[c][t];
-            const float b[4] = {ok ? bf16_to_f32(q2[0] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[0] >> 16) : 0.f,
-                                ok ? bf16_to_f32(q2[1] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[1] >> 16) : 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q], vf[q], acc[t], 0, 0, 0);
-        }
+        for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_step(braw[c][t], vh, acc[t]);
     }
     if (yr >= 0) y_store<DT, VECY>(yv, int64_t(yr) * ldy, ncol0, g, d_out, yt, acc, scale);
 }
@@ -708,9 +774,13 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
     const int ysafe = CONTIG ? ybase : yrows[0];
     VStage<UPT> vst;
     if constexpr (!Pre::kWaits) stage_v_load<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
-    float bf[NCH][4][4];
+    float bf[NCH][4][4]; // fp32 B
+    u32x2 br[NCH][4];    // bf16 B
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) load_bfrag<DT, BV>(mem, Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
+    for (int c = 0; c < NCH; ++c) {
+        if constexpr (DT == LORA_BF16) load_braw<BV>(mem, Bv, r, 16 * c + 4 * g, ncol0, m, d_out, br[c]);
+        else load_bfrag<DT, BV>(mem, Bv, r, 16 * c + 4 * g, ncol0, m, d_out, bf[c]);
+    }
     // rows past the chunk read the first row again (never stored)
     YTile<DT> yt[RB];
 #pragma unroll
@@ -736,11 +806,17 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
             const int j0 = 16 * c + 4 * g;
             floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
             if (row >= nrows || j0 >= ldl) vf = floatx4{};
+            if constexpr (DT == LORA_BF16) {
+                const VHalves vh = v_halves(vf);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_step(br[c][t], vh, acc[t]);
+            } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[c][t][q], vf[q], acc[t], 0, 0, 0);
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[c][t][q], vf[q], acc[t], 0, 0, 0);
+            }
         }
         if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc, scale);
     }
@@ -951,6 +1027,7 @@ __device__ __forceinline__ void expand_chunk_wide(const float *__restrict__ v, i
         for (int c = 0; c < NCH; ++c) {
             const int j0 = 16 * c + 4 * g;
             braw[c][t] = *(global_ptr<u32x2>)(mem.template at<uint16_t>(Bv, rowoff + (j0 < r ? j0 : 0)));
+            if (!(cok[t] && j0 < r)) braw[c][t] = u32x2{0u, 0u};
         }
     }
     YTile<DT> yt[RB];
@@ -979,15 +1056,9 @@ __device__ __forceinline__ void expand_chunk_wide(const float *__restrict__ v, i
             const int j0 = 16 * c + 4 * g;
             floatx4 vf = *reinterpret_cast<const floatx4 *>(vrow + (j0 < ldl ? j0 : 0));
             if (row >= nrows || j0 >= ldl) vf = floatx4{};
+            const VHalves vh = v_halves(vf);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bool ok = cok[t] && j0 < r;
-                const u32x2 q2 = braw[c][t];
-                const float b[4] = {ok ? bf16_to_f32(q2[0] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[0] >> 16) : 0.f,
-                                    ok ? bf16_to_f32(q2[1] & 0xffffu) : 0.f, ok ? bf16_to_f32(q2[1] >> 16) : 0.f};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q], vf[q], acc[t], 0, 0, 0);
-            }
+            for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_step(braw[c][t], vh, acc[t]);
         }
         if (yr[i] >= 0) y_store<DT, VECY>(yv, int64_t(yr[i]) * ldy, ncol0, g, d_out, yt[i], acc, scale);
     }
