@@ -197,19 +197,29 @@ __device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, cons
 // Results of the W waves are added in wave order through LDS (`red`, W*RT*1 KB).
 // Output row of block row mm: orows[mm] if orows (LDS) is given, else orow0 + mm.
 // ----------------------------------------------------------------------------
-// Stores of a result another workgroup reads in the same launch: device-scope
-// (write-through) stores, so that the reader's device-scope loads see them.
-template <bool SCOPED> __device__ __forceinline__ void put_result(float *p, float v)
+// Result stores.  MODE 0: plain.  MODE 1: a result another workgroup reads in
+// the same launch: device-scope (write-through) stores, so that the reader's
+// device-scope loads see them.  MODE 2: element e of `out` is a 64-bit word,
+// the value's bits in the low half and the launch's tag in the high half,
+// stored with one device-scope 64-bit store: a reader that sees the tag sees
+// the value written with it (no flag, no wait for the store to complete).
+template <int MODE> __device__ __forceinline__ void put_result(float *out, int64_t e, float v, uint32_t tag)
 {
-    if constexpr (SCOPED) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *p = v;
+    if constexpr (MODE == 2)
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(out) + e,
+                           (uint64_t(tag) << 32) | uint64_t(__float_as_uint(v)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    else if constexpr (MODE == 1)
+        __hip_atomic_store(out + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        out[e] = v;
 }
 
-template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem, bool SCOPED = false>
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem, int SCOPED = 0>
 __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xr, int xr0,
                                              const void *__restrict__ Av, int d_in, int r, int k_begin, int k_end,
                                              float *__restrict__ out, int64_t ldo, int orow0, const int *orows, int n,
-                                             float *red, const M &mem = M{})
+                                             float *red, const M &mem = M{}, uint32_t tag = 0)
 {
     using F = Frag<DT>;
     using T = typename F::T;
@@ -262,7 +272,8 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int mm = 4 * g + q, j = 16 * (rt0 + i) + m;
-                    if (mm < n && j < r) put_result<SCOPED>(out + int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, acc[i][q]);
+                    if (mm < n && j < r)
+                        put_result<SCOPED>(out, int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, acc[i][q], tag);
                 }
         } else {
 #pragma unroll
@@ -276,7 +287,7 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
                 for (int w = 0; w < W; ++w) sum += red[((w * RT + i) * 64 + l2) * 4 + q];
                 const int mm = 4 * (l2 >> 4) + q, j = 16 * (rt0 + i) + (l2 & 15);
-                if (mm < n && j < r) put_result<SCOPED>(out + int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, sum);
+                if (mm < n && j < r) put_result<SCOPED>(out, int64_t(orows ? orows[mm] : orow0 + mm) * ldo + j, sum, tag);
             }
             __syncthreads();
         }
@@ -556,6 +567,56 @@ __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_
     }
 }
 
+// stage_v_load for partial sums stored as tagged 64-bit words (put_result mode
+// 2): the loads are repeated (s_sleep between rounds) until every word this
+// thread needs holds `tag`, at most `limit` rounds (limit < 0: gives up at
+// once).  Returns false when it gave up; st then holds no meaningful values.
+template <bool BV, bool VIND, int UPT>
+__device__ __forceinline__ bool stage_v_wait_tagged(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+                                                    int nsl, const int *yrows, int vrow0, int nrows, int r, int ldl,
+                                                    VStage<UPT> &st, uint32_t tag, int limit)
+{
+    const uint64_t *w = reinterpret_cast<const uint64_t *>(v);
+    const int q4 = ldl >> 2;
+    const int units = nrows * q4;
+    if (limit < 0) return false; // the host forces every wait to give up at once
+    int64_t base[UPT];
+    int jj[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const int u = threadIdx.x + k * int(blockDim.x);
+        st.uok[k] = u < units;
+        const int uu = st.uok[k] ? u : 0;
+        const int row = uu / q4, j = 4 * (uu - row * q4);
+        st.off[k] = row * ldl + j;
+        int vr;
+        if constexpr (VIND) vr = yrows[row]; // LDS
+        else vr = vrow0 + row;
+        st.vok[k] = st.uok[k] && vr >= 0 && j < r;
+        base[k] = int64_t(st.vok[k] ? vr : 0) * ldv + (j < r ? j : 0);
+        jj[k] = j;
+    }
+    for (int round = 0;; ++round) {
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < UPT; ++k)
+#pragma unroll
+            for (int sl = 0; sl < kMaxSlices; ++sl)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool need = st.vok[k] && sl < nsl && (BV || jj[k] + e < r);
+                    const uint64_t q = need ? __hip_atomic_load(w + base[k] + sl * sl_stride + e, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT)
+                                            : uint64_t(tag) << 32;
+                    all = all && uint32_t(q >> 32) == tag;
+                    st.w[k][sl][e] = __uint_as_float(uint32_t(q));
+                }
+        if (all) return true;
+        if (limit < 0 || round >= limit) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 // LDS of an expand workgroup: its rows (16 or 64) of ldl floats, then one spare float4
 // (at float offset `spare`) that absorbs the stores of units past the rows.
 template <bool BV, int UPT>
@@ -589,6 +650,7 @@ __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare
 // the body then stores nothing.  NoPre keeps the plain order (v first).
 struct NoPre {
     static constexpr bool kWaits = false;
+    static constexpr bool kTagged = false;
     __device__ __forceinline__ bool operator()() const { return true; }
 };
 
@@ -617,12 +679,20 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     else load_bfrag<DT, BV>(mem, Bv, r, 4 * g, ncol0, m, d_out, bf);
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
-    if constexpr (Pre::kWaits) {
+    bool got = true;
+    if constexpr (Pre::kTagged) {
+        got = stage_v_wait_tagged<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, pre.tag,
+                                                 pre.limit);
+    } else if constexpr (Pre::kWaits) {
         if (!pre()) return;
         stage_v_load<BV, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     }
     stage_v_store<BV, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
-    __syncthreads();
+    if constexpr (Pre::kTagged) {
+        if (!pre.settle(got)) return;
+    } else {
+        __syncthreads();
+    }
 
     floatx4 acc[4];
 #pragma unroll
@@ -688,12 +758,20 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
     }
     YTile<DT> yt;
     y_load<DT, VECY>(yv, int64_t(yr >= 0 ? yr : ysafe) * ldy, ncol0, g, d_out, yt);
-    if constexpr (Pre::kWaits) {
+    bool got = true;
+    if constexpr (Pre::kTagged) {
+        got = stage_v_wait_tagged<true, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, pre.tag,
+                                                   pre.limit);
+    } else if constexpr (Pre::kWaits) {
         if (!pre()) return;
         stage_v_load<true, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     }
     stage_v_store<true, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
-    __syncthreads();
+    if constexpr (Pre::kTagged) {
+        if (!pre.settle(got)) return;
+    } else {
+        __syncthreads();
+    }
 
     floatx4 acc[4];
 #pragma unroll
@@ -831,7 +909,7 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
 // tiles its own rank needs (the launch's RT covers the largest rank): one
 // wave-uniform branch before any load.  Each tile's sum is formed in the same
 // order whatever RT is.
-template <int DT, bool VEC, int W, int NSTEP, int RT, class M, bool SCOPED = false>
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M, int SCOPED = 0>
 __device__ __forceinline__ void shrink_block_slice(const void *__restrict__ x, int64_t ldx, int d_in,
                                                    const int *__restrict__ rows, int n, int p0, const void *A, int r,
                                                    int c, int slice_len, float *__restrict__ out, int64_t ldo,
@@ -1178,12 +1256,14 @@ __device__ bool bgmv_group(const int32_t *__restrict__ ids, int T, int t, int a,
 // of them).  The adapter tables are read in parallel with the ids scan.
 // Group gx (an adapter when SLOT, else a leader token), d_in slice c.  Returns
 // true when the group has tokens and this workgroup wrote their partial sums.
-template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M = DenseMem, bool SCOPED = false>
+// SCOPED 2: `out` holds tagged 64-bit words (slice c starts c * sl_stride words in).
+template <int DT, bool VEC, int W, int NSTEP, int RT, bool SLOT, class M = DenseMem, int SCOPED = 0>
 __device__ __forceinline__ bool bgmv_shrink_body(const void *__restrict__ x, int64_t ldx, int d_in, int T,
                                                  const int32_t *__restrict__ ids, const uint64_t *__restrict__ pool_A,
                                                  const int32_t *__restrict__ pool_rank, int n_adapters, int max_rank,
                                                  int slice_len, float *__restrict__ out, int64_t ldo,
-                                                 int64_t sl_stride, int gx, int c, const M &mem = M{})
+                                                 int64_t sl_stride, int gx, int c, const M &mem = M{},
+                                                 uint32_t tag = 0)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     __shared__ Group grp;
@@ -1202,8 +1282,10 @@ __device__ __forceinline__ bool bgmv_shrink_body(const void *__restrict__ x, int
         const int n = grp.n, total = grp.total;
         if (n == 0) return false;
         const int xr = grp.rows[threadIdx.x & 15];
-        shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end,
-                                                       out + c * sl_stride, ldo, 0, grp.rows, n, red, mem);
+        float *o = SCOPED == 2 ? reinterpret_cast<float *>(reinterpret_cast<uint64_t *>(out) + c * sl_stride)
+                               : out + c * sl_stride;
+        shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end, o, ldo, 0,
+                                                       grp.rows, n, red, mem, tag);
         if (kRows * (pass + 1) >= total) break;
     }
     return true;
@@ -1252,7 +1334,7 @@ __device__ __forceinline__ bool bgmv_expand_body(const float *__restrict__ v, in
         if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return false;
         const int n = grp.n, total = grp.total;
         if (n == 0) return false;
-        if (pass == 0) {
+        if (pass == 0 || Pre::kTagged) { // tagged partials are waited for on every pass
             expand_rows<DT, VECY, true, UPT, M, 0, Pre>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncol_wg,
                                                         vec_b, grp.rows, -1, n, reinterpret_cast<float *>(vl4), ldl,
                                                         mem, pre);
@@ -1315,6 +1397,7 @@ __device__ __forceinline__ uint64_t launch_key()
 
 struct Waiter {
     static constexpr bool kWaits = true;
+    static constexpr bool kTagged = false;
     const uint64_t *flags; // the group's kc slice flags
     uint64_t key;          // this launch's key
     int need;              // slices of the group (kc <= 64)
@@ -1345,6 +1428,27 @@ struct Waiter {
     __device__ __forceinline__ bool ok() const { return *flag != 0; }
 };
 
+// Hook of an expand body whose partial sums arrive as tagged words: each
+// thread waits for its own words (stage_v_wait_tagged); settle() then joins
+// the workgroup (one barrier) and tells every thread whether all of it got
+// its data; a thread that gave up sets the status word.
+struct TagWait {
+    static constexpr bool kWaits = true;
+    static constexpr bool kTagged = true;
+    uint32_t tag;
+    int32_t *status;
+    int limit;
+    mutable bool failed = false;
+    __device__ __forceinline__ bool operator()() const { return true; }
+    __device__ __forceinline__ bool settle(bool got) const
+    {
+        if (!got) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        failed = __syncthreads_or(!got) != 0;
+        return !failed;
+    }
+    __device__ __forceinline__ bool ok() const { return !failed; }
+};
+
 struct OnepassArgs {
     const void *x;
     const int32_t *ids;
@@ -1352,9 +1456,9 @@ struct OnepassArgs {
     const uint64_t *pool_B;
     const int32_t *pool_rank;
     const float *pool_alpha;
-    float *part;       // slice partial sums [kc][T][ldw]
+    float *part;       // slice partial sums [kc][T][ldw] as tagged 64-bit words
     void *y;
-    int32_t *status;   // control words: status, then flags[groups][kc]
+    int32_t *status;   // control words: status
     uint64_t *flags;
     int64_t ldx, ldw, sl_stride, ldy;
     int32_t d_in, T, n_adapters, max_rank, slice_len, kc;
@@ -1362,33 +1466,28 @@ struct OnepassArgs {
 };
 
 template <int DT, int NSTEP, int RT, bool SLOT, int UPT, class M>
-__global__ __launch_bounds__(256) void bgmv_onepass_kernel(const OnepassArgs a, const M mem)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bgmv_onepass_kernel(const OnepassArgs a, const M mem)
 {
     const int b = int(blockIdx.x);
     const int n_prod = a.groups * a.kc;
-    const uint64_t key = launch_key();
+    // the launch's tag: the high bit set (never the zero of a cleared
+    // workspace), then 31 bits of the launch key, which differ between any
+    // two of 2^31 consecutive launches on one queue
+    const uint32_t tag = 0x80000000u | (uint32_t(launch_key()) & 0x7fffffffu);
     if (b < n_prod) {
         const int g = b / a.kc, c = b - (b / a.kc) * a.kc;
-        const bool did = bgmv_shrink_body<DT, true, 4, NSTEP, RT, SLOT, M, true>(
-            a.x, a.ldx, a.d_in, a.T, a.ids, a.pool_A, a.pool_rank, a.n_adapters, a.max_rank, a.slice_len, a.part,
-            a.ldw, a.sl_stride, g, c, mem);
-        if (did) {
-            // every wave's partial sums are complete before the flag moves
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
-            if (threadIdx.x == 0)
-                __hip_atomic_store(a.flags + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        bgmv_shrink_body<DT, true, 4, NSTEP, RT, SLOT, M, 2>(a.x, a.ldx, a.d_in, a.T, a.ids, a.pool_A, a.pool_rank,
+                                                             a.n_adapters, a.max_rank, a.slice_len, a.part, a.ldw,
+                                                             a.sl_stride, g, c, mem, tag);
         return;
     }
-    __shared__ int go;
     const int q = b - n_prod;
     const int g = q / a.ncol, col = q - (q / a.ncol) * a.ncol;
-    const Waiter w{a.flags + int64_t(g) * a.kc, key, a.kc, a.status, a.wait_limit, &go};
-    bgmv_expand_body<DT, SLOT, true, UPT, M, Waiter>(a.part, a.ldw, a.sl_stride, a.kc, a.T, a.ids, a.pool_B,
-                                                      a.pool_rank, a.pool_alpha, a.n_adapters, a.max_rank, a.y,
-                                                      a.ldy, a.d_out, a.vec_b != 0, a.ldl, col * kExpandCols, g, mem,
-                                                      w);
+    const TagWait w{tag, a.status, a.wait_limit};
+    bgmv_expand_body<DT, SLOT, true, UPT, M, TagWait>(a.part, a.ldw, a.sl_stride, a.kc, a.T, a.ids, a.pool_B,
+                                                       a.pool_rank, a.pool_alpha, a.n_adapters, a.max_rank, a.y,
+                                                       a.ldy, a.d_out, a.vec_b != 0, a.ldl, col * kExpandCols, g, mem,
+                                                       w);
 }
 
 // ----------------------------------------------------------------------------
@@ -2212,9 +2311,12 @@ size_t bgmv_ctl_bytes(int32_t T)
     return (256 + 8 * size_t(kMaxSlices) * 2 * size_t(T < 1 ? 1 : T) + 255) / 256 * 256;
 }
 
+// Control words, the two-kernel form's fp32 partial sums, then the one-launch
+// form's tagged 64-bit partial sums (a region of their own, so that the bytes
+// of one form are never read as the other's).
 size_t bgmv_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank)
 {
-    return bgmv_ctl_bytes(T) + combined_workspace_bytes(T, d_in, max_rank);
+    return bgmv_ctl_bytes(T) + 3 * combined_workspace_bytes(T, d_in, max_rank);
 }
 
 int &wait_limit()
@@ -2247,10 +2349,10 @@ int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32
     a.pool_B = pool_B;
     a.pool_rank = pool_rank;
     a.pool_alpha = pool_alpha;
-    a.part = static_cast<float *>(ws);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + combined_workspace_bytes(T, sa.d_in, max_rank));
     a.y = ea.y;
     a.status = ctl;
-    a.flags = reinterpret_cast<uint64_t *>(ctl + 64);
+    a.flags = nullptr;
     a.ldx = sa.ldx;
     a.ldw = (max_rank + 3) / 4 * 4;
     a.sl_stride = int64_t(T) * a.ldw;
