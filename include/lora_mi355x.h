@@ -266,14 +266,13 @@ int lora_sgmv_expand(void *stream, int dtype, const float *v, int64_t ldv,
  * expand (same section): y[perm[p], :] += scale_s (x[perm[p], :] A_s) B_s.
  * The low-rank intermediate stays in the workspace as fp32 partial sums over
  * slices of d_in (summed in a fixed order by the expand, so results are
- * reproducible run to run).  Small plans (about one round of resident
- * workgroups) with x and y rows 16-byte aligned, d_out % 16 == 0 and every
- * rank <= 32 run in one kernel launch: the shrink workgroups, then the expand
- * workgroups of every (64-row chunk, 256 columns), which wait for their
- * chunk's partial sums through launch-keyed flags in the workspace (as
- * lora_bgmv).  Larger plans run as two launches.  Both forms give the same
- * result.  The int32 at the start of the workspace is the same sticky status
- * word as lora_bgmv's.
+ * reproducible run to run).  Small plans (grids of up to 1536 workgroups)
+ * with x and y rows 16-byte aligned, d_out % 16 == 0 and every rank <= 32
+ * run in one kernel launch: the shrink workgroups, then the expand workgroups
+ * of every (64-row chunk, 256 columns), which wait for their chunk's partial
+ * sums, stored as tagged words in the workspace (as lora_bgmv).  Other plans
+ * run as two launches.  Both forms give the same result.  The int32 at the
+ * start of the workspace is the same sticky status word as lora_bgmv's.
  * Needs ws_bytes >= lora_workspace_bytes(LORA_OP_SGMV, T, d_in, d_out, max_rank)
  * with T >= seg->num_tokens and max_rank >= seg->max_rank.
  * Errors: as lora_sgmv_shrink, plus LORA_ERR_WORKSPACE. */
@@ -314,16 +313,20 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
  *
  * One kernel launch when x and y rows are 16-byte aligned, d_out % 16 == 0
  * and max_rank <= 64 (else two): its first workgroups compute the partial
- * sums of (adapter, d_in slice) and publish each by writing the launch's key
- * (from its dispatch id and queue) into a flag in the workspace; the others
- * load their B tile and y rows, wait until their adapter's flags hold the key,
- * then expand (the per-launch cost the pages put on naive per-adapter
- * launches, "Multi-LoRA Serving in Production ...", section "Mathematical
- * Formulation and the Batching Challenge", paid once).  Both forms compute
- * the same sums in the same order, so their outputs are equal.
+ * sums of (adapter, d_in slice) and store each as one 64-bit word, the value
+ * in the low half and the launch's tag in the high half (the top bit set,
+ * then 31 bits of a key made from the launch's dispatch id and queue); the
+ * others load their B tile and y rows, then load their partial sums until
+ * every word holds the tag, then expand (the per-launch cost the pages put on
+ * naive per-adapter launches, "Multi-LoRA Serving in Production ...", section
+ * "Mathematical Formulation and the Batching Challenge", paid once).  Both
+ * forms compute the same sums in the same order, so their outputs are equal.
  *
- * Workspace: the flags need no preparation and no reset (a value left by an
- * earlier launch never equals a new launch's key).  Calls that share a
+ * Workspace: control words, the two-launch form's fp32 partial sums, then the
+ * one-launch form's tagged words (a region of their own).  Nothing needs
+ * preparation or reset between calls: a word left by an earlier launch holds
+ * another tag (tags differ between any two of 2^31 consecutive launches on a
+ * queue, and never equal the zero of a cleared workspace).  Calls that share a
  * workspace must be ordered on one stream.  The int32 at the start of the
  * workspace is a status word, sticky: nonzero once a wait of the one-launch
  * form gave up (see lora_debug_wait_limit; that call's output is incomplete);

@@ -238,9 +238,9 @@ size_t lora_workspace_bytes(int op, int32_t T, int32_t d_in, int32_t d_out, int3
     case LORA_OP_BGMV_SHRINK:
     case LORA_OP_BGMV_EXPAND: return 0;
     case LORA_OP_FUSED: return fused_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
-    case LORA_OP_SGMV:
+    case LORA_OP_SGMV: // control words, fp32 partials (two kernels), tagged partials (one launch)
         return sgmv_ctl_bytes(T < 0 ? 0 : T) +
-               combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
+               3 * combined_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     case LORA_OP_BGMV:
         return bgmv_workspace_bytes(T < 0 ? 0 : T, d_in < 1 ? 1 : d_in, max_rank < 1 ? 1 : max_rank);
     default: return size_t(-1);
@@ -519,9 +519,11 @@ int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
     if (h->num_sorted == 0) return LORA_OK;
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
-    // control words (status, a flag per block and slice), then the partials
+    // control words (status, a flag per block and slice), then the fp32
+    // partials of the two-kernel form, then the tagged 64-bit partials of the
+    // one-launch form
     const size_t ctl_bytes = sgmv_ctl_bytes(h->num_blocks);
-    const size_t need = ctl_bytes + combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    const size_t need = ctl_bytes + 3 * combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t ldw = (h->max_rank + 3) / 4 * 4;
@@ -601,9 +603,10 @@ int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t
     if (h->num_sorted == 0) return LORA_OK;
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
-    // the workspace of lora_sgmv: control words, then the partials
+    // the workspace of lora_sgmv (this call runs the two-kernel form and uses
+    // its control words and fp32 partials)
     const size_t ctl_bytes = sgmv_ctl_bytes(h->num_blocks);
-    const size_t need = ctl_bytes + combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
+    const size_t need = ctl_bytes + 3 * combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const int64_t ldw = (h->max_rank + 3) / 4 * 4;

@@ -50,7 +50,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRows = LORA_PLAN_ROW_BLOCK; // rows per block (MFMA M)
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
+
 constexpr int kExpandCols = 256;          // output columns per expand workgroup (4 waves x 64)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -197,20 +197,18 @@ __device__ __forceinline__ floatx4 mfma_step(const typename Frag<DT>::V &a, cons
 // Results of the W waves are added in wave order through LDS (`red`, W*RT*1 KB).
 // Output row of block row mm: orows[mm] if orows (LDS) is given, else orow0 + mm.
 // ----------------------------------------------------------------------------
-// Result stores.  MODE 0: plain.  MODE 1: a result another workgroup reads in
-// the same launch: device-scope (write-through) stores, so that the reader's
-// device-scope loads see them.  MODE 2: element e of `out` is a 64-bit word,
-// the value's bits in the low half and the launch's tag in the high half,
-// stored with one device-scope 64-bit store: a reader that sees the tag sees
-// the value written with it (no flag, no wait for the store to complete).
+// Result stores.  MODE 0: plain.  MODE 2: a result another workgroup reads in
+// the same launch: element e of `out` is a 64-bit word, the value's bits in
+// the low half and the launch's tag in the high half, stored with one
+// device-scope 64-bit store, so a reader that sees the tag sees the value
+// written with it (no flag, no wait for the store to complete).
 template <int MODE> __device__ __forceinline__ void put_result(float *out, int64_t e, float v, uint32_t tag)
 {
+    static_assert(MODE == 0 || MODE == 2, "result store mode");
     if constexpr (MODE == 2)
         __hip_atomic_store(reinterpret_cast<uint64_t *>(out) + e,
                            (uint64_t(tag) << 32) | uint64_t(__float_as_uint(v)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    else if constexpr (MODE == 1)
-        __hip_atomic_store(out + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
         out[e] = v;
 }
@@ -526,13 +524,7 @@ template <int UPT> struct VStage {
     int off[UPT];
 };
 
-// A float written by another workgroup of the same launch (device-scope load).
-__device__ __forceinline__ float get_result(const float *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <bool BV, bool VIND, int UPT, bool SCOPED = false>
+template <bool BV, bool VIND, int UPT>
 __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl,
                                              const int *yrows, int vrow0, int nrows, int r, int ldl, VStage<UPT> &st,
                                              int unit0 = 0)
@@ -554,10 +546,7 @@ __device__ __forceinline__ void stage_v_load(const float *__restrict__ v, int64_
 #pragma unroll
         for (int sl = 0; sl < kMaxSlices; ++sl) {
             const float *ps = p + (sl < nsl ? sl : 0) * sl_stride;
-            if constexpr (SCOPED) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st.w[k][sl][e] = get_result(ps + (BV || j + e < r ? e : 0));
-            } else if constexpr (BV) {
+            if constexpr (BV) {
                 st.w[k][sl] = *reinterpret_cast<const floatx4 *>(ps);
             } else {
 #pragma unroll
@@ -644,10 +633,10 @@ __device__ __forceinline__ void stage_v_store(int nsl, int r, int ldl, int spare
     (void)q4;
 }
 
-// A hook an expand body runs after it has issued its B and y loads and before
-// it loads v: the one-launch BGMV waits there for the shrink results of its
-// group.  Returns false when the workgroup must not use v (the wait gave up);
-// the body then stores nothing.  NoPre keeps the plain order (v first).
+// How an expand body gets v.  NoPre: plain loads, issued first.  TagWait (the
+// one-launch calls): B and y loads first, then the partial sums are loaded
+// until every word holds the launch's tag; a workgroup whose wait gave up
+// stores nothing.
 struct NoPre {
     static constexpr bool kWaits = false;
     static constexpr bool kTagged = false;
@@ -683,9 +672,6 @@ __device__ __forceinline__ void expand_rows_impl(const float *__restrict__ v, in
     if constexpr (Pre::kTagged) {
         got = stage_v_wait_tagged<BV, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, pre.tag,
                                                  pre.limit);
-    } else if constexpr (Pre::kWaits) {
-        if (!pre()) return;
-        stage_v_load<BV, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     }
     stage_v_store<BV, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
     if constexpr (Pre::kTagged) {
@@ -762,9 +748,6 @@ __device__ __forceinline__ void expand_rows_packed(const float *__restrict__ v, 
     if constexpr (Pre::kTagged) {
         got = stage_v_wait_tagged<true, VIND, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, pre.tag,
                                                    pre.limit);
-    } else if constexpr (Pre::kWaits) {
-        if (!pre()) return;
-        stage_v_load<true, VIND, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
     }
     stage_v_store<true, UPT>(nsl, r, ldl, kRows * ldl, vst, vl);
     if constexpr (Pre::kTagged) {
@@ -863,12 +846,17 @@ __device__ __forceinline__ void expand_chunk_impl(const float *__restrict__ v, i
     YTile<DT> yt[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) y_load<DT, VECY>(yv, int64_t(yr[i] >= 0 ? yr[i] : ysafe) * ldy, ncol0, g, d_out, yt[i]);
-    if constexpr (Pre::kWaits) {
-        if (!pre()) return;
-        stage_v_load<BV, false, UPT, true>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst);
+    bool got = true;
+    if constexpr (Pre::kTagged) {
+        got = stage_v_wait_tagged<BV, false, UPT>(v, ldv, sl_stride, nsl, yrows, vrow0, nrows, r, ldl, vst, pre.tag,
+                                                  pre.limit);
     }
     stage_v_store<BV, UPT>(nsl, r, ldl, RB * kRows * ldl, vst, vl);
-    __syncthreads();
+    if constexpr (Pre::kTagged) {
+        if (!pre.settle(got)) return;
+    } else {
+        __syncthreads();
+    }
 
     const int nblk = (nrows + kRows - 1) / kRows;
 #pragma unroll
@@ -913,30 +901,32 @@ template <int DT, bool VEC, int W, int NSTEP, int RT, class M, int SCOPED = 0>
 __device__ __forceinline__ void shrink_block_slice(const void *__restrict__ x, int64_t ldx, int d_in,
                                                    const int *__restrict__ rows, int n, int p0, const void *A, int r,
                                                    int c, int slice_len, float *__restrict__ out, int64_t ldo,
-                                                   int64_t sl_stride, const M &mem)
+                                                   int64_t sl_stride, const M &mem, uint32_t tag = 0)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
     const int xr = rows[threadIdx.x & 15];
     const int xr0 = rows[0];
     const int k_begin = c * slice_len;
     const int k_end = min(d_in, k_begin + slice_len);
-    float *o = out + c * sl_stride;
+    // SCOPED 2: `out` holds tagged 64-bit words
+    float *o = SCOPED == 2 ? reinterpret_cast<float *>(reinterpret_cast<uint64_t *>(out) + c * sl_stride)
+                           : out + c * sl_stride;
     if constexpr (RT >= 2) {
         if (r <= 16) {
             shrink_block<DT, VEC, W, NSTEP, 1, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
-                                                          nullptr, n, red, mem);
+                                                          nullptr, n, red, mem, tag);
             return;
         }
     }
     if constexpr (RT >= 4) {
         if (r <= 32) {
             shrink_block<DT, VEC, W, NSTEP, 2, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
-                                                          nullptr, n, red, mem);
+                                                          nullptr, n, red, mem, tag);
             return;
         }
     }
     shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0, nullptr,
-                                                   n, red, mem);
+                                                   n, red, mem, tag);
 }
 
 // Item b of a shrink launch (b = the workgroup's index along x).
@@ -1367,25 +1357,26 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(const float *__restric
 // One-launch BGMV.  The two halves of the decode correction run in one grid:
 // workgroups [0, groups * kc) are the shrink of (group, d_in slice); the rest
 // are the expand of (group, column tile), which issue their B and y loads,
-// wait until every slice of their group is published, then load the partial
-// sums.  A consumer never waits on a workgroup of higher index and producers
-// wait on nothing, so the grid completes under any dispatch that starts
-// workgroups in index order within an XCD; the wait is bounded all the same.
+// then load their group's partial sums until all of them are there.  A
+// consumer never waits on a workgroup of higher index and producers wait on
+// nothing, so the grid completes under any dispatch that starts workgroups in
+// index order within an XCD; the wait is bounded all the same.
 //
-// Hand-over without cache maintenance.  Every launch has a 64-bit key made
-// from its HSA dispatch id (unique per launch on a hardware queue, replays of
-// a graph included) and its queue's address.  A producer writes its partial
-// sums with device-scope stores, waits until they are complete
-// (s_waitcnt vmcnt(0) in every wave), and then thread 0 writes the key into the
-// slice's flag (device-scope store).  A consumer polls its group's kc flags
-// with device-scope loads until all hold the key, then reads the partial sums
-// with device-scope loads.  Device-scope accesses bypass the XCD-local caches
-// that are not coherent across XCDs, so no L2 write-back or invalidate is
-// needed (measured: one agent-scope acquire fence per consumer wave made the
-// launch two to three times slower).  A flag holds the key of the last launch
-// that wrote it, so nothing is reset between calls: a stale or arbitrary value
-// equals a new launch's key only by a 64-bit coincidence.  A consumer that
-// gives up sets *status (sticky) and stores nothing.
+// Hand-over without flags or cache maintenance.  Every launch has a 64-bit key
+// made from its HSA dispatch id (unique per launch on a hardware queue,
+// replays of a graph included) and its queue's address, and a 32-bit tag: the
+// top bit set, then 31 bits of the key (distinct for 2^31 consecutive
+// dispatches on a queue, since the key is an odd multiple of the dispatch id
+// plus a constant).  A producer stores each partial sum as one 64-bit word,
+// value and tag, with a device-scope store; a consumer thread loads its words
+// with device-scope loads until every one holds the tag.  A 64-bit store is
+// seen whole or not at all, so no store has to be waited for, and
+// device-scope accesses bypass the XCD-local caches that are not coherent
+// across XCDs (measured: one agent-scope acquire fence per consumer wave made
+// the launch two to three times slower; a flag stored after the partial sums,
+// and polled before loading them, cost two more round trips than the tags).
+// Nothing is reset between calls: a word left by another launch holds another
+// tag.  A consumer that gives up sets *status (sticky) and stores nothing.
 // ----------------------------------------------------------------------------
 extern "C" __device__ uint64_t lora_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
 
@@ -1395,45 +1386,14 @@ __device__ __forceinline__ uint64_t launch_key()
     return (lora_dispatch_id() + 1) * 0x9E3779B97F4A7C15ull ^ q;
 }
 
-struct Waiter {
-    static constexpr bool kWaits = true;
-    static constexpr bool kTagged = false;
-    const uint64_t *flags; // the group's kc slice flags
-    uint64_t key;          // this launch's key
-    int need;              // slices of the group (kc <= 64)
-    int32_t *status;       // set to 1 when the wait gives up
-    int limit;             // polls before giving up; < 0: give up at once
-    int *flag;             // LDS word: 1 = go on, 0 = gave up
-    __device__ __forceinline__ bool operator()() const
-    {
-        if (threadIdx.x < 64) {
-            const int lane = threadIdx.x;
-            bool ok = limit >= 0;
-            for (int spins = 0; ok; ++spins) {
-                const uint64_t f = lane < need
-                                       ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                       : key;
-                if (__all(f == key)) break;
-                if (spins >= limit) ok = false;
-                else __builtin_amdgcn_s_sleep(1);
-            }
-            if (lane == 0) {
-                if (!ok) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                *flag = ok ? 1 : 0;
-            }
-        }
-        __syncthreads();
-        return *flag != 0;
-    }
-    __device__ __forceinline__ bool ok() const { return *flag != 0; }
-};
+
 
 // Hook of an expand body whose partial sums arrive as tagged words: each
 // thread waits for its own words (stage_v_wait_tagged); settle() then joins
 // the workgroup (one barrier) and tells every thread whether all of it got
 // its data; a thread that gave up sets the status word.
 struct TagWait {
-    static constexpr bool kWaits = true;
+    static constexpr bool kWaits = true; // B and y before v
     static constexpr bool kTagged = true;
     uint32_t tag;
     int32_t *status;
@@ -1459,7 +1419,6 @@ struct OnepassArgs {
     float *part;       // slice partial sums [kc][T][ldw] as tagged 64-bit words
     void *y;
     int32_t *status;   // control words: status
-    uint64_t *flags;
     int64_t ldx, ldw, sl_stride, ldy;
     int32_t d_in, T, n_adapters, max_rank, slice_len, kc;
     int32_t d_out, ncol, ldl, vec_b, groups, wait_limit;
@@ -1491,17 +1450,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 }
 
 // ----------------------------------------------------------------------------
-// One-launch SGMV for small plans (where the second launch and the gap between
-// two kernels are a large part of the time).  The grid holds every shrink item
-// ((block, d_in slice), numbered as the shrink kernel numbers them), then one
-// expand item per (64-row chunk, 256 output columns); an expand item waits for
-// the flags of its chunk's (block, slice) items, which have lower indices, so
-// the grid completes under any dispatch in index order within an XCD.
-// Hand-over as in the one-launch BGMV (launch key in a per-(block, slice)
-// flag, device-scope stores and loads of the partial sums, no reset).
-// Measured on the prefill workload (2,200 workgroups) it is slower than the
-// two kernels (34.2 against 32.7 us; ordering the grid chunk by chunk, 42.7),
-// so large plans keep the two kernels.
+// One-launch SGMV.  The grid holds every shrink item ((block, d_in slice),
+// numbered as the shrink kernel numbers them), then one expand item per
+// (64-row chunk, 256 output columns); an expand item waits for the partial
+// sums of its chunk's (block, slice) items, which have lower indices, so the
+// grid completes under any dispatch in index order within an XCD.  Hand-over
+// as in the one-launch BGMV (tagged 64-bit partial sums, no flags, no reset).
 // ----------------------------------------------------------------------------
 struct SgmvOnepassArgs {
     const void *x;
@@ -1510,19 +1464,18 @@ struct SgmvOnepassArgs {
     float *part;       // slice partial sums [kc][T'][ldw]
     void *y;
     int32_t *status;
-    uint64_t *flags;   // [n_blocks][kc]
     int64_t ldx, ldw, sl_stride, ldy;
     int32_t d_in, slice_len, kc, d_out, ncol, ldl, vec_b, wait_limit;
     int32_t nblk, nchunk;
 };
 
 template <int DT, int NSTEP, int RT, int NCH, int UPT>
-__global__ __launch_bounds__(256) void sgmv_onepass_kernel(const SgmvOnepassArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sgmv_onepass_kernel(const SgmvOnepassArgs a)
 {
     extern __shared__ floatx4 vl4[];
-    __shared__ int go;
     const int b = int(blockIdx.x);
-    const uint64_t key = launch_key();
+    // the launch's tag, as in the one-launch BGMV
+    const uint32_t tag = 0x80000000u | (uint32_t(launch_key()) & 0x7fffffffu);
     // shrink items first, numbered as the shrink kernel's (XCD-grouped)
     const int n_prod = (a.nblk * a.kc + 7) / 8 * 8;
     if (b < n_prod) {
@@ -1532,14 +1485,9 @@ __global__ __launch_bounds__(256) void sgmv_onepass_kernel(const SgmvOnepassArgs
         if (item >= total) return;
         const int blk = item % a.nblk, sl = item / a.nblk;
         const lora_blk_desc *bd = a.blks + blk;
-        shrink_block_slice<DT, true, 4, NSTEP, RT, DenseMem, true>(
+        shrink_block_slice<DT, true, 4, NSTEP, RT, DenseMem, 2>(
             a.x, a.ldx, a.d_in, bd->rows, bd->n, bd->p0, reinterpret_cast<const void *>(bd->A), bd->rank, sl,
-            a.slice_len, a.part, a.ldw, a.sl_stride, DenseMem{});
-        // every wave's partial sums are complete before the flag moves
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_store(a.flags + int64_t(blk) * a.kc + sl, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.slice_len, a.part, a.ldw, a.sl_stride, DenseMem{}, tag);
         return;
     }
     const int q = b - n_prod;
@@ -1547,15 +1495,15 @@ __global__ __launch_bounds__(256) void sgmv_onepass_kernel(const SgmvOnepassArgs
     const lora_chunk_desc *cd = a.chunks + ci;
     const int r = cd->rank;
     const int n = min(cd->n, kChunkRB * kRows);
-    const Waiter w{a.flags + int64_t(cd->first_blk) * a.kc, key, cd->nblk * a.kc, a.status, a.wait_limit, &go};
+    const TagWait w{tag, a.status, a.wait_limit};
     const void *B = reinterpret_cast<const void *>(cd->B);
     float *vl = reinterpret_cast<float *>(vl4);
     if (a.vec_b && (r & 3) == 0)
-        expand_chunk_impl<DT, true, true, NCH, UPT, kChunkRB, false, DenseMem, Waiter>(
+        expand_chunk_impl<DT, true, true, NCH, UPT, kChunkRB, false, DenseMem, TagWait>(
             a.part, a.ldw, a.sl_stride, a.kc, B, r, cd->scale, a.y, a.ldy, a.d_out, col * kExpandCols, cd->rows,
             cd->p0, n, vl, a.ldl, 0, DenseMem{}, w);
     else
-        expand_chunk_impl<DT, true, false, NCH, UPT, kChunkRB, false, DenseMem, Waiter>(
+        expand_chunk_impl<DT, true, false, NCH, UPT, kChunkRB, false, DenseMem, TagWait>(
             a.part, a.ldw, a.sl_stride, a.kc, B, r, cd->scale, a.y, a.ldy, a.d_out, col * kExpandCols, cd->rows,
             cd->p0, n, vl, a.ldl, 0, DenseMem{}, w);
 }
@@ -2142,10 +2090,12 @@ int shrink_split(hipStream_t s, const ShrinkArgs &sa, const PlanView &p, float *
 }
 
 // Largest grid of the one-launch SGMV.  Producers take the lowest workgroup
-// ids and never wait, so any grid drains; the bound only keeps the grid size
-// a valid launch dimension (measured: a prefill plan of ~2200 workgroups runs
-// 31.6 us in one launch against 32.2 us of kernel time in two).
-constexpr int64_t kOnepassMaxGrid = int64_t(1) << 30;
+// ids and never wait, so any grid would drain; the bound is about time.  Each
+// expand workgroup reads its chunk's tagged partial sums (8 bytes a value,
+// every slice) once per column tile, which small plans hide and large ones do
+// not: a prefill plan (~2,200 workgroups) takes 34.9 us in one launch against
+// 32.2 us of kernel time in two; a decode batch on this path 8.0 against 9.1.
+constexpr int64_t kOnepassMaxGrid = 1536;
 
 template <int DT, int NSTEP, int RT, int NCH, int UPT>
 void sgmv_onepass_go(hipStream_t s, dim3 grid, size_t shm, const SgmvOnepassArgs &a)
@@ -2172,10 +2122,11 @@ int sgmv_combined(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, con
             a.blks = plan_blocks(p);
             a.nblk = p.h->num_blocks;
             a.nchunk = p.h->num_chunks;
-            a.part = static_cast<float *>(ws);
+            // tagged 64-bit partial sums, after the two-kernel form's fp32 ones
+            a.part = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                               combined_workspace_bytes(p.h->num_sorted, sa.d_in, p.h->max_rank));
             a.y = ea.y;
             a.status = ctl;
-            a.flags = reinterpret_cast<uint64_t *>(ctl + 64);
             a.ldx = sa.ldx;
             a.ldw = (p.h->max_rank + 3) / 4 * 4;
             a.sl_stride = int64_t(p.h->num_sorted) * a.ldw;
@@ -2250,8 +2201,8 @@ int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const
 
 size_t sgmv_ctl_bytes(int32_t n_blocks)
 {
-    // status block (256 B), then a 64-bit flag per (block, d_in slice)
-    return (256 + 8 * size_t(kMaxSlices) * size_t(n_blocks < 1 ? 1 : n_blocks) + 255) / 256 * 256;
+    (void)n_blocks;
+    return 256; // the status block: word 0 is the sticky give-up status
 }
 
 int launch_sgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws,
@@ -2305,10 +2256,8 @@ void onepass_dispatch(hipStream_t s, int dtype, int rt, bool two, dim3 grid, siz
 
 size_t bgmv_ctl_bytes(int32_t T)
 {
-    // status block (256 B), then a 64-bit flag per (group, d_in slice): a
-    // group is an adapter (pools of at most 2T adapters) or a leader token,
-    // and there are at most kMaxSlices slices
-    return (256 + 8 * size_t(kMaxSlices) * 2 * size_t(T < 1 ? 1 : T) + 255) / 256 * 256;
+    (void)T;
+    return 256; // the status block: word 0 is the sticky give-up status
 }
 
 // Control words, the two-kernel form's fp32 partial sums, then the one-launch
@@ -2352,7 +2301,6 @@ int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32
     a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + combined_workspace_bytes(T, sa.d_in, max_rank));
     a.y = ea.y;
     a.status = ctl;
-    a.flags = nullptr;
     a.ldx = sa.ldx;
     a.ldw = (max_rank + 3) / 4 * 4;
     a.sl_stride = int64_t(T) * a.ldw;

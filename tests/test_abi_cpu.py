@@ -345,12 +345,11 @@ def test_combined_argument_errors():
     assert sg(None, 1, None, 0, 0, empty.dev(None), None, 0, 0, None, 0) == 0
     bg = B.lora_bgmv
     needb = B.lora_workspace_bytes(B.LORA_OP_BGMV, 64, 4096, 4096, 16)
-    # control words (256 B status block, a 64-bit flag per group and d_in
-    # slice: 2T groups, 4 slices at most) in front of the fp32 partial sums of
-    # 4 d_in slices (the two-kernel form), then the same sums as tagged 64-bit
-    # words (the one-launch form)
+    # a 256 B status block in front of the fp32 partial sums of 4 d_in slices
+    # (the two-kernel form), then the same sums as tagged 64-bit words (the
+    # one-launch form)
     part = 4 * 64 * 16 * 4 + 256
-    assert needb == (256 + 8 * 4 * 2 * 64 + 255) // 256 * 256 + 3 * part
+    assert needb == 256 + 3 * part
     assert bg(None, 1, 0, None, 0, 0, None, None, None, None, None, 0, 16, None, 0, 0, None, 0) == 0
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, FX, FX, FX, 32, 16, FX, 4096, 4096, FX, needb - 1) == -6
     assert bg(None, 1, 64, FX, 4096, 4096, FX, FX, None, FX, FX, 32, 16, FX, 4096, 4096, FX, needb) == -1

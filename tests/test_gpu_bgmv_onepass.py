@@ -1,6 +1,6 @@
 """The one-launch form of lora_bgmv (shrink and expand workgroups in one grid,
-handing over through per-slice flags in the workspace that hold the key of
-the launch that published them).
+handing over through partial sums stored as 64-bit words that carry the tag
+of the launch that wrote them).
 
 * parity with the oracle on decode batches whose groups take several 16-token
   passes, and on pools larger than twice the batch (one group per leader
