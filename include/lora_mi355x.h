@@ -352,12 +352,12 @@ int lora_workspace_clear(void *stream, void *ws, size_t ws_bytes);
 int lora_debug_wait_limit(int32_t polls);
 
 /* ------------------------------------------------------------ grouped BGMV
- * Several projections of a layer in one shrink launch and one expand launch,
- * after the pages' grouped invocation that serves every active adapter of all
- * projections at once instead of one launch per projection ("Multi-LoRA
- * Serving in Production ...", section "Ragged Batching and FlashInfer Grouped
- * GEMM"; the per-launch cost it removes is in section "Kernel Architectures:
- * SGMV, MBGMV, and Grouped GEMMs").  Every projection p applies
+ * Several projections of a layer in one kernel launch (or one shrink launch
+ * and one expand launch), after the pages' grouped invocation that serves
+ * every active adapter of all projections at once instead of one launch per
+ * projection ("Multi-LoRA Serving in Production ...", section "Ragged Batching
+ * and FlashInfer Grouped GEMM"; the per-launch cost it removes is in section
+ * "Kernel Architectures: SGMV, MBGMV, and Grouped GEMMs").  Every projection p applies
  *     y_p[t, :] += (alpha_{i,p} / r_{i,p}) (x_p[t, :] A_{i,p}) B_{i,p},  i = ids[t],
  * with one adapter id per token for all projections and its own x, y, sizes
  * and adapter tables.  Projections whose inputs are the same tensor (q, k, v;
@@ -380,12 +380,22 @@ typedef struct lora_proj {
 
 /* Workspace bytes of lora_bgmv_grouped for T tokens and these projections
  * (host array of n_proj, 1 <= n_proj <= LORA_MAX_PROJ); 0 if the arguments
- * are invalid. */
+ * are invalid.  Layout: lora_bgmv's 256-byte status block, then for each
+ * projection its two-launch fp32 partial sums and its one-launch tagged words
+ * (twice those bytes). */
 size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj);
 
 /*   ids_dev  [T] device int32, -1 = none; n_adapters entries in every table
  *   projs    host array of n_proj projections (read during the call)
  *   ws       device, 16-byte aligned, >= lora_bgmv_grouped_workspace_bytes
+ * One kernel launch when every projection has 16-byte aligned x and y rows,
+ * d_out % 16 == 0 and max_rank <= 64: the shrink workgroups of all
+ * projections first, then their expand workgroups, with lora_bgmv's hand-over
+ * (tagged partial sums, no flags, nothing reset between calls) and its sticky
+ * status word at the start of the workspace (nonzero once a wait gave up; see
+ * lora_debug_wait_limit); allocate the workspace zero-filled or clear it with
+ * lora_workspace_clear.  Otherwise one shrink and one expand launch.  Calls
+ * that share a workspace must be ordered on one stream.
  * Errors: LORA_ERR_ARG (also: two projections with the same y), LORA_ERR_DTYPE,
  * LORA_ERR_RANK, LORA_ERR_ALIGN, LORA_ERR_WORKSPACE, LORA_ERR_HIP. */
 int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev, int32_t n_adapters,

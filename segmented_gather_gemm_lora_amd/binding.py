@@ -950,7 +950,8 @@ def bgmv_grouped_workspace(T: int, projs, device="cuda"):
     nbytes = lora_bgmv_grouped_workspace_bytes(T, ctypes.cast(projs, _vp), len(projs))
     if nbytes == 0 and T > 0:
         raise ValueError("invalid projections for a grouped workspace")
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    # zero-filled: the status word at its start must begin at zero
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def bgmv_grouped(xs, ids_dev, pools, ys, ws, dtype: str, max_ranks=None, stream=None, projs=None):

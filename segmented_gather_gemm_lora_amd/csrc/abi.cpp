@@ -717,11 +717,13 @@ int lora_sgmv_grouped(void *stream, int dtype, const lora_sgmv_proj *projs, int3
 size_t lora_bgmv_grouped_workspace_bytes(int32_t T, const lora_proj *projs, int32_t n_proj)
 {
     if (T < 0 || !projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;
-    size_t total = 0;
+    // the status block, then per projection: the two-launch form's fp32
+    // partial sums and the one-launch form's tagged words (twice the bytes)
+    size_t total = bgmv_ctl_bytes(T);
     for (int p = 0; p < n_proj; ++p) {
         const lora_proj &q = projs[p];
         if (q.max_rank < 1 || q.max_rank > LORA_MAX_RANK) return 0;
-        total += grouped_region_bytes(T, q.d_in < 1 ? 1 : q.d_in, q.max_rank);
+        total += 3 * grouped_region_bytes(T, q.d_in < 1 ? 1 : q.d_in, q.max_rank);
     }
     return total;
 }
@@ -752,7 +754,8 @@ int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);
     if (!aligned16(ws)) return fail(LORA_ERR_ALIGN, "workspace is not 16-byte aligned");
     GroupedProj gp[LORA_MAX_PROJ];
-    char *region = static_cast<char *>(ws);
+    int32_t *ctl = static_cast<int32_t *>(ws);
+    char *region = static_cast<char *>(ws) + bgmv_ctl_bytes(T);
     for (int p = 0; p < n_proj; ++p) {
         const lora_proj &q = projs[p];
         const int64_t ldw = (q.max_rank + 3) / 4 * 4;
@@ -764,9 +767,11 @@ int lora_bgmv_grouped(void *stream, int dtype, int32_t T, const int32_t *ids_dev
         gp[p].pool_rank = q.pool_rank_dev;
         gp[p].pool_alpha = q.pool_alpha_dev;
         gp[p].max_rank = q.max_rank;
-        region += grouped_region_bytes(T, q.d_in, q.max_rank);
+        const size_t rb = grouped_region_bytes(T, q.d_in, q.max_rank);
+        gp[p].part = reinterpret_cast<float *>(region + rb);
+        region += 3 * rb;
     }
-    return launch_bgmv_grouped(static_cast<hipStream_t>(stream), T, ids_dev, n_adapters, gp, n_proj);
+    return launch_bgmv_grouped(static_cast<hipStream_t>(stream), T, ids_dev, n_adapters, gp, n_proj, ctl);
 }
 
 int lora_bgmv_shrink(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,

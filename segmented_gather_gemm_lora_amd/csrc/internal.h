@@ -99,10 +99,13 @@ struct GroupedProj {
     const uint64_t *pool_B;
     const int32_t *pool_rank;
     const float *pool_alpha;
+    float *part; // the one-launch form's tagged partial sums (a region of their own)
     int32_t max_rank;
 };
+// ctl: the workspace's status block (one launch when every projection fits
+// it), or null for the two-launch form.
 int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
-                        int n);
+                        int n, int32_t *ctl);
 // One projection of a grouped SGMV call: its plan, shrink and expand
 // arguments, and its workspace region (the fp32 slice partials of v).
 struct GroupedSgmv {

@@ -213,18 +213,40 @@ template <int MODE> __device__ __forceinline__ void put_result(float *out, int64
         out[e] = v;
 }
 
+// Exchange of two loaded fragments between lanes m and m ^ 8 of each 16-lane
+// row (DPP row rotation by 8).  The lane with low = (m < 8) loaded `la` for its
+// own row and `lb` for its partner's; the other lane the reverse.  Returns the
+// lane's own two fragments f0, f1.
+template <class V>
+__device__ __forceinline__ void swap_halves(const V &la, const V &lb, bool low, V &f0, V &f1)
+{
+    const u32x4 a = __builtin_bit_cast(u32x4, la), b = __builtin_bit_cast(u32x4, lb);
+    const u32x4 send = low ? b : a;
+    u32x4 recv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) recv[e] = uint32_t(__builtin_amdgcn_update_dpp(0, int(send[e]), 0x128, 0xf, 0xf, false));
+    f0 = __builtin_bit_cast(V, low ? a : recv);
+    f1 = __builtin_bit_cast(V, low ? recv : b);
+}
+
+// Rows (of x) of the block are xrA (m < 8 half) and xrB (m >= 8 half) as seen
+// from a lane: xrA = row (lane & 7), xrB = row (lane & 7) + 8; -1 past n, which
+// then repeat the block's first row xr0 (their MFMA rows are never stored).
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M = DenseMem, int SCOPED = 0>
-__device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xr, int xr0,
+__device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_t ldx, int xrA, int xrB, int xr0,
                                              const void *__restrict__ Av, int d_in, int r, int k_begin, int k_end,
                                              float *__restrict__ out, int64_t ldo, int orow0, const int *orows, int n,
                                              float *red, const M &mem = M{}, uint32_t tag = 0)
 {
     using F = Frag<DT>;
     using T = typename F::T;
+    using V = typename F::V;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
-    // rows past n repeat the block's first row: their MFMA rows are never stored
-    const global_ptr<T> xrow = as_global<T>(xv) + int64_t(xr >= 0 ? xr : xr0) * ldx;
+    const int mlo = m & 7, hi = m >> 3;
+    const bool low = hi == 0;
+    const global_ptr<T> xrowA = as_global<T>(xv) + int64_t(xrA >= 0 ? xrA : xr0) * ldx;
+    const global_ptr<T> xrowB = as_global<T>(xv) + int64_t(xrB >= 0 ? xrB : xr0) * ldx;
     const int ntiles = (r + 15) >> 4;
 
     for (int rt0 = 0; rt0 < ntiles; rt0 += RT) {
@@ -232,36 +254,60 @@ __device__ __forceinline__ void shrink_block(const void *__restrict__ xv, int64_
 #pragma unroll
         for (int i = 0; i < RT; ++i) acc[i] = floatx4{};
         // ranks past r repeat row r-1: their MFMA columns are never stored
-        int64_t aoff[RT];
+        int64_t aoffA[RT], aoffB[RT];
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            const int j = 16 * (rt0 + i) + m;
-            aoff[i] = int64_t(j < r ? j : r - 1) * d_in;
+            const int ja = 16 * (rt0 + i) + mlo, jb = ja + 8;
+            aoffA[i] = int64_t(ja < r ? ja : r - 1) * d_in;
+            aoffB[i] = int64_t(jb < r ? jb : r - 1) * d_in;
         }
         for (int kb = k_begin + wave * NSTEP * F::kStep; kb < k_end; kb += W * NSTEP * F::kStep) {
-            typename F::V xf[NSTEP][4];
-            typename F::V af[NSTEP][RT][4];
-            // issue every load of this chunk first
-#pragma unroll
-            for (int s = 0; s < NSTEP; ++s) {
-                // fragment u of lane group g: k = kb + s*kStep + (4u + g)*kVec, so one
-                // load instruction covers 4*kVec contiguous elements of each row
-                const int k0 = kb + s * F::kStep + F::kVec * g;
-                // A rows first: their addresses are known before the token rows are
-#pragma unroll
-                for (int i = 0; i < RT; ++i)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        af[s][i][u] = load_frag_m<DT, VEC>(mem, Av, aoff[i], k0 + 4 * F::kVec * u, k_end);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) xf[s][u] = load_frag<DT, VEC>(xrow, k0 + 4 * F::kVec * u, k_end);
-            }
+            // MFMA u of step s takes, in lane group g, the kVec elements from
+            // k = kb + s*kStep + (4u + g)*kVec of its row (token m, rank m).
+            // Fragments u = 2P and 2P + 1 are loaded together: the lanes of the
+            // low half (m < 8) fetch fragment 2P, the high half fragment 2P + 1,
+            // first of rows 0..7, then of rows 8..15, so each load instruction
+            // reads 8 rows x 8 kVec contiguous elements (128 bytes for bf16:
+            // whole cache lines); swap_halves then hands every lane its own
+            // row's pair.  The MFMA operands are the same as with one load per
+            // fragment.
+            V xa[NSTEP][2], xb[NSTEP][2];
+            V aa[NSTEP][RT][2], ab[NSTEP][RT][2];
+            // issue every load of this chunk first, A rows first: their
+            // addresses are known before the token rows are
 #pragma unroll
             for (int s = 0; s < NSTEP; ++s)
 #pragma unroll
-                for (int i = 0; i < RT; ++i)
+                for (int P = 0; P < 2; ++P) {
+                    const int kk = kb + s * F::kStep + F::kVec * g + 4 * F::kVec * (2 * P + hi);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[i] = mfma_step<DT>(xf[s][u], af[s][i][u], acc[i]);
+                    for (int i = 0; i < RT; ++i) {
+                        aa[s][i][P] = load_frag_m<DT, VEC>(mem, Av, aoffA[i], kk, k_end);
+                        ab[s][i][P] = load_frag_m<DT, VEC>(mem, Av, aoffB[i], kk, k_end);
+                    }
+                }
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+                for (int P = 0; P < 2; ++P) {
+                    const int kk = kb + s * F::kStep + F::kVec * g + 4 * F::kVec * (2 * P + hi);
+                    xa[s][P] = load_frag<DT, VEC>(xrowA, kk, k_end);
+                    xb[s][P] = load_frag<DT, VEC>(xrowB, kk, k_end);
+                }
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+                for (int P = 0; P < 2; ++P) {
+                    V x0, x1;
+                    swap_halves(xa[s][P], xb[s][P], low, x0, x1);
+#pragma unroll
+                    for (int i = 0; i < RT; ++i) {
+                        V a0, a1;
+                        swap_halves(aa[s][i][P], ab[s][i][P], low, a0, a1);
+                        acc[i] = mfma_step<DT>(x0, a0, acc[i]);
+                        acc[i] = mfma_step<DT>(x1, a1, acc[i]);
+                    }
+                }
         }
         // lane l of tile i holds D[4*(l/16) + q][l%16] = (row in block, rank in tile)
         if constexpr (W == 1) {
@@ -904,7 +950,7 @@ __device__ __forceinline__ void shrink_block_slice(const void *__restrict__ x, i
                                                    int64_t sl_stride, const M &mem, uint32_t tag = 0)
 {
     __shared__ float red[W > 1 ? W * RT * 256 : 1];
-    const int xr = rows[threadIdx.x & 15];
+    const int xrA = rows[threadIdx.x & 7], xrB = rows[(threadIdx.x & 7) + 8];
     const int xr0 = rows[0];
     const int k_begin = c * slice_len;
     const int k_end = min(d_in, k_begin + slice_len);
@@ -913,19 +959,19 @@ __device__ __forceinline__ void shrink_block_slice(const void *__restrict__ x, i
                            : out + c * sl_stride;
     if constexpr (RT >= 2) {
         if (r <= 16) {
-            shrink_block<DT, VEC, W, NSTEP, 1, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
+            shrink_block<DT, VEC, W, NSTEP, 1, M, SCOPED>(x, ldx, xrA, xrB, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
                                                           nullptr, n, red, mem, tag);
             return;
         }
     }
     if constexpr (RT >= 4) {
         if (r <= 32) {
-            shrink_block<DT, VEC, W, NSTEP, 2, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
+            shrink_block<DT, VEC, W, NSTEP, 2, M, SCOPED>(x, ldx, xrA, xrB, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0,
                                                           nullptr, n, red, mem, tag);
             return;
         }
     }
-    shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0, nullptr,
+    shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xrA, xrB, xr0, A, d_in, r, k_begin, k_end, o, ldo, p0, nullptr,
                                                    n, red, mem, tag);
 }
 
@@ -1271,10 +1317,10 @@ __device__ __forceinline__ bool bgmv_shrink_body(const void *__restrict__ x, int
         if (!bgmv_group(ids, T, t, a, pass, grp, cnt, id0)) return false;
         const int n = grp.n, total = grp.total;
         if (n == 0) return false;
-        const int xr = grp.rows[threadIdx.x & 15];
+        const int xrA = grp.rows[threadIdx.x & 7], xrB = grp.rows[(threadIdx.x & 7) + 8];
         float *o = SCOPED == 2 ? reinterpret_cast<float *>(reinterpret_cast<uint64_t *>(out) + c * sl_stride)
                                : out + c * sl_stride;
-        shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xr, grp.rows[0], A, d_in, r, k_begin, k_end, o, ldo, 0,
+        shrink_block<DT, VEC, W, NSTEP, RT, M, SCOPED>(x, ldx, xrA, xrB, grp.rows[0], A, d_in, r, k_begin, k_end, o, ldo, 0,
                                                        grp.rows, n, red, mem, tag);
         if (kRows * (pass + 1) >= total) break;
     }
@@ -1578,6 +1624,62 @@ __global__ __launch_bounds__(256) void bgmv_expand_grouped_kernel(int T, const i
     bgmv_expand_body<DT, SLOT, VECY, UPT>(P.v, P.ldv, P.sl_stride, P.nsl, T, ids, P.pool_B, P.pool_rank, P.pool_alpha,
                                           n_adapters, P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl,
                                           col * kExpandCols, int(blockIdx.x));
+}
+
+// One-launch grouped BGMV: the shrink workgroups of every projection (in
+// projection order, each (group, d_in slice) as in the one-launch BGMV), then
+// the expand workgroups of every projection ((group, column tile)); the
+// hand-over is the one-launch BGMV's (tagged partial sums in each
+// projection's own region, no flags, no reset).  Every producer has a lower
+// index than every consumer and never waits.
+struct GOnepass {
+    const void *x;
+    const uint64_t *pool_A;
+    const uint64_t *pool_B;
+    const int32_t *pool_rank;
+    const float *pool_alpha;
+    float *part;   // tagged 64-bit partial sums [kc][T][ldw]
+    void *y;
+    int64_t ldx, ldw, sl_stride, ldy;
+    int32_t d_in, max_rank, slice_len, kc;
+    int32_t d_out, ncol, ldl, vec_b;
+    int32_t prod0, cons0; // first shrink and first expand workgroup of the projection
+};
+struct GOnepassTable {
+    GOnepass p[LORA_MAX_PROJ];
+    const int32_t *ids;
+    int32_t *status;
+    int32_t T, n_adapters, n_proj, n_prod, wait_limit, pad;
+};
+
+template <int DT, int NSTEP, int RT, bool SLOT, int UPT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bgmv_grouped_onepass_kernel(
+    const GOnepassTable tab)
+{
+    const int b = int(blockIdx.x);
+    const uint32_t tag = 0x80000000u | (uint32_t(launch_key()) & 0x7fffffffu);
+    if (b < tab.n_prod) {
+        int p = 0;
+        for (int q = 1; q < tab.n_proj; ++q)
+            if (b >= tab.p[q].prod0) p = q;
+        const GOnepass &P = tab.p[p];
+        const int i = b - P.prod0, g = i / P.kc, c = i - g * P.kc;
+        bgmv_shrink_body<DT, true, 4, NSTEP, RT, SLOT, DenseMem, 2>(P.x, P.ldx, P.d_in, tab.T, tab.ids, P.pool_A,
+                                                                    P.pool_rank, tab.n_adapters, P.max_rank,
+                                                                    P.slice_len, P.part, P.ldw, P.sl_stride, g, c,
+                                                                    DenseMem{}, tag);
+        return;
+    }
+    int p = 0;
+    for (int q = 1; q < tab.n_proj; ++q)
+        if (b >= tab.p[q].cons0) p = q;
+    const GOnepass &P = tab.p[p];
+    const int i = b - P.cons0, g = i / P.ncol, col = i - g * P.ncol;
+    const TagWait w{tag, tab.status, tab.wait_limit};
+    bgmv_expand_body<DT, SLOT, true, UPT, DenseMem, TagWait>(P.part, P.ldw, P.sl_stride, P.kc, tab.T, tab.ids,
+                                                             P.pool_B, P.pool_rank, P.pool_alpha, tab.n_adapters,
+                                                             P.max_rank, P.y, P.ldy, P.d_out, P.vec_b != 0, P.ldl,
+                                                             col * kExpandCols, g, DenseMem{}, w);
 }
 
 // ----------------------------------------------------------------------------
@@ -2351,10 +2453,103 @@ size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank)
     return (combined_workspace_bytes(T, d_in, max_rank) + 255) / 256 * 256;
 }
 
+namespace {
+template <int DT, int NSTEP, int RT, bool SLOT>
+void grouped_onepass_go(hipStream_t s, dim3 grid, size_t shm, const GOnepassTable &t)
+{
+    launch_kernel(bgmv_grouped_onepass_kernel<DT, NSTEP, RT, SLOT, 1>, grid, dim3(256), shm, s, t);
+}
+
+template <bool SLOT>
+void grouped_onepass_dispatch(hipStream_t s, int dtype, int rt, bool two, dim3 grid, size_t shm,
+                              const GOnepassTable &t)
+{
+    if (dtype == LORA_F32) {
+        grouped_onepass_go<LORA_F32, 1, 4, SLOT>(s, grid, shm, t);
+    } else if (rt == 1) {
+        if (two) grouped_onepass_go<LORA_BF16, 2, 1, SLOT>(s, grid, shm, t);
+        else grouped_onepass_go<LORA_BF16, 1, 1, SLOT>(s, grid, shm, t);
+    } else if (rt == 2) {
+        if (two) grouped_onepass_go<LORA_BF16, 2, 2, SLOT>(s, grid, shm, t);
+        else grouped_onepass_go<LORA_BF16, 1, 2, SLOT>(s, grid, shm, t);
+    } else {
+        grouped_onepass_go<LORA_BF16, 1, 4, SLOT>(s, grid, shm, t);
+    }
+}
+
+// The one-launch form of a grouped BGMV call, when every projection fits it
+// (aligned rows, d_out % 16 == 0, ranks up to 64); returns false otherwise.
+bool bgmv_grouped_onepass(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
+                          int n, int32_t *ctl)
+{
+    const int dtype = pr[0].sa.dtype;
+    const bool slot = slot_major(T, n_adapters);
+    const int groups = slot ? n_adapters : T;
+    GOnepassTable t{};
+    bool two = true;
+    int rt = 1, ldl_max = 4;
+    int64_t prod = 0, cons = 0;
+    for (int p = 0; p < n; ++p) {
+        const GroupedProj &g = pr[p];
+        const int ldl = lds_pitch(g.max_rank);
+        if (!g.part || !g.sa.vec || !g.ea.vec_y || g.ea.d_out % 16 != 0 || ldl > 64) return false;
+        const Split sp = choose_split(g.sa.d_in, groups, dtype);
+        const int ncol = (g.ea.d_out + kExpandCols - 1) / kExpandCols;
+        GOnepass &q = t.p[p];
+        q.x = g.sa.x;
+        q.pool_A = g.pool_A;
+        q.pool_B = g.pool_B;
+        q.pool_rank = g.pool_rank;
+        q.pool_alpha = g.pool_alpha;
+        q.part = g.part;
+        q.y = g.ea.y;
+        q.ldx = g.sa.ldx;
+        q.ldw = (g.max_rank + 3) / 4 * 4;
+        q.sl_stride = int64_t(T) * q.ldw;
+        q.ldy = g.ea.ldy;
+        q.d_in = g.sa.d_in;
+        q.max_rank = g.max_rank;
+        q.slice_len = sp.slice_len;
+        q.kc = sp.kc;
+        q.d_out = g.ea.d_out;
+        q.ncol = ncol;
+        q.ldl = ldl;
+        q.vec_b = g.ea.vec_b ? 1 : 0;
+        q.prod0 = int32_t(prod);
+        prod += int64_t(groups) * sp.kc;
+        cons += int64_t(groups) * ncol;
+        two = two && sp.nstep == 2;
+        rt = rt > rank_tiles(g.max_rank) ? rt : rank_tiles(g.max_rank);
+        ldl_max = ldl_max > ldl ? ldl_max : ldl;
+    }
+    if (prod + cons >= (int64_t(1) << 31)) return false;
+    int64_t c0 = prod;
+    for (int p = 0; p < n; ++p) {
+        t.p[p].cons0 = int32_t(c0);
+        c0 += int64_t(groups) * t.p[p].ncol;
+    }
+    t.ids = ids;
+    t.status = ctl;
+    t.T = T;
+    t.n_adapters = n_adapters;
+    t.n_proj = n;
+    t.n_prod = int32_t(prod);
+    const int lim = wait_limit();
+    t.wait_limit = lim == 0 ? (1 << 22) : (lim < 0 ? -1 : lim);
+    const size_t shm = (size_t(kRows) * ldl_max + 4) * sizeof(float);
+    two = two && rt < 4;
+    const dim3 grid(unsigned(prod + cons));
+    if (slot) grouped_onepass_dispatch<true>(s, dtype, rt, two, grid, shm, t);
+    else grouped_onepass_dispatch<false>(s, dtype, rt, two, grid, shm, t);
+    return true;
+}
+} // namespace
+
 int launch_bgmv_grouped(hipStream_t s, int32_t T, const int32_t *ids, int32_t n_adapters, const GroupedProj *pr,
-                        int n)
+                        int n, int32_t *ctl)
 {
     if (n_adapters == 0 || n == 0) return LORA_OK;
+    if (ctl && bgmv_grouped_onepass(s, T, ids, n_adapters, pr, n, ctl)) return check_launch("bgmv grouped one-launch");
     const int dtype = pr[0].sa.dtype;
     const bool slot = slot_major(T, n_adapters);
     GShrinkTable stab{};

@@ -67,10 +67,11 @@ int main(void)
     CHECK(lora_segments_bind((char *)aligned + 4, T, &small) == LORA_ERR_ALIGN);
     CHECK(lora_profile_launches(NULL, NULL, -1) == LORA_ERR_ARG);
 
-    /* grouped BGMV: workspace is the sum of 256-byte-rounded per-projection
-     * regions of fp32 slice partial sums (4 slices of d_in, T rows of
-     * round4(rank), plus 256 B of slack; a single lora_bgmv workspace also holds
-     * control words); malformed calls are rejected on the host */
+    /* grouped BGMV: workspace is a 256-byte status block, then per projection
+     * three times its 256-byte-rounded region of fp32 slice partial sums (4
+     * slices of d_in, T rows of round4(rank), plus 256 B of slack): those sums,
+     * then the one-launch form's 8-byte tagged words; malformed calls are
+     * rejected on the host */
     lora_proj pr[2];
     memset(pr, 0, sizeof(pr));
     for (int p = 0; p < 2; ++p) {
@@ -90,7 +91,7 @@ int main(void)
     const size_t r1 = 4u * 64u * 64u * 4u + 256u;
     CHECK(lora_workspace_bytes(LORA_OP_BGMV, 64, 4096, 1024, 16) > r0);
     CHECK(lora_workspace_bytes(LORA_OP_SGMV, 64, 4096, 1024, 16) > r0);
-    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == (r0 + 255) / 256 * 256 + (r1 + 255) / 256 * 256);
+    CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 2) == 256 + 3 * ((r0 + 255) / 256 * 256) + 3 * ((r1 + 255) / 256 * 256));
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, 0) == 0);
     CHECK(lora_bgmv_grouped_workspace_bytes(64, pr, LORA_MAX_PROJ + 1) == 0);
     CHECK(lora_bgmv_grouped(NULL, LORA_BF16, 64, NULL, 4, pr, LORA_MAX_PROJ + 1, NULL, 0) == LORA_ERR_ARG);

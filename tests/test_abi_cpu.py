@@ -358,8 +358,10 @@ def test_combined_argument_errors():
 
 
 def test_grouped_bgmv_host_checks():
-    """Grouped BGMV: the workspace is the sum of the projections' 256-byte
-    rounded regions, and malformed calls are rejected before any GPU work."""
+    """Grouped BGMV: the workspace is the 256-byte status block plus, per
+    projection, three times its 256-byte rounded region of fp32 partial sums
+    (those sums, then the one-launch form's 8-byte tagged words), and malformed
+    calls are rejected before any GPU work."""
     import ctypes as C
 
     projs = (B.LoraProj * 3)()
@@ -368,8 +370,8 @@ def test_grouped_bgmv_host_checks():
     def partials(T, d_in, r):  # fp32 partial sums over at most 4 slices of 256+ elements of d_in, plus slack
         return min((d_in + 255) // 256, 4) * T * ((r + 3) // 4 * 4) * 4 + 256
 
-    want = sum((partials(64, d_in, r) + 255) // 256 * 256
-               for d_in, d_out, r in [(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)])
+    want = 256 + sum(3 * ((partials(64, d_in, r) + 255) // 256 * 256)
+                     for d_in, d_out, r in [(4096, 4096, 16), (4096, 1024, 8), (4096, 1024, 64)])
     ptr = C.cast(projs, C.c_void_p)
     assert B.lora_bgmv_grouped_workspace_bytes(64, ptr, 3) == want
     assert B.lora_bgmv_grouped_workspace_bytes(64, ptr, 0) == 0

@@ -1,12 +1,16 @@
 """Parity of the grouped BGMV entry (several projections of a layer in one
-shrink launch and one expand launch) with the fp64 oracle, through the C ABI.
+launch, or one shrink launch and one expand launch when a projection does not
+fit the one-launch form) with the fp64 oracle, through the C ABI.
 
 Every projection is its own problem (x, y, d_in, d_out, adapter tables) with
 the same per-token adapter ids; each is checked against the oracle of that
 problem at the usual tolerances (fp32 |gpu - ref| <= 1e-5 (|ref| + 1); bf16
 |gpu - ref| <= 2e-2 (|ref| + 1e-2)), rows of tokens without an adapter must be
 untouched, and where every projection takes the same kernel variant as a
-single lora_bgmv call the bits must equal that call's.
+single lora_bgmv call the bits must equal that call's.  The one-launch form is
+also run repeatedly on one workspace and with its waits forced to give up from
+the host (the kernel must still end, set the status word and leave y as it
+was).
 """
 
 import numpy as np
@@ -165,3 +169,82 @@ def test_rejects_shared_output():
     ws = B.bgmv_grouped_workspace(3, projs)
     with pytest.raises(B.LoraError):
         B.bgmv_grouped(xs, cases[0].ids_dev, pools, ys, ws, "bf16", projs=projs)
+
+
+def _qkv_small(seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, 24, 48).astype(np.int32)
+    ids[rng.random(48) < 0.1] = -1
+    specs = [(512, 512, [16] * 24), (512, 128, [8] * 24), (512, 128, [32] * 24)]
+    return projections(ids, specs, "bf16", seed=seed, share_x=True)
+
+
+def test_grouped_onepass_repeated_calls():
+    """Eight calls in a row of the one-launch grouped form on one workspace,
+    nothing reset in between: every call gives the same bits as a single
+    lora_bgmv call of each projection, and the status word stays zero."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    probs = _qkv_small(101)
+    cases = [GpuCase(p, y_init="zero") for p in probs]
+    for c in cases[1:]:
+        c.x = cases[0].x
+    xs, pools, ys = [c.x for c in cases], [c.pool for c in cases], [c.y for c in cases]
+    projs = B.proj_array(xs, pools, ys)
+    ws = B.bgmv_grouped_workspace(probs[0].T, projs)
+    singles = []
+    for prob in probs:
+        s = GpuCase(prob, y_init="zero")
+        s.x = cases[0].x
+        w1 = B.workspace(B.LORA_OP_BGMV, prob.T, prob.d_in, prob.d_out, prob.max_rank)
+        B.bgmv(s.x, s.ids_dev, s.pool, s.y, w1, "bf16")
+        torch.cuda.synchronize()
+        singles.append(B.to_host_bits(s.y, "bf16"))
+    say("case grouped one-launch repeated calls")
+    for _ in range(8):
+        for c in cases:
+            c.y.zero_()
+        B.bgmv_grouped(xs, cases[0].ids_dev, pools, ys, ws, "bf16", projs=projs)
+        torch.cuda.synchronize()
+        assert B.workspace_status(ws) == 0
+        for p, c in enumerate(cases):
+            assert np.array_equal(B.to_host_bits(c.y, "bf16"), singles[p]), f"proj{p} differs from lora_bgmv"
+
+
+def test_grouped_onepass_forced_give_up_ends_normally():
+    """The host forces every wait of the one-launch grouped kernel to give up
+    at once: the kernel still ends, the status word is set and every y is left
+    as it was.  The next call (default wait) is correct; lora_workspace_clear
+    resets the status."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    probs = _qkv_small(102)
+    cases = [GpuCase(p) for p in probs]
+    for c in cases[1:]:
+        c.x = cases[0].x
+    xs, pools, ys = [c.x for c in cases], [c.pool for c in cases], [c.y for c in cases]
+    before = [B.to_host_bits(c.y, "bf16") for c in cases]
+    projs = B.proj_array(xs, pools, ys)
+    ws = B.bgmv_grouped_workspace(probs[0].T, projs)
+    say("case grouped one-launch forced give-up")
+    B.debug_wait_limit(-1)
+    try:
+        B.bgmv_grouped(xs, cases[0].ids_dev, pools, ys, ws, "bf16", projs=projs)
+        torch.cuda.synchronize()
+    finally:
+        B.debug_wait_limit(0)
+    assert B.workspace_status(ws) == 1
+    for p, c in enumerate(cases):
+        assert np.array_equal(B.to_host_bits(c.y, "bf16"), before[p]), f"proj{p}: a consumer that gave up wrote y"
+    say("case grouped one-launch after a give-up")
+    B.bgmv_grouped(xs, cases[0].ids_dev, pools, ys, ws, "bf16", projs=projs)
+    torch.cuda.synchronize()
+    check_against_oracle(probs, cases, "after give-up")
+    assert B.workspace_status(ws) == 1  # sticky until cleared
+    B.workspace_clear(ws)
+    torch.cuda.synchronize()
+    assert B.workspace_status(ws) == 0
