@@ -995,8 +995,18 @@ __device__ __forceinline__ void sgmv_shrink_item(const void *__restrict__ x, int
                                                  slice_len, out, ldo, sl_stride, mem);
 }
 
+// Waves per SIMD for the bf16 rank <= 16 form: five over a dense pool (90
+// registers, no spills), four over a page pool (its address arithmetic needs
+// more), so that a prefill plan's ~1,060 items run in one round.
 template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
-__global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
+constexpr int shrink_waves()
+{
+    return DT == LORA_BF16 && VEC && W == 4 && NSTEP == 2 && RT == 1 ? (std::is_same_v<M, DenseMem> ? 5 : 4) : 1;
+}
+
+template <int DT, bool VEC, int W, int NSTEP, int RT, class M>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(shrink_waves<DT, VEC, W, NSTEP, RT, M>())))
+void sgmv_shrink_kernel(const void *__restrict__ x, int64_t ldx, int d_in,
                                                              const lora_blk_desc *__restrict__ blks, int nblk, int kc,
                                                              int slice_len, float *__restrict__ out, int64_t ldo,
                                                              int64_t sl_stride, const M mem)
@@ -1006,7 +1016,8 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_kernel(const void *__restr
 }
 
 template <int DT, bool VECY, int UPT, class M, int MAXNCH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(std::is_same_v<M, DenseMem> ? 6 : 5)))
+void sgmv_expand_kernel(const float *__restrict__ v, int64_t ldv, int64_t sl_stride,
                                                           int nsl, const lora_blk_desc *__restrict__ blks,
                                                           void *__restrict__ y, int64_t ldy, int d_out, bool vec_b,
                                                           int ldl, const M mem)
@@ -1066,8 +1077,19 @@ struct ChunkArgs {
     u32x8 c[kArgChunks]; // ChunkArg bits
 };
 
+// Five waves per SIMD for the bf16 rank <= 16 form (86 registers, no spills):
+// a prefill plan's 1,100-odd workgroups then run in one round instead of
+// leaving a second round of ~150 behind the first (19.7 against 20.1 us); the
+// other forms need more registers than five waves leave.
+template <int DT, bool VECY, int NCH, int UPT>
+constexpr int chunk_arg_waves()
+{
+    return DT == LORA_BF16 && VECY && NCH == 1 && UPT == 1 ? 5 : 1;
+}
+
 template <int DT, bool VECY, int NCH, int UPT, class M>
-__global__ __launch_bounds__(256) void sgmv_expand_chunk_arg_kernel(const float *__restrict__ v, int64_t ldv,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(chunk_arg_waves<DT, VECY, NCH, UPT>())))
+void sgmv_expand_chunk_arg_kernel(const float *__restrict__ v, int64_t ldv,
                                                                     int64_t sl_stride, int nsl,
                                                                     const lora_chunk_desc *__restrict__ chunks,
                                                                     void *__restrict__ y, int64_t ldy, int d_out,
@@ -1190,10 +1212,11 @@ __device__ __forceinline__ void expand_chunk_wide(const float *__restrict__ v, i
 // Chunk forms of other shapes (fp32, ranks not a multiple of 4) run the block
 // form once per 16-row block of the chunk.  Every form computes each output
 // with the same sums in the same order as the block form.
-template <int DT, bool VECY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sgmv_expand_mixed_kernel(
+template <int DT, bool VECY, class M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(std::is_same_v<M, DenseMem> ? 3 : 2)))
+void sgmv_expand_mixed_kernel(
     const float *__restrict__ v, int64_t ldv, int64_t sl_stride, int nsl, const lora_chunk_desc *__restrict__ chunks,
-    void *__restrict__ y, int64_t ldy, int d_out, int vec_b)
+    void *__restrict__ y, int64_t ldy, int d_out, int vec_b, const M mem)
 {
     extern __shared__ floatx4 vl4[];
     const lora_chunk_desc *d = chunks + blockIdx.y;
@@ -1207,26 +1230,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     const bool bv = vec_b && (r & 3) == 0;
     if (n > kRows && bv) {
         if (r <= 16)
-            expand_chunk_impl<DT, VECY, true, 1, 1, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw,
-                                                              d->rows, d->p0, n, vl, ldl);
+            expand_chunk_impl<DT, VECY, true, 1, 1, kChunkRB, false, M>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
+                                                                        d_out, ncw, d->rows, d->p0, n, vl, ldl, 0,
+                                                                        mem);
         else if (r <= 32)
-            expand_chunk_impl<DT, VECY, true, 2, 2, kChunkRB>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw,
-                                                              d->rows, d->p0, n, vl, ldl);
+            expand_chunk_impl<DT, VECY, true, 2, 2, kChunkRB, false, M>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy,
+                                                                        d_out, ncw, d->rows, d->p0, n, vl, ldl, 0,
+                                                                        mem);
         else if constexpr (DT == LORA_BF16)
-            expand_chunk_wide<VECY>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, d->rows, d->p0, n, vl,
-                                    DenseMem{});
+            expand_chunk_wide<VECY, M>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, d->rows, d->p0, n,
+                                       vl, mem);
         else
             for (int q0 = 0; q0 < n; q0 += kRows) {
                 if (q0) __syncthreads();
-                expand_rows<DT, VECY, false, 1>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, true,
-                                                d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl);
+                expand_rows<DT, VECY, false, 1, M>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, true,
+                                                   d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl, mem);
             }
         return;
     }
     for (int q0 = 0; q0 < n; q0 += kRows) {
         if (q0) __syncthreads(); // the previous block is done with vl
-        expand_rows<DT, VECY, false, 1, DenseMem, 4>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, bv,
-                                                    d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl);
+        expand_rows<DT, VECY, false, 1, M, 4>(v, ldv, sl_stride, nsl, B, r, scale, y, ldy, d_out, ncw, bv,
+                                             d->rows + q0, d->p0 + q0, min(kRows, n - q0), vl, ldl, mem);
     }
 }
 
@@ -1715,7 +1740,8 @@ struct SGExpandTable {
 };
 
 template <int DT, bool VEC, int W, int NSTEP, int RT>
-__global__ __launch_bounds__(W * 64) void sgmv_shrink_grouped_kernel(const SGShrinkTable tab)
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(shrink_waves<DT, VEC, W, NSTEP, RT, DenseMem>())))
+void sgmv_shrink_grouped_kernel(const SGShrinkTable tab)
 {
     const SGShrink &P = tab.p[blockIdx.z];
     sgmv_shrink_item<DT, VEC, W, NSTEP, RT>(P.x, P.ldx, P.d_in, P.blks, P.nblk, P.kc, P.slice_len, P.out, P.ldo,
@@ -1726,7 +1752,8 @@ __global__ __launch_bounds__(W * 64) void sgmv_shrink_grouped_kernel(const SGShr
 // fastest, projections in order: no workgroup is idle when the projections
 // have different widths.
 template <int DT, bool VECY, int NCH, int UPT>
-__global__ __launch_bounds__(256) void sgmv_expand_chunk_grouped_kernel(const SGExpandTable tab, int n_proj)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(chunk_arg_waves<DT, VECY, NCH, UPT>())))
+void sgmv_expand_chunk_grouped_kernel(const SGExpandTable tab, int n_proj)
 {
     extern __shared__ floatx4 vl4[];
     const int b = int(blockIdx.x);
@@ -2062,17 +2089,17 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     // chunk kernel serves (ranks <= 32, enough chunk items): one launch whose
     // workgroups choose the block or chunk form per plan chunk.
     const bool arg_chunks = p.h->num_chunks * ncol >= 1024 && ldl <= 32 && p.h->num_chunks <= kArgChunks;
-    if (std::is_same_v<M, DenseMem> && ldl <= 64 && !arg_chunks) {
+    if (ldl <= 64 && !arg_chunks) {
         const dim3 grid(ncol, p.h->num_chunks);
         const size_t shm = (size_t(kChunkRB * kRows) * 64 + 4) * sizeof(float);
         const lora_chunk_desc *d = plan_chunks(p);
         const int vb = a.vec_b ? 1 : 0;
         if (a.dtype == LORA_BF16) {
-            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, true>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
-            else launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, false>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, true, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb, mem);
+            else launch_kernel(sgmv_expand_mixed_kernel<LORA_BF16, false, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb, mem);
         } else {
-            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, true>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
-            else launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, false>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb);
+            if (vecy) launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, true, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb, mem);
+            else launch_kernel(sgmv_expand_mixed_kernel<LORA_F32, false, M>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl, d, a.y, a.ldy, a.d_out, vb, mem);
         }
         return;
     }
