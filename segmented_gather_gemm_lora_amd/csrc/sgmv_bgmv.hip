@@ -2038,7 +2038,7 @@ void sgmv_expand_chunk_go(hipStream_t s, const ExpandArgs &a, const float *v, in
         return;
     }
     // paged launches take chunks only through the argument table (the
-    // launcher sends larger plans to the block kernel)
+    // launcher sends larger paged plans to the mixed kernel)
     if constexpr (std::is_same_v<M, DenseMem>) switch (units_per_thread(kChunkRB, ldl)) {
     case 1:
         launch_kernel(sgmv_expand_chunk_kernel<DT, VECY, NCH, 1>, grid, dim3(256), shm, s, v, ldv, sl_stride, nsl,
@@ -2085,9 +2085,9 @@ void sgmv_expand_launch(hipStream_t s, const ExpandArgs &a, const float *v, int6
     const int ncol = (a.d_out + kExpandCols - 1) / kExpandCols;
     const int ldl = lds_pitch(p.h->max_rank);
     const bool vecy = a.vec_y && a.d_out % 16 == 0;
-    // Dense plans with ranks up to 64, except the ones the argument-table
-    // chunk kernel serves (ranks <= 32, enough chunk items): one launch whose
-    // workgroups choose the block or chunk form per plan chunk.
+    // Plans with ranks up to 64 (dense or paged), except the ones the
+    // argument-table chunk kernel serves (ranks <= 32, enough chunk items): one
+    // launch whose workgroups choose the block or chunk form per plan chunk.
     const bool arg_chunks = p.h->num_chunks * ncol >= 1024 && ldl <= 32 && p.h->num_chunks <= kArgChunks;
     if (ldl <= 64 && !arg_chunks) {
         const dim3 grid(ncol, p.h->num_chunks);
