@@ -592,7 +592,8 @@ int lora_sgmv_paged(void *stream, int dtype, const void *x, int64_t ldx, int32_t
                     void *y, int64_t ldy, int32_t d_out, void *ws, size_t ws_bytes);
 
 /* lora_bgmv over paged adapters: pool_A_dev[i] / pool_B_dev[i] are the
- * device addresses of adapter i's A and B page tables.
+ * device addresses of adapter i's A and B page tables.  Same workspace,
+ * one-launch condition, hand-over and status word as lora_bgmv.
  * Errors: as lora_bgmv, plus LORA_ERR_ARG / LORA_ERR_ALIGN for pages or
  * page_bytes. */
 int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t ldx, int32_t d_in,

@@ -645,7 +645,8 @@ int lora_bgmv_paged(void *stream, int dtype, int32_t T, const void *x, int64_t l
     ExpandArgs ea{};
     if ((st = make_expand_args(dtype, part, ldw, max_rank, y, ldy, d_out, true, &ea))) return st;
     return launch_bgmv_paged(static_cast<hipStream_t>(stream), sa, ea, T, ids_dev, pool_A_dev, pool_B_dev,
-                             pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, part, pages, shift);
+                             pool_rank_dev, pool_alpha_dev, n_adapters, max_rank, part, static_cast<int32_t *>(ws),
+                             pages, shift);
 }
 
 size_t lora_sgmv_grouped_workspace_bytes(const lora_sgmv_proj *projs, int32_t n_proj)

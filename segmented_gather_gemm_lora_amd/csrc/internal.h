@@ -60,14 +60,14 @@ int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const
 // (status, a flag per block and d_in slice; 256-byte multiple).
 size_t sgmv_ctl_bytes(int32_t n_blocks);
 // The combined BGMV: one launch (shrink and expand workgroups in one grid,
-// handing over through the status word and flags at `ctl`) when one_launch
-// and the shapes allow it, else the shrink and expand kernels.  ws: the slice
-// partials.
+// handing over through tagged partial sums after the slice partials, with
+// the sticky status word at `ctl`) when one_launch and the shapes allow it,
+// else the shrink and expand kernels.  ws: the slice partials.
 int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                 const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                 int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl, bool one_launch);
-// A BGMV workspace: control words (status, a flag per group and slice;
-// 256-byte multiple), then the slice partials.
+// A BGMV workspace: the 256-byte status block, the two-launch form's slice
+// partials, then the one-launch form's tagged words (twice those bytes).
 size_t bgmv_ctl_bytes(int32_t T);
 size_t bgmv_workspace_bytes(int32_t T, int32_t d_in, int32_t max_rank);
 // Argument checks of x, y and the partials, then launch_bgmv.  part: the slice
@@ -88,8 +88,8 @@ int launch_sgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea,
                       const void *pages, int page_shift);
 int launch_bgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                       const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank,
-                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, const void *pages,
-                      int page_shift);
+                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl,
+                      const void *pages, int page_shift);
 // One projection of a grouped BGMV call: its shrink (x, d_in, v = its
 // workspace region) and expand (y, d_out) arguments and its adapter tables.
 struct GroupedProj {

@@ -1496,7 +1496,8 @@ struct OnepassArgs {
 };
 
 template <int DT, int NSTEP, int RT, bool SLOT, int UPT, class M>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bgmv_onepass_kernel(const OnepassArgs a, const M mem)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(std::is_same_v<M, DenseMem> ? 3 : 2)))
+void bgmv_onepass_kernel(const OnepassArgs a, const M mem)
 {
     const int b = int(blockIdx.x);
     const int n_prod = a.groups * a.kc;
@@ -2360,25 +2361,26 @@ int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int3
 }
 
 namespace {
-template <int DT, int NSTEP, int RT, bool SLOT>
-void onepass_go(hipStream_t s, dim3 grid, size_t shm, const OnepassArgs &a)
+template <int DT, int NSTEP, int RT, bool SLOT, class M>
+void onepass_go(hipStream_t s, dim3 grid, size_t shm, const OnepassArgs &a, const M &mem)
 {
-    launch_kernel(bgmv_onepass_kernel<DT, NSTEP, RT, SLOT, 1, DenseMem>, grid, dim3(256), shm, s, a, DenseMem{});
+    launch_kernel(bgmv_onepass_kernel<DT, NSTEP, RT, SLOT, 1, M>, grid, dim3(256), shm, s, a, mem);
 }
 
-template <bool SLOT>
-void onepass_dispatch(hipStream_t s, int dtype, int rt, bool two, dim3 grid, size_t shm, const OnepassArgs &a)
+template <bool SLOT, class M>
+void onepass_dispatch(hipStream_t s, int dtype, int rt, bool two, dim3 grid, size_t shm, const OnepassArgs &a,
+                      const M &mem)
 {
     if (dtype == LORA_F32) {
-        onepass_go<LORA_F32, 1, 4, SLOT>(s, grid, shm, a);
+        onepass_go<LORA_F32, 1, 4, SLOT>(s, grid, shm, a, mem);
     } else if (rt == 1) {
-        if (two) onepass_go<LORA_BF16, 2, 1, SLOT>(s, grid, shm, a);
-        else onepass_go<LORA_BF16, 1, 1, SLOT>(s, grid, shm, a);
+        if (two) onepass_go<LORA_BF16, 2, 1, SLOT>(s, grid, shm, a, mem);
+        else onepass_go<LORA_BF16, 1, 1, SLOT>(s, grid, shm, a, mem);
     } else if (rt == 2) {
-        if (two) onepass_go<LORA_BF16, 2, 2, SLOT>(s, grid, shm, a);
-        else onepass_go<LORA_BF16, 1, 2, SLOT>(s, grid, shm, a);
+        if (two) onepass_go<LORA_BF16, 2, 2, SLOT>(s, grid, shm, a, mem);
+        else onepass_go<LORA_BF16, 1, 2, SLOT>(s, grid, shm, a, mem);
     } else {
-        onepass_go<LORA_BF16, 1, 4, SLOT>(s, grid, shm, a);
+        onepass_go<LORA_BF16, 1, 4, SLOT>(s, grid, shm, a, mem);
     }
 }
 } // namespace
@@ -2403,23 +2405,23 @@ int &wait_limit()
     return limit;
 }
 
-int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
-                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
-                int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl, bool one_launch)
+namespace {
+// The one-launch BGMV when the shapes allow it (aligned rows, d_out % 16 == 0,
+// ranks up to 64); returns false, launching nothing, otherwise.  ws: the
+// two-launch form's partials, followed by the tagged words.
+template <class M>
+bool bgmv_onepass_launch(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                         const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank,
+                         const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl,
+                         const M &mem)
 {
-    if (n_adapters == 0) return LORA_OK;
     const bool slot = slot_major(T, n_adapters);
     const int groups = slot ? n_adapters : T;
     const int ncol = (ea.d_out + kExpandCols - 1) / kExpandCols;
     const Split sp = choose_split(sa.d_in, groups, sa.dtype);
     const int64_t grid = int64_t(groups) * (sp.kc + ncol);
-    // one launch for aligned rows and ranks up to 64 (one float4 of staged v
-    // per thread); otherwise the shrink and expand kernels
-    const bool fits = one_launch && ctl && sa.vec && ea.vec_y && ea.d_out % 16 == 0 && lds_pitch(max_rank) <= 64 &&
-                      grid < (int64_t(1) << 31);
-    if (!fits)
-        return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
-                             DenseMem{});
+    if (!ctl || !sa.vec || !ea.vec_y || ea.d_out % 16 != 0 || lds_pitch(max_rank) > 64 || grid >= (int64_t(1) << 31))
+        return false;
     OnepassArgs a{};
     a.x = sa.x;
     a.ids = ids;
@@ -2450,9 +2452,22 @@ int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32
     const size_t shm = (size_t(kRows) * a.ldl + 4) * sizeof(float);
     const int rt = rank_tiles(max_rank);
     const bool two = sp.nstep == 2 && rt < 4;
-    if (slot) onepass_dispatch<true>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a);
-    else onepass_dispatch<false>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a);
-    return check_launch("bgmv one-launch");
+    if (slot) onepass_dispatch<true>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a, mem);
+    else onepass_dispatch<false>(s, sa.dtype, rt, two, dim3(unsigned(grid)), shm, a, mem);
+    return true;
+}
+} // namespace
+
+int launch_bgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
+                const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
+                int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl, bool one_launch)
+{
+    if (n_adapters == 0) return LORA_OK;
+    if (one_launch && bgmv_onepass_launch(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters,
+                                          max_rank, ws, ctl, DenseMem{}))
+        return check_launch("bgmv one-launch");
+    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
+                         DenseMem{});
 }
 
 int launch_workspace_clear(hipStream_t s, void *ws, size_t bytes)
@@ -2468,11 +2483,15 @@ int launch_workspace_clear(hipStream_t s, void *ws, size_t bytes)
 
 int launch_bgmv_paged(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, int32_t T, const int32_t *ids,
                       const uint64_t *pool_A, const uint64_t *pool_B, const int32_t *pool_rank,
-                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, const void *pages,
-                      int page_shift)
+                      const float *pool_alpha, int32_t n_adapters, int32_t max_rank, void *ws, int32_t *ctl,
+                      const void *pages, int page_shift)
 {
-    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws,
-                         PagedMem{static_cast<const char *>(pages), page_shift});
+    if (n_adapters == 0) return LORA_OK;
+    const PagedMem mem{static_cast<const char *>(pages), page_shift};
+    if (bgmv_onepass_launch(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws, ctl,
+                            mem))
+        return check_launch("bgmv paged one-launch");
+    return bgmv_combined(s, sa, ea, T, ids, pool_A, pool_B, pool_rank, pool_alpha, n_adapters, max_rank, ws, mem);
 }
 
 size_t grouped_region_bytes(int32_t T, int32_t d_in, int32_t max_rank)

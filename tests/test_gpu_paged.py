@@ -13,7 +13,9 @@ Paging changes where the adapter bytes live, not what is computed, so:
     (fp32 |gpu - ref| <= 1e-5 (|ref| + 1); bf16 <= 2e-2 (|ref| + 1e-2)).
 Page sizes span 64 B (every row straddles many pages) to 64 KB, frames are
 handed out in a seeded random order, and the cases cover the vector and the
-scalar load paths (d_in not a multiple of 8, odd ranks).
+scalar load paths (d_in not a multiple of 8, odd ranks).  The paged BGMV's
+one-launch form is also run repeatedly on one workspace and with its waits
+forced to give up from the host.
 """
 
 import numpy as np
@@ -172,3 +174,41 @@ def test_paged_max_rank(path):
     prob = make_problem(name="paged_rank256", dtype="bf16", ids=ids, ranks=[256, 100, 3], alphas=[64.0, 32.0, 8.0],
                         d_in=512, d_out=520, seed=31, a_std=0.05, b_std=0.05)
     _paged_vs_dense(prob, 256, path)
+
+
+def test_paged_bgmv_one_launch_give_up_and_repeat():
+    """lora_bgmv_paged takes lora_bgmv's one-launch form for the decode
+    workload: repeated calls on one workspace (nothing reset) give the dense
+    call's bits with the status word at zero; a wait forced to give up from
+    the host ends the kernel, sets the status word and leaves y unchanged."""
+    import torch
+
+    from segmented_gather_gemm_lora_amd import binding as B
+
+    prob = make_config(2)
+    dense = GpuCase(prob, y_init="zero")
+    dense.run("bgmv")
+    y_dense = B.to_host_bits(dense.y, prob.dtype)
+    pool = B.PagedPool.from_problem(prob, page_bytes=16384, shuffle_seed=7)
+    ws = B.workspace(B.LORA_OP_BGMV, prob.T, prob.d_in, prob.d_out, prob.max_rank)
+    y = B.to_device(dense.y_host_in, prob.dtype)
+    say("case paged bgmv one-launch repeated calls")
+    for _ in range(4):
+        y.zero_()
+        B.bgmv_paged(dense.x, dense.ids_dev, pool, y, ws, prob.dtype)
+        torch.cuda.synchronize()
+        assert B.workspace_status(ws) == 0
+        assert np.array_equal(B.to_host_bits(y, prob.dtype), y_dense)
+    say("case paged bgmv one-launch forced give-up")
+    y.zero_()
+    B.debug_wait_limit(-1)
+    try:
+        B.bgmv_paged(dense.x, dense.ids_dev, pool, y, ws, prob.dtype)
+        torch.cuda.synchronize()
+    finally:
+        B.debug_wait_limit(0)
+    assert B.workspace_status(ws) == 1
+    assert not B.to_host_bits(y, prob.dtype).any(), "a consumer that gave up wrote y"
+    B.workspace_clear(ws)
+    torch.cuda.synchronize()
+    assert B.workspace_status(ws) == 0
