@@ -322,8 +322,9 @@ int lora_bgmv_expand(void *stream, int dtype, int32_t T, const float *v, int64_t
  * "Mathematical Formulation and the Batching Challenge", paid once).  Both
  * forms compute the same sums in the same order, so their outputs are equal.
  *
- * Workspace: control words, the two-launch form's fp32 partial sums, then the
- * one-launch form's tagged words (a region of their own).  Nothing needs
+ * Workspace: a 256-byte status block, the two-launch form's fp32 partial
+ * sums, then the one-launch form's tagged words (a region of their own, twice
+ * the bytes of the fp32 sums).  Nothing needs
  * preparation or reset between calls: a word left by an earlier launch holds
  * another tag (tags differ between any two of 2^31 consecutive launches on a
  * queue, and never equal the zero of a cleared workspace).  Calls that share a

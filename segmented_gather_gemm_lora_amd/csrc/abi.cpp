@@ -519,9 +519,8 @@ int lora_sgmv(void *stream, int dtype, const void *x, int64_t ldx, int32_t d_in,
     if (h->num_sorted == 0) return LORA_OK;
     if (!plan_dev) return fail(LORA_ERR_ARG, "the segments' device buffer is NULL");
     if (h->num_blocks > 65535) return fail(LORA_ERR_ARG, "plan has %d blocks (> 65535)", h->num_blocks);
-    // control words (status, a flag per block and slice), then the fp32
-    // partials of the two-kernel form, then the tagged 64-bit partials of the
-    // one-launch form
+    // the 256-byte status block, then the fp32 partials of the two-kernel
+    // form, then the tagged 64-bit partials of the one-launch form
     const size_t ctl_bytes = sgmv_ctl_bytes(h->num_blocks);
     const size_t need = ctl_bytes + 3 * combined_workspace_bytes(h->num_sorted, d_in < 1 ? 1 : d_in, h->max_rank);
     if (!ws || ws_bytes < need) return fail(LORA_ERR_WORKSPACE, "workspace %zu B < %zu B needed", ws_bytes, need);

@@ -52,12 +52,13 @@ int launch_bgmv_expand(hipStream_t s, const ExpandArgs &a, int32_t T, const int3
                        const uint64_t *pool_B, const int32_t *pool_rank, const float *pool_alpha,
                        int32_t n_adapters, int32_t max_rank);
 // The combined SGMV: one launch over the plan's chunks (shrink and expand
-// items handing over through the status word and flags at `ctl`) when ctl is
-// given and the shapes allow it, else the shrink and expand kernels.
+// items handing over through tagged partial sums, with the sticky status word
+// at `ctl`) when ctl is given and the shapes allow it, else the shrink and
+// expand kernels.
 int launch_sgmv(hipStream_t s, const ShrinkArgs &sa, const ExpandArgs &ea, const PlanView &p, void *ws,
                 int32_t *ctl = nullptr);
-// Control words of an SGMV workspace for a plan of up to n_blocks blocks
-// (status, a flag per block and d_in slice; 256-byte multiple).
+// Control words of an SGMV workspace for a plan of up to n_blocks blocks:
+// the 256-byte status block.
 size_t sgmv_ctl_bytes(int32_t n_blocks);
 // The combined BGMV: one launch (shrink and expand workgroups in one grid,
 // handing over through tagged partial sums after the slice partials, with
